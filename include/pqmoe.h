@@ -1,0 +1,275 @@
+/*
+ * pqmoe.h -- C ABI of the block-scaled quantizer and MoE grouped-GEMM
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the data-parallel core of the low-precision RL
+ * precision contract described in:
+ *   [BW] "Towards Blackwell-Native 8-bit and 4-bit RL"
+ *   [MT] "miniTE technical report: stable training and efficient
+ *        implementation of native NVFP4 RL"
+ *   [PR] "PR #2396 report: docs: refresh MXFP8 and NVFP4 RL guide"
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers named d_* or documented as "device" are device pointers (HBM);
+ *    the caller owns every buffer.  The library never allocates, frees or
+ *    synchronizes; all work is enqueued on `stream` (NULL = the null stream)
+ *    and returns before it runs.
+ *  - bf16 tensors are passed as 16-bit bit patterns (uint16_t).  Inputs must
+ *    be finite; NaN and infinity are outside the contract.
+ *  - Shapes are row-major.  `ld` is the row stride of an input in elements.
+ *  - Argument errors are reported synchronously, before anything is
+ *    enqueued: PQM_ERR_NULL (a required pointer is NULL), PQM_ERR_SHAPE
+ *    (a size is negative or not a multiple of the block length),
+ *    PQM_ERR_ALIGN (a vector-loaded pointer or stride is not 16-byte
+ *    aligned), PQM_ERR_ENUM (unknown format/kind/dtype), PQM_ERR_WORKSPACE
+ *    (workspace too small).  A failed launch returns PQM_ERR_HIP.
+ *  - Results are deterministic: the same inputs give bitwise identical
+ *    outputs on every run (fixed reduction order, no split-K atomics),
+ *    following the deterministic-mode rule of [MT] 4.5.
+ *  - Zero-sized inputs (rows == 0, or an empty group) are legal and enqueue
+ *    nothing for the empty part.
+ */
+#ifndef PQMOE_H
+#define PQMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pqm_status {
+    PQM_OK = 0,
+    PQM_ERR_NULL = 1,
+    PQM_ERR_SHAPE = 2,
+    PQM_ERR_ALIGN = 3,
+    PQM_ERR_ENUM = 4,
+    PQM_ERR_WORKSPACE = 5,
+    PQM_ERR_HIP = 6
+} pqm_status;
+
+typedef enum pqm_format {
+    PQM_FMT_BF16 = 0,  /* plain bf16 operands */
+    PQM_FMT_MXFP8 = 1, /* E4M3 data, one E8M0 scale per 32 along the row */
+    PQM_FMT_NVFP4 = 2  /* packed E2M1, one E4M3 scale per 16, FP32 outer */
+} pqm_format;
+
+typedef enum pqm_gemm_kind {
+    PQM_GEMM_FPROP = 0, /* Y[m,:] = A[m,:] . B_g^T,  B [G, N, K]          */
+    PQM_GEMM_DGRAD = 1, /* Y[m,:] = A[m,:] . B_g,    B [G, K, N] (bf16)   */
+    PQM_GEMM_WGRAD = 2  /* Y_g = A_g^T . B_g over the group's rows (bf16) */
+} pqm_gemm_kind;
+
+typedef enum pqm_dtype {
+    PQM_OUT_BF16 = 0,
+    PQM_OUT_FP32 = 1
+} pqm_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *pqm_status_string(pqm_status s);
+
+/* Version of the ABI described by this header. */
+int pqm_abi_version(void);
+
+/*
+ * MXFP8 quantization ([BW] Format background: MXFP8; Recipe 1: training).
+ *
+ * Each 1x32 block of E4M3 values shares one E8M0 (power of two) scale,
+ * rounded up so the block maximum is never clipped: the scale is 2^e with
+ * e the smallest integer for which max|x| <= 448 * 2^e (e >= -127; an
+ * all-zero block gets e = -127).  Elements are x / 2^e rounded to the
+ * nearest E4M3 value, ties to even; a negative input that rounds to zero
+ * keeps its sign (0x80).
+ *
+ * Row-wise and column-wise copies are both quantized independently from
+ * the bf16 input in the same pass (never one from the other):
+ *   x       [rows, cols] bf16, row stride ld elements           (device)
+ *   q_row   [rows, cols]       E4M3 bytes, 1x32 blocks along rows  (device)
+ *   s_row   [rows, cols/32]    E8M0 bytes                          (device)
+ *   q_colT  [cols, rows]       E4M3 bytes of the 32x1 blocks down each
+ *                              column, stored transposed so each block is
+ *                              contiguous                          (device)
+ *   s_colT  [cols, rows/32]    E8M0 bytes                          (device)
+ * Either output pair may be NULL to skip that copy, not both.
+ * Requires cols % 32 == 0; rows % 32 == 0 when the column copy is asked
+ * for; x and ld 16-byte aligned (ld % 8 == 0).
+ */
+pqm_status pqm_quantize_mxfp8(const uint16_t *x, int64_t rows, int64_t cols,
+                              int64_t ld, uint8_t *q_row, uint8_t *s_row,
+                              uint8_t *q_colT, uint8_t *s_colT,
+                              hipStream_t stream);
+
+/*
+ * NVFP4 quantization with an online FP32 outer scale ([BW] Format
+ * background: NVFP4; Recipe 2: per-token activation scaling, gate/up
+ * pairing; [MT] 2.2 decode x^ = q s_b s_g; [MT] 5.6 gs = gamax / 2688).
+ *
+ * Rows are split into scope groups of `rows_per_scale` consecutive rows;
+ * each group has one FP32 outer scale s_g:
+ *   rows_per_scale = 1    per token (the activation recipe): one fused pass
+ *                         reads each row once and writes all three outputs;
+ *   rows_per_scale = R_e  one scale per expert tensor; for fused gate/up
+ *                         weights [gate; up] of R_e rows this is the joint
+ *                         option: gate and up share one outer scale.
+ * For a group with absolute maximum A:
+ *   s_g   = A / 2688 rounded once to binary32 (2688 = 6 * 448);
+ *   s_b   = nearest E4M3 to a_b / (6 s_g) for each 1x16 block with block
+ *           maximum a_b, ties to even, saturating at 448 (0 if s_g == 0);
+ *   q     = nearest E2M1 to x / (s_b s_g), ties to even, saturating at 6
+ *           (+-0 if s_b == 0); all quotients are exact, not approximated.
+ * Outputs (device):
+ *   q        [rows, cols/2]  packed E2M1, element 2j in the low nibble
+ *   s_block  [rows, cols/16] E4M3 bytes
+ *   s_outer  [rows / rows_per_scale] binary32 decode scales s_g
+ * Requires cols % 16 == 0, rows % rows_per_scale == 0, x and ld 16-byte
+ * aligned.  When rows_per_scale > 1 the group maximum is reduced across
+ * workgroups through `workspace` (device, >= pqm_quantize_nvfp4_workspace
+ * bytes, 4-byte aligned; contents on entry are ignored); it may be NULL
+ * when rows_per_scale == 1.
+ */
+pqm_status pqm_quantize_nvfp4_per_token(const uint16_t *x, int64_t rows,
+                                        int64_t cols, int64_t ld,
+                                        int64_t rows_per_scale, uint8_t *q,
+                                        uint8_t *s_block, float *s_outer,
+                                        void *workspace,
+                                        size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/* Workspace bytes pqm_quantize_nvfp4_per_token needs for these sizes. */
+size_t pqm_quantize_nvfp4_workspace(int64_t rows, int64_t cols,
+                                    int64_t rows_per_scale);
+
+/*
+ * Dequantize to bf16 for the dequantized-backward mode ([BW]
+ * High-precision and dequantized backward: the backward GEMMs run in BF16
+ * on the BF16 dequantization of the exact forward operands).
+ *
+ * y = the exact decoded value rounded once to the nearest bf16 (ties to
+ * even; values beyond bf16 range become +-inf):
+ *   PQM_FMT_MXFP8: q [rows, cols] E4M3, s_block [rows, cols/32] E8M0,
+ *                  s_outer unused (may be NULL);  y = q * 2^(s - 127)
+ *   PQM_FMT_NVFP4: q [rows, cols/2] packed E2M1, s_block [rows, cols/16]
+ *                  E4M3, s_outer [rows / rows_per_scale] binary32;
+ *                  y = q * s_b * s_g
+ * y [rows, cols] bf16 (device).  The orientation of y is that of q: a
+ * column-wise (transposed) MXFP8 copy dequantizes to the transpose.
+ * Requires cols % 32 == 0 (MXFP8) or cols % 16 == 0 (NVFP4).
+ */
+pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q,
+                          const uint8_t *s_block, const float *s_outer,
+                          int64_t rows, int64_t cols, int64_t rows_per_scale,
+                          uint16_t *y, hipStream_t stream);
+
+/*
+ * Grouped GEMM over routed experts ([MT] 5.2: one contiguous buffer with
+ * expert offsets handed to a dense grouped GEMM, metadata on the device,
+ * empty experts handled inside; [MT] 5.4: ACC = block-scaled GEMM(A, B),
+ * ACC *= alpha_a[m] (* alpha_b)).
+ *
+ * offsets [G+1] int64 (device): group g owns rows offsets[g] ..
+ * offsets[g+1]-1 of A; offsets[0] = 0, non-decreasing, offsets[G] =
+ * M_total.  Empty groups are legal.  Values outside this contract are
+ * undefined behaviour.
+ *
+ *   PQM_GEMM_FPROP (all formats):   Y[m, n] = sum_k A[m, k] B_g[n, k]
+ *       A [M_total, K] and B [G, N, K], both with K contiguous;
+ *       Y [M_total, N].
+ *   PQM_GEMM_DGRAD (PQM_FMT_BF16):  Y[m, n] = sum_k A[m, k] B_g[k, n]
+ *       A [M_total, K], B [G, K, N] (N contiguous); Y [M_total, N].
+ *   PQM_GEMM_WGRAD (PQM_FMT_BF16):  Y_g[n, k] = sum_{m in g} A[m, n] B[m, k]
+ *       A [M_total, N], B [M_total, K]; Y [G, N, K] (zero for empty g).
+ *
+ * Operand encodings (all device):
+ *   PQM_FMT_BF16:  a, b bf16; scales and outer scales unused (NULL).
+ *   PQM_FMT_MXFP8: a = E4M3 [M_total, K], a_scale = E8M0 [M_total, K/32];
+ *                  b = E4M3 [G, N, K], b_scale = E8M0 [G, N, K/32].
+ *   PQM_FMT_NVFP4: a = packed E2M1 [M_total, K/2], a_scale = E4M3
+ *                  [M_total, K/16], a_outer = binary32 [M_total] (per
+ *                  token); b = packed E2M1 [G, N, K/2], b_scale = E4M3
+ *                  [G, N, K/16], b_outer = binary32 [(G*N) /
+ *                  b_rows_per_scale] (b_rows_per_scale = N: one scale per
+ *                  expert, e.g. joint gate/up).
+ * The products use the exact operand values; accumulation is binary32 and
+ * the outer scales are applied to the binary32 accumulator.
+ * out: Y in bf16 (rounded once) or binary32 per out_dtype.
+ * K % 32 == 0 (MXFP8), K % 16 == 0 (NVFP4), K % 8 and N % 8 == 0 (BF16);
+ * WGRAD needs N % 8 == 0 and K % 8 == 0.  No workspace is needed today:
+ * pass NULL / 0 (the arguments keep the ABI stable).
+ */
+pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,
+                                const void *a, const uint8_t *a_scale,
+                                const float *a_outer, const void *b,
+                                const uint8_t *b_scale, const float *b_outer,
+                                int64_t b_rows_per_scale,
+                                const int64_t *offsets, int64_t G,
+                                int64_t M_total, int64_t N, int64_t K,
+                                void *out, pqm_dtype out_dtype,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * MoE glue around the grouped GEMM ([MT] 5.2: quantized rows are placed in
+ * one contiguous buffer with offsets marking the expert boundaries, built
+ * on the device; [MT] 5.4: D = act(gate, up) x prob; [BW] Fine-grained
+ * precision control: routed outputs go through a high-precision weighted
+ * reduction).
+ */
+
+/*
+ * Stable counting sort of token -> expert assignments.
+ *   topk_ids  [tokens, k] int32 expert ids in [0, num_experts)   (device)
+ *   offsets   [num_experts + 1] int64: expert e owns positions
+ *             offsets[e] .. offsets[e+1]-1                       (device)
+ *   src_row   [tokens * k] int32: flat assignment index t*k + j stored at
+ *             each position; within an expert, flat order is kept (device)
+ *   slot      [tokens, k] int32: position of assignment (t, j)  (device)
+ *   workspace >= pqm_moe_route_workspace(...) bytes, 4-byte aligned.
+ * num_experts <= 4096, tokens * k < 2^31.  Ids outside [0, num_experts)
+ * are undefined behaviour.
+ */
+size_t pqm_moe_route_workspace(int64_t tokens, int64_t k, int64_t num_experts);
+pqm_status pqm_moe_route(const int32_t *topk_ids, int64_t tokens, int64_t k,
+                         int64_t num_experts, int64_t *offsets, int32_t *src_row,
+                         int32_t *slot, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Row gather: out row i = src row (index[i] / divisor), rows of row_bytes
+ * bytes (quantized data, scale bytes or FP32 token scales).  With
+ * index = src_row from pqm_moe_route and divisor = k this places each
+ * token's already-quantized row at its expert-sorted positions: per-row
+ * blocks run along K, so gathering quantized rows gives the same bytes as
+ * quantizing gathered rows.  index entries must be < src_rows * divisor.
+ */
+pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_bytes,
+                               const int32_t *index, int64_t n, int64_t divisor,
+                               void *out, hipStream_t stream);
+
+/*
+ * Weighted SwiGLU: d[m, j] = bf16( silu(g) * u * p ) with g = c[m, j],
+ * u = c[m, inter + j] (c = [gate | up], bf16 [rows, 2*inter]),
+ * silu(z) = z / (1 + exp(-z)), p = prob[src[m]] (prob binary32 indexed by
+ * flat assignment; src may be NULL to index prob by m).  Binary32 math.
+ * d bf16 [rows, inter]; inter % 8 == 0.
+ */
+pqm_status pqm_swiglu_prob(const uint16_t *c, const float *prob, const int32_t *src,
+                           int64_t rows, int64_t inter, uint16_t *d, hipStream_t stream);
+
+/*
+ * Combine: out[t, n] = bf16( sum_j y_rows[slot[t, j], n] + shared[t, n] ),
+ * summed in binary32 in j order (shared may be NULL).  y_rows, shared, out
+ * bf16 with N contiguous; N % 8 == 0.
+ */
+pqm_status pqm_moe_combine(const uint16_t *y_rows, const int32_t *slot,
+                           const uint16_t *shared, int64_t tokens, int64_t k, int64_t N,
+                           uint16_t *out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQMOE_H */

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) block-scaled quantizers and MoE grouped GEMM.
+
+Thin Python binding over the C ABI in ``include/pqmoe.h`` (``libpqmoe.so``,
+built in-tree by ``precision_quantization_moe_amd.build``).  The functions
+here only marshal arguments: they allocate outputs with torch on the
+tensor's device and call the library on torch's current stream.  Every step
+runs in the library's HIP kernels; if the library is missing, importing the
+binding raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    FMT_BF16, FMT_MXFP8, FMT_NVFP4, GEMM_DGRAD, GEMM_FPROP, GEMM_WGRAD,
+    OUT_BF16, OUT_FP32, PqmError, dequantize, lib, moe_combine, moe_gather_rows,
+    moe_grouped_gemm, moe_route, quantize_mxfp8, quantize_nvfp4_per_token,
+    swiglu_prob, LIB_PATH,
+)

@@ -1,0 +1,130 @@
+// api.hip -- the C ABI declared in include/pqmoe.h: host-side argument
+// validation (synchronous, nothing is enqueued on error) and dispatch to the
+// kernel launchers.
+#include "pqmoe.h"
+#include "pqm_internal.hpp"
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+pqm_status from_hip(hipError_t e) { return e == hipSuccess ? PQM_OK : PQM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pqm_status_string(pqm_status s) {
+  switch (s) {
+    case PQM_OK: return "ok";
+    case PQM_ERR_NULL: return "required pointer is NULL";
+    case PQM_ERR_SHAPE: return "invalid shape or size";
+    case PQM_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case PQM_ERR_ENUM: return "unknown or unsupported format/kind/dtype";
+    case PQM_ERR_WORKSPACE: return "workspace too small";
+    case PQM_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int pqm_abi_version(void) { return 1; }
+
+pqm_status pqm_quantize_mxfp8(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
+                              uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT,
+                              uint8_t *s_colT, hipStream_t stream) {
+  const bool row = q_row || s_row, col = q_colT || s_colT;
+  if (rows < 0 || cols < 0 || ld < cols || cols % 32) return PQM_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return PQM_OK;
+  if (!x) return PQM_ERR_NULL;
+  if (!row && !col) return PQM_ERR_NULL;
+  if (row && (!q_row || !s_row)) return PQM_ERR_NULL;
+  if (col && (!q_colT || !s_colT)) return PQM_ERR_NULL;
+  if (rows < 0 || cols < 0 || ld < cols || cols % 32) return PQM_ERR_SHAPE;
+  if (col && rows % 32) return PQM_ERR_SHAPE;
+  if (rows / 128 >= 65535) return PQM_ERR_SHAPE;
+  if (!aligned(x, 16) || ld % 8) return PQM_ERR_ALIGN;
+  if (row && !aligned(q_row, 16)) return PQM_ERR_ALIGN;
+  if (col && !aligned(q_colT, 16)) return PQM_ERR_ALIGN;
+  return from_hip(pqm::launch_quantize_mxfp8(x, rows, cols, ld, row ? q_row : nullptr, s_row,
+                                             col ? q_colT : nullptr, s_colT, stream));
+}
+
+size_t pqm_quantize_nvfp4_workspace(int64_t rows, int64_t cols, int64_t rows_per_scale) {
+  (void)cols;
+  if (rows <= 0 || rows_per_scale <= 0) return 0;
+  return pqm::nvfp4_workspace_bytes(rows, rows_per_scale);
+}
+
+pqm_status pqm_quantize_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t cols,
+                                        int64_t ld, int64_t rows_per_scale, uint8_t *q,
+                                        uint8_t *s_block, float *s_outer, void *workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || ld < cols || cols % 16 || rows_per_scale < 1)
+    return PQM_ERR_SHAPE;
+  if (rows % rows_per_scale) return PQM_ERR_SHAPE;
+  if (cols > pqm::nvfp4_max_cols()) return PQM_ERR_SHAPE;
+  if (rows > 0 && (!x || !q || !s_block || !s_outer)) return PQM_ERR_NULL;
+  if (rows > 0 && (!aligned(x, 16) || ld % 8 || !aligned(q, 8))) return PQM_ERR_ALIGN;
+  if (rows > 0 && !aligned(s_outer, 4)) return PQM_ERR_ALIGN;
+  const size_t need = pqm::nvfp4_workspace_bytes(rows, rows_per_scale);
+  if (need) {
+    if (!workspace) return PQM_ERR_NULL;
+    if (workspace_bytes < need) return PQM_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return PQM_ERR_ALIGN;
+  }
+  return from_hip(pqm::launch_quantize_nvfp4(x, rows, cols, ld, rows_per_scale, q, s_block,
+                                             s_outer, workspace, stream));
+}
+
+pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q, const uint8_t *s_block,
+                          const float *s_outer, int64_t rows, int64_t cols,
+                          int64_t rows_per_scale, uint16_t *y, hipStream_t stream) {
+  if (fmt != PQM_FMT_MXFP8 && fmt != PQM_FMT_NVFP4) return PQM_ERR_ENUM;
+  if (rows < 0 || cols < 0) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_MXFP8 && cols % 32) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_NVFP4) {
+    if (cols % 16 || rows_per_scale < 1 || rows % rows_per_scale) return PQM_ERR_SHAPE;
+  }
+  if (rows == 0 || cols == 0) return PQM_OK;
+  if (!q || !s_block || !y) return PQM_ERR_NULL;
+  if (fmt == PQM_FMT_NVFP4 && !s_outer) return PQM_ERR_NULL;
+  if (!aligned(y, 16)) return PQM_ERR_ALIGN;
+  if (fmt == PQM_FMT_MXFP8 && !aligned(q, 16)) return PQM_ERR_ALIGN;
+  if (fmt == PQM_FMT_NVFP4 && (!aligned(q, 8) || !aligned(s_outer, 4))) return PQM_ERR_ALIGN;
+  return from_hip(pqm::launch_dequantize((int)fmt, q, s_block, s_outer, rows, cols,
+                                         rows_per_scale, y, stream));
+}
+
+pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *a,
+                                const uint8_t *a_scale, const float *a_outer, const void *b,
+                                const uint8_t *b_scale, const float *b_outer,
+                                int64_t b_rows_per_scale, const int64_t *offsets, int64_t G,
+                                int64_t M_total, int64_t N, int64_t K, void *out,
+                                pqm_dtype out_dtype, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (fmt != PQM_FMT_BF16 && fmt != PQM_FMT_MXFP8 && fmt != PQM_FMT_NVFP4) return PQM_ERR_ENUM;
+  if (kind != PQM_GEMM_FPROP && kind != PQM_GEMM_DGRAD && kind != PQM_GEMM_WGRAD)
+    return PQM_ERR_ENUM;
+  if (out_dtype != PQM_OUT_BF16 && out_dtype != PQM_OUT_FP32) return PQM_ERR_ENUM;
+  if (fmt != PQM_FMT_BF16 && kind != PQM_GEMM_FPROP) return PQM_ERR_ENUM;
+  if (G < 0 || M_total < 0 || N < 0 || K < 0) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_MXFP8 && K % 32) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_NVFP4 && K % 16) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_BF16 && (K % 8 || N % 8)) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_NVFP4 && (b_rows_per_scale < 1 || (G * N) % b_rows_per_scale))
+    return PQM_ERR_SHAPE;
+  if (G == 0) return PQM_OK;
+  if (!offsets || !out) return PQM_ERR_NULL;
+  if ((M_total > 0 || kind == PQM_GEMM_WGRAD) && (!a || !b)) return PQM_ERR_NULL;
+  if (fmt != PQM_FMT_BF16 && (!a_scale || !b_scale)) return PQM_ERR_NULL;
+  if (fmt == PQM_FMT_NVFP4 && (!a_outer || !b_outer)) return PQM_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(offsets, 8))
+    return PQM_ERR_ALIGN;
+  return from_hip(pqm::launch_grouped_gemm((int)fmt, (int)kind, a, a_scale, a_outer, b, b_scale,
+                                           b_outer, b_rows_per_scale, offsets, G, M_total, N,
+                                           K, out, out_dtype == PQM_OUT_FP32, stream));
+}
+
+}  // extern "C"

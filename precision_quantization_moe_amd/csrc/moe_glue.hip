@@ -1,0 +1,304 @@
+// moe_glue.hip -- routing into a contiguous expert-sorted buffer, row
+// gather, weighted SwiGLU and combine ("miniTE technical report", 5.2: the
+// quantized rows go into one contiguous buffer with offsets for the expert
+// boundaries, built on the device; 5.4: D = act(gate, up) x prob; "Towards
+// Blackwell-Native 8-bit and 4-bit RL": routed outputs are reduced in high
+// precision).
+#include "pqm_device.hpp"
+#include "pqm_internal.hpp"
+#include "pqmoe.h"
+
+namespace pqm {
+
+constexpr int ROUTE_CHUNK = 1024;  // assignments per workgroup
+
+// Per-chunk histogram of expert ids: counts[chunk * E + e].
+__global__ __launch_bounds__(256) void k_route_hist(const int32_t *__restrict__ ids,
+                                                    int64_t n, int64_t E,
+                                                    int32_t *__restrict__ counts) {
+  extern __shared__ int32_t h[];
+  for (int64_t e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * ROUTE_CHUNK;
+  for (int i = threadIdx.x; i < ROUTE_CHUNK; i += 256) {
+    const int64_t a = base + i;
+    if (a < n) {
+      const int32_t e = ids[a];
+      if (e >= 0 && e < E) atomicAdd(&h[e], 1);  // ids outside [0, E) are skipped
+    }
+  }
+  __syncthreads();
+  for (int64_t e = threadIdx.x; e < E; e += 256) counts[blockIdx.x * E + e] = h[e];
+}
+
+// One workgroup: offsets (exclusive scan of expert totals) and, in place,
+// the start position of every (chunk, expert) pair.
+__global__ __launch_bounds__(256) void k_route_scan(int32_t *__restrict__ counts,
+                                                    int64_t nchunks, int64_t E,
+                                                    int64_t *__restrict__ offsets) {
+  extern __shared__ int64_t tot[];
+  for (int64_t e = threadIdx.x; e < E; e += 256) {
+    int64_t s = 0;
+    for (int64_t c = 0; c < nchunks; ++c) s += counts[c * E + e];
+    tot[e] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t run = 0;
+    for (int64_t e = 0; e < E; ++e) {
+      const int64_t t = tot[e];
+      tot[e] = run;
+      offsets[e] = run;
+      run += t;
+    }
+    offsets[E] = run;
+  }
+  __syncthreads();
+  for (int64_t e = threadIdx.x; e < E; e += 256) {
+    int64_t run = tot[e];
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const int32_t k = counts[c * E + e];
+      counts[c * E + e] = (int32_t)run;
+      run += k;
+    }
+  }
+}
+
+// Scatter each chunk in flat order: position = start of (chunk, expert) +
+// number of earlier assignments of the same expert in the chunk.
+__global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict__ ids,
+                                                       int64_t n, int64_t E,
+                                                       const int32_t *__restrict__ start,
+                                                       int32_t *__restrict__ src_row,
+                                                       int32_t *__restrict__ slot) {
+  extern __shared__ int32_t sh[];
+  int32_t *run = sh;          // [E]
+  int32_t *round_ids = sh + E;  // [256]
+  for (int64_t e = threadIdx.x; e < E; e += 256) run[e] = start[blockIdx.x * E + e];
+  const int64_t base = (int64_t)blockIdx.x * ROUTE_CHUNK;
+  for (int r = 0; r < ROUTE_CHUNK / 256; ++r) {
+    const int64_t a = base + r * 256 + threadIdx.x;
+    int32_t e = a < n ? ids[a] : -1;
+    if (e >= E) e = -1;
+    round_ids[threadIdx.x] = e;
+    __syncthreads();
+    if (e >= 0) {
+      int32_t rank = 0;
+      for (int j = 0; j < (int)threadIdx.x; ++j) rank += (round_ids[j] == e) ? 1 : 0;
+      const int32_t pos = run[e] + rank;
+      src_row[pos] = (int32_t)a;
+      slot[a] = pos;
+    }
+    __syncthreads();
+    if (e >= 0) atomicAdd(&run[e], 1);
+    __syncthreads();
+  }
+}
+
+size_t route_workspace_bytes(int64_t T, int64_t k, int64_t E) {
+  const int64_t n = T * k;
+  const int64_t nchunks = (n + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+  return (size_t)(nchunks * E) * sizeof(int32_t);
+}
+
+hipError_t launch_route(const int32_t *ids, int64_t T, int64_t k, int64_t E, int64_t *offsets,
+                        int32_t *src_row, int32_t *slot, void *ws, hipStream_t st) {
+  const int64_t n = T * k;
+  const int64_t nchunks = (n + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+  int32_t *counts = static_cast<int32_t *>(ws);
+  if (nchunks > 0)
+    hipLaunchKernelGGL(k_route_hist, dim3((unsigned)nchunks), dim3(256), E * sizeof(int32_t),
+                       st, ids, n, E, counts);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), E * sizeof(int64_t), st, counts,
+                     nchunks, E, offsets);
+  if (nchunks > 0)
+    hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nchunks), dim3(256),
+                       (E + 256) * sizeof(int32_t), st, ids, n, E, counts, src_row, slot);
+  return hipGetLastError();
+}
+
+// out[i] = src[index[i] / divisor], rows of row_bytes bytes.
+template <typename V>
+__global__ __launch_bounds__(256) void k_gather(const uint8_t *__restrict__ src,
+                                                int64_t row_bytes,
+                                                const int32_t *__restrict__ index, int64_t n,
+                                                int64_t divisor, uint8_t *__restrict__ out) {
+  const int64_t per_row = row_bytes / sizeof(V);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * per_row) return;
+  const int64_t r = i / per_row, c = i % per_row;
+  const int64_t s = index[r] / divisor;
+  reinterpret_cast<V *>(out + r * row_bytes)[c] =
+      reinterpret_cast<const V *>(src + s * row_bytes)[c];
+}
+
+hipError_t launch_gather(const void *src, int64_t row_bytes, const int32_t *index, int64_t n,
+                         int64_t divisor, void *out, hipStream_t st) {
+  if (n == 0 || row_bytes == 0) return hipSuccess;
+  const uint8_t *s = static_cast<const uint8_t *>(src);
+  uint8_t *o = static_cast<uint8_t *>(out);
+  const bool a16 = row_bytes % 16 == 0 && (uintptr_t)s % 16 == 0 && (uintptr_t)o % 16 == 0;
+  const bool a4 = row_bytes % 4 == 0 && (uintptr_t)s % 4 == 0 && (uintptr_t)o % 4 == 0;
+  if (a16) {
+    const int64_t tot = n * (row_bytes / 16);
+    hipLaunchKernelGGL(k_gather<uint4>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
+                       s, row_bytes, index, n, divisor, o);
+  } else if (a4) {
+    const int64_t tot = n * (row_bytes / 4);
+    hipLaunchKernelGGL(k_gather<uint32_t>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
+                       st, s, row_bytes, index, n, divisor, o);
+  } else {
+    const int64_t tot = n * row_bytes;
+    hipLaunchKernelGGL(k_gather<uint8_t>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
+                       st, s, row_bytes, index, n, divisor, o);
+  }
+  return hipGetLastError();
+}
+
+// d[m, j] = bf16( silu(g) * u * p ), g = c[m, j], u = c[m, I + j], p = the
+// router probability of the assignment stored at row m.  Eight outputs per
+// lane (16-byte bf16 loads and stores).
+__global__ __launch_bounds__(256) void k_swiglu_prob(const uint16_t *__restrict__ c,
+                                                     const float *__restrict__ prob,
+                                                     const int32_t *__restrict__ src,
+                                                     int64_t M, int64_t I,
+                                                     uint16_t *__restrict__ d) {
+  const int64_t per_row = I / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * per_row) return;
+  const int64_t m = i / per_row, j = (i % per_row) * 8;
+  const float p = prob[src ? src[m] : m];
+  const uint4 gv = *reinterpret_cast<const uint4 *>(c + m * 2 * I + j);
+  const uint4 uv = *reinterpret_cast<const uint4 *>(c + m * 2 * I + I + j);
+  const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t h[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float g = t ? bf16_hi_f32(gw[k]) : bf16_lo_f32(gw[k]);
+      const float u = t ? bf16_hi_f32(uw[k]) : bf16_lo_f32(uw[k]);
+      const float s = g / (1.0f + expf(-g));
+      h[t] = f32_to_bf16_rne(s * u * p);
+    }
+    o[k] = h[0] | (h[1] << 16);
+  }
+  *reinterpret_cast<uint4 *>(d + m * I + j) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_swiglu(const uint16_t *c, const float *prob, const int32_t *src, int64_t M,
+                         int64_t I, uint16_t *d, hipStream_t st) {
+  const int64_t tot = M * (I / 8);
+  if (tot == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_swiglu_prob, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, c,
+                     prob, src, M, I, d);
+  return hipGetLastError();
+}
+
+// out[t, n] = bf16( sum_j y[slot[t, j], n] (+ shared[t, n]) ), summed in
+// binary32 in j order.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ y,
+                                                 const int32_t *__restrict__ slot,
+                                                 const uint16_t *__restrict__ shared,
+                                                 int64_t T, int64_t k, int64_t N,
+                                                 uint16_t *__restrict__ out) {
+  const int64_t per_row = N / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * per_row) return;
+  const int64_t t = i / per_row, n = (i % per_row) * 8;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t j = 0; j < k; ++j) {
+    const int64_t r = slot[t * k + j];
+    const uint4 v = *reinterpret_cast<const uint4 *>(y + r * N + n);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += bf16_lo_f32(w[q]);
+      acc[2 * q + 1] += bf16_hi_f32(w[q]);
+    }
+  }
+  if (shared) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(shared + t * N + n);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += bf16_lo_f32(w[q]);
+      acc[2 * q + 1] += bf16_hi_f32(w[q]);
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = f32_to_bf16_rne(acc[2 * q]) | (f32_to_bf16_rne(acc[2 * q + 1]) << 16);
+  *reinterpret_cast<uint4 *>(out + t * N + n) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_combine(const uint16_t *y, const int32_t *slot, const uint16_t *shared,
+                          int64_t T, int64_t k, int64_t N, uint16_t *out, hipStream_t st) {
+  const int64_t tot = T * (N / 8);
+  if (tot == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, y, slot,
+                     shared, T, k, N, out);
+  return hipGetLastError();
+}
+
+}  // namespace pqm
+
+namespace {
+bool al(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+pqm_status st_of(hipError_t e) { return e == hipSuccess ? PQM_OK : PQM_ERR_HIP; }
+}  // namespace
+
+extern "C" {
+
+size_t pqm_moe_route_workspace(int64_t tokens, int64_t k, int64_t num_experts) {
+  if (tokens <= 0 || k <= 0 || num_experts <= 0) return 0;
+  return pqm::route_workspace_bytes(tokens, k, num_experts);
+}
+
+pqm_status pqm_moe_route(const int32_t *topk_ids, int64_t tokens, int64_t k,
+                         int64_t num_experts, int64_t *offsets, int32_t *src_row,
+                         int32_t *slot, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (tokens < 0 || k < 1 || num_experts < 1 || num_experts > 4096) return PQM_ERR_SHAPE;
+  if (tokens * k > (int64_t)0x7FFFFFFF) return PQM_ERR_SHAPE;
+  if (!offsets) return PQM_ERR_NULL;
+  if (tokens > 0 && (!topk_ids || !src_row || !slot || !workspace)) return PQM_ERR_NULL;
+  if (workspace_bytes < pqm::route_workspace_bytes(tokens, k, num_experts))
+    return PQM_ERR_WORKSPACE;
+  if (!al(offsets, 8) || (workspace && !al(workspace, 4))) return PQM_ERR_ALIGN;
+  return st_of(pqm::launch_route(topk_ids, tokens, k, num_experts, offsets, src_row, slot,
+                                 workspace, stream));
+}
+
+pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_bytes,
+                               const int32_t *index, int64_t n, int64_t divisor, void *out,
+                               hipStream_t stream) {
+  (void)src_rows;
+  if (src_rows < 0 || row_bytes < 0 || n < 0 || divisor < 1) return PQM_ERR_SHAPE;
+  if (n == 0 || row_bytes == 0) return PQM_OK;
+  if (!src || !index || !out) return PQM_ERR_NULL;
+  return st_of(pqm::launch_gather(src, row_bytes, index, n, divisor, out, stream));
+}
+
+pqm_status pqm_swiglu_prob(const uint16_t *c, const float *prob, const int32_t *src,
+                           int64_t rows, int64_t inter, uint16_t *d, hipStream_t stream) {
+  if (rows < 0 || inter < 0 || inter % 8) return PQM_ERR_SHAPE;
+  if (rows == 0 || inter == 0) return PQM_OK;
+  if (!c || !prob || !d) return PQM_ERR_NULL;
+  if (!al(c, 16) || !al(d, 16)) return PQM_ERR_ALIGN;
+  return st_of(pqm::launch_swiglu(c, prob, src, rows, inter, d, stream));
+}
+
+pqm_status pqm_moe_combine(const uint16_t *y_rows, const int32_t *slot, const uint16_t *shared,
+                           int64_t tokens, int64_t k, int64_t N, uint16_t *out,
+                           hipStream_t stream) {
+  if (tokens < 0 || k < 1 || N < 0 || N % 8) return PQM_ERR_SHAPE;
+  if (tokens == 0 || N == 0) return PQM_OK;
+  if (!y_rows || !slot || !out) return PQM_ERR_NULL;
+  if (!al(y_rows, 16) || !al(out, 16) || (shared && !al(shared, 16))) return PQM_ERR_ALIGN;
+  return st_of(pqm::launch_combine(y_rows, slot, shared, tokens, k, N, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// pqm_internal.hpp -- launchers shared between the kernel files and the
+// C-ABI layer (not part of the public interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pqm {
+
+hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
+                                 uint8_t *q, uint8_t *s, uint8_t *qT, uint8_t *sT,
+                                 hipStream_t st);
+
+hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
+                                 int64_t rows_per_scale, uint8_t *q, uint8_t *sb, float *sg,
+                                 void *workspace, hipStream_t st);
+size_t nvfp4_workspace_bytes(int64_t R, int64_t rows_per_scale);
+int64_t nvfp4_max_cols();
+
+hipError_t launch_dequantize(int fmt, const uint8_t *q, const uint8_t *s, const float *sg,
+                             int64_t R, int64_t C, int64_t rows_per_scale, uint16_t *y,
+                             hipStream_t st);
+
+hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *a_scale,
+                               const float *a_outer, const void *b, const uint8_t *b_scale,
+                               const float *b_outer, int64_t b_rows_per_scale,
+                               const int64_t *offsets, int64_t G, int64_t M, int64_t N,
+                               int64_t K, void *out, int out_fp32, hipStream_t st);
+
+}  // namespace pqm

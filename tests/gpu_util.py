@@ -1,0 +1,42 @@
+"""Helpers for the GPU parity tests: host <-> device transfers of bf16 bit
+patterns and byte tensors.  No method arithmetic."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(),
+                                  reason="needs an MI355X GPU")
+
+
+def dev_bf16(x: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> device bfloat16 tensor (same bytes)."""
+    t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().cpu().numpy()
+
+
+def first_mismatch(a: np.ndarray, b: np.ndarray) -> str:
+    idx = np.argwhere(a != b)
+    if idx.size == 0:
+        return "equal"
+    i = tuple(idx[0])
+    return f"{len(idx)} mismatches; first at {i}: got {a[i]!r} want {b[i]!r}"
+
+
+def assert_bytes_equal(got: np.ndarray, want: np.ndarray, what: str):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if not np.array_equal(got, want):
+        raise AssertionError(f"{what}: {first_mismatch(got, want)}")

@@ -1,0 +1,121 @@
+"""The C-ABI library loads and exports every entry point include/pqmoe.h
+declares; host-side argument validation returns synchronously (these calls
+never reach the device).  CPU only."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_quantization_moe_amd as pqm
+from precision_quantization_moe_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pqmoe.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(pqm_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = pqm.lib()
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_binding.SIGNATURES), "binding covers the header"
+
+
+def test_abi_version_and_status_strings():
+    L = pqm.lib()
+    assert L.pqm_abi_version() == 1
+    for code in range(7):
+        assert L.pqm_status_string(code)
+    assert L.pqm_status_string(99) == b"unknown status"
+
+
+# Fake device addresses: 16-byte aligned values never dereferenced, because
+# every call below fails validation before any launch.
+A16 = ctypes.c_void_p(0x10000)
+BAD = ctypes.c_void_p(0x10002)
+
+
+def test_quantize_mxfp8_validation():
+    L = pqm.lib()
+    f = L.pqm_quantize_mxfp8
+    assert f(A16, 64, 64, 64, None, None, None, None, None) == 1    # no output
+    assert f(A16, 64, 64, 64, A16, None, None, None, None) == 1     # half pair
+    assert f(A16, 64, 48, 64, A16, A16, None, None, None) == 2      # cols % 32
+    assert f(A16, 48, 64, 64, None, None, A16, A16, None) == 2      # rows % 32
+    assert f(A16, 64, 64, 32, A16, A16, None, None, None) == 2      # ld < cols
+    assert f(A16, -1, 64, 64, A16, A16, None, None, None) == 2
+    assert f(BAD, 64, 64, 64, A16, A16, None, None, None) == 3      # x align
+    assert f(A16, 64, 64, 68, A16, A16, None, None, None) == 3      # ld % 8
+    assert f(A16, 64, 64, 64, BAD, A16, None, None, None) == 3
+    assert f(None, 64, 64, 64, A16, A16, None, None, None) == 1
+
+
+def test_quantize_nvfp4_validation():
+    L = pqm.lib()
+    f = L.pqm_quantize_nvfp4_per_token
+    assert f(A16, 64, 40, 40, 1, A16, A16, A16, None, 0, None) == 2   # cols % 16
+    assert f(A16, 64, 64, 64, 3, A16, A16, A16, A16, 4096, None) == 2  # rows % rps
+    assert f(A16, 64, 64, 64, 0, A16, A16, A16, None, 0, None) == 2
+    assert f(A16, 64, 64, 64, 1, None, A16, A16, None, 0, None) == 1
+    assert f(A16, 64, 64, 64, 32, A16, A16, A16, None, 0, None) == 1   # ws needed
+    need = L.pqm_quantize_nvfp4_workspace(64, 64, 32)
+    assert need == 8
+    assert f(A16, 64, 64, 64, 32, A16, A16, A16, A16, need - 1, None) == 5
+    assert f(BAD, 64, 64, 64, 1, A16, A16, A16, None, 0, None) == 3
+    assert f(A16, 64, 1 << 20, 1 << 20, 1, A16, A16, A16, None, 0, None) == 2
+    assert L.pqm_quantize_nvfp4_workspace(64, 64, 1) == 0
+
+
+def test_dequantize_validation():
+    L = pqm.lib()
+    f = L.pqm_dequantize
+    assert f(7, A16, A16, None, 4, 32, 1, A16, None) == 4
+    assert f(1, A16, A16, None, 4, 48, 1, A16, None) == 2
+    assert f(2, A16, A16, None, 4, 32, 1, A16, None) == 1          # no s_outer
+    assert f(2, A16, A16, A16, 4, 24, 1, A16, None) == 2
+    assert f(1, A16, A16, None, 4, 32, 1, BAD, None) == 3
+    assert f(1, A16, A16, None, 0, 32, 1, None, None) == 0         # empty: no-op
+
+
+def test_grouped_gemm_validation():
+    L = pqm.lib()
+    f = L.pqm_moe_grouped_gemm
+    args = lambda **kw: [kw.get("fmt", 1), kw.get("kind", 0), A16, A16, None, A16, A16, None,
+                         kw.get("brps", 0), A16, kw.get("G", 4), kw.get("M", 64), 64,
+                         kw.get("K", 64), A16, kw.get("out", 1), None, 0, None]
+    assert f(*args(fmt=5)) == 4
+    assert f(*args(kind=9)) == 4
+    assert f(*args(out=3)) == 4
+    assert f(*args(kind=1)) == 4                    # MXFP8 dgrad not offered
+    assert f(*args(K=48)) == 2
+    assert f(*args(fmt=2, K=40)) == 2
+    assert f(*args(fmt=2, brps=3)) == 2
+    assert f(*args(fmt=0, K=12)) == 2
+    assert f(*args(G=-1)) == 2
+    assert f(*args(G=0)) == 0                       # nothing to do
+    a = args()
+    a[2] = BAD
+    assert f(*a) == 3
+
+
+def test_glue_validation():
+    L = pqm.lib()
+    assert L.pqm_moe_route(A16, 8, 0, 4, A16, A16, A16, A16, 1 << 20, None) == 2
+    assert L.pqm_moe_route(A16, 8, 2, 5000, A16, A16, A16, A16, 1 << 20, None) == 2
+    assert L.pqm_moe_route(A16, 8, 2, 4, A16, A16, A16, A16, 0, None) == 5
+    assert L.pqm_moe_route_workspace(8192, 8, 128) == 64 * 128 * 4
+    assert L.pqm_moe_gather_rows(A16, 4, 16, A16, 4, 0, A16, None) == 2
+    assert L.pqm_swiglu_prob(A16, A16, None, 4, 12, A16, None) == 2
+    assert L.pqm_swiglu_prob(BAD, A16, None, 4, 16, A16, None) == 3
+    assert L.pqm_moe_combine(A16, A16, None, 4, 0, 16, A16, None) == 2
+    assert L.pqm_moe_combine(A16, None, None, 4, 2, 16, A16, None) == 1
