@@ -72,6 +72,7 @@ def lib():
         L.pqo_bf16_round.restype = ctypes.c_uint16
         L.pqo_bf16_round_array.argtypes = [P, Lg, P]
         L.pqo_inexact_count.restype = ctypes.c_long
+        L.pqo_omp_threads.restype = ctypes.c_int
         L.pqo_fp32_div.argtypes = [ctypes.c_float, ctypes.c_float]
         L.pqo_fp32_div.restype = ctypes.c_float
         _lib = L

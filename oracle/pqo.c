@@ -23,6 +23,7 @@
  * code that takes it.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -397,3 +398,5 @@ void pqo_bf16_round_array(const double *v, long n, uint16_t *out)
     for (long i = 0; i < n; ++i)
         out[i] = bf16_round(v[i]);
 }
+
+int pqo_omp_threads(void) { return omp_get_max_threads(); }

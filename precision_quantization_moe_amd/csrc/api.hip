@@ -117,7 +117,7 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
     return PQM_ERR_SHAPE;
   if (G == 0) return PQM_OK;
   if (!offsets || !out) return PQM_ERR_NULL;
-  if ((M_total > 0 || kind == PQM_GEMM_WGRAD) && (!a || !b)) return PQM_ERR_NULL;
+  if (M_total > 0 && (!a || !b)) return PQM_ERR_NULL;
   if (fmt != PQM_FMT_BF16 && (!a_scale || !b_scale)) return PQM_ERR_NULL;
   if (fmt == PQM_FMT_NVFP4 && (!a_outer || !b_outer)) return PQM_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(offsets, 8))

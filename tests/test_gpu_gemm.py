@@ -1,0 +1,198 @@
+"""GPU parity of the grouped GEMMs against the oracle's binary64 product of
+the same exactly-decoded operands.
+
+Bar: relative L2 <= 1e-3 on binary32 output, per row (a row whose oracle
+values overflow binary32 is excluded).  bf16 output is compared against the
+oracle's product rounded once to bf16, by the same per-row relative L2 (the
+binary32 accumulation differs only where a value straddles a bf16 rounding
+boundary, or is a near-cancellation far below the row's norm).
+
+The oracle quantizes the operands itself from the same generated bf16 bytes
+(byte equality of the two quantizers is established separately)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_quantization_moe_amd as pqm
+from precision_quantization_moe_amd import workloads as wl
+from gpu_util import dev, dev_bf16, host, host_u16, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+TOL = 1e-3
+F32_MAX = float(np.finfo(np.float32).max)
+
+
+def rel_l2_rows(got: np.ndarray, want: np.ndarray) -> np.ndarray:
+    got = got.astype(np.float64)
+    ok = np.isfinite(want).all(axis=1) & (np.abs(want).max(axis=1) < F32_MAX)
+    num = np.linalg.norm(got - want, axis=1)
+    den = np.linalg.norm(want, axis=1)
+    out = np.where(den > 0, num / np.where(den > 0, den, 1), num)
+    return np.where(ok, out, 0.0)
+
+
+def check_rows(got, want, what):
+    r = rel_l2_rows(got, want)
+    print(f"[gemm] {what}: max row rel-L2 {r.max():.3e}", flush=True)
+    assert r.max() <= TOL, (what, float(r.max()), int(r.argmax()))
+
+
+def bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    def key(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
+def _offsets(sizes):
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+# ------------------------------------------------------------------ MXFP8
+
+def _mxfp8_case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32):
+    G = len(sizes)
+    M = int(sum(sizes))
+    x = wl.activations(max(M, 1), K, seed=seed)[:M]
+    w = wl.normal_bf16((G * N, K), std=0.02, seed=seed + 1)
+    off = _offsets(sizes)
+    qa, sa, _, _ = pqm.quantize_mxfp8(dev_bf16(x), colwise=False)
+    qb, sb, _, _ = pqm.quantize_mxfp8(dev_bf16(w), colwise=False)
+    y = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, qb, dev(off), N, K,
+                             a_scale=sa, b_scale=sb, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ra, rsa = oracle.quantize_mxfp8_rowwise(x)
+    rb, rsb = oracle.quantize_mxfp8_rowwise(w)
+    want = oracle.grouped_gemm(oracle.decode_mxfp8(ra, rsa),
+                               oracle.decode_mxfp8(rb, rsb).reshape(G, N, K), off)
+    return y, want
+
+
+@pytest.mark.parametrize("case", [
+    ([0, 37, 128, 1, 300], 192, 320),
+    ([128], 256, 256),
+    ([5, 0, 0, 250], 96, 64),
+    ([513], 128, 4096),
+])
+def test_mxfp8_fprop_ragged(case):
+    sizes, N, K = case
+    y, want = _mxfp8_case(sizes, N, K, seed=3)
+    check_rows(host(y), want, f"mxfp8 {sizes} N={N} K={K}")
+
+
+def test_mxfp8_fprop_bf16_out():
+    y, want = _mxfp8_case([64, 0, 100], 128, 256, seed=4, out_dtype=pqm.OUT_BF16)
+    got = oracle.bf16_to_f64(host_u16(y))
+    ref = oracle.bf16_to_f64(oracle.f64_to_bf16(want))
+    d = bf16_ulp_diff(host_u16(y), oracle.f64_to_bf16(want))
+    assert (d == 0).mean() > 0.97          # almost all bytes equal
+    check_rows(got, ref, "mxfp8 bf16 out vs rounded oracle")
+
+
+def test_mxfp8_tiny_contract_expert_gemm():
+    """128 x 256 contract tensor (outliers, a zero row, a bf16-max row)
+    times a 256 x 256 expert weight."""
+    x = wl.tiny_contract_tensor()
+    w = wl.normal_bf16((256, 256), std=0.02, seed=5)
+    off = np.array([0, 128], np.int64)
+    qa, sa, _, _ = pqm.quantize_mxfp8(dev_bf16(x), colwise=False)
+    qb, sb, _, _ = pqm.quantize_mxfp8(dev_bf16(w), colwise=False)
+    y = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, qb, dev(off), 256, 256,
+                             a_scale=sa, b_scale=sb)
+    ra, rsa = oracle.quantize_mxfp8_rowwise(x)
+    rb, rsb = oracle.quantize_mxfp8_rowwise(w)
+    want = oracle.grouped_gemm(oracle.decode_mxfp8(ra, rsa),
+                               oracle.decode_mxfp8(rb, rsb)[None], off)
+    got = host(y)
+    assert not got[1].any()                        # the all-zero row
+    check_rows(got, want, "tiny contract")
+
+
+def test_mxfp8_qwen3_gate_up_full_sampled():
+    """Full Qwen3-30B-A3B FC1 shape: 8192 tokens x top-8 over 128 experts
+    with Zipf(1.1) load (65536 rows), N = 1536, K = 2048.  All rows are
+    computed on the GPU; sampled rows of every expert are checked."""
+    T, E, k, H, N = 8192, 128, 8, 2048, 1536
+    ids = wl.zipf_routing(T, E, k)
+    off, src, _ = oracle.route(ids, E)
+    x = wl.activations(T, H)
+    xg = x[src // k]                                # expert-sorted rows
+    M = xg.shape[0]
+    qa, sa, _, _ = pqm.quantize_mxfp8(dev_bf16(xg), colwise=False)
+    w = wl.expert_weights(E, N, H, 0.02)
+    qb, sb, _, _ = pqm.quantize_mxfp8(dev_bf16(w.reshape(E * N, H)), colwise=False)
+    y = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, qb, dev(off), N, H,
+                             a_scale=sa, b_scale=sb)
+    torch.cuda.synchronize()
+    yh = host(y)
+    rng = np.random.Generator(np.random.PCG64(17))
+    experts = sorted(set(rng.choice(E, 12, replace=False).tolist()) | {0, E - 1})
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 6)]))
+        ra, rsa = oracle.quantize_mxfp8_rowwise(xg[rows])
+        rb, rsb = oracle.quantize_mxfp8_rowwise(w[e])
+        want = oracle.decode_mxfp8(ra, rsa) @ oracle.decode_mxfp8(rb, rsb).T
+        check_rows(yh[rows], want, f"qwen3 fc1 expert {e} ({hi - lo} rows)")
+    assert M == T * k
+
+
+# ------------------------------------------------------------------- BF16
+
+def _bf16_operands(M, N, K, G, seed):
+    a = wl.normal_bf16((M, K), seed=seed)
+    b = wl.normal_bf16((G, N, K), std=0.05, seed=seed + 1)
+    return a, b
+
+
+@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([200], 256, 64)])
+def test_bf16_fprop(sizes, N, K):
+    G = len(sizes)
+    M = int(sum(sizes))
+    a, b = _bf16_operands(M, N, K, G, 7)
+    off = _offsets(sizes)
+    y = pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_FPROP, dev_bf16(a),
+                             dev_bf16(b.reshape(G * N, K)), dev(off), N, K)
+    want = oracle.grouped_gemm(oracle.bf16_to_f64(a),
+                               oracle.bf16_to_f64(b.reshape(-1, K)).reshape(G, N, K), off)
+    check_rows(host(y), want, f"bf16 fprop {sizes}")
+
+
+@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([64, 64], 136, 72)])
+def test_bf16_dgrad(sizes, N, K):
+    """dX[m, n] = sum_k dY[m, k] W_g[k, n]: W stored [G, K, N] (the forward
+    weight [out, in] with the contraction over its rows)."""
+    G = len(sizes)
+    M = int(sum(sizes))
+    dy = wl.normal_bf16((M, K), seed=9)
+    w = wl.normal_bf16((G, K, N), std=0.05, seed=10)
+    off = _offsets(sizes)
+    y = pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_DGRAD, dev_bf16(dy),
+                             dev_bf16(w.reshape(G * K, N)), dev(off), N, K)
+    wt = np.ascontiguousarray(np.transpose(oracle.bf16_to_f64(w.reshape(-1, N)).reshape(G, K, N),
+                                           (0, 2, 1)))
+    want = oracle.grouped_gemm(oracle.bf16_to_f64(dy), wt, off)
+    check_rows(host(y), want, f"bf16 dgrad {sizes}")
+
+
+@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([700], 64, 136)])
+def test_bf16_wgrad(sizes, N, K):
+    G = len(sizes)
+    M = int(sum(sizes))
+    dy = wl.normal_bf16((max(M, 1), N), seed=11)[:M]
+    x = wl.normal_bf16((max(M, 1), K), seed=12)[:M]
+    off = _offsets(sizes)
+    y = pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_WGRAD, dev_bf16(dy), dev_bf16(x),
+                             dev(off), N, K)
+    want = oracle.grouped_gemm_wgrad(oracle.bf16_to_f64(dy), oracle.bf16_to_f64(x), off)
+    got = host(y)
+    assert got.shape == (G, N, K)
+    for g in range(G):
+        if sizes[g] == 0:
+            assert not got[g].any()
+        else:
+            check_rows(got[g], want[g], f"bf16 wgrad group {g}")
