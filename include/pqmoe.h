@@ -96,7 +96,8 @@ int pqm_abi_version(void);
  *   s_colT  [cols, rows/32]    E8M0 bytes                          (device)
  * Either output pair may be NULL to skip that copy, not both.
  * Requires cols % 32 == 0; rows % 32 == 0 when the column copy is asked
- * for; x and ld 16-byte aligned (ld % 8 == 0).
+ * for; x, q_row, q_colT and ld 16-byte aligned (ld % 8 == 0); s_row and
+ * s_colT 4-byte aligned.
  */
 pqm_status pqm_quantize_mxfp8(const uint16_t *x, int64_t rows, int64_t cols,
                               int64_t ld, uint8_t *q_row, uint8_t *s_row,

@@ -4,6 +4,36 @@
 #include "pqmoe.h"
 #include "pqm_internal.hpp"
 
+#include <mutex>
+#include <map>
+#include <utility>
+
+namespace pqm {
+
+int64_t resident_workgroups(const void *kernel, int block, size_t dyn_lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void *, int>, int64_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(kernel, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, dyn_lds) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const int64_t r = (int64_t)per_cu * cus;
+  cache[key] = r;
+  return r;
+}
+
+}  // namespace pqm
+
 namespace {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -43,8 +73,8 @@ pqm_status pqm_quantize_mxfp8(const uint16_t *x, int64_t rows, int64_t cols, int
   if (col && rows % 32) return PQM_ERR_SHAPE;
   if (rows / 128 >= 65535) return PQM_ERR_SHAPE;
   if (!aligned(x, 16) || ld % 8) return PQM_ERR_ALIGN;
-  if (row && !aligned(q_row, 16)) return PQM_ERR_ALIGN;
-  if (col && !aligned(q_colT, 16)) return PQM_ERR_ALIGN;
+  if (row && (!aligned(q_row, 16) || !aligned(s_row, 4))) return PQM_ERR_ALIGN;
+  if (col && (!aligned(q_colT, 16) || !aligned(s_colT, 4))) return PQM_ERR_ALIGN;
   return from_hip(pqm::launch_quantize_mxfp8(x, rows, cols, ld, row ? q_row : nullptr, s_row,
                                              col ? q_colT : nullptr, s_colT, stream));
 }

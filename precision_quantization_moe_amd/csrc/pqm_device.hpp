@@ -155,6 +155,65 @@ __device__ __forceinline__ uint32_t e2m1_code(float a, const E2M1Thresholds &th)
   return c;
 }
 
+// ---------------------------------------------------------------------
+// Hardware conversions.  Both were compared on gfx950 against the exact
+// rules: v_cvt_scalef32_pk_fp8_bf16 gives the nearest-even E4M3 of x/scale
+// for every bf16 x and power-of-two scales (the MXFP8 case); the E2M1
+// conversion v_cvt_scalef32_pk_fp4_f32 with scale 1.0 gives the
+// nearest-even, saturating, sign-keeping E2M1 of every binary32 input.
+
+typedef __bf16 pqm_v2bf __attribute__((ext_vector_type(2)));
+typedef short pqm_v2s __attribute__((ext_vector_type(2)));
+
+// Four E4M3 bytes of x/scale for the bf16 pairs w0, w1 (element order
+// w0.lo, w0.hi, w1.lo, w1.hi); scale = 2^e with e >= -126.
+__device__ __forceinline__ uint32_t cvt4_e4m3_bf16(uint32_t w0, uint32_t w1, float scale) {
+  pqm_v2s r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(pqm_v2bf, w0), scale,
+                                                 false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(pqm_v2bf, w1), scale,
+                                                 true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two E4M3 bytes (low 16 bits) of binary32 values holding exact values of
+// at most 8 significant bits, |v| <= 448.
+__device__ __forceinline__ uint32_t cvt2_e4m3_f32(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// E4M3 bytes of four bf16 elements (pairs w0, w1) divided by 2^(sb - 127).
+// A scale byte of 0 (2^-127, a binary32 subnormal) takes the exact binary32
+// route: x * 2^127 is exact and has at most 8 significant bits.  That case
+// (blocks whose maximum is below 448 * 2^-126) is rare, so it sits behind a
+// wave-uniform branch and costs nothing when no lane of the wave needs it.
+__device__ __forceinline__ uint32_t mx_encode4(uint32_t w0, uint32_t w1, uint32_t sb) {
+  uint32_t out = cvt4_e4m3_bf16(w0, w1, __uint_as_float(sb << 23));
+  if (__builtin_amdgcn_ballot_w64(sb == 0) != 0) {
+    if (sb == 0) {
+      const float k = 0x1p127f;
+      const uint32_t lo = cvt2_e4m3_f32(bf16_lo_f32(w0) * k, bf16_hi_f32(w0) * k);
+      const uint32_t hi = cvt2_e4m3_f32(bf16_lo_f32(w1) * k, bf16_hi_f32(w1) * k);
+      out = lo | (hi << 16);
+    }
+  }
+  return out;
+}
+
+// Packed E2M1 nibbles of two binary32 values into byte `sel` of `old`.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt2_e2m1(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+typedef unsigned short pqm_us2 __attribute__((ext_vector_type(2)));
+
+// Per-half unsigned maximum of two packed 16-bit pairs.
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(pqm_us2, a),
+                                                                __builtin_bit_cast(pqm_us2, b)));
+}
+
 // Wave-wide maximum of a non-negative float (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

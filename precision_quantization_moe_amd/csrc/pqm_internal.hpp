@@ -8,6 +8,17 @@
 
 namespace pqm {
 
+// Number of workgroups of `kernel` (block threads, dynamic LDS bytes) that
+// can be resident on the current device at once: occupancy per CU times
+// the CU count.  Cached per (kernel, device); host-only queries.
+int64_t resident_workgroups(const void *kernel, int block, size_t dyn_lds);
+
+// Persistent grid size: min(work items, resident workgroups).
+inline unsigned persistent_grid(const void *kernel, int block, size_t dyn_lds, int64_t work) {
+  const int64_t r = resident_workgroups(kernel, block, dyn_lds);
+  return (unsigned)(work < r ? (work > 0 ? work : 1) : r);
+}
+
 hipError_t launch_quantize_mxfp8(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
                                  uint8_t *q, uint8_t *s, uint8_t *qT, uint8_t *sT,
                                  hipStream_t st);

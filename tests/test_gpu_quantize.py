@@ -61,6 +61,37 @@ def test_mxfp8_test_sets(name):
     _check_mxfp8(_inputs()[name], name)
 
 
+def _exhaustive_scale_tensor(seed: int = 3) -> np.ndarray:
+    """Every positive finite bf16 magnitude under every E8M0 scale byte
+    0..247: block b's first element is the largest value with that scale
+    (448 * 2^(byte-127), or bf16 max), the other 31 sweep every bf16
+    magnitude not above it, with random signs.  Rows of 256 elements."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    mags = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    blocks = []
+    for b in range(248):
+        if b < 247:
+            top = wl.f32_to_bf16_bits(np.array([448.0 * 2.0 ** (b - 127)], np.float32))[0]
+        else:
+            top = np.uint16(wl.BF16_MAX_BITS)
+        pool = mags[mags <= top]
+        n = (pool.size + 30) // 31
+        pool = np.concatenate([pool, np.zeros(n * 31 - pool.size, np.uint16)])
+        blk = np.concatenate([np.full((n, 1), top, np.uint16), pool.reshape(n, 31)], axis=1)
+        blocks.append(blk)
+    x = np.concatenate(blocks).reshape(-1)
+    x = x | (rng.integers(0, 2, x.size).astype(np.uint16) << 15)
+    pad = (-x.size) % (256 * 32)
+    x = np.concatenate([x, np.zeros(pad, np.uint16)])
+    return x.reshape(-1, 256)
+
+
+def test_mxfp8_exhaustive_values_and_scales():
+    x = _exhaustive_scale_tensor()
+    _check_mxfp8(x, "exhaustive rowwise")
+    _check_mxfp8(np.ascontiguousarray(x.T), "exhaustive colwise")
+
+
 @pytest.mark.parametrize("shape", [(160, 96), (32, 32), (128, 128), (288, 416), (96, 2048)])
 def test_mxfp8_ragged_tiles(shape):
     x = wl.activations(*shape, seed=7)
