@@ -4,24 +4,30 @@ MI355X.
 One step is one pass of every hot-path row over one batch of synthetic,
 seeded input, with all inputs resident in HBM:
 
-  mxfp8_quant      MXFP8 row-wise + column-wise quantize, 16384 x 2048 bf16
-                   activations (Qwen3-30B-A3B hidden size)   <- headline value
-  nvfp4_token      per-token NVFP4 quantize of the same-shaped activations
-  nvfp4_joint_w    joint gate/up NVFP4 quantize of 128 experts' [1536 x 2048]
-  moe_mxfp8_fwd    MXFP8 MoE expert layer forward, 8192 tokens top-8 over 128
-                   experts (Zipf 1.1 load): weight quantize, route, token
-                   quantize, gather, gate_up grouped GEMM, SwiGLU x prob,
-                   quantize, down grouped GEMM, combine
-  dequant_bwd      dequantize of the forward operands (dequantized backward)
-  bf16_bwd         BF16 dgrad + wgrad grouped GEMMs of both expert GEMMs on
-                   the dequantized operands
+  mxfp8_quant       MXFP8 row-wise + column-wise quantize, 16384 x 2048 bf16
+                    activations (Qwen3-30B-A3B hidden size)  <- headline value
+  nvfp4_token       per-token NVFP4 quantize of same-shaped activations
+  nvfp4_joint_w     joint gate/up NVFP4 quantize, 128 experts' [1536 x 2048]
+  q3_wquant         Qwen3-30B-A3B experts: MXFP8 quantize of W1 and W2
+  q3_fwd            MXFP8 MoE expert layer forward: 8192 tokens, top-8 of 128
+                    experts (Zipf 1.1): route, token quantize, gather,
+                    gate_up GEMM, SwiGLU x prob, quantize, down GEMM, combine
+  q3_gemm           the two MXFP8 grouped GEMMs of q3_fwd alone
+  q3_dequant        dequantize of the forward operands (dequantized backward)
+  q3_bwd            BF16 dgrad + wgrad of both expert GEMMs on them
+  ds_wquant         DeepSeek-V3 experts (256 routed + 1 shared, hidden 7168,
+                    intermediate 2048): NVFP4 weights, gate/up jointly scaled
+  ds_fwd            NVFP4 MoE expert layer forward, 4096 tokens top-8 + shared
+  ds_gemm           the two NVFP4 grouped GEMMs of ds_fwd alone
+  ds_reconstruct    bf16 reconstruction of the forward operands (activations
+                    and all 257 experts' weights) for the dequantized backward
 
 Quantizer inputs rotate over several buffer sets larger than the 256 MB
 Infinity Cache so their rate is HBM's.  Each row is timed with HIP events
-on the stream its kernels run on; `value` is the MXFP8 quantizer's HBM
-rate (algorithmic bytes / kernel time).
+on the stream its kernels run on (torch's current stream); `value` is the
+MXFP8 quantizer's HBM rate (algorithmic bytes / kernel time).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows a,b,...]
 """
 from __future__ import annotations
 
@@ -38,18 +44,20 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # dense MFMA FP8
-BF16_PEAK_TFLOPS = 2500.0      # dense MFMA BF16
+BF16_PEAK_TFLOPS = 2500.0      # dense MFMA BF16 / FP16
+
+ALL_ROWS = ["mxfp8_quant", "nvfp4_token", "nvfp4_joint_w", "q3_wquant", "q3_fwd", "q3_gemm",
+            "q3_dequant", "q3_bwd", "ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"]
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--sets", type=int, default=3, help="rotating quantizer input sets")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--rows", default="all",
-                   help="comma list of rows to run (default all)")
+    p.add_argument("--rows", default="all", help="comma list of rows (default all)")
     return p.parse_args()
 
 
@@ -60,144 +68,223 @@ def log(*a):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; "
-                          "multi-GPU runs are not part of this build",
-                          "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are "
+                          "not part of this build", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     import precision_quantization_moe_amd as pqm
+    from precision_quantization_moe_amd import moe_layer
     from precision_quantization_moe_amd import workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs an MI355X GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    rows_sel = None if args.rows == "all" else set(args.rows.split(","))
-    want = lambda r: rows_sel is None or r in rows_sel
+    sel = ALL_ROWS if args.rows == "all" else [r for r in ALL_ROWS if r in args.rows.split(",")]
+    need = lambda *names: any(n in sel for n in names)
 
-    def to_dev_bf16(a: np.ndarray):
+    def to_dev(a: np.ndarray):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
             torch.bfloat16).to(dev)
+
+    def gpu_normal(rows, cols, std, seed, chunk_rows=1 << 16):
+        g = torch.Generator(device=dev).manual_seed(seed)
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+        for r in range(0, rows, chunk_rows):
+            n = min(chunk_rows, rows - r)
+            out[r:r + n] = (torch.randn(n, cols, generator=g, device=dev) * std).to(torch.bfloat16)
+        return out
 
     # ------------------------------------------------------------ inputs
     T2, H = 16384, 2048
     log("generating inputs")
-    sets = [to_dev_bf16(wl.activations(T2, H, seed=100 + i)) for i in range(args.sets)]
+    st = {}
+    if need("mxfp8_quant", "nvfp4_token"):
+        st["sets"] = [to_dev(wl.activations(T2, H, seed=100 + i)) for i in range(args.sets)]
     E, I2 = 128, 1536
-    w_joint = to_dev_bf16(wl.expert_weights(E, I2, H, 0.02, tag=7).reshape(E * I2, H)) \
-        if want("nvfp4_joint_w") else None
-    # MXFP8 MoE layer (Qwen3-30B-A3B experts)
+    if need("nvfp4_joint_w"):
+        st["w_joint"] = to_dev(wl.expert_weights(E, I2, H, 0.02, tag=7).reshape(E * I2, H))
+    # Qwen3-30B-A3B expert layer
     T4, K4, I4 = 8192, 8, 768
-    x4 = to_dev_bf16(wl.activations(T4, H, seed=4))
-    ids = torch.from_numpy(wl.zipf_routing(T4, E, K4)).to(dev)
-    prob = torch.from_numpy(wl.router_probs(T4, K4).reshape(-1)).to(dev)
-    W1 = to_dev_bf16(wl.expert_weights(E, 2 * I4, H, 0.02).reshape(E * 2 * I4, H))
-    W2 = to_dev_bf16(wl.expert_weights(E, H, I4, 0.02, tag=1).reshape(E * H, I4))
     M4 = T4 * K4
-    dY = to_dev_bf16(wl.output_grad(M4, H))
-    dC = to_dev_bf16(wl.output_grad(M4, 2 * I4, seed=5))
+    if need("q3_wquant", "q3_fwd", "q3_gemm", "q3_dequant", "q3_bwd"):
+        st["x4"] = to_dev(wl.activations(T4, H, seed=4))
+        st["ids4"] = torch.from_numpy(wl.zipf_routing(T4, E, K4)).to(dev)
+        st["prob4"] = torch.from_numpy(wl.router_probs(T4, K4).reshape(-1)).to(dev)
+        st["W1"] = to_dev(wl.expert_weights(E, 2 * I4, H, 0.02).reshape(E * 2 * I4, H))
+        st["W2"] = to_dev(wl.expert_weights(E, H, I4, 0.02, tag=1).reshape(E * H, I4))
+        st["dY"] = to_dev(wl.output_grad(M4, H))
+        st["dC"] = to_dev(wl.output_grad(M4, 2 * I4, seed=5))
+    # DeepSeek-V3 expert layer (weights drawn on the GPU from a seeded stream)
+    T5, K5, E5, H5, I5 = 4096, 8, 256, 7168, 2048
+    M5 = T5 * K5 + T5
+    if need("ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"):
+        st["x5"] = to_dev(wl.activations(T5, H5, seed=6))
+        st["ids5"] = torch.from_numpy(wl.uniform_plus_zipf_routing(T5, E5, K5)).to(dev)
+        p5 = torch.from_numpy(wl.router_probs(T5, K5, seed=7).reshape(-1)).to(dev)
+        st["prob5"] = torch.cat([p5, torch.ones(T5, dtype=torch.float32, device=dev)])
+        st["W1d"] = gpu_normal((E5 + 1) * 2 * I5, H5, 0.01, seed=11)
+        st["W2d"] = gpu_normal((E5 + 1) * H5, I5, 0.01, seed=12)
     torch.cuda.synchronize()
     log("inputs ready")
 
+    # ------------------------------------------------------------- rows
+    # outputs of the quantizer rows are allocated once (one per input set),
+    # so the timed region holds only the kernels
+    if need("mxfp8_quant"):
+        st["mx_out"] = [pqm.quantize_mxfp8(x) for x in st["sets"]]
+    if need("nvfp4_token"):
+        st["nv_out"] = [pqm.quantize_nvfp4_per_token(x) for x in st["sets"]]
+    if need("nvfp4_joint_w"):
+        st["jw_out"] = pqm.quantize_nvfp4_per_token(st["w_joint"], rows_per_scale=I2)
+
+    def r_mxfp8(s):
+        k = s % len(st["sets"])
+        pqm.quantize_mxfp8(st["sets"][k], out=st["mx_out"][k])
+
+    def r_nvfp4(s):
+        k = s % len(st["sets"])
+        pqm.quantize_nvfp4_per_token(st["sets"][k], out=st["nv_out"][k])
+
+    def r_joint(s):
+        pqm.quantize_nvfp4_per_token(st["w_joint"], rows_per_scale=I2, out=st["jw_out"])
+
+    def r_q3_wquant(s):
+        st["q3w"] = moe_layer.quantize_expert_weights_mxfp8(st["W1"], st["W2"])
+
+    def r_q3_fwd(s):
+        st["q3"] = moe_layer.mxfp8_moe_forward(st["x4"], st["ids4"], st["prob4"], *st["q3w"], E,
+                                               I4)
+
+    def r_q3_gemm(s):
+        o, (w1q, w1s, w2q, w2s) = st["q3"], st["q3w"]
+        pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, o["qa"], w1q, o["off"], 2 * I4, H,
+                             a_scale=o["sa"], b_scale=w1s, out_dtype=pqm.OUT_BF16, out=o["c"])
+        pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, o["qd"], w2q, o["off"], H, I4,
+                             a_scale=o["sd"], b_scale=w2s, out_dtype=pqm.OUT_BF16, out=o["y"])
+
+    def r_q3_dequant(s):
+        o, (w1q, w1s, w2q, w2s) = st["q3"], st["q3w"]
+        prev = st.get("deq", {})
+        st["deq"] = dict(w1=pqm.dequantize(pqm.FMT_MXFP8, w1q, w1s, out=prev.get("w1")),
+                         w2=pqm.dequantize(pqm.FMT_MXFP8, w2q, w2s, out=prev.get("w2")),
+                         a=pqm.dequantize(pqm.FMT_MXFP8, o["qa"], o["sa"], out=prev.get("a")),
+                         d=pqm.dequantize(pqm.FMT_MXFP8, o["qd"], o["sd"], out=prev.get("d")))
+
+    def r_q3_bwd(s):
+        d, off = st["deq"], st["q3"]["off"]
+        # FC2: dD = dY . W2 (W2 [E, H, I], contraction over H); dW2 = dY^T D
+        pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_DGRAD, st["dY"], d["w2"], off, I4, H,
+                             out_dtype=pqm.OUT_BF16)
+        pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_WGRAD, st["dY"], d["d"], off, H, I4,
+                             out_dtype=pqm.OUT_FP32)
+        # FC1: dX = dC . W1 (W1 [E, 2I, H]); dW1 = dC^T A
+        pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_DGRAD, st["dC"], d["w1"], off, H, 2 * I4,
+                             out_dtype=pqm.OUT_BF16)
+        pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_WGRAD, st["dC"], d["a"], off, 2 * I4, H,
+                             out_dtype=pqm.OUT_FP32)
+
+    def r_ds_wquant(s):
+        st["dsw"] = moe_layer.quantize_expert_weights_nvfp4(st["W1d"], st["W2d"], I5, H5)
+
+    def r_ds_fwd(s):
+        st["ds"] = moe_layer.nvfp4_moe_forward(st["x5"], st["ids5"], st["prob5"], *st["dsw"],
+                                               E5, I5)
+
+    def r_ds_gemm(s):
+        o, (w1q, w1b, w1g, w2q, w2b, w2g) = st["ds"], st["dsw"]
+        pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, o["qa"], w1q, o["off"], 2 * I5, H5,
+                             a_scale=o["sba"], a_outer=o["sga"], b_scale=w1b, b_outer=w1g,
+                             b_rows_per_scale=2 * I5, out_dtype=pqm.OUT_BF16, out=o["c"])
+        pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, o["qd"], w2q, o["off"], H5, I5,
+                             a_scale=o["sbd"], a_outer=o["sgd"], b_scale=w2b, b_outer=w2g,
+                             b_rows_per_scale=H5, out_dtype=pqm.OUT_BF16, out=o["y"])
+
+    def r_ds_reconstruct(s):
+        o, (w1q, w1b, w1g, w2q, w2b, w2g) = st["ds"], st["dsw"]
+        prev = st.get("dsr", {})
+        st["dsr"] = dict(
+            a=pqm.dequantize(pqm.FMT_NVFP4, o["qa"], o["sba"], o["sga"], out=prev.get("a")),
+            w1=pqm.dequantize(pqm.FMT_NVFP4, w1q, w1b, w1g, rows_per_scale=2 * I5,
+                              out=prev.get("w1")),
+            w2=pqm.dequantize(pqm.FMT_NVFP4, w2q, w2b, w2g, rows_per_scale=H5,
+                              out=prev.get("w2")))
+
+    fns = {"mxfp8_quant": r_mxfp8, "nvfp4_token": r_nvfp4, "nvfp4_joint_w": r_joint,
+           "q3_wquant": r_q3_wquant, "q3_fwd": r_q3_fwd, "q3_gemm": r_q3_gemm,
+           "q3_dequant": r_q3_dequant, "q3_bwd": r_q3_bwd, "ds_wquant": r_ds_wquant,
+           "ds_fwd": r_ds_fwd, "ds_gemm": r_ds_gemm, "ds_reconstruct": r_ds_reconstruct}
+    deps = {"q3_fwd": ["q3_wquant"], "q3_gemm": ["q3_wquant", "q3_fwd"],
+            "q3_dequant": ["q3_wquant", "q3_fwd"], "q3_bwd": ["q3_wquant", "q3_fwd", "q3_dequant"],
+            "ds_fwd": ["ds_wquant"], "ds_gemm": ["ds_wquant", "ds_fwd"],
+            "ds_reconstruct": ["ds_wquant", "ds_fwd"]}
+    run = []
+    for r in sel:
+        for d in deps.get(r, []) + [r]:
+            if d not in run:
+                run.append(d)
+    run = [r for r in ALL_ROWS if r in run]
+
     stream = torch.cuda.current_stream(dev)
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-
-    state = {}
-
-    def row_mxfp8(s):
-        pqm.quantize_mxfp8(sets[s % len(sets)])
-
-    def row_nvfp4(s):
-        pqm.quantize_nvfp4_per_token(sets[s % len(sets)])
-
-    def row_joint(s):
-        pqm.quantize_nvfp4_per_token(w_joint, rows_per_scale=I2)
-
-    def row_layer(s):
-        w1q, w1s, _, _ = pqm.quantize_mxfp8(W1, colwise=False)
-        w2q, w2s, _, _ = pqm.quantize_mxfp8(W2, colwise=False)
-        off, src, slot = pqm.moe_route(ids, E)
-        qx, sx, _, _ = pqm.quantize_mxfp8(x4, colwise=False)
-        qa = pqm.moe_gather_rows(qx, src, K4)
-        sa = pqm.moe_gather_rows(sx, src, K4)
-        c = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, w1q, off, 2 * I4, H,
-                                 a_scale=sa, b_scale=w1s, out_dtype=pqm.OUT_BF16)
-        d = pqm.swiglu_prob(c, prob, src)
-        qd, sd, _, _ = pqm.quantize_mxfp8(d, colwise=False)
-        y = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qd, w2q, off, H, I4,
-                                 a_scale=sd, b_scale=w2s, out_dtype=pqm.OUT_BF16)
-        out = pqm.moe_combine(y, slot)
-        state.update(w1q=w1q, w1s=w1s, w2q=w2q, w2s=w2s, off=off, qa=qa, sa=sa, qd=qd, sd=sd,
-                     out=out)
-
-    def row_dequant(s):
-        st = state
-        state["w1d"] = pqm.dequantize(pqm.FMT_MXFP8, st["w1q"], st["w1s"])
-        state["w2d"] = pqm.dequantize(pqm.FMT_MXFP8, st["w2q"], st["w2s"])
-        state["ad"] = pqm.dequantize(pqm.FMT_MXFP8, st["qa"], st["sa"])
-        state["dd"] = pqm.dequantize(pqm.FMT_MXFP8, st["qd"], st["sd"])
-
-    def row_bwd(s):
-        st = state
-        off = st["off"]
-        # FC2: dD = dY . W2 (W2 [E, H, I]: contraction over H rows); dW2 = dY^T D
-        pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_DGRAD, dY, st["w2d"], off, I4, H,
-                             out_dtype=pqm.OUT_BF16)
-        pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_WGRAD, dY, st["dd"], off, H, I4,
-                             out_dtype=pqm.OUT_FP32)
-        # FC1: dX = dC . W1 (W1 [E, 2I, H]); dW1 = dC^T X
-        pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_DGRAD, dC, st["w1d"], off, H, 2 * I4,
-                             out_dtype=pqm.OUT_BF16)
-        pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_WGRAD, dC, st["ad"], off, 2 * I4, H,
-                             out_dtype=pqm.OUT_FP32)
-
-    rows = [("mxfp8_quant", row_mxfp8), ("nvfp4_token", row_nvfp4),
-            ("nvfp4_joint_w", row_joint), ("moe_mxfp8_fwd", row_layer),
-            ("dequant_bwd", row_dequant), ("bf16_bwd", row_bwd)]
-    rows = [(n, f) for n, f in rows if want(n)]
-    if any(n in ("dequant_bwd", "bf16_bwd") for n, _ in rows) and not want("moe_mxfp8_fwd"):
-        rows.insert(0, ("moe_mxfp8_fwd", row_layer))
-
-    timings = {n: [] for n, _ in rows}
+    timings = {n: [] for n in run}
+    pending = []
+    t0 = time.perf_counter()
     for step in range(args.warmup + args.steps):
         if step == args.warmup:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
         evs = []
-        for n, f in rows:
-            a, b = ev(), ev()
+        for n in run:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            f(step)
+            fns[n](step)
             b.record(stream)
             evs.append((n, a, b))
         if step >= args.warmup:
-            state.setdefault("_evs", []).append(evs)
+            pending.append(evs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for evs in state["_evs"]:
+    for evs in pending:
         for n, a, b in evs:
             timings[n].append(a.elapsed_time(b) * 1e-3)
 
+    # ------------------------------------------------------ figures
     comp = {}
     R2 = T2 * H
-    fl1 = 2.0 * M4 * (2 * I4) * H
-    fl2 = 2.0 * M4 * H * I4
+    fl_q3 = 2.0 * M4 * (2 * I4) * H + 2.0 * M4 * H * I4
+    fl_ds = 2.0 * M5 * (2 * I5) * H5 + 2.0 * M5 * H5 * I5
+
+    def hbm(c, byt, t):
+        c.update(bytes=byt, gbs=byt / t / 1e9, frac_hbm=byt / t / 1e9 / HBM_PEAK_GBS)
+
     for n, ts in timings.items():
+        if n not in sel:
+            continue
         t = float(np.mean(ts))
-        c = {"time_us": round(t * 1e6, 2)}
+        c = {"time_us": t * 1e6}
         if n == "mxfp8_quant":
-            byt = R2 * (2 + 2 * (1 + 1 / 32))
-            c.update(bytes=byt, gbs=byt / t / 1e9, frac_hbm=byt / t / 1e9 / HBM_PEAK_GBS)
+            hbm(c, R2 * (2 + 2 * (1 + 1 / 32)), t)
         elif n == "nvfp4_token":
-            byt = R2 * (2 + 0.5 + 1 / 16) + T2 * 4
-            c.update(bytes=byt, gbs=byt / t / 1e9, frac_hbm=byt / t / 1e9 / HBM_PEAK_GBS)
+            hbm(c, R2 * (2 + 0.5 + 1 / 16) + T2 * 4, t)
         elif n == "nvfp4_joint_w":
-            byt = E * I2 * H * (2 + 0.5 + 1 / 16) + E * 4
-            c.update(bytes=byt, gbs=byt / t / 1e9, frac_hbm=byt / t / 1e9 / HBM_PEAK_GBS)
-        elif n == "moe_mxfp8_fwd":
-            c.update(gemm_flop=fl1 + fl2, layer_tflops=(fl1 + fl2) / t / 1e12)
-        elif n == "bf16_bwd":
-            fl = 2 * (fl1 + fl2)
+            hbm(c, E * I2 * H * (2 + 0.5 + 1 / 16) + E * 4, t)
+        elif n == "q3_wquant":
+            hbm(c, (E * 2 * I4 * H + E * H * I4) * (2 + 1 + 1 / 32), t)
+        elif n in ("q3_fwd", "q3_gemm"):
+            c.update(flop=fl_q3, tflops=fl_q3 / t / 1e12, frac_fp8=fl_q3 / t / 1e12 / FP8_PEAK_TFLOPS)
+        elif n == "q3_dequant":
+            el = E * 2 * I4 * H + E * H * I4 + M4 * H + M4 * I4
+            hbm(c, el * (1 + 1 / 32 + 2), t)
+        elif n == "q3_bwd":
+            fl = 2 * fl_q3
             c.update(flop=fl, tflops=fl / t / 1e12, frac_bf16=fl / t / 1e12 / BF16_PEAK_TFLOPS)
+        elif n == "ds_wquant":
+            hbm(c, ((E5 + 1) * (2 * I5 * H5 + H5 * I5)) * (2 + 0.5 + 1 / 16), t)
+        elif n in ("ds_fwd", "ds_gemm"):
+            c.update(flop=fl_ds, tflops=fl_ds / t / 1e12,
+                     frac_bf16=fl_ds / t / 1e12 / BF16_PEAK_TFLOPS)
+        elif n == "ds_reconstruct":
+            el = M5 * H5 + (E5 + 1) * (2 * I5 * H5 + H5 * I5)
+            hbm(c, el * (0.5 + 1 / 16 + 2), t)
         for k, v in list(c.items()):
             if isinstance(v, float):
                 c[k] = round(v, 4)
@@ -206,9 +293,9 @@ def main():
 
     # ------------------------------------------------------ CPU baseline
     cpu = None
-    if not args.no_cpu_baseline and want("mxfp8_quant"):
+    if not args.no_cpu_baseline and "mxfp8_quant" in sel:
         import oracle
-        host = sets[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        host = st["sets"][0].view(torch.int16).cpu().numpy().view(np.uint16)
         oracle.build()
         reps, t_cpu, t_start = 0, 0.0, time.perf_counter()
         while reps < 10 and time.perf_counter() - t_start < 10.0:
@@ -219,12 +306,13 @@ def main():
         byt = R2 * (2 + 2 * (1 + 1 / 32))
         cpu = {"value": round(byt * reps / t_cpu / 1e9, 4), "unit": "GB/s",
                "cores": int(oracle.lib().pqo_omp_threads()), "kind": "oracle",
-               "sample": f"MXFP8 row+col quantize of the full 16384x2048 activation "
-                         f"set, {reps} repetitions ({t_cpu:.1f} s)"}
+               "sample": f"MXFP8 row+col quantize of the full 16384x2048 activation set, "
+                         f"{reps} repetitions ({t_cpu:.1f} s)"}
         log("cpu baseline", cpu)
 
     head = comp.get("mxfp8_quant", {})
     value = head.get("gbs")
+    gem = comp.get("q3_gemm", {})
     out = {
         "metric": "quantize HBM GB/s + MXFP8/NVFP4 MoE grouped-GEMM TFLOPS, 1 MI355X",
         "value": value,
@@ -239,9 +327,11 @@ def main():
         "dtype": "u8",
         "data": "synthetic",
         "config": {"workload": "MXFP8 row-wise + column-wise quantize of 16384 x 2048 bf16 "
-                               "activations (log-normal token scale, outlier channels); "
+                               "activations (log-normal token scale, outlier channels); the "
                                "step also runs every other hot-path row (components)",
                    "tokens": T2, "hidden": H},
+        "gemm_mxfp8_tflops": gem.get("tflops"),
+        "gemm_nvfp4_tflops": comp.get("ds_gemm", {}).get("tflops"),
         "roofline": {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4) if value else None,
                      "traffic": None, "kernel": "k_quantize_mxfp8<true,true>"},

@@ -223,28 +223,34 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,
 /*
  * Stable counting sort of token -> expert assignments.
  *   topk_ids  [tokens, k] int32 expert ids in [0, num_experts)   (device)
- *   offsets   [num_experts + 1] int64: expert e owns positions
- *             offsets[e] .. offsets[e+1]-1                       (device)
- *   src_row   [tokens * k] int32: flat assignment index t*k + j stored at
- *             each position; within an expert, flat order is kept (device)
- *   slot      [tokens, k] int32: position of assignment (t, j)  (device)
+ *   shared_expert  0, or 1 to append one more group (index num_experts)
+ *             holding every token in order, for an always-active shared
+ *             expert run through the same grouped GEMM
+ *   offsets   [num_experts + 1 + shared_expert] int64: group e owns
+ *             positions offsets[e] .. offsets[e+1]-1              (device)
+ *   src_row   [tokens * (k + shared_expert)] int32: the assignment index
+ *             t*k + j stored at each position (tokens*k + t for the shared
+ *             expert's row of token t); within an expert, flat order is
+ *             kept                                               (device)
+ *   token     [same] int32: the token of each position           (device)
+ *   slot      [tokens, k] int32: position of assignment (t, j)   (device)
  *   workspace >= pqm_moe_route_workspace(...) bytes, 4-byte aligned.
- * num_experts <= 4096, tokens * k < 2^31.  Ids outside [0, num_experts)
- * are undefined behaviour.
+ * num_experts <= 4096, tokens * (k + 1) < 2^31.  Ids outside
+ * [0, num_experts) are undefined behaviour.
  */
 size_t pqm_moe_route_workspace(int64_t tokens, int64_t k, int64_t num_experts);
 pqm_status pqm_moe_route(const int32_t *topk_ids, int64_t tokens, int64_t k,
-                         int64_t num_experts, int64_t *offsets, int32_t *src_row,
-                         int32_t *slot, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+                         int64_t num_experts, int shared_expert, int64_t *offsets,
+                         int32_t *src_row, int32_t *token, int32_t *slot,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Row gather: out row i = src row (index[i] / divisor), rows of row_bytes
  * bytes (quantized data, scale bytes or FP32 token scales).  With
- * index = src_row from pqm_moe_route and divisor = k this places each
- * token's already-quantized row at its expert-sorted positions: per-row
- * blocks run along K, so gathering quantized rows gives the same bytes as
- * quantizing gathered rows.  index entries must be < src_rows * divisor.
+ * index = token from pqm_moe_route (divisor 1) this places each token's
+ * already-quantized row at its expert-sorted positions: per-row blocks run
+ * along K, so gathering quantized rows gives the same bytes as quantizing
+ * gathered rows.  index entries must be < src_rows * divisor.
  */
 pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_bytes,
                                const int32_t *index, int64_t n, int64_t divisor,
@@ -254,7 +260,9 @@ pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_by
  * Weighted SwiGLU: d[m, j] = bf16( silu(g) * u * p ) with g = c[m, j],
  * u = c[m, inter + j] (c = [gate | up], bf16 [rows, 2*inter]),
  * silu(z) = z / (1 + exp(-z)), p = prob[src[m]] (prob binary32 indexed by
- * flat assignment; src may be NULL to index prob by m).  Binary32 math.
+ * assignment, i.e. src_row from pqm_moe_route; with a shared expert prob
+ * holds tokens*k + tokens entries, the last tokens of them 1.0; src may be
+ * NULL to index prob by m).  Binary32 math.
  * d bf16 [rows, inter]; inter % 8 == 0.
  */
 pqm_status pqm_swiglu_prob(const uint16_t *c, const float *prob, const int32_t *src,

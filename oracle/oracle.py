@@ -258,13 +258,15 @@ def grouped_gemm_wgrad(dy: np.ndarray, x: np.ndarray,
 # outputs are reduced in high precision)
 # --------------------------------------------------------------------------
 
-def route(topk_ids: np.ndarray, num_experts: int):
+def route(topk_ids: np.ndarray, num_experts: int, shared_expert: bool = False):
     """Counting sort of token->expert assignments into a contiguous buffer.
 
     topk_ids: [T, k] expert ids.  Assignment (t, j) has flat index t*k + j.
-    Returns (offsets[G+1] int64, src_row[T*k] int64 = flat index of the
+    Returns (offsets[G+1] int64, src_row[M] int64 = flat index of the
     assignment stored at each position, slot[T, k] int64 = position of each
-    assignment).  Within an expert, assignments keep their flat order.
+    assignment).  Within an expert, assignments keep their flat order.  With
+    shared_expert, one more group of T rows follows (row T*k + t holds token
+    t, flat index T*k + t) and G = num_experts + 1.
     """
     ids = np.asarray(topk_ids, np.int64)
     T, k = ids.shape
@@ -281,7 +283,17 @@ def route(topk_ids: np.ndarray, num_experts: int):
         src_row[fill[e]] = i
         slot[i] = fill[e]
         fill[e] += 1
+    if shared_expert:
+        offsets = np.concatenate([offsets, [T * k + T]])
+        src_row = np.concatenate([src_row, T * k + np.arange(T)])
     return offsets, src_row, slot.reshape(T, k)
+
+
+def route_token(src_row: np.ndarray, T: int, k: int) -> np.ndarray:
+    """Token of each stored row: t for assignment t*k + j, and t for the
+    shared expert's row T*k + t."""
+    src_row = np.asarray(src_row, np.int64)
+    return np.where(src_row < T * k, src_row // k, src_row - T * k)
 
 
 def silu(z: np.ndarray) -> np.ndarray:

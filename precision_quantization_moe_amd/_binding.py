@@ -37,7 +37,7 @@ SIGNATURES = {
     "pqm_dequantize": ([I32, P, P, P, I64, I64, I64, P, P], I32),
     "pqm_moe_grouped_gemm": ([I32, I32, P, P, P, P, P, P, I64, P, I64, I64, I64, I64,
                               P, I32, P, SZ, P], I32),
-    "pqm_moe_route": ([P, I64, I64, I64, P, P, P, P, SZ, P], I32),
+    "pqm_moe_route": ([P, I64, I64, I64, I32, P, P, P, P, P, SZ, P], I32),
     "pqm_moe_route_workspace": ([I64, I64, I64], SZ),
     "pqm_moe_gather_rows": ([P, I64, I64, P, I64, I64, P, P], I32),
     "pqm_swiglu_prob": ([P, P, P, I64, I64, P, P], I32),
@@ -87,36 +87,43 @@ def _bf16_2d(x: torch.Tensor) -> torch.Tensor:
 
 # ---------------------------------------------------------------- quantizers
 
-def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = True):
+def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, out=None):
     """MXFP8 row-wise and/or column-wise copies of a bf16 [R, C] tensor.
     Returns (q[R, C], s[R, C/32], qT[C, R], sT[C, R/32]) as uint8 tensors,
-    None for a copy that was not requested."""
+    None for a copy that was not requested.  `out` may pass that tuple
+    preallocated."""
     x = _bf16_2d(x)
     R, C = x.shape
     dev = x.device
     u8 = dict(dtype=torch.uint8, device=dev)
-    q = torch.empty((R, C), **u8) if rowwise else None
-    s = torch.empty((R, C // 32), **u8) if rowwise else None
-    qT = torch.empty((C, R), **u8) if colwise else None
-    sT = torch.empty((C, R // 32), **u8) if colwise else None
+    if out is not None:
+        q, s, qT, sT = out
+    else:
+        q = torch.empty((R, C), **u8) if rowwise else None
+        s = torch.empty((R, C // 32), **u8) if rowwise else None
+        qT = torch.empty((C, R), **u8) if colwise else None
+        sT = torch.empty((C, R // 32), **u8) if colwise else None
     _check(lib().pqm_quantize_mxfp8(_ptr(x), R, C, x.stride(0), _ptr(q), _ptr(s),
                                     _ptr(qT), _ptr(sT), _stream(dev)),
            "pqm_quantize_mxfp8")
     return q, s, qT, sT
 
 
-def quantize_nvfp4_per_token(x: torch.Tensor, rows_per_scale: int = 1):
+def quantize_nvfp4_per_token(x: torch.Tensor, rows_per_scale: int = 1, out=None):
     """NVFP4 with one FP32 outer scale per rows_per_scale rows (1 = per
     token; an expert's [gate; up] row count = joint gate/up scale).
     Returns (q[R, C/2] uint8, s_block[R, C/16] uint8,
-    s_outer[R/rows_per_scale] float32)."""
+    s_outer[R/rows_per_scale] float32); `out` may pass them preallocated."""
     x = _bf16_2d(x)
     R, C = x.shape
     dev = x.device
-    q = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
-    sb = torch.empty((R, C // 16), dtype=torch.uint8, device=dev)
-    n_scales = R // rows_per_scale if rows_per_scale > 0 else 0
-    sg = torch.empty((n_scales,), dtype=torch.float32, device=dev)
+    if out is not None:
+        q, sb, sg = out
+    else:
+        q = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+        sb = torch.empty((R, C // 16), dtype=torch.uint8, device=dev)
+        n_scales = R // rows_per_scale if rows_per_scale > 0 else 0
+        sg = torch.empty((n_scales,), dtype=torch.float32, device=dev)
     L = lib()
     ws_bytes = L.pqm_quantize_nvfp4_workspace(R, C, rows_per_scale)
     ws = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=dev)
@@ -128,11 +135,11 @@ def quantize_nvfp4_per_token(x: torch.Tensor, rows_per_scale: int = 1):
 
 
 def dequantize(fmt: int, q: torch.Tensor, s_block: torch.Tensor,
-               s_outer: torch.Tensor | None = None, rows_per_scale: int = 1):
+               s_outer: torch.Tensor | None = None, rows_per_scale: int = 1, out=None):
     """bf16 [R, C] reconstruction of an MXFP8 or NVFP4 tensor."""
     R = q.shape[0]
     C = q.shape[1] * (2 if fmt == FMT_NVFP4 else 1)
-    y = torch.empty((R, C), dtype=torch.bfloat16, device=q.device)
+    y = out if out is not None else torch.empty((R, C), dtype=torch.bfloat16, device=q.device)
     _check(lib().pqm_dequantize(fmt, _ptr(q), _ptr(s_block), _ptr(s_outer), R, C,
                                 rows_per_scale, _ptr(y), _stream(q.device)),
            "pqm_dequantize")
@@ -163,20 +170,25 @@ def moe_grouped_gemm(fmt: int, kind: int, a, b, offsets: torch.Tensor, N: int, K
 
 # ---------------------------------------------------------------- MoE glue
 
-def moe_route(topk_ids: torch.Tensor, num_experts: int):
+def moe_route(topk_ids: torch.Tensor, num_experts: int, shared_expert: bool = False):
     """Counting sort of assignments by expert.  topk_ids int32 [T, k].
-    Returns (offsets int64 [E+1], src_row int32 [T*k], slot int32 [T, k])."""
+    Returns (offsets int64 [E+1(+1)], src_row int32 [M], token int32 [M],
+    slot int32 [T, k]) with M = T*k (+T with a shared expert group)."""
     T, k = topk_ids.shape
     dev = topk_ids.device
-    offsets = torch.empty((num_experts + 1,), dtype=torch.int64, device=dev)
-    src = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    sh = 1 if shared_expert else 0
+    M = T * k + sh * T
+    offsets = torch.empty((num_experts + 1 + sh,), dtype=torch.int64, device=dev)
+    src = torch.empty((M,), dtype=torch.int32, device=dev)
+    tok = torch.empty((M,), dtype=torch.int32, device=dev)
     slot = torch.empty((T, k), dtype=torch.int32, device=dev)
     L = lib()
     ws_bytes = L.pqm_moe_route_workspace(T, k, num_experts)
     ws = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=dev)
-    _check(L.pqm_moe_route(_ptr(topk_ids), T, k, num_experts, _ptr(offsets), _ptr(src),
-                           _ptr(slot), _ptr(ws), ws_bytes, _stream(dev)), "pqm_moe_route")
-    return offsets, src, slot
+    _check(L.pqm_moe_route(_ptr(topk_ids), T, k, num_experts, sh, _ptr(offsets), _ptr(src),
+                           _ptr(tok), _ptr(slot), _ptr(ws), ws_bytes, _stream(dev)),
+           "pqm_moe_route")
+    return offsets, src, tok, slot
 
 
 def moe_gather_rows(src: torch.Tensor, index: torch.Tensor, divisor: int = 1):

@@ -151,11 +151,13 @@ __device__ __forceinline__ v8i frag_fp8(const uint8_t *lds, int row, int s) {
   return r;
 }
 
+// Write one 32x32 accumulator tile (rows row0 + rbase .., cols n0 + cbase ..),
+// optionally scaled in binary32 by alpha_row[row] and alpha_col(col).
 template <bool OUT_F32>
 __device__ __forceinline__ void store_acc(const v16f &acc, void *out, int64_t ldo, int64_t row0,
                                           int64_t row_end, int64_t n0, int64_t N, int rbase,
-                                          int cbase, float alpha_row_dummy) {
-  (void)alpha_row_dummy;
+                                          int cbase, const float *alpha_row = nullptr,
+                                          float alpha_col = 1.0f) {
   const int lane = threadIdx.x & 63;
   const int64_t col = n0 + cbase + (lane & 31);
   if (col >= N) return;
@@ -163,10 +165,15 @@ __device__ __forceinline__ void store_acc(const v16f &acc, void *out, int64_t ld
   for (int i = 0; i < 16; ++i) {
     const int64_t row = row0 + rbase + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
     if (row < row_end) {
+      float v = acc[i];
+      // alpha_a * alpha_b is exact in binary64; one scaling of the
+      // accumulator avoids an intermediate binary32 overflow (a bf16-max
+      // token has alpha_a near 2^116)
+      if (alpha_row) v = (float)((double)v * ((double)alpha_row[row] * (double)alpha_col));
       if (OUT_F32)
-        static_cast<float *>(out)[row * ldo + col] = acc[i];
+        static_cast<float *>(out)[row * ldo + col] = v;
       else
-        static_cast<uint16_t *>(out)[row * ldo + col] = (uint16_t)f32_to_bf16_rne(acc[i]);
+        static_cast<uint16_t *>(out)[row * ldo + col] = (uint16_t)f32_to_bf16_rne(v);
     }
   }
 }
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(256) void k_gemm_mxfp8(
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
-                         wn * 64 + 32 * j, 1.0f);
+                         wn * 64 + 32 * j);
 }
 
 // ------------------------------------------------------------------- BF16
@@ -360,7 +367,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_rows(
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
-                         wn * 64 + 32 * j, 1.0f);
+                         wn * 64 + 32 * j);
 }
 
 // WGRAD: Y_g[n, k] = sum_{m in g} A[m, n] B[m, k]; A [M, N], B [M, K], both
@@ -426,8 +433,151 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_wgrad(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      store_acc<OUT_F32>(acc[i][j], o, K, n0, N, k0, K, wm * 64 + 32 * i, wn * 64 + 32 * j,
-                         1.0f);
+      store_acc<OUT_F32>(acc[i][j], o, K, n0, N, k0, K, wm * 64 + 32 * i, wn * 64 + 32 * j);
+}
+
+// ------------------------------------------------------------------ NVFP4
+//
+// E2M1 x E4M3 (q * s_b) has at most 2 + 4 significant bits and lies in
+// [2^-10, 2688], so it is exact in fp16; the matrix cores then see the exact
+// block-scaled operand values, and the FP32 outer scales (per token for A,
+// per expert tensor for B) multiply the binary32 accumulator.  Per-16 E4M3
+// scales are not a CDNA4 matrix-core scale format, hence the decode while
+// staging into LDS.
+//
+// Decode of one 32-bit word (8 nibbles, element 2j in the low nibble of
+// byte j): the magnitude codes are looked up as the high byte of the fp16
+// value in an 8-entry byte table with v_perm_b32 (four lookups per
+// instruction), the sign bit is ORed in, the bytes are interleaved into
+// fp16 pairs and multiplied by s_b with one packed fp16 multiply per pair.
+
+typedef _Float16 pqm_v2h __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void nvfp4_word_to_f16(uint32_t w, pqm_v2h sb2, uint32_t out[4]) {
+  const uint32_t LUT_LO = 0x3E3C3800u, LUT_HI = 0x46444240u;  // 0,.5,1,1.5 | 2,3,4,6
+  const uint32_t hlo = __builtin_amdgcn_perm(LUT_HI, LUT_LO, w & 0x07070707u) |
+                       ((w & 0x08080808u) << 4);  // elements 0,2,4,6
+  const uint32_t hhi = __builtin_amdgcn_perm(LUT_HI, LUT_LO, (w >> 4) & 0x07070707u) |
+                       (w & 0x80808080u);         // elements 1,3,5,7
+  const uint32_t sel[4] = {0x040C000Cu, 0x050C010Cu, 0x060C020Cu, 0x070C030Cu};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t pr = __builtin_amdgcn_perm(hhi, hlo, sel[j]);
+    const pqm_v2h v = __builtin_bit_cast(pqm_v2h, pr) * sb2;  // exact
+    out[j] = __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// Stage a 128-row x 64-element NVFP4 operand tile as fp16 [row][k] in LDS.
+// Lane t owns row t/2, elements 32 (t%2) .. +31 of the step: 16 bytes of
+// packed data and 2 scale bytes.
+struct Nvfp4Loader {
+  uint4 v;
+  uint32_t sc;  // two E4M3 bytes
+  __device__ void load(const uint8_t *__restrict__ q, const uint8_t *__restrict__ s,
+                       int64_t rows, int64_t k0, int64_t K) {
+    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const int64_t e = k0 + 32 * h;
+    v = make_uint4(0, 0, 0, 0);
+    sc = 0;
+    if (r < rows && e < K) {
+      const uint8_t *qr = q + r * (K / 2) + e / 2;
+      if (e + 32 <= K) {
+        v = *reinterpret_cast<const uint4 *>(qr);
+        sc = (uint32_t)s[r * (K / 16) + e / 16] | ((uint32_t)s[r * (K / 16) + e / 16 + 1] << 8);
+      } else {  // K % 16 == 0: a 16-element remainder
+        const uint2 u = *reinterpret_cast<const uint2 *>(qr);
+        v.x = u.x;
+        v.y = u.y;
+        sc = (uint32_t)s[r * (K / 16) + e / 16];
+      }
+    }
+  }
+  __device__ void store(uint8_t *lds) const {
+    const int r = threadIdx.x >> 1, h = threadIdx.x & 1;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 sbh = (_Float16)e4m3_value((sc >> (8 * (i >> 1))) & 0x7Fu);
+      const pqm_v2h sb2 = {sbh, sbh};
+      nvfp4_word_to_f16(w[i], sb2, o + 4 * i);
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(lds + r * GT_PITCH + 64 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+  }
+};
+
+__device__ __forceinline__ v8h frag_f16(const uint8_t *lds, int row, int s) {
+  const int lane = threadIdx.x & 63;
+  const uint4 v = *reinterpret_cast<const uint4 *>(lds + row * GT_PITCH + 32 * s +
+                                                   16 * (lane >> 5));
+  return __builtin_bit_cast(v8h, v);
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void k_gemm_nvfp4(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const float *__restrict__ Ao, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    void *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lA[GT_M * GT_PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t lB[GT_N * GT_PITCH];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile(offsets, G, ntn, ti, sh)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t rows_a = ti.row_end - ti.row0;
+  const int64_t rows_b = N - ti.n0;
+  const uint8_t *Aq = A + ti.row0 * (K / 2), *Asb = As + ti.row0 * (K / 16);
+  const uint8_t *Bq = B + (ti.g * N + ti.n0) * (K / 2), *Bsb = Bs + (ti.g * N + ti.n0) * (K / 16);
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  Nvfp4Loader la, lb;
+  la.load(Aq, Asb, rows_a, 0, K);
+  lb.load(Bq, Bsb, rows_b, 0, K);
+  const int nk = (int)((K + 63) / 64);
+  for (int kt = 0; kt < nk; ++kt) {
+    la.store(lA);
+    lb.store(lB);
+    __syncthreads();
+    if (kt + 1 < nk) {
+      la.load(Aq, Asb, rows_a, (int64_t)(kt + 1) * 64, K);
+      lb.load(Bq, Bsb, rows_b, (int64_t)(kt + 1) * 64, K);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v8h fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = frag_f16(lA, wm * 64 + 32 * i + (lane & 31), s);
+        fb[i] = frag_f16(lB, wn * 64 + 32 * i + (lane & 31), s);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t col = ti.n0 + wn * 64 + 32 * j + (lane & 31);
+    const float ab = col < N ? Bo[(ti.g * N + col) / b_rps] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
+                         wn * 64 + 32 * j, Ao, ab);
+  }
 }
 
 // ------------------------------------------------------------------ launch
@@ -439,9 +589,6 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
                                const float *b_outer, int64_t b_rows_per_scale,
                                const int64_t *offsets, int64_t G, int64_t M, int64_t N,
                                int64_t K, void *out, int out_fp32, hipStream_t st) {
-  (void)a_outer;
-  (void)b_outer;
-  (void)b_rows_per_scale;
   if (G == 0 || N == 0) return hipSuccess;
   if (kind == 2) {  // WGRAD (bf16)
     if (K == 0) return hipSuccess;
@@ -490,7 +637,17 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     }
     return hipGetLastError();
   }
-  return hipErrorNotSupported;  // NVFP4 path: see the NVFP4 kernel below
+  if (fmt == 2) {
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, dim3(256), 0, st, A, a_scale, a_outer, B,
+                         b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out);
+    else
+      hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, dim3(256), 0, st, A, a_scale, a_outer, B,
+                         b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out);
+    return hipGetLastError();
+  }
+  return hipErrorNotSupported;
 }
 
 }  // namespace pqm

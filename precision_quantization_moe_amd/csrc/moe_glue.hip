@@ -32,9 +32,12 @@ __global__ __launch_bounds__(256) void k_route_hist(const int32_t *__restrict__ 
 }
 
 // One workgroup: offsets (exclusive scan of expert totals) and, in place,
-// the start position of every (chunk, expert) pair.
+// the start position of every (chunk, expert) pair.  With a shared expert,
+// offsets[E+1] closes one more group of `shared_rows` rows after the routed
+// ones.
 __global__ __launch_bounds__(256) void k_route_scan(int32_t *__restrict__ counts,
                                                     int64_t nchunks, int64_t E,
+                                                    int64_t shared_rows,
                                                     int64_t *__restrict__ offsets) {
   extern __shared__ int64_t tot[];
   for (int64_t e = threadIdx.x; e < E; e += 256) {
@@ -52,6 +55,7 @@ __global__ __launch_bounds__(256) void k_route_scan(int32_t *__restrict__ counts
       run += t;
     }
     offsets[E] = run;
+    if (shared_rows > 0) offsets[E + 1] = run + shared_rows;
   }
   __syncthreads();
   for (int64_t e = threadIdx.x; e < E; e += 256) {
@@ -67,9 +71,10 @@ __global__ __launch_bounds__(256) void k_route_scan(int32_t *__restrict__ counts
 // Scatter each chunk in flat order: position = start of (chunk, expert) +
 // number of earlier assignments of the same expert in the chunk.
 __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict__ ids,
-                                                       int64_t n, int64_t E,
+                                                       int64_t n, int64_t E, int64_t k,
                                                        const int32_t *__restrict__ start,
                                                        int32_t *__restrict__ src_row,
+                                                       int32_t *__restrict__ token,
                                                        int32_t *__restrict__ slot) {
   extern __shared__ int32_t sh[];
   int32_t *run = sh;          // [E]
@@ -87,6 +92,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
       for (int j = 0; j < (int)threadIdx.x; ++j) rank += (round_ids[j] == e) ? 1 : 0;
       const int32_t pos = run[e] + rank;
       src_row[pos] = (int32_t)a;
+      token[pos] = (int32_t)(a / k);
       slot[a] = pos;
     }
     __syncthreads();
@@ -101,8 +107,19 @@ size_t route_workspace_bytes(int64_t T, int64_t k, int64_t E) {
   return (size_t)(nchunks * E) * sizeof(int32_t);
 }
 
-hipError_t launch_route(const int32_t *ids, int64_t T, int64_t k, int64_t E, int64_t *offsets,
-                        int32_t *src_row, int32_t *slot, void *ws, hipStream_t st) {
+// The shared expert's rows: row n + t is token t (assignment index n + t).
+__global__ void k_route_shared(int64_t n, int64_t T, int32_t *__restrict__ src_row,
+                               int32_t *__restrict__ token) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < T) {
+    src_row[n + t] = (int32_t)(n + t);
+    token[n + t] = (int32_t)t;
+  }
+}
+
+hipError_t launch_route(const int32_t *ids, int64_t T, int64_t k, int64_t E, int shared,
+                        int64_t *offsets, int32_t *src_row, int32_t *token, int32_t *slot,
+                        void *ws, hipStream_t st) {
   const int64_t n = T * k;
   const int64_t nchunks = (n + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
   int32_t *counts = static_cast<int32_t *>(ws);
@@ -110,10 +127,14 @@ hipError_t launch_route(const int32_t *ids, int64_t T, int64_t k, int64_t E, int
     hipLaunchKernelGGL(k_route_hist, dim3((unsigned)nchunks), dim3(256), E * sizeof(int32_t),
                        st, ids, n, E, counts);
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), E * sizeof(int64_t), st, counts,
-                     nchunks, E, offsets);
+                     nchunks, E, shared ? T : (int64_t)0, offsets);
   if (nchunks > 0)
     hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nchunks), dim3(256),
-                       (E + 256) * sizeof(int32_t), st, ids, n, E, counts, src_row, slot);
+                       (E + 256) * sizeof(int32_t), st, ids, n, E, k, counts, src_row, token,
+                       slot);
+  if (shared && T > 0)
+    hipLaunchKernelGGL(k_route_shared, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, n,
+                       T, src_row, token);
   return hipGetLastError();
 }
 
@@ -258,18 +279,20 @@ size_t pqm_moe_route_workspace(int64_t tokens, int64_t k, int64_t num_experts) {
 }
 
 pqm_status pqm_moe_route(const int32_t *topk_ids, int64_t tokens, int64_t k,
-                         int64_t num_experts, int64_t *offsets, int32_t *src_row,
-                         int32_t *slot, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         int64_t num_experts, int shared_expert, int64_t *offsets,
+                         int32_t *src_row, int32_t *token, int32_t *slot, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
   if (tokens < 0 || k < 1 || num_experts < 1 || num_experts > 4096) return PQM_ERR_SHAPE;
-  if (tokens * k > (int64_t)0x7FFFFFFF) return PQM_ERR_SHAPE;
+  if (tokens * (k + 1) > (int64_t)0x7FFFFFFF) return PQM_ERR_SHAPE;
   if (!offsets) return PQM_ERR_NULL;
-  if (tokens > 0 && (!topk_ids || !src_row || !slot || !workspace)) return PQM_ERR_NULL;
+  if (shared_expert != 0 && shared_expert != 1) return PQM_ERR_ENUM;
+  if (tokens > 0 && (!topk_ids || !src_row || !token || !slot || !workspace))
+    return PQM_ERR_NULL;
   if (workspace_bytes < pqm::route_workspace_bytes(tokens, k, num_experts))
     return PQM_ERR_WORKSPACE;
   if (!al(offsets, 8) || (workspace && !al(workspace, 4))) return PQM_ERR_ALIGN;
-  return st_of(pqm::launch_route(topk_ids, tokens, k, num_experts, offsets, src_row, slot,
-                                 workspace, stream));
+  return st_of(pqm::launch_route(topk_ids, tokens, k, num_experts, shared_expert, offsets,
+                                 src_row, token, slot, workspace, stream));
 }
 
 pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_bytes,

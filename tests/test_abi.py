@@ -110,9 +110,11 @@ def test_grouped_gemm_validation():
 
 def test_glue_validation():
     L = pqm.lib()
-    assert L.pqm_moe_route(A16, 8, 0, 4, A16, A16, A16, A16, 1 << 20, None) == 2
-    assert L.pqm_moe_route(A16, 8, 2, 5000, A16, A16, A16, A16, 1 << 20, None) == 2
-    assert L.pqm_moe_route(A16, 8, 2, 4, A16, A16, A16, A16, 0, None) == 5
+    assert L.pqm_moe_route(A16, 8, 0, 4, 0, A16, A16, A16, A16, A16, 1 << 20, None) == 2
+    assert L.pqm_moe_route(A16, 8, 2, 5000, 0, A16, A16, A16, A16, A16, 1 << 20, None) == 2
+    assert L.pqm_moe_route(A16, 8, 2, 4, 0, A16, A16, A16, A16, A16, 0, None) == 5
+    assert L.pqm_moe_route(A16, 8, 2, 4, 3, A16, A16, A16, A16, A16, 1 << 20, None) == 4
+    assert L.pqm_moe_route(A16, 8, 2, 4, 1, A16, A16, None, A16, A16, 1 << 20, None) == 1
     assert L.pqm_moe_route_workspace(8192, 8, 128) == 64 * 128 * 4
     assert L.pqm_moe_gather_rows(A16, 4, 16, A16, 4, 0, A16, None) == 2
     assert L.pqm_swiglu_prob(A16, A16, None, 4, 12, A16, None) == 2

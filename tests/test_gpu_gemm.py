@@ -2,10 +2,8 @@
 the same exactly-decoded operands.
 
 Bar: relative L2 <= 1e-3 on binary32 output, per row (a row whose oracle
-values overflow binary32 is excluded).  bf16 output is compared against the
-oracle's product rounded once to bf16, by the same per-row relative L2 (the
-binary32 accumulation differs only where a value straddles a bf16 rounding
-boundary, or is a near-cancellation far below the row's norm).
+values overflow binary32 is excluded).  bf16 output adds one rounding of
+at most 2^-9 relative per element to that bar.
 
 The oracle quantizes the operands itself from the same generated bf16 bytes
 (byte equality of the two quantizers is established separately)."""
@@ -85,12 +83,13 @@ def test_mxfp8_fprop_ragged(case):
 
 
 def test_mxfp8_fprop_bf16_out():
+    """bf16 output vs the binary64 product: the GEMM bar (1e-3) plus one
+    bf16 rounding of the output (at most 2^-9 relative per element)."""
     y, want = _mxfp8_case([64, 0, 100], 128, 256, seed=4, out_dtype=pqm.OUT_BF16)
     got = oracle.bf16_to_f64(host_u16(y))
-    ref = oracle.bf16_to_f64(oracle.f64_to_bf16(want))
-    d = bf16_ulp_diff(host_u16(y), oracle.f64_to_bf16(want))
-    assert (d == 0).mean() > 0.97          # almost all bytes equal
-    check_rows(got, ref, "mxfp8 bf16 out vs rounded oracle")
+    r = rel_l2_rows(got, want)
+    print(f"[gemm] mxfp8 bf16 out vs fp64: max row rel-L2 {r.max():.3e}", flush=True)
+    assert r.max() <= TOL + 2.0 ** -9
 
 
 def test_mxfp8_tiny_contract_expert_gemm():
@@ -196,3 +195,93 @@ def test_bf16_wgrad(sizes, N, K):
             assert not got[g].any()
         else:
             check_rows(got[g], want[g], f"bf16 wgrad group {g}")
+
+
+# ------------------------------------------------------------------ NVFP4
+
+def _nvfp4_case(sizes, N, K, seed, brps=None):
+    """A per-token NVFP4, B one outer scale per expert tensor (brps = N) or
+    per half (gate / up separately)."""
+    G = len(sizes)
+    M = int(sum(sizes))
+    brps = brps or N
+    x = wl.activations(max(M, 1), K, seed=seed)[:M]
+    w = wl.normal_bf16((G * N, K), std=0.01, seed=seed + 1)
+    off = _offsets(sizes)
+    qa, sa, ga = pqm.quantize_nvfp4_per_token(dev_bf16(x))
+    qb, sb, gb = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=brps)
+    y = pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, qa, qb, dev(off), N, K,
+                             a_scale=sa, a_outer=ga, b_scale=sb, b_outer=gb,
+                             b_rows_per_scale=brps)
+    torch.cuda.synchronize()
+    ra, rsa, rga = oracle.quantize_nvfp4(x)
+    rb, rsb, rgb = oracle.quantize_nvfp4(w, rows_per_group=brps)
+    want = oracle.grouped_gemm(oracle.decode_nvfp4(ra, rsa, rga),
+                               oracle.decode_nvfp4(rb, rsb, rgb, brps).reshape(G, N, K), off)
+    return y, want
+
+
+@pytest.mark.parametrize("case", [
+    ([0, 37, 128, 1, 300], 192, 320, None),
+    ([64, 0, 200], 128, 336, None),           # K % 64 == 16: remainder step
+    ([100, 60], 256, 512, 128),               # gate and up scaled separately
+])
+def test_nvfp4_fprop_ragged(case):
+    sizes, N, K, brps = case
+    y, want = _nvfp4_case(sizes, N, K, seed=21, brps=brps)
+    check_rows(host(y), want, f"nvfp4 {sizes} N={N} K={K}")
+
+
+def test_nvfp4_tiny_contract_expert_gemm():
+    x = wl.tiny_contract_tensor()
+    w = wl.normal_bf16((256, 256), std=0.02, seed=5)
+    off = np.array([0, 128], np.int64)
+    qa, sa, ga = pqm.quantize_nvfp4_per_token(dev_bf16(x))
+    qb, sb, gb = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=256)
+    y = pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, qa, qb, dev(off), 256, 256,
+                             a_scale=sa, a_outer=ga, b_scale=sb, b_outer=gb,
+                             b_rows_per_scale=256)
+    ra, rsa, rga = oracle.quantize_nvfp4(x)
+    rb, rsb, rgb = oracle.quantize_nvfp4(w, rows_per_group=256)
+    want = oracle.grouped_gemm(oracle.decode_nvfp4(ra, rsa, rga),
+                               oracle.decode_nvfp4(rb, rsb, rgb, 256)[None], off)
+    got = host(y)
+    assert not got[1].any()
+    check_rows(got, want, "nvfp4 tiny contract")
+
+
+def test_nvfp4_deepseek_gate_up_full_sampled():
+    """DeepSeek-V3 expert shape: 4096 tokens top-8 over 256 routed experts
+    (half uniform, half Zipf) plus the shared expert as group 256 with every
+    token; gate_up N = 4096, K = 7168; weights N(0, 0.01) drawn on the GPU
+    from a seeded generator, quantized with one outer scale per expert
+    (joint gate/up).  Sampled rows of sampled experts vs the oracle."""
+    T, E, k, H, N = 4096, 256, 8, 7168, 4096
+    ids = wl.uniform_plus_zipf_routing(T, E, k)
+    off_r, src, _ = oracle.route(ids, E)
+    M_r = T * k
+    off = np.concatenate([off_r, [M_r + T]]).astype(np.int64)
+    x = wl.activations(T, H, seed=5)
+    rows_tok = np.concatenate([src // k, np.arange(T)])
+    xg = x[rows_tok]
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    w = (torch.randn((E + 1) * N, H, generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+    qa, sa, ga = pqm.quantize_nvfp4_per_token(dev_bf16(xg))
+    qb, sb, gb = pqm.quantize_nvfp4_per_token(w, rows_per_scale=N)
+    y = pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, qa, qb, dev(off), N, H,
+                             a_scale=sa, a_outer=ga, b_scale=sb, b_outer=gb,
+                             b_rows_per_scale=N, out_dtype=pqm.OUT_FP32)
+    torch.cuda.synchronize()
+    yh = host(y)
+    rng = np.random.Generator(np.random.PCG64(23))
+    for e in [0, int(rng.integers(1, E)), E - 1, E]:        # E = the shared expert
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 4)]))
+        we = host_u16(w[e * N:(e + 1) * N])
+        ra, rsa, rga = oracle.quantize_nvfp4(xg[rows])
+        rb, rsb, rgb = oracle.quantize_nvfp4(we, rows_per_group=N)
+        want = oracle.decode_nvfp4(ra, rsa, rga) @ oracle.decode_nvfp4(rb, rsb, rgb, N).T
+        check_rows(yh[rows], want, f"deepseek fc1 expert {e} ({hi - lo} rows)")
+    del w, qb
