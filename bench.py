@@ -22,10 +22,17 @@ seeded input, with all inputs resident in HBM:
   ds_reconstruct    bf16 reconstruction of the forward operands (activations
                     and all 257 experts' weights) for the dequantized backward
 
-Quantizer inputs rotate over several buffer sets larger than the 256 MB
-Infinity Cache so their rate is HBM's.  Each row is timed with HIP events
-on the stream its kernels run on (torch's current stream); `value` is the
-MXFP8 quantizer's HBM rate (algorithmic bytes / kernel time).
+Not part of a step unless named in --rows:
+  hbm_copy          torch's device copy of 512 MiB: a plain copy kernel of
+                    known size whose FETCH_SIZE / WRITE_SIZE counter readings
+                    calibrate the counters read on the other kernels
+
+The two activation-quantizer rows launch their kernel --reps times per step,
+rotating over --sets input/output buffer sets (about 1 GB in all, well above
+the 256 MB Infinity Cache) so that their rate is HBM's; their time is per
+launch.  Each row is timed with HIP events on the stream its kernels run on
+(torch's current stream); `value` is the MXFP8 quantizer's HBM rate
+(algorithmic bytes / kernel time).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows a,b,...]
 """
@@ -48,6 +55,36 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA BF16 / FP16
 
 ALL_ROWS = ["mxfp8_quant", "nvfp4_token", "nvfp4_joint_w", "q3_wquant", "q3_fwd", "q3_gemm",
             "q3_dequant", "q3_bwd", "ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"]
+EXTRA_ROWS = ["hbm_copy"]
+COPY_BYTES = 512 << 20
+REPEAT_ROWS = ("mxfp8_quant", "nvfp4_token")
+
+# HBM bytes of one launch of the headline kernel, from two rocprofv3 counter
+# runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
+#   bench.py --rows mxfp8_quant,nvfp4_token,hbm_copy --steps 3 --warmup 1 --sets 3
+# each scaled by what the same counter reads on the 512 MiB device copy of the
+# hbm_copy row (FETCH_SIZE reads 0.5x the copied bytes, WRITE_SIZE 1.0x).
+# The figure belongs to the kernel source it was taken on: it is reported only
+# while the files hash to the values below.
+TRAFFIC = {
+    "kernel": "k_quantize_mxfp8<true,true>",
+    "fetch_kib": 32859.6, "fetch_scale": 2.0,
+    "write_kib": 74885.5, "write_scale": 1.0,
+    "sources": {
+        "precision_quantization_moe_amd/csrc/quantize_mxfp8.hip": "737e786d0a174de49a1acca43d8ed89a2790ee42895627165c7cca62cf4a84f8",
+        "precision_quantization_moe_amd/csrc/pqm_device.hpp": "3f33e8b180f1730621dcf94d4a0caa09ff663c01cb550f40856a5ecbee5832a2",
+    },
+}
+
+
+def measured_traffic():
+    import hashlib
+    for rel, want in TRAFFIC["sources"].items():
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != want:
+                return None
+    return (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"]
+            + TRAFFIC["write_kib"] * TRAFFIC["write_scale"]) * 1024.0
 
 
 def parse():
@@ -55,7 +92,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--sets", type=int, default=3, help="rotating quantizer input sets")
+    p.add_argument("--sets", type=int, default=8, help="rotating quantizer input sets")
+    p.add_argument("--reps", type=int, default=10,
+                   help="launches per step of the activation-quantizer rows")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--rows", default="all", help="comma list of rows (default all)")
     return p.parse_args()
@@ -79,7 +118,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs an MI355X GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    sel = ALL_ROWS if args.rows == "all" else [r for r in ALL_ROWS if r in args.rows.split(",")]
+    order = ALL_ROWS + EXTRA_ROWS
+    sel = ALL_ROWS if args.rows == "all" else [r for r in order if r in args.rows.split(",")]
     need = lambda *names: any(n in sel for n in names)
 
     def to_dev(a: np.ndarray):
@@ -124,6 +164,9 @@ def main():
         st["prob5"] = torch.cat([p5, torch.ones(T5, dtype=torch.float32, device=dev)])
         st["W1d"] = gpu_normal((E5 + 1) * 2 * I5, H5, 0.01, seed=11)
         st["W2d"] = gpu_normal((E5 + 1) * H5, I5, 0.01, seed=12)
+    if need("hbm_copy"):
+        st["cp_src"] = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        st["cp_dst"] = torch.empty_like(st["cp_src"])
     torch.cuda.synchronize()
     log("inputs ready")
 
@@ -137,13 +180,17 @@ def main():
     if need("nvfp4_joint_w"):
         st["jw_out"] = pqm.quantize_nvfp4_per_token(st["w_joint"], rows_per_scale=I2)
 
+    nset = args.sets
+
     def r_mxfp8(s):
-        k = s % len(st["sets"])
-        pqm.quantize_mxfp8(st["sets"][k], out=st["mx_out"][k])
+        for j in range(args.reps):
+            k = (s * args.reps + j) % nset
+            pqm.quantize_mxfp8(st["sets"][k], out=st["mx_out"][k])
 
     def r_nvfp4(s):
-        k = s % len(st["sets"])
-        pqm.quantize_nvfp4_per_token(st["sets"][k], out=st["nv_out"][k])
+        for j in range(args.reps):
+            k = (s * args.reps + j) % nset
+            pqm.quantize_nvfp4_per_token(st["sets"][k], out=st["nv_out"][k])
 
     def r_joint(s):
         pqm.quantize_nvfp4_per_token(st["w_joint"], rows_per_scale=I2, out=st["jw_out"])
@@ -209,7 +256,10 @@ def main():
             w2=pqm.dequantize(pqm.FMT_NVFP4, w2q, w2b, w2g, rows_per_scale=H5,
                               out=prev.get("w2")))
 
-    fns = {"mxfp8_quant": r_mxfp8, "nvfp4_token": r_nvfp4, "nvfp4_joint_w": r_joint,
+    def r_copy(s):
+        st["cp_dst"].copy_(st["cp_src"])
+
+    fns = {"hbm_copy": r_copy, "mxfp8_quant": r_mxfp8, "nvfp4_token": r_nvfp4, "nvfp4_joint_w": r_joint,
            "q3_wquant": r_q3_wquant, "q3_fwd": r_q3_fwd, "q3_gemm": r_q3_gemm,
            "q3_dequant": r_q3_dequant, "q3_bwd": r_q3_bwd, "ds_wquant": r_ds_wquant,
            "ds_fwd": r_ds_fwd, "ds_gemm": r_ds_gemm, "ds_reconstruct": r_ds_reconstruct}
@@ -222,7 +272,7 @@ def main():
         for d in deps.get(r, []) + [r]:
             if d not in run:
                 run.append(d)
-    run = [r for r in ALL_ROWS if r in run]
+    run = [r for r in order if r in run]
 
     stream = torch.cuda.current_stream(dev)
     timings = {n: [] for n in run}
@@ -259,7 +309,7 @@ def main():
     for n, ts in timings.items():
         if n not in sel:
             continue
-        t = float(np.mean(ts))
+        t = float(np.mean(ts)) / (args.reps if n in REPEAT_ROWS else 1)
         c = {"time_us": t * 1e6}
         if n == "mxfp8_quant":
             hbm(c, R2 * (2 + 2 * (1 + 1 / 32)), t)
@@ -285,6 +335,8 @@ def main():
         elif n == "ds_reconstruct":
             el = M5 * H5 + (E5 + 1) * (2 * I5 * H5 + H5 * I5)
             hbm(c, el * (0.5 + 1 / 16 + 2), t)
+        elif n == "hbm_copy":
+            hbm(c, 2 * COPY_BYTES, t)
         for k, v in list(c.items()):
             if isinstance(v, float):
                 c[k] = round(v, 4)
@@ -334,7 +386,7 @@ def main():
         "gemm_nvfp4_tflops": comp.get("ds_gemm", {}).get("tflops"),
         "roofline": {"bound": "hbm", "achieved": value, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(value / HBM_PEAK_GBS, 4) if value else None,
-                     "traffic": None, "kernel": "k_quantize_mxfp8<true,true>"},
+                     "traffic": measured_traffic(), "kernel": TRAFFIC["kernel"]},
         "cpu_baseline": cpu,
         "components": comp,
     }
