@@ -96,8 +96,9 @@ int pqm_abi_version(void);
  *   s_colT  [cols, rows/32]    E8M0 bytes                          (device)
  * Either output pair may be NULL to skip that copy, not both.
  * Requires cols % 32 == 0; rows % 32 == 0 when the column copy is asked
- * for; x, q_row, q_colT and ld 16-byte aligned (ld % 8 == 0); s_row and
- * s_colT 4-byte aligned.
+ * for; fewer than 2^31 tiles of 128 x 128 (PQM_ERR_SHAPE otherwise); x,
+ * q_row, q_colT and ld 16-byte aligned (ld % 8 == 0); s_row and s_colT
+ * 4-byte aligned (PQM_ERR_ALIGN otherwise).
  */
 pqm_status pqm_quantize_mxfp8(const uint16_t *x, int64_t rows, int64_t cols,
                               int64_t ld, uint8_t *q_row, uint8_t *s_row,
@@ -126,8 +127,9 @@ pqm_status pqm_quantize_mxfp8(const uint16_t *x, int64_t rows, int64_t cols,
  *   q        [rows, cols/2]  packed E2M1, element 2j in the low nibble
  *   s_block  [rows, cols/16] E4M3 bytes
  *   s_outer  [rows / rows_per_scale] binary32 decode scales s_g
- * Requires cols % 16 == 0, rows % rows_per_scale == 0, x and ld 16-byte
- * aligned.  When rows_per_scale > 1 the group maximum is reduced across
+ * Requires cols % 16 == 0, cols <= 16384, rows < 2^31, rows % rows_per_scale
+ * == 0, x and ld 16-byte aligned, q 8-byte aligned, s_outer 4-byte aligned
+ * (PQM_ERR_SHAPE / PQM_ERR_ALIGN otherwise).  When rows_per_scale > 1 the group maximum is reduced across
  * workgroups through `workspace` (device, >= pqm_quantize_nvfp4_workspace
  * bytes, 4-byte aligned; contents on entry are ignored); it may be NULL
  * when rows_per_scale == 1.

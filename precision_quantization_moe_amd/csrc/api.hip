@@ -69,9 +69,8 @@ pqm_status pqm_quantize_mxfp8(const uint16_t *x, int64_t rows, int64_t cols, int
   if (!row && !col) return PQM_ERR_NULL;
   if (row && (!q_row || !s_row)) return PQM_ERR_NULL;
   if (col && (!q_colT || !s_colT)) return PQM_ERR_NULL;
-  if (rows < 0 || cols < 0 || ld < cols || cols % 32) return PQM_ERR_SHAPE;
   if (col && rows % 32) return PQM_ERR_SHAPE;
-  if (rows / 128 >= 65535) return PQM_ERR_SHAPE;
+  if (((rows + 127) / 128) * ((cols + 127) / 128) >= ((int64_t)1 << 31)) return PQM_ERR_SHAPE;
   if (!aligned(x, 16) || ld % 8) return PQM_ERR_ALIGN;
   if (row && (!aligned(q_row, 16) || !aligned(s_row, 4))) return PQM_ERR_ALIGN;
   if (col && (!aligned(q_colT, 16) || !aligned(s_colT, 4))) return PQM_ERR_ALIGN;
@@ -92,7 +91,7 @@ pqm_status pqm_quantize_nvfp4_per_token(const uint16_t *x, int64_t rows, int64_t
   if (rows < 0 || cols < 0 || ld < cols || cols % 16 || rows_per_scale < 1)
     return PQM_ERR_SHAPE;
   if (rows % rows_per_scale) return PQM_ERR_SHAPE;
-  if (cols > pqm::nvfp4_max_cols()) return PQM_ERR_SHAPE;
+  if (cols > pqm::nvfp4_max_cols() || rows >= ((int64_t)1 << 31)) return PQM_ERR_SHAPE;
   if (rows > 0 && (!x || !q || !s_block || !s_outer)) return PQM_ERR_NULL;
   if (rows > 0 && (!aligned(x, 16) || ld % 8 || !aligned(q, 8))) return PQM_ERR_ALIGN;
   if (rows > 0 && !aligned(s_outer, 4)) return PQM_ERR_ALIGN;

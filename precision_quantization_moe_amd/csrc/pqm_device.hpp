@@ -47,18 +47,6 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
   return sign | (uint32_t)n;  // n == 128 is the smallest normal, bits 0x80
 }
 
-// Magnitude code (0..126) of the E4M3 value nearest v, for 0 <= v <= 448
-// given as binary32 holding the exact value.  Ties to even.
-__device__ __forceinline__ uint32_t e4m3_code_f32(float v) {
-  if (v < 0x1p-6f) {
-    // subnormal quantum 2^-9: v * 512 is exact; rint rounds ties to even
-    return (uint32_t)__builtin_rintf(v * 512.0f);
-  }
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFFu + ((u >> 20) & 1u);  // keep 3 mantissa bits, RNE
-  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
-}
-
 // Magnitude code (0..126) of the E4M3 value nearest q (q >= 0, binary64),
 // saturating at 448.  q is a correctly rounded quotient whose exact value
 // is either an E4M3 midpoint exactly or at least 2^-32 (relative) away from
@@ -94,24 +82,12 @@ __device__ __forceinline__ float e8m0_value(uint32_t b) {
 // maximum (amax = (1 + f/128) 2^(E-127)): the smallest e with
 // amax <= 448 * 2^e = 1.75 * 2^(8+e) is E - 127 - 8 + [f > 0x60], clamped
 // at e = -127; a zero or subnormal maximum gives e = -127.  Returns e + 127.
+// With f > 0x60 exactly when f + 0x1F carries into E, this is
+// max(0, ((amax_bits + 0x1F) >> 7) - 8); zero and subnormal maxima (E = 0)
+// land below 0.
 __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
-  int E = (int)(amax_bits >> 7);
-  int f = (int)(amax_bits & 0x7F);
-  if (E == 0) return 0u;
-  int b = E - 8 + (f > 0x60 ? 1 : 0);
-  return (uint32_t)(b < 0 ? 0 : b);
-}
-
-// 2^-(b-127) as binary32 for a scale byte b in [0, 247].
-__device__ __forceinline__ float mx_inv_scale(uint32_t b) {
-  return __uint_as_float((254u - b) << 23);
-}
-
-// E4M3 byte of a bf16 element (bits in the low 16 of w) divided by a
-// power-of-two scale whose inverse is inv (exact scaling).
-__device__ __forceinline__ uint32_t mx_encode(uint32_t bf16bits, float inv) {
-  float v = __uint_as_float((bf16bits & 0x7FFFu) << 16) * inv;
-  return e4m3_code_f32(v) | ((bf16bits >> 8) & 0x80u);
+  const int b = (int)((amax_bits + 0x1Fu) >> 7) - 8;
+  return (uint32_t)max(b, 0);
 }
 
 // NVFP4 block: thresholds for the E2M1 decisions.  The element with
@@ -156,17 +132,21 @@ __device__ __forceinline__ uint32_t e2m1_code(float a, const E2M1Thresholds &th)
 }
 
 // ---------------------------------------------------------------------
-// Hardware conversions.  Both were compared on gfx950 against the exact
-// rules: v_cvt_scalef32_pk_fp8_bf16 gives the nearest-even E4M3 of x/scale
-// for every bf16 x and power-of-two scales (the MXFP8 case); the E2M1
-// conversion v_cvt_scalef32_pk_fp4_f32 with scale 1.0 gives the
-// nearest-even, saturating, sign-keeping E2M1 of every binary32 input.
+// Hardware conversions, each compared on gfx950 against the exact rules:
+//  * v_cvt_scalef32_pk_fp8_bf16 with the scale operand given as the bits
+//    b << 23 (b an E8M0 byte 0..254; b = 0 is the pattern of +0.0f) gives the
+//    sign-keeping nearest-even E4M3 of x / 2^(b-127) for every bf16 x whose
+//    quotient is at most 448 in magnitude -- all 8.85 million such (x, b)
+//    cases, so the scale operand acts exactly as an E8M0 exponent, 2^-127
+//    included;
+//  * v_cvt_scalef32_pk_fp4_f32 with scale 1.0 gives the nearest-even,
+//    saturating, sign-keeping E2M1 of every binary32 input.
 
 typedef __bf16 pqm_v2bf __attribute__((ext_vector_type(2)));
 typedef short pqm_v2s __attribute__((ext_vector_type(2)));
 
-// Four E4M3 bytes of x/scale for the bf16 pairs w0, w1 (element order
-// w0.lo, w0.hi, w1.lo, w1.hi); scale = 2^e with e >= -126.
+// Four E4M3 bytes of x / 2^(b-127) for the bf16 pairs w0, w1 (element order
+// w0.lo, w0.hi, w1.lo, w1.hi); scale holds the bits b << 23 of an E8M0 byte b.
 __device__ __forceinline__ uint32_t cvt4_e4m3_bf16(uint32_t w0, uint32_t w1, float scale) {
   pqm_v2s r = {0, 0};
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(pqm_v2bf, w0), scale,
@@ -174,30 +154,6 @@ __device__ __forceinline__ uint32_t cvt4_e4m3_bf16(uint32_t w0, uint32_t w1, flo
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(pqm_v2bf, w1), scale,
                                                  true);
   return __builtin_bit_cast(uint32_t, r);
-}
-
-// Two E4M3 bytes (low 16 bits) of binary32 values holding exact values of
-// at most 8 significant bits, |v| <= 448.
-__device__ __forceinline__ uint32_t cvt2_e4m3_f32(float a, float b) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
-}
-
-// E4M3 bytes of four bf16 elements (pairs w0, w1) divided by 2^(sb - 127).
-// A scale byte of 0 (2^-127, a binary32 subnormal) takes the exact binary32
-// route: x * 2^127 is exact and has at most 8 significant bits.  That case
-// (blocks whose maximum is below 448 * 2^-126) is rare, so it sits behind a
-// wave-uniform branch and costs nothing when no lane of the wave needs it.
-__device__ __forceinline__ uint32_t mx_encode4(uint32_t w0, uint32_t w1, uint32_t sb) {
-  uint32_t out = cvt4_e4m3_bf16(w0, w1, __uint_as_float(sb << 23));
-  if (__builtin_amdgcn_ballot_w64(sb == 0) != 0) {
-    if (sb == 0) {
-      const float k = 0x1p127f;
-      const uint32_t lo = cvt2_e4m3_f32(bf16_lo_f32(w0) * k, bf16_hi_f32(w0) * k);
-      const uint32_t hi = cvt2_e4m3_f32(bf16_lo_f32(w1) * k, bf16_hi_f32(w1) * k);
-      out = lo | (hi << 16);
-    }
-  }
-  return out;
 }
 
 // Packed E2M1 nibbles of two binary32 values into byte `sel` of `old`.

@@ -6,7 +6,9 @@
 // Per-token scope: one wave owns one row.  The row is read once into
 // registers with 16-byte loads (one 1x16 block per lane per step), its
 // maximum is reduced across the wave, and all three outputs (packed E2M1,
-// E4M3 block scales, FP32 token scale) are written from registers.
+// E4M3 block scales, FP32 token scale) are written from registers.  Both
+// roundings run on binary32 brackets whose rare disagreements are settled by
+// the sign of A - 2688 s_g (see nvfp4_block); no per-element division.
 //
 // Group scope (one outer scale for rows_per_scale rows, e.g. an expert's
 // fused gate/up weight): a first kernel reduces each group's maximum into a
@@ -19,52 +21,137 @@
 
 namespace pqm {
 
-// Quantize one 1x16 block held as 8 words of bf16 pairs.  Returns 8 bytes
-// of packed nibbles (element 2j low) and the E4M3 scale byte in *sbc_out.
+// Row constants of the NVFP4 encoding (one wave per row, so all of these are
+// wave-uniform).
+struct Nvfp4Row {
+  float s_g;    // outer scale A / 2688, one correctly rounded division
+  float inv6;   // 1 / (6 s_g) rounded to binary32 (within 2^-24)
+  int dir;      // sign of A - 2688 s_g: +1, -1, or 0 when s_g is exact
+  bool fast;    // s_g normal and small enough for the bracketed paths
+};
+
+__device__ __forceinline__ Nvfp4Row nvfp4_row(float A) {
+  Nvfp4Row r;
+  r.s_g = __fdiv_rn(A, 2688.0f);
+  const float res = __builtin_fmaf(-2688.0f, r.s_g, A);  // exact sign of A - 2688 s_g
+  r.dir = res > 0.0f ? 1 : (res < 0.0f ? -1 : 0);
+  // s_g >= 2^-90 keeps d = s_b s_g >= 2^-99, so that d's trailing binary32
+  // part is normal; s_g <= 2^116 keeps d and 1/d normal
+  r.fast = r.s_g >= 0x1p-90f && r.s_g <= 0x1p116f;
+  r.inv6 = r.fast ? (float)(1.0 / (6.0 * (double)r.s_g)) : 0.0f;
+  return r;
+}
+
+// Magnitude code (0..126) of the E4M3 value nearest v >= 0 (binary32),
+// ties to even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_code_f32_sat(float v) {
+  uint32_t c;
+  if (v < 0x1p-6f) {
+    c = (uint32_t)__builtin_rintf(v * 512.0f);  // subnormal quantum 2^-9: exact scaling
+  } else {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // keep 3 mantissa bits, nearest even
+    c = (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+  }
+  return min(c, 126u);
+}
+
+// Of two codes that differ (or not), the one a near-tie resolves to: the
+// quotient the codes were taken from is Q / (1 + eta) with Q the quotient
+// computed with A / 2688 in place of s_g and s_g = (A / 2688)(1 + eta).
+// dir > 0 (eta < 0): above Q; dir < 0: below; dir == 0: Q itself, a tie
+// going to the even code (low bit of the magnitude code clear).
+__device__ __forceinline__ uint32_t resolve_code(uint32_t lo, uint32_t hi, int dir) {
+  if (dir > 0) return hi;
+  if (dir < 0) return lo;
+  return (lo & 1u) ? hi : lo;
+}
+
+// Quantize one 1x16 block held as 8 words of bf16 pairs.  Returns 8 bytes of
+// packed nibbles (element 2j low) and the E4M3 scale code in *sbc_out.
 //
-// s_b: the quotient a_b / (6 s_g) is taken by a correctly rounded binary64
-// division, which decides the E4M3 rounding exactly (see e4m3_code_f64_sat).
-//
-// Elements, fast path: with d = s_b * s_g (exact in binary64) and inv an
-// approximation of 1/d within 2^-22 (binary32 reciprocal of d rounded to
-// binary32: at most 1.5 ulp), lo = x * inv (1 - 2^-20) and
-// hi = x * inv (1 + 2^-20), each rounded to binary32, bracket the exact
-// quotient r = x / d strictly (all roundings together stay below 2^-21, half
-// the margin).  E2M1 rounding is monotone, so when lo and hi convert to the
-// same codes those are the nearest-even E2M1 of r.  They differ only when
-// some r lies within 2^-20 of a rounding midpoint (an exact tie among them);
-// such a block, a zero scale, or a tiny d is redone on the exact path, which
-// compares each |x| with thresholds derived from the exact midpoints t * d.
-// The exact path sits behind a wave-uniform branch: it costs nothing unless
-// a lane of the wave needs it.
-__device__ __forceinline__ uint2 nvfp4_block(const uint32_t w[8], float s_g, uint32_t *sbc_out) {
+// Both roundings are taken from binary32 quotients bracketed tightly enough
+// that a disagreement between the two ends can only come from an exact
+// rational tie of the ideal quotient, which the row's dir then resolves:
+//  * s_b = E4M3(a_b / (6 s_g)): v = a_b * inv6 is within 2^-23 of the exact
+//    quotient; v (1 -+ 2^-21) bracket it.  When the two ends round to
+//    different codes, a midpoint m lies within 2^-19.9 of a_b / (6 s_g), and
+//    so within 2^-19.8 of P = 448 a_b / A.  P - m is a ratio of integers of
+//    at most 17 bits over A (448 = 7 * 2^6, 8-bit a_b and A, 5-bit m), so it
+//    is either 0 or at least 2^-16.8 relative: P = m exactly, and the true
+//    quotient P / (1 + eta) lies on the side dir says.
+//  * elements: with d = s_b s_g (exact in binary64) and inv the binary32
+//    rounding of 1/d (one Newton step on the binary32 reciprocal of d's
+//    leading part, with d's trailing part), x * inv (1 -+ 2^-22) bracket
+//    x / d strictly.  A disagreement puts an E2M1 midpoint t within 2^-20.2
+//    of x / d, hence within 2^-20.1 of Q = 2688 x / (s_b A); Q - t is either
+//    0 or at least 2^-19.38 relative (8-bit x and A, 4-bit s_b, 3-bit odd
+//    part of t, 2688 = 21 * 2^7), so Q = t and dir decides again.  Where the
+//    ends agree, E2M1 rounding being monotone, their code is the exact one.
+// Blocks with s_b = 0 (all elements encode to a signed zero) and rows whose
+// s_g lies outside the range the bracket arithmetic covers (zero rows
+// included; their s_b comes from a correctly rounded binary64 division) take
+// the exact threshold path behind a wave-uniform branch.
+__device__ __forceinline__ uint2 nvfp4_block(const uint32_t w[8], const Nvfp4Row &row,
+                                             uint32_t *sbc_out) {
   uint32_t mm = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) mm = pk_max_u16(mm, w[i] & 0x7FFF7FFFu);
   const uint32_t mb = max(mm & 0xFFFFu, mm >> 16);
   const float ab = __uint_as_float(mb << 16);
-  uint32_t sbc = 0;
-  if (s_g != 0.0f) sbc = e4m3_code_f64_sat((double)ab / (6.0 * (double)s_g));
-  *sbc_out = sbc;
-  const double d = (double)e4m3_value(sbc) * (double)s_g;  // <= 28 bits: exact
-  const bool fast_ok = sbc != 0 && d >= 0x1p-120 && d <= 0x1p125;
-  const float inv = __builtin_amdgcn_rcpf((float)d);
-  const float ilo = inv * (1.0f - 0x1p-20f), ihi = inv * (1.0f + 0x1p-20f);
-  uint32_t lo[2] = {0, 0}, hi[2] = {0, 0};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t *ww = w + 4 * h;
-    lo[h] = cvt2_e2m1<0>(lo[h], bf16_lo_f32(ww[0]) * ilo, bf16_hi_f32(ww[0]) * ilo);
-    lo[h] = cvt2_e2m1<1>(lo[h], bf16_lo_f32(ww[1]) * ilo, bf16_hi_f32(ww[1]) * ilo);
-    lo[h] = cvt2_e2m1<2>(lo[h], bf16_lo_f32(ww[2]) * ilo, bf16_hi_f32(ww[2]) * ilo);
-    lo[h] = cvt2_e2m1<3>(lo[h], bf16_lo_f32(ww[3]) * ilo, bf16_hi_f32(ww[3]) * ilo);
-    hi[h] = cvt2_e2m1<0>(hi[h], bf16_lo_f32(ww[0]) * ihi, bf16_hi_f32(ww[0]) * ihi);
-    hi[h] = cvt2_e2m1<1>(hi[h], bf16_lo_f32(ww[1]) * ihi, bf16_hi_f32(ww[1]) * ihi);
-    hi[h] = cvt2_e2m1<2>(hi[h], bf16_lo_f32(ww[2]) * ihi, bf16_hi_f32(ww[2]) * ihi);
-    hi[h] = cvt2_e2m1<3>(hi[h], bf16_lo_f32(ww[3]) * ihi, bf16_hi_f32(ww[3]) * ihi);
+  // ---- block scale -------------------------------------------------------
+  uint32_t sbc;
+  if (row.fast) {
+    const float v = ab * row.inv6;
+    sbc = resolve_code(e4m3_code_f32_sat(v * (1.0f - 0x1p-21f)),
+                       e4m3_code_f32_sat(v * (1.0f + 0x1p-21f)), row.dir);
+  } else {
+    // correctly rounded binary64 quotient: decides the E4M3 rounding exactly
+    // (see e4m3_code_f64_sat); s_g = 0 is a zero row
+    sbc = row.s_g != 0.0f ? e4m3_code_f64_sat((double)ab / (6.0 * (double)row.s_g)) : 0u;
   }
-  uint2 out = make_uint2(lo[0], lo[1]);
-  const bool need = !(fast_ok && lo[0] == hi[0] && lo[1] == hi[1]);
+  *sbc_out = sbc;
+  // ---- elements ----------------------------------------------------------
+  const double d = (double)e4m3_value(sbc) * (double)row.s_g;  // <= 28 bits: exact
+  const float dh = (float)d;
+  const float dl = (float)(d - (double)dh);
+  const float i0 = __builtin_amdgcn_rcpf(dh);
+  const float e = __builtin_fmaf(-dl, i0, __builtin_fmaf(-dh, i0, 1.0f));
+  const float inv = __builtin_fmaf(i0, e, i0);
+  uint2 out;
+  if (row.dir != 0) {
+    const float k = inv * (row.dir > 0 ? 1.0f + 0x1p-22f : 1.0f - 0x1p-22f);
+    uint32_t o[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t *ww = w + 4 * h;
+      o[h] = cvt2_e2m1<0>(o[h], bf16_lo_f32(ww[0]) * k, bf16_hi_f32(ww[0]) * k);
+      o[h] = cvt2_e2m1<1>(o[h], bf16_lo_f32(ww[1]) * k, bf16_hi_f32(ww[1]) * k);
+      o[h] = cvt2_e2m1<2>(o[h], bf16_lo_f32(ww[2]) * k, bf16_hi_f32(ww[2]) * k);
+      o[h] = cvt2_e2m1<3>(o[h], bf16_lo_f32(ww[3]) * k, bf16_hi_f32(ww[3]) * k);
+    }
+    out = make_uint2(o[0], o[1]);
+  } else {
+    const float klo = inv * (1.0f - 0x1p-22f), khi = inv * (1.0f + 0x1p-22f);
+    uint32_t lo[2] = {0, 0}, hi[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t *ww = w + 4 * h;
+      lo[h] = cvt2_e2m1<0>(lo[h], bf16_lo_f32(ww[0]) * klo, bf16_hi_f32(ww[0]) * klo);
+      lo[h] = cvt2_e2m1<1>(lo[h], bf16_lo_f32(ww[1]) * klo, bf16_hi_f32(ww[1]) * klo);
+      lo[h] = cvt2_e2m1<2>(lo[h], bf16_lo_f32(ww[2]) * klo, bf16_hi_f32(ww[2]) * klo);
+      lo[h] = cvt2_e2m1<3>(lo[h], bf16_lo_f32(ww[3]) * klo, bf16_hi_f32(ww[3]) * klo);
+      hi[h] = cvt2_e2m1<0>(hi[h], bf16_lo_f32(ww[0]) * khi, bf16_hi_f32(ww[0]) * khi);
+      hi[h] = cvt2_e2m1<1>(hi[h], bf16_lo_f32(ww[1]) * khi, bf16_hi_f32(ww[1]) * khi);
+      hi[h] = cvt2_e2m1<2>(hi[h], bf16_lo_f32(ww[2]) * khi, bf16_hi_f32(ww[2]) * khi);
+      hi[h] = cvt2_e2m1<3>(hi[h], bf16_lo_f32(ww[3]) * khi, bf16_hi_f32(ww[3]) * khi);
+      // exact ties: of two differing nibbles take the one with an even code
+      const uint32_t odd = (lo[h] & 0x11111111u) * 0xFu;
+      lo[h] = (lo[h] & ~odd) | (hi[h] & odd);
+    }
+    out = make_uint2(lo[0], lo[1]);
+  }
+  const bool need = sbc == 0 || !row.fast;
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
     if (need) {  // exact path
       E2M1Thresholds th;
@@ -83,27 +170,24 @@ __device__ __forceinline__ uint2 nvfp4_block(const uint32_t w[8], float s_g, uin
   return out;
 }
 
-// One wave per row, one row per wave (the hardware dispatcher balances the
-// rows over the CUs; a persistent loop left a partial last round).  Lane l
-// owns the 1x16 blocks l + 64 j (two 16-byte loads each), all issued before
-// any use; NB blocks per lane (cols <= 1024 NB).  When amax_ws is non-null
-// the outer scale comes from the group word amax_ws[row / rows_per_scale]
-// instead of the row.
+// One wave per row, one row per wave.  Lane l owns the 1x16 blocks l + 64 j
+// (two 16-byte loads each), all issued before any use; NB blocks per lane
+// (cols <= 1024 NB).  When amax_ws is non-null the outer scale comes from
+// the group word amax_ws[row / rows_per_scale] instead of the row.
 template <int NB>
 __global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
-    const uint16_t *__restrict__ x, int64_t R, int64_t C, int64_t ld,
-    int64_t row_begin, int64_t row_end, int64_t rows_per_scale,
-    const uint32_t *__restrict__ amax_ws, uint8_t *__restrict__ q,
-    uint8_t *__restrict__ sb, float *__restrict__ sg) {
+    const uint16_t *__restrict__ x, uint32_t C, int64_t ld, uint32_t row_begin,
+    uint32_t row_end, uint32_t rows_per_scale, const uint32_t *__restrict__ amax_ws,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ sb, float *__restrict__ sg) {
   const int lane = threadIdx.x & 63;
-  const int64_t nblk = C / 16;
-  const int64_t row = row_begin + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const uint32_t nblk = C / 16;
+  const uint32_t row = row_begin + blockIdx.x * 4u + (threadIdx.x >> 6);
   if (row >= row_end) return;  // whole wave exits together
-  const uint16_t *xr = x + row * ld;
+  const uint16_t *xr = x + (int64_t)row * ld;
   uint32_t w[NB][8];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int64_t blk = lane + 64 * b;
+    const uint32_t blk = lane + 64 * b;
     uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
     if (blk < nblk) {
       v0 = *reinterpret_cast<const uint4 *>(xr + blk * 16);
@@ -112,9 +196,10 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
     w[b][0] = v0.x; w[b][1] = v0.y; w[b][2] = v0.z; w[b][3] = v0.w;
     w[b][4] = v1.x; w[b][5] = v1.y; w[b][6] = v1.z; w[b][7] = v1.w;
   }
+  const uint32_t grp = amax_ws ? row / rows_per_scale : row;
   float A;
   if (amax_ws) {
-    A = __uint_as_float(amax_ws[row / rows_per_scale] << 16);
+    A = __uint_as_float(amax_ws[grp] << 16);
   } else {
     uint32_t m = 0;
 #pragma unroll
@@ -126,18 +211,19 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
     A = __uint_as_float(m << 16);
   }
-  const float s_g = __fdiv_rn(A, 2688.0f);  // one correctly rounded division
-  if (lane == 0 && (amax_ws == nullptr || row % rows_per_scale == 0))
-    sg[row / rows_per_scale] = s_g;
+  const Nvfp4Row rc = nvfp4_row(A);
+  if (lane == 0 && (amax_ws == nullptr || row == grp * rows_per_scale)) sg[grp] = rc.s_g;
+  uint8_t *qr = q + (int64_t)row * (C / 2);
+  uint8_t *sbr = sb + (int64_t)row * nblk;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    if ((int64_t)64 * b < nblk) {  // uniform: the exact path's ballot needs the wave
-      const int64_t blk = lane + 64 * b;
+    if (64u * b < nblk) {  // uniform: the exact path's ballot needs the wave
+      const uint32_t blk = lane + 64 * b;
       uint32_t code;
-      const uint2 packed = nvfp4_block(w[b], s_g, &code);
+      const uint2 packed = nvfp4_block(w[b], rc, &code);
       if (blk < nblk) {
-        *reinterpret_cast<uint2 *>(q + row * (C / 2) + blk * 8) = packed;
-        sb[row * nblk + blk] = (uint8_t)code;
+        *reinterpret_cast<uint2 *>(qr + blk * 8) = packed;
+        sbr[blk] = (uint8_t)code;
       }
     }
   }
@@ -195,9 +281,10 @@ template <int NB>
 static void launch_rows(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int64_t rb,
                         int64_t re, int64_t rps, const uint32_t *ws, uint8_t *q,
                         uint8_t *sb, float *sg, hipStream_t st) {
+  (void)R;
   const unsigned grid = (unsigned)((re - rb + 3) / 4);
-  hipLaunchKernelGGL((k_quantize_nvfp4_rows<NB>), dim3(grid), dim3(256), 0, st, x, R, C, ld,
-                     rb, re, rps, ws, q, sb, sg);
+  hipLaunchKernelGGL((k_quantize_nvfp4_rows<NB>), dim3(grid), dim3(256), 0, st, x, (uint32_t)C,
+                     ld, (uint32_t)rb, (uint32_t)re, (uint32_t)rps, ws, q, sb, sg);
 }
 
 static void dispatch_rows(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int64_t rb,

@@ -92,7 +92,8 @@ def test_mxfp8_exhaustive_values_and_scales():
     _check_mxfp8(np.ascontiguousarray(x.T), "exhaustive colwise")
 
 
-@pytest.mark.parametrize("shape", [(160, 96), (32, 32), (128, 128), (288, 416), (96, 2048)])
+@pytest.mark.parametrize("shape", [(160, 96), (32, 32), (128, 128), (288, 416), (96, 2048),
+                                   (384, 256), (512, 512), (416, 160), (640, 2048)])
 def test_mxfp8_ragged_tiles(shape):
     x = wl.activations(*shape, seed=7)
     _check_mxfp8(x, f"ragged{shape}")
