@@ -76,17 +76,19 @@ __device__ __forceinline__ uint32_t resolve_code(uint32_t lo, uint32_t hi, int d
 //  * s_b = E4M3(a_b / (6 s_g)): v = a_b * inv6 is within 2^-23 of the exact
 //    quotient; v (1 -+ 2^-21) bracket it.  When the two ends round to
 //    different codes, a midpoint m lies within 2^-19.9 of a_b / (6 s_g), and
-//    so within 2^-19.8 of P = 448 a_b / A.  P - m is a ratio of integers of
-//    at most 17 bits over A (448 = 7 * 2^6, 8-bit a_b and A, 5-bit m), so it
-//    is either 0 or at least 2^-16.8 relative: P = m exactly, and the true
-//    quotient P / (1 + eta) lies on the side dir says.
+//    so within 2^-19.8 of P = 448 a_b / A.  P - m is a ratio of short
+//    integers (448 = 7 * 2^6, 8-bit a_b and A, 5-bit m), so it is either 0
+//    or at least 2^-16.8 relative (2^-12.8 by exhaustive search over all
+//    significands): P = m exactly, and the true quotient P / (1 + eta) lies
+//    on the side dir says.
 //  * elements: with d = s_b s_g (exact in binary64) and inv the binary32
 //    rounding of 1/d (one Newton step on the binary32 reciprocal of d's
 //    leading part, with d's trailing part), x * inv (1 -+ 2^-22) bracket
 //    x / d strictly.  A disagreement puts an E2M1 midpoint t within 2^-20.2
 //    of x / d, hence within 2^-20.1 of Q = 2688 x / (s_b A); Q - t is either
 //    0 or at least 2^-19.38 relative (8-bit x and A, 4-bit s_b, 3-bit odd
-//    part of t, 2688 = 21 * 2^7), so Q = t and dir decides again.  Where the
+//    part of t, 2688 = 21 * 2^7; 2^-13.8 by exhaustive search over all
+//    significands and scales), so Q = t and dir decides again.  Where the
 //    ends agree, E2M1 rounding being monotone, their code is the exact one.
 // Blocks with s_b = 0 (all elements encode to a signed zero) and rows whose
 // s_g lies outside the range the bracket arithmetic covers (zero rows
