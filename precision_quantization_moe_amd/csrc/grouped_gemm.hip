@@ -11,7 +11,9 @@
 //
 // MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 consumes E4M3 operands with one
 // E8M0 scale per 32 K-values per row, which is the MXFP8 block layout, so
-// the scales go to the matrix core unchanged.  Lane layout (verified on the
+// the scales go to the matrix core unchanged.  K % 128 == 0 (K <= 3072) runs
+// the pipelined 128 x 256 kernel (k_gemm_mxfp8_pipe); other K the simpler
+// 128 x 128 kernel with register-staged tiles.  Lane layout (verified on the
 // hardware): a lane holds row (lane % 32); its bytes 0-15 are K
 // 16*(lane/32) .. +15 of the first 32-block and bytes 16-31 the same offsets
 // in the second block; lane 32*b + r supplies the scale of row r, block b.
@@ -47,6 +49,7 @@ struct TileInfo {
 // hardware places workgroup b on XCD b % 8; b is remapped so that each XCD
 // owns a contiguous range of logical tiles (the tiles of one expert share
 // its weight slices in that XCD's L2).  Returns false if no tile.
+template <int TN = GT_N>
 __device__ bool lookup_row_tile(const int64_t *__restrict__ offsets, int64_t G, int64_t ntn,
                                 TileInfo &ti, int64_t *sh) {
   const int lane = threadIdx.x & 63;
@@ -101,7 +104,7 @@ __device__ bool lookup_row_tile(const int64_t *__restrict__ offsets, int64_t G, 
         sh[0] = found_g;
         sh[1] = row0;
         sh[2] = row_end;
-        sh[3] = (T % ntn) * GT_N;
+        sh[3] = (T % ntn) * TN;
       }
     } else if (lane == 0) {
       sh[0] = -1;
@@ -257,6 +260,214 @@ __global__ __launch_bounds__(256) void k_gemm_mxfp8(
     for (int j = 0; j < 2; ++j)
       store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
                          wn * 64 + 32 * j);
+}
+
+// ------------------------------------------------- MXFP8, pipelined large tiles
+//
+// Workgroup tile 128 rows x 256 columns, one workgroup (4 waves) per CU;
+// wave (wm, wn) owns rows 64 wm .. +63 and columns 128 wn .. +127 (2 x 4
+// accumulators of 32 x 32 in AGPRs).  Per 64-K step and wave: 12 fragment
+// reads (12 KB of LDS) feed 8 MFMAs, and the workgroup moves 24 KB from L2.
+//
+// Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4:
+// lane l's 16 bytes land at M0 + 16 l), issued from inline assembly so that
+// the compiler does not serialise them against the LDS reads of other ring
+// slots; the code waits for them explicitly.  The ring has 4 slots of one
+// 64-K step each; step k+3 is requested while step k is multiplied; before
+// step k a wave waits until only its 12 operations of steps k+1 and k+2 are
+// pending and then meets the others at a barrier, which publishes step k and
+// frees slot (k+3) % 4 (read during step k-1).  Rows of a slot are 64 bytes
+// whose 16-byte chunks are XOR-swizzled by (row / 4) % 4; the swizzle goes
+// into the global addresses.  All scale bytes of the tile's rows are loaded
+// once, dword-major ([dword][row]), so that 32 lanes reading 32 rows hit 32
+// banks.  Rows past the expert's end (A) or past N (B) load a clamped valid
+// row; their results are never stored.  Requires K % 128 == 0 and
+// K <= 2048 * 4 (the scale area).
+namespace mx3 {
+constexpr int TN = 256;                           // workgroup tile columns
+constexpr int SLOT = (GT_M + TN) * 64;            // 24 KB per ring slot
+constexpr int NSLOT = 4;
+constexpr int MAX_KS = 96;                        // scale bytes per row (K <= 3072)
+constexpr int SCALES = (GT_M + TN) * MAX_KS;      // 36 KB
+constexpr int LDS = NSLOT * SLOT + SCALES;        // 132 KB
+constexpr int OPS = 6;                            // DMA operations per lane per step
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from global `src` into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(const void *src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+}
+// 4 bytes per lane from global `src` into LDS at m0 + 4 * lane.
+__device__ __forceinline__ void dma4(const void *src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int n>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+struct Mx3 {
+  const uint8_t *Ab, *Bb;  // tile bases
+  uint32_t oa[2], ob[4];   // per-lane sources of the step's chunks (step 0)
+  uint32_t ring;           // LDS address of slot 0 (wave-uniform)
+  uint32_t wave_off;       // wave * 1024
+};
+
+template <int SLOTI>
+__device__ __forceinline__ void mx3_issue(const Mx3 &L, int kt) {
+  const uint32_t kb = (uint32_t)kt * 64u;
+  const uint32_t base = L.ring + SLOTI * mx3::SLOT + L.wave_off;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    dma16(L.Ab + (L.oa[i] + kb), __builtin_amdgcn_readfirstlane(base + i * 4096));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma16(L.Bb + (L.ob[i] + kb), __builtin_amdgcn_readfirstlane(base + GT_M * 64 + i * 4096));
+}
+
+// Byte offset of 16-byte chunk `chunk` of row `row` in a ring slot.
+__device__ __forceinline__ int mx3_off(int row, int chunk) {
+  return row * 64 + ((chunk ^ (row >> 2)) & 3) * 16;
+}
+
+__device__ __forceinline__ v8i mx3_frag(const uint8_t *tile, int r, int h) {
+  const uint4 lo = *reinterpret_cast<const uint4 *>(tile + mx3_off(r, h));
+  const uint4 hi = *reinterpret_cast<const uint4 *>(tile + mx3_off(r, 2 + h));
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Multiply step kt held in slot SLOTI.  Scale byte (row, block b) sits at
+// sc[(b / 4) * rows * 4 + row * 4 + b % 4].
+template <int SLOTI>
+__device__ __forceinline__ void mx3_compute(const uint8_t *lds, int kt, v16f (&acc)[2][4],
+                                            int wm, int wn, int lane) {
+  const uint8_t *cur = lds + SLOTI * mx3::SLOT;
+  const uint8_t *sca = lds + mx3::NSLOT * mx3::SLOT;
+  const uint8_t *scb = sca + GT_M * 4;  // B rows follow A rows in each dword plane
+  const int h = lane >> 5, r32 = lane & 31;
+  const int blk = 2 * kt + h;
+  const int plane = (blk >> 2) * (GT_M + mx3::TN) * 4, sub = blk & 3;
+  const int sa0 = sca[plane + (wm * 64 + r32) * 4 + sub];
+  const int sa1 = sca[plane + (wm * 64 + 32 + r32) * 4 + sub];
+  const v8i fa0 = mx3_frag(cur, wm * 64 + r32, h);
+  const v8i fa1 = mx3_frag(cur, wm * 64 + 32 + r32, h);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rb = wn * 128 + 32 * j + r32;
+    const v8i fb = mx3_frag(cur + GT_M * 64, rb, h);
+    const int sb = scb[plane + rb * 4 + sub];
+    acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0, fb, acc[0][j], 0, 0, 0, sa0,
+                                                                 0, sb);
+    acc[1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1, fb, acc[1][j], 0, 0, 0, sa1,
+                                                                 0, sb);
+  }
+}
+
+template <int SLOTI>
+__device__ __forceinline__ void mx3_step(const Mx3 &L, const uint8_t *lds, int kt, int nk,
+                                         v16f (&acc)[2][4], int wm, int wn, int lane) {
+  // own loads of step kt complete: at most steps kt+1, kt+2 still pending
+  if (kt + 2 < nk) vm_wait<2 * mx3::OPS>();
+  else if (kt + 1 < nk) vm_wait<mx3::OPS>();
+  else vm_wait<0>();
+  __builtin_amdgcn_s_barrier();
+  if (kt + 3 < nk) mx3_issue<(SLOTI + 3) % 4>(L, kt + 3);
+  mx3_compute<SLOTI>(lds, kt, acc, wm, wn, lane);
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    void *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[mx3::LDS];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<mx3::TN>(offsets, G, ntn, ti, sh)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t KS = (uint32_t)(K / 32), Ku = (uint32_t)K;
+  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)GT_M);
+  const int rows_b = (int)min(N - ti.n0, (int64_t)mx3::TN);
+  Mx3 L;
+  L.Ab = A + ti.row0 * K;
+  L.Bb = B + (ti.g * N + ti.n0) * K;
+  L.ring = lds_addr(lds);
+  L.wave_off = (uint32_t)wave * 1024u;
+  // ring chunk c = 256 i + tid: row c / 4, physical chunk c % 4, which holds
+  // logical chunk (c % 4) ^ ((row / 4) % 4)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.oa[i] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * k;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.ob[i] = (uint32_t)min(r, rows_b - 1) * Ku + 16u * k;
+  }
+  // scale bytes: dword plane p holds dword p of every row (A rows, then B
+  // rows); lane t of the p-th pass over 384 rows loads (row, dword p)
+  {
+    const uint8_t *Asb = As + ti.row0 * (int64_t)KS;
+    const uint8_t *Bsb = Bs + (ti.g * N + ti.n0) * (int64_t)KS;
+    const uint32_t sbase = lds_addr(lds) + mx3::NSLOT * mx3::SLOT;
+    const int nd = (int)(KS / 4);  // dwords per row
+    for (int p = 0; p < nd; ++p) {
+      // 384 rows per plane: waves 0..3 cover rows 64 w .. +63, then 256 + ...
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int row = q * 256 + tid;  // 0..511, rows >= 384 unused
+        if (q == 1 && wave >= 2) continue;  // rows 384..511 do not exist
+        const uint8_t *src = row < GT_M
+                                 ? Asb + (int64_t)min(row, rows_a - 1) * KS + 4 * p
+                                 : Bsb + (int64_t)min(row - GT_M, rows_b - 1) * KS + 4 * p;
+        dma4(src, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(p * (GT_M + mx3::TN) * 4) +
+                                                 (uint32_t)(q * 1024 + wave * 256)));
+      }
+    }
+  }
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (int)(K / 64);
+  mx3_issue<0>(L, 0);
+  if (nk > 1) mx3_issue<1>(L, 1);
+  if (nk > 2) mx3_issue<2>(L, 2);
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    mx3_step<0>(L, lds, kt, nk, acc, wm, wn, lane);
+    mx3_step<1>(L, lds, kt + 1, nk, acc, wm, wn, lane);
+    mx3_step<2>(L, lds, kt + 2, nk, acc, wm, wn, lane);
+    mx3_step<3>(L, lds, kt + 3, nk, acc, wm, wn, lane);
+  }
+  if (kt < nk) mx3_step<0>(L, lds, kt, nk, acc, wm, wn, lane);
+  if (kt + 1 < nk) mx3_step<1>(L, lds, kt + 1, nk, acc, wm, wn, lane);
+  if (kt + 2 < nk) mx3_step<2>(L, lds, kt + 2, nk, acc, wm, wn, lane);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
+                         wn * 128 + 32 * j);
 }
 
 // ------------------------------------------------------------------- BF16
@@ -608,6 +819,18 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
   int64_t tiles = (cdiv(M, GT_M) + G) * ntn;
   tiles = cdiv(tiles, 8) * 8;
   const dim3 grid((unsigned)tiles);
+  if (fmt == 1 && K % 128 == 0 && K / 32 <= mx3::MAX_KS) {
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    const int64_t ntn_b = cdiv(N, mx3::TN);
+    const dim3 grid_b((unsigned)(cdiv((cdiv(M, GT_M) + G) * ntn_b, 8) * 8));
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_b, out);
+    else
+      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_b, out);
+    return hipGetLastError();
+  }
   if (fmt == 1) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     if (out_fp32)

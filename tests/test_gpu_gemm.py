@@ -75,6 +75,8 @@ def _mxfp8_case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32):
     ([128], 256, 256),
     ([5, 0, 0, 250], 96, 64),
     ([513], 128, 4096),
+    ([0, 37, 128, 1, 300], 200, 384),        # K % 128 == 0: large-tile kernel
+    ([260, 0, 3], 1536, 768),
 ])
 def test_mxfp8_fprop_ragged(case):
     sizes, N, K = case
