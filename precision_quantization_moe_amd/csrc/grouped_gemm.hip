@@ -49,7 +49,7 @@ struct TileInfo {
 // hardware places workgroup b on XCD b % 8; b is remapped so that each XCD
 // owns a contiguous range of logical tiles (the tiles of one expert share
 // its weight slices in that XCD's L2).  Returns false if no tile.
-template <int TN = GT_N>
+template <int TN = GT_N, int TM = GT_M>
 __device__ bool lookup_row_tile(const int64_t *__restrict__ offsets, int64_t G, int64_t ntn,
                                 TileInfo &ti, int64_t *sh) {
   const int lane = threadIdx.x & 63;
@@ -59,7 +59,7 @@ __device__ bool lookup_row_tile(const int64_t *__restrict__ offsets, int64_t G, 
     for (int64_t c0 = 0; c0 < G; c0 += 64) {
       const int64_t g = c0 + lane;
       int64_t cnt = 0;
-      if (g < G) cnt = (offsets[g + 1] - offsets[g] + GT_M - 1) / GT_M;
+      if (g < G) cnt = (offsets[g + 1] - offsets[g] + TM - 1) / TM;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
       total += cnt;
@@ -78,7 +78,7 @@ __device__ bool lookup_row_tile(const int64_t *__restrict__ offsets, int64_t G, 
         if (g < G) {
           lo = offsets[g];
           hi = offsets[g + 1];
-          cnt = (hi - lo + GT_M - 1) / GT_M;
+          cnt = (hi - lo + TM - 1) / TM;
         }
         int64_t incl = cnt;
 #pragma unroll
@@ -95,7 +95,7 @@ __device__ bool lookup_row_tile(const int64_t *__restrict__ offsets, int64_t G, 
           const int64_t h0 = __shfl(hi, src, 64);
           const int64_t ex = __shfl(incl - cnt, src, 64);
           found_g = gg;
-          row0 = l0 + (mt - base - ex) * GT_M;
+          row0 = l0 + (mt - base - ex) * TM;
           row_end = h0;
         }
         base += __shfl(incl, 63, 64);
@@ -264,34 +264,41 @@ __global__ __launch_bounds__(256) void k_gemm_mxfp8(
 
 // ------------------------------------------------- MXFP8, pipelined large tiles
 //
-// Workgroup tile 128 rows x 256 columns, one workgroup (4 waves) per CU;
-// wave (wm, wn) owns rows 64 wm .. +63 and columns 128 wn .. +127 (2 x 4
-// accumulators of 32 x 32 in AGPRs).  Per 64-K step and wave: 12 fragment
-// reads (12 KB of LDS) feed 8 MFMAs, and the workgroup moves 24 KB from L2.
+// Workgroup tile TM rows x 256 columns (TM = 256 or 128), one workgroup of
+// 4 waves per CU; wave (wm, wn) owns rows TM/2 wm .. and columns 128 wn ..
+// as FI x 4 accumulators of 32 x 32 in AGPRs (FI = TM / 64).  Per 64-K step
+// and wave, 2 (FI + 4) fragment reads feed 4 FI MFMAs: with TM = 256 a wave
+// reads 8 KB of LDS for 16 MFMAs, half the traffic per flop of TM = 128.
 //
 // Operands reach LDS by direct global->LDS loads (global_load_lds_dwordx4:
 // lane l's 16 bytes land at M0 + 16 l), issued from inline assembly so that
 // the compiler does not serialise them against the LDS reads of other ring
-// slots; the code waits for them explicitly.  The ring has 4 slots of one
-// 64-K step each; step k+3 is requested while step k is multiplied; before
-// step k a wave waits until only its 12 operations of steps k+1 and k+2 are
-// pending and then meets the others at a barrier, which publishes step k and
-// frees slot (k+3) % 4 (read during step k-1).  Rows of a slot are 64 bytes
-// whose 16-byte chunks are XOR-swizzled by (row / 4) % 4; the swizzle goes
-// into the global addresses.  All scale bytes of the tile's rows are loaded
-// once, dword-major ([dword][row]), so that 32 lanes reading 32 rows hit 32
-// banks.  Rows past the expert's end (A) or past N (B) load a clamped valid
-// row; their results are never stored.  Requires K % 128 == 0 and
-// K <= 2048 * 4 (the scale area).
-namespace mx3 {
-constexpr int TN = 256;                           // workgroup tile columns
-constexpr int SLOT = (GT_M + TN) * 64;            // 24 KB per ring slot
-constexpr int NSLOT = 4;
-constexpr int MAX_KS = 96;                        // scale bytes per row (K <= 3072)
-constexpr int SCALES = (GT_M + TN) * MAX_KS;      // 36 KB
-constexpr int LDS = NSLOT * SLOT + SCALES;        // 132 KB
-constexpr int OPS = 6;                            // DMA operations per lane per step
-}
+// slots; the code waits for them explicitly.  The ring has 3 slots of one
+// 64-K step each.  During step k a wave multiplies operands it read from
+// LDS during step k-1, reads step k+1's operands and requests step k+3 into
+// the slot step k came from.  Before step k it waits until only its loads of
+// step k+2 are pending (and its LDS reads are done) and meets the other
+// waves at a barrier, which publishes step k+1 and frees slot k % 3.  Past
+// the last step the requests repeat the last step (in bounds, never read)
+// and reads take stale slots, so the loop has no branches; the kernel drains
+// its loads before it exits.  Rows of a slot are 64 bytes whose 16-byte
+// chunks are XOR-swizzled by (row / 4) % 4; the swizzle goes into the global
+// addresses.  All scale bytes of the tile's rows are loaded once, in groups
+// of 16 rows.  Rows past
+// the expert's end (A) or past N (B) load a clamped valid row; their results
+// are never stored.  Requires K % 128 == 0 and K / 32 <= MAX_KS.
+template <int TM>
+struct Mx3 {
+  static constexpr int TN = 256;                  // workgroup tile columns
+  static constexpr int ROWS = TM + TN;            // staged rows per step
+  static constexpr int SLOT = ROWS * 64;          // bytes per ring slot
+  static constexpr int NSLOT = 3;
+  static constexpr int MAX_KS = TM == 256 ? 64 : 96;  // scale bytes per row
+  static constexpr int LDS = NSLOT * SLOT + ROWS * MAX_KS;
+  static constexpr int CA = TM / 64, CB = TN / 64;    // 16-byte chunks per lane per step
+  static constexpr int OPS = CA + CB;                 // loads per lane per step
+  static constexpr int FI = TM / 64, FJ = 4;          // fragments per wave
+};
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -312,28 +319,29 @@ __device__ __forceinline__ void vm_wait() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+__device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)p;
 }
 
-struct Mx3 {
-  const uint8_t *Ab, *Bb;  // tile bases
-  uint32_t oa[2], ob[4];   // per-lane sources of the step's chunks (step 0)
-  uint32_t ring;           // LDS address of slot 0 (wave-uniform)
-  uint32_t wave_off;       // wave * 1024
+template <int TM>
+struct Mx3Src {
+  const uint8_t *Ab, *Bb;                    // tile bases
+  uint32_t oa[Mx3<TM>::CA], ob[Mx3<TM>::CB];  // per-lane sources of a step's chunks (step 0)
+  uint32_t dst;                              // LDS address of slot 0, this wave's chunks
 };
 
-template <int SLOTI>
-__device__ __forceinline__ void mx3_issue(const Mx3 &L, int kt) {
+// Request step kt into slot `slot`.
+template <int TM>
+__device__ __forceinline__ void mx3_issue(const Mx3Src<TM> &L, int kt, int slot) {
+  using C = Mx3<TM>;
   const uint32_t kb = (uint32_t)kt * 64u;
-  const uint32_t base = L.ring + SLOTI * mx3::SLOT + L.wave_off;
+  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    dma16(L.Ab + (L.oa[i] + kb), __builtin_amdgcn_readfirstlane(base + i * 4096));
+  for (int i = 0; i < C::CA; ++i) dma16(L.Ab + (L.oa[i] + kb), base + i * 4096);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    dma16(L.Bb + (L.ob[i] + kb), __builtin_amdgcn_readfirstlane(base + GT_M * 64 + i * 4096));
+  for (int i = 0; i < C::CB; ++i) dma16(L.Bb + (L.ob[i] + kb), base + TM * 64 + i * 4096);
 }
 
 // Byte offset of 16-byte chunk `chunk` of row `row` in a ring slot.
@@ -341,132 +349,235 @@ __device__ __forceinline__ int mx3_off(int row, int chunk) {
   return row * 64 + ((chunk ^ (row >> 2)) & 3) * 16;
 }
 
-__device__ __forceinline__ v8i mx3_frag(const uint8_t *tile, int r, int h) {
-  const uint4 lo = *reinterpret_cast<const uint4 *>(tile + mx3_off(r, h));
-  const uint4 hi = *reinterpret_cast<const uint4 *>(tile + mx3_off(r, 2 + h));
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
+// A wave's operands of one 64-K step and their scale bytes.
+template <int TM>
+struct Mx3Frags {
+  v8i a[Mx3<TM>::FI], b[Mx3<TM>::FJ];
+  int sa[Mx3<TM>::FI], sb[Mx3<TM>::FJ];
+};
 
-// Multiply step kt held in slot SLOTI.  Scale byte (row, block b) sits at
-// sc[(b / 4) * rows * 4 + row * 4 + b % 4].
-template <int SLOTI>
-__device__ __forceinline__ void mx3_compute(const uint8_t *lds, int kt, v16f (&acc)[2][4],
-                                            int wm, int wn, int lane) {
-  const uint8_t *cur = lds + SLOTI * mx3::SLOT;
-  const uint8_t *sca = lds + mx3::NSLOT * mx3::SLOT;
-  const uint8_t *scb = sca + GT_M * 4;  // B rows follow A rows in each dword plane
-  const int h = lane >> 5, r32 = lane & 31;
-  const int blk = 2 * kt + h;
-  const int plane = (blk >> 2) * (GT_M + mx3::TN) * 4, sub = blk & 3;
-  const int sa0 = sca[plane + (wm * 64 + r32) * 4 + sub];
-  const int sa1 = sca[plane + (wm * 64 + 32 + r32) * 4 + sub];
-  const v8i fa0 = mx3_frag(cur, wm * 64 + r32, h);
-  const v8i fa1 = mx3_frag(cur, wm * 64 + 32 + r32, h);
+// Per-lane LDS offsets of the operands within a slot (fragment f of a row
+// group sits 2048 f bytes after fragment 0: rows 32 apart share the swizzle)
+// and of the scale bytes (16-row groups, dword-major within a group).
+struct Mx3Lane {
+  int a_lo, a_hi, b_lo, b_hi;  // chunks h and 2 + h of the first A / B row
+  int sa, sb;                  // first scale byte of the first A / B row
+  int ks;                      // scale bytes per row
+};
+
+template <int TM>
+__device__ __forceinline__ void mx3_read(const uint8_t *lds, int kt, int slot, const Mx3Lane &o,
+                                         Mx3Frags<TM> &F) {
+  using C = Mx3<TM>;
+  const uint8_t *cur = lds + slot * C::SLOT;
+  const int blk = 2 * kt + ((threadIdx.x & 63) >> 5);
+  const uint8_t *sc = lds + C::NSLOT * C::SLOT + (blk >> 2) * 64 + (blk & 3);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rb = wn * 128 + 32 * j + r32;
-    const v8i fb = mx3_frag(cur + GT_M * 64, rb, h);
-    const int sb = scb[plane + rb * 4 + sub];
-    acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0, fb, acc[0][j], 0, 0, 0, sa0,
-                                                                 0, sb);
-    acc[1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1, fb, acc[1][j], 0, 0, 0, sa1,
-                                                                 0, sb);
+  for (int i = 0; i < C::FI; ++i) {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(cur + o.a_lo + 2048 * i);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(cur + o.a_hi + 2048 * i);
+    F.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    F.sa[i] = sc[o.sa + 2 * i * o.ks * 16];
+  }
+#pragma unroll
+  for (int j = 0; j < C::FJ; ++j) {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(cur + o.b_lo + 2048 * j);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(cur + o.b_hi + 2048 * j);
+    F.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    F.sb[j] = sc[o.sb + 2 * j * o.ks * 16];
   }
 }
 
-template <int SLOTI>
-__device__ __forceinline__ void mx3_step(const Mx3 &L, const uint8_t *lds, int kt, int nk,
-                                         v16f (&acc)[2][4], int wm, int wn, int lane) {
-  // own loads of step kt complete: at most steps kt+1, kt+2 still pending
-  if (kt + 2 < nk) vm_wait<2 * mx3::OPS>();
-  else if (kt + 1 < nk) vm_wait<mx3::OPS>();
-  else vm_wait<0>();
-  __builtin_amdgcn_s_barrier();
-  if (kt + 3 < nk) mx3_issue<(SLOTI + 3) % 4>(L, kt + 3);
-  mx3_compute<SLOTI>(lds, kt, acc, wm, wn, lane);
+// The weight fragment is the instruction's first operand, the token
+// fragment its second, so each accumulator holds a transposed 32 x 32 tile:
+// lane l owns token row l % 32 and output columns 8 g + 4 (l / 32) + 0..3
+// (g = 0..3), four runs of 4 consecutive columns (see mx3_store).
+template <int TM>
+__device__ __forceinline__ void mx3_mma(const Mx3Frags<TM> &F,
+                                        v16f (&acc)[Mx3<TM>::FI][Mx3<TM>::FJ]) {
+#pragma unroll
+  for (int j = 0; j < Mx3<TM>::FJ; ++j)
+#pragma unroll
+    for (int i = 0; i < Mx3<TM>::FI; ++i)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0, 0,
+                                                                   0, F.sb[j], 0, F.sa[i]);
 }
 
+// Write one transposed accumulator (token rows row0 + rbase + 0..31, output
+// columns n0 + cbase + 0..31).  Lane l holds columns 8 g + 4 (l / 32) + 0..3
+// of its row; the gfx950 lane swap between lanes l and l + 32 trades run
+// g = 1 (3) of the low half for run 0 (2) of the high half, after which lane
+// l holds columns 16 p + 8 (l / 32) + 0..7, p = 0, 1: two 16-byte (bf16) or
+// 32-byte (binary32) stores per lane.
 template <bool OUT_F32>
+__device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N, int64_t row0,
+                                          int64_t row_end, int64_t n0, int rbase, int cbase) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int64_t row = row0 + rbase + (lane & 31);
+  const bool vec = (N & 7) == 0;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    // runs 2p (own) and 2p+1 (own); the low half keeps run 2p and receives
+    // the high half's run 2p, the high half keeps run 2p+1 and receives the
+    // low half's run 2p+1
+    float lo[4], hi[4];  // this lane's first and second 4 columns after the swap
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = acc[8 * p + e], b = acc[8 * p + 4 + e];  // runs 2p, 2p+1
+      // swap: low-half lanes give b (run 2p+1) and get the high half's a
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h ? a : b),
+                                                       __float_as_uint(h ? a : b), false, false);
+      // the value from the other half arrives in element 1 (the second
+      // operand's new value) for low-half lanes and element 0 for high ones
+      const float got = __uint_as_float(h ? sw[0] : sw[1]);
+      lo[e] = h ? got : a;   // high half: the low half's run 2p+1 comes first
+      hi[e] = h ? b : got;
+    }
+    const int64_t col = n0 + cbase + 16 * p + 8 * h;
+    if (row >= row_end) continue;
+    if (vec && col + 7 < N) {
+      if (OUT_F32) {
+        float *dst = static_cast<float *>(out) + row * N + col;
+        *reinterpret_cast<float4 *>(dst) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<float4 *>(dst + 4) = make_float4(hi[0], hi[1], hi[2], hi[3]);
+      } else {
+        const uint4 w = make_uint4(f32_to_bf16_rne(lo[0]) | (f32_to_bf16_rne(lo[1]) << 16),
+                                   f32_to_bf16_rne(lo[2]) | (f32_to_bf16_rne(lo[3]) << 16),
+                                   f32_to_bf16_rne(hi[0]) | (f32_to_bf16_rne(hi[1]) << 16),
+                                   f32_to_bf16_rne(hi[2]) | (f32_to_bf16_rne(hi[3]) << 16));
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + row * N + col) = w;
+      }
+    } else {
+      const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (col + e < N) {
+          if (OUT_F32)
+            static_cast<float *>(out)[row * N + col + e] = v[e];
+          else
+            static_cast<uint16_t *>(out)[row * N + col + e] = (uint16_t)f32_to_bf16_rne(v[e]);
+        }
+      }
+    }
+  }
+}
+
+// Step kt from slot `slot`: operands in `cur` (read during the previous
+// step).  Publish step kt+1, refill `slot` with step kt+3, read step kt+1's
+// operands into `next`, multiply `cur`.
+template <int TM>
+__device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds,
+                                         const Mx3Lane &o, int kt, int nk, int slot,
+                                         v16f (&acc)[Mx3<TM>::FI][Mx3<TM>::FJ],
+                                         const Mx3Frags<TM> &cur, Mx3Frags<TM> &next) {
+  vm_wait<Mx3<TM>::OPS>();  // own loads of step kt+1 done; step kt+2 may be pending
+  lgkm_wait0();             // own reads of `slot` done before it is refilled
+  __builtin_amdgcn_s_barrier();
+  // keep the order: loads out first, then the operand reads, then the MFMAs
+  // (which need none of them)
+  mx3_issue<TM>(L, min(kt + 3, nk - 1), slot);
+  __builtin_amdgcn_sched_barrier(0);
+  mx3_read<TM>(lds, kt + 1, slot == 2 ? 0 : slot + 1, o, next);
+  __builtin_amdgcn_sched_barrier(0);
+  mx3_mma<TM>(cur, acc);
+}
+
+template <bool OUT_F32, int TM>
 __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
     void *__restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[mx3::LDS];
+  using C = Mx3<TM>;
+  constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
   __shared__ int64_t sh[4];
   TileInfo ti;
-  if (!lookup_row_tile<mx3::TN>(offsets, G, ntn, ti, sh)) return;
+  if (!lookup_row_tile<TN, TM>(offsets, G, ntn, ti, sh)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
   const uint32_t KS = (uint32_t)(K / 32), Ku = (uint32_t)K;
-  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)GT_M);
-  const int rows_b = (int)min(N - ti.n0, (int64_t)mx3::TN);
-  Mx3 L;
+  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)TM);
+  const int rows_b = (int)min(N - ti.n0, (int64_t)TN);
+  Mx3Src<TM> L;
   L.Ab = A + ti.row0 * K;
   L.Bb = B + (ti.g * N + ti.n0) * K;
-  L.ring = lds_addr(lds);
-  L.wave_off = (uint32_t)wave * 1024u;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
   // ring chunk c = 256 i + tid: row c / 4, physical chunk c % 4, which holds
   // logical chunk (c % 4) ^ ((row / 4) % 4)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < C::CA; ++i) {
     const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
     L.oa[i] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * k;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < C::CB; ++i) {
     const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
     L.ob[i] = (uint32_t)min(r, rows_b - 1) * Ku + 16u * k;
   }
-  // scale bytes: dword plane p holds dword p of every row (A rows, then B
-  // rows); lane t of the p-th pass over 384 rows loads (row, dword p)
+  Mx3Lane o;
+  {
+    const int ra = wm * (TM / 2) + r32, rb = wn * 128 + r32;
+    o.a_lo = mx3_off(ra, h);
+    o.a_hi = mx3_off(ra, 2 + h);
+    o.b_lo = TM * 64 + mx3_off(rb, h);
+    o.b_hi = TM * 64 + mx3_off(rb, 2 + h);
+    // group g = row / 16 starts at byte g * KS * 16; row rr of it at 4 rr
+    o.sa = (ra >> 4) * (int)KS * 16 + (ra & 15) * 4;
+    o.sb = ((TM + rb) >> 4) * (int)KS * 16 + ((TM + rb) & 15) * 4;
+    o.ks = (int)KS;
+  }
+  // scale bytes of the tile's rows (A rows, then B rows) in groups of 16
+  // rows, each group dword-major: dword dw of row 16 g + rr sits at dword
+  // (g * KS/4 + dw) * 16 + rr.  A load instruction (64 consecutive dwords of
+  // the area) reads 16 bytes from each of 16 rows; the 32 lanes reading one
+  // block of 32 rows hit two runs of 16 consecutive dwords.
   {
     const uint8_t *Asb = As + ti.row0 * (int64_t)KS;
     const uint8_t *Bsb = Bs + (ti.g * N + ti.n0) * (int64_t)KS;
-    const uint32_t sbase = lds_addr(lds) + mx3::NSLOT * mx3::SLOT;
-    const int nd = (int)(KS / 4);  // dwords per row
-    for (int p = 0; p < nd; ++p) {
-      // 384 rows per plane: waves 0..3 cover rows 64 w .. +63, then 256 + ...
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int row = q * 256 + tid;  // 0..511, rows >= 384 unused
-        if (q == 1 && wave >= 2) continue;  // rows 384..511 do not exist
-        const uint8_t *src = row < GT_M
-                                 ? Asb + (int64_t)min(row, rows_a - 1) * KS + 4 * p
-                                 : Bsb + (int64_t)min(row - GT_M, rows_b - 1) * KS + 4 * p;
-        dma4(src, __builtin_amdgcn_readfirstlane(sbase + (uint32_t)(p * (GT_M + mx3::TN) * 4) +
-                                                 (uint32_t)(q * 1024 + wave * 256)));
-      }
+    const uint32_t sbase =
+        __builtin_amdgcn_readfirstlane(lds_addr(lds) + C::NSLOT * C::SLOT + (uint32_t)wave * 256u);
+    const int dpr = (int)(KS / 4);                  // dwords per row
+    const int nq = (C::ROWS * dpr + 255) / 256;     // passes of 256 dwords
+    for (int q = 0; q < nq; ++q) {
+      const int d = 256 * q + tid;
+      const int g = d / (16 * dpr), rem = d - g * 16 * dpr;
+      const int row = min(16 * g + (rem & 15), C::ROWS - 1), dw = rem >> 4;
+      const uint8_t *src = row < TM ? Asb + (int64_t)min(row, rows_a - 1) * KS + 4 * dw
+                                    : Bsb + (int64_t)min(row - TM, rows_b - 1) * KS + 4 * dw;
+      dma4(src, sbase + 1024u * (uint32_t)q);
     }
   }
 
-  v16f acc[2][4];
+  v16f acc[FI][FJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (int)(K / 64);
-  mx3_issue<0>(L, 0);
-  if (nk > 1) mx3_issue<1>(L, 1);
-  if (nk > 2) mx3_issue<2>(L, 2);
-  int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    mx3_step<0>(L, lds, kt, nk, acc, wm, wn, lane);
-    mx3_step<1>(L, lds, kt + 1, nk, acc, wm, wn, lane);
-    mx3_step<2>(L, lds, kt + 2, nk, acc, wm, wn, lane);
-    mx3_step<3>(L, lds, kt + 3, nk, acc, wm, wn, lane);
+  const int nk = (int)(K / 64);  // even, >= 2
+  mx3_issue<TM>(L, 0, 0);
+  mx3_issue<TM>(L, 1, 1);
+  mx3_issue<TM>(L, min(2, nk - 1), 2);
+  vm_wait<2 * C::OPS>();  // the scale area and step 0
+  __builtin_amdgcn_s_barrier();
+  Mx3Frags<TM> F0, F1;
+  mx3_read<TM>(lds, 0, 0, o, F0);
+  int slot = 0;
+  for (int kt = 0; kt < nk; kt += 2) {
+    mx3_step<TM>(L, lds, o, kt, nk, slot, acc, F0, F1);
+    slot = slot == 2 ? 0 : slot + 1;
+    mx3_step<TM>(L, lds, o, kt + 1, nk, slot, acc, F1, F0);
+    slot = slot == 2 ? 0 : slot + 1;
   }
-  if (kt < nk) mx3_step<0>(L, lds, kt, nk, acc, wm, wn, lane);
-  if (kt + 1 < nk) mx3_step<1>(L, lds, kt + 1, nk, acc, wm, wn, lane);
-  if (kt + 2 < nk) mx3_step<2>(L, lds, kt + 2, nk, acc, wm, wn, lane);
+  vm_wait<0>();  // no load may still target this workgroup's LDS at exit
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
+    for (int j = 0; j < FJ; ++j)
+      mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (TM / 2) + 32 * i,
                          wn * 128 + 32 * j);
 }
 
@@ -795,6 +906,11 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+#ifndef PQM_MX_PIPE_TM
+#define PQM_MX_PIPE_TM 256
+#endif
+constexpr int MX_PIPE_TM = PQM_MX_PIPE_TM;  // row tile of the pipelined MXFP8 kernel
+
 hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *a_scale,
                                const float *a_outer, const void *b, const uint8_t *b_scale,
                                const float *b_outer, int64_t b_rows_per_scale,
@@ -819,15 +935,16 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
   int64_t tiles = (cdiv(M, GT_M) + G) * ntn;
   tiles = cdiv(tiles, 8) * 8;
   const dim3 grid((unsigned)tiles);
-  if (fmt == 1 && K % 128 == 0 && K / 32 <= mx3::MAX_KS) {
+  if (fmt == 1 && K % 128 == 0 && K / 32 <= Mx3<MX_PIPE_TM>::MAX_KS) {
+    constexpr int TM = MX_PIPE_TM;
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
-    const int64_t ntn_b = cdiv(N, mx3::TN);
-    const dim3 grid_b((unsigned)(cdiv((cdiv(M, GT_M) + G) * ntn_b, 8) * 8));
+    const int64_t ntn_b = cdiv(N, Mx3<TM>::TN);
+    const dim3 grid_b((unsigned)(cdiv((cdiv(M, TM) + G) * ntn_b, 8) * 8));
     if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, B,
+      hipLaunchKernelGGL((k_gemm_mxfp8_pipe<true, TM>), grid_b, dim3(256), 0, st, A, a_scale, B,
                          b_scale, offsets, G, N, K, ntn_b, out);
     else
-      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, B,
+      hipLaunchKernelGGL((k_gemm_mxfp8_pipe<false, TM>), grid_b, dim3(256), 0, st, A, a_scale, B,
                          b_scale, offsets, G, N, K, ntn_b, out);
     return hipGetLastError();
   }
