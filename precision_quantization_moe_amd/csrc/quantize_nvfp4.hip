@@ -11,15 +11,21 @@
 // the sign of A - 2688 s_g (see nvfp4_block); no per-element division.
 //
 // Group scope (one outer scale for rows_per_scale rows, e.g. an expert's
-// fused gate/up weight): a first kernel reduces each group's maximum into a
-// device word with atomicMax on the bf16 magnitude bits; the second kernel
-// is the per-row kernel reading that word.  Groups are processed in chunks
-// of about 64 MB so the second read of a chunk is served from the
-// Infinity Cache rather than HBM.
+// fused gate/up weight): a first kernel reduces each group's maximum with
+// atomicMax on the bf16 magnitude bits into AMAX_SLOTS words of the group,
+// each in its own 128-byte line (same-line atomics from hundreds of
+// workgroups serialise and cost as much as the whole read); the second
+// kernel is the per-row kernel, whose waves fold the slots.  Groups are
+// processed in chunks of about 64 MB so the second read of a chunk is
+// served from the Infinity Cache rather than HBM.
 #include "pqm_device.hpp"
 #include "pqm_internal.hpp"
 
 namespace pqm {
+
+// Group-maximum slots per group and their spacing in 32-bit words.
+constexpr int AMAX_SLOTS = 16;
+constexpr int AMAX_STRIDE = 32;
 
 // Row constants of the NVFP4 encoding (one wave per row, so all of these are
 // wave-uniform).
@@ -175,7 +181,7 @@ __device__ __forceinline__ uint2 nvfp4_block(const uint32_t w[8], const Nvfp4Row
 // One wave per row, one row per wave.  Lane l owns the 1x16 blocks l + 64 j
 // (two 16-byte loads each), all issued before any use; NB blocks per lane
 // (cols <= 1024 NB).  When amax_ws is non-null the outer scale comes from
-// the group word amax_ws[row / rows_per_scale] instead of the row.
+// the group's slot words (row / rows_per_scale) instead of the row.
 template <int NB>
 __global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
     const uint16_t *__restrict__ x, uint32_t C, int64_t ld, uint32_t row_begin,
@@ -201,7 +207,10 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
   const uint32_t grp = amax_ws ? row / rows_per_scale : row;
   float A;
   if (amax_ws) {
-    A = __uint_as_float(amax_ws[grp] << 16);
+    uint32_t m = lane < AMAX_SLOTS ? amax_ws[((size_t)grp * AMAX_SLOTS + lane) * AMAX_STRIDE] : 0u;
+#pragma unroll
+    for (int o = AMAX_SLOTS / 2; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    A = __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)m) << 16);
   } else {
     uint32_t m = 0;
 #pragma unroll
@@ -233,8 +242,9 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
 
 // Group maximum: each workgroup reduces rows_per_wg rows of one group (wave
 // w takes rows w, w+4, ...; 16-byte loads, packed 16-bit max) and folds the
-// result into amax_ws[group] with one atomicMax (bf16 magnitude bits:
-// integer order equals value order for non-negative finite values).
+// result with one atomicMax into slot blockIdx % AMAX_SLOTS of its group
+// (bf16 magnitude bits: integer order equals value order for non-negative
+// finite values).
 template <int NB>
 __global__ __launch_bounds__(256) void k_group_amax(
     const uint16_t *__restrict__ x, int64_t C, int64_t ld, int64_t row_begin,
@@ -270,7 +280,9 @@ __global__ __launch_bounds__(256) void k_group_amax(
   __syncthreads();
   if (threadIdx.x == 0) {
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    atomicMax(&amax_ws[r0 / rows_per_scale], m);
+    atomicMax(&amax_ws[((r0 / rows_per_scale) * AMAX_SLOTS + blockIdx.x % AMAX_SLOTS) *
+                       AMAX_STRIDE],
+              m);
   }
 }
 
@@ -304,7 +316,7 @@ int64_t nvfp4_max_cols() { return 16 * 1024; }
 
 size_t nvfp4_workspace_bytes(int64_t R, int64_t rows_per_scale) {
   if (rows_per_scale <= 1 || R == 0) return 0;
-  return (size_t)(R / rows_per_scale) * sizeof(uint32_t);
+  return (size_t)(R / rows_per_scale) * AMAX_SLOTS * AMAX_STRIDE * sizeof(uint32_t);
 }
 
 hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
@@ -317,13 +329,16 @@ hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t R, int64_t C, int64_
   }
   uint32_t *ws = static_cast<uint32_t *>(workspace);
   const int64_t G = R / rows_per_scale;
-  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((G + 255) / 256)), dim3(256), 0, st, ws, G, 0u);
+  const int64_t nws = G * AMAX_SLOTS * AMAX_STRIDE;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nws + 255) / 256)), dim3(256), 0, st, ws, nws,
+                     0u);
   const int64_t group_bytes = rows_per_scale * C * 2;
   int64_t groups_per_chunk = ((int64_t)64 << 20) / (group_bytes > 0 ? group_bytes : 1);
   if (groups_per_chunk < 1) groups_per_chunk = 1;
-  // rows per amax workgroup: about 64 KB of input each, within one group
-  int64_t rpw = (65536 / (C * 2));
-  if (rpw < 1) rpw = 1;
+  // rows per amax workgroup: about 16 KB of input each (at least one row
+  // per wave), within one group
+  int64_t rpw = 16384 / (C * 2);
+  if (rpw < 4) rpw = 4;
   while (rows_per_scale % rpw) --rpw;
   const int64_t per_lane = (C / 16 + 63) / 64;
   for (int64_t g0 = 0; g0 < G; g0 += groups_per_chunk) {

@@ -69,7 +69,7 @@ def test_quantize_nvfp4_validation():
     assert f(A16, 64, 64, 64, 1, None, A16, A16, None, 0, None) == 1
     assert f(A16, 64, 64, 64, 32, A16, A16, A16, None, 0, None) == 1   # ws needed
     need = L.pqm_quantize_nvfp4_workspace(64, 64, 32)
-    assert need == 8
+    assert need == 2 * 16 * 128   # 2 groups x 16 max slots, one 128-byte line each
     assert f(A16, 64, 64, 64, 32, A16, A16, A16, A16, need - 1, None) == 5
     assert f(BAD, 64, 64, 64, 1, A16, A16, A16, None, 0, None) == 3
     assert f(A16, 64, 1 << 20, 1 << 20, 1, A16, A16, A16, None, 0, None) == 2
