@@ -11,13 +11,13 @@
 // the sign of A - 2688 s_g (see nvfp4_block); no per-element division.
 //
 // Group scope (one outer scale for rows_per_scale rows, e.g. an expert's
-// fused gate/up weight): a first kernel reduces each group's maximum with
-// atomicMax on the bf16 magnitude bits into AMAX_SLOTS words of the group,
-// each in its own 128-byte line (same-line atomics from hundreds of
-// workgroups serialise and cost as much as the whole read); the second
-// kernel is the per-row kernel, whose waves fold the slots.  Groups are
-// processed in chunks of about 64 MB so the second read of a chunk is
-// served from the Infinity Cache rather than HBM.
+// fused gate/up weight): the group maximum is reduced with atomicMax on the
+// bf16 magnitude bits into AMAX_SLOTS words of the group, each in its own
+// 128-byte line (same-line atomics from hundreds of workgroups serialise
+// and cost as much as the whole read); the quantizing waves fold the slots.
+// Groups go in chunks of about 64 MB, and one launch both quantizes chunk
+// j-1 and reduces the maxima of chunk j, so chunk j-1's second read is
+// served from the Infinity Cache while chunk j streams in from HBM.
 #include "pqm_device.hpp"
 #include "pqm_internal.hpp"
 
@@ -178,19 +178,18 @@ __device__ __forceinline__ uint2 nvfp4_block(const uint32_t w[8], const Nvfp4Row
   return out;
 }
 
-// One wave per row, one row per wave.  Lane l owns the 1x16 blocks l + 64 j
-// (two 16-byte loads each), all issued before any use; NB blocks per lane
-// (cols <= 1024 NB).  When amax_ws is non-null the outer scale comes from
-// the group's slot words (row / rows_per_scale) instead of the row.
+// One wave per row: lane l owns the 1x16 blocks l + 64 j (two 16-byte loads
+// each), all issued before any use; NB blocks per lane (cols <= 1024 NB).
+// When amax_ws is non-null the outer scale comes from the group's slot
+// words (row / rows_per_scale) instead of the row.
 template <int NB>
-__global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
-    const uint16_t *__restrict__ x, uint32_t C, int64_t ld, uint32_t row_begin,
-    uint32_t row_end, uint32_t rows_per_scale, const uint32_t *__restrict__ amax_ws,
-    uint8_t *__restrict__ q, uint8_t *__restrict__ sb, float *__restrict__ sg) {
+__device__ __forceinline__ void nvfp4_row_wave(const uint16_t *__restrict__ x, uint32_t C,
+                                               int64_t ld, uint32_t row, uint32_t rows_per_scale,
+                                               const uint32_t *__restrict__ amax_ws,
+                                               uint8_t *__restrict__ q, uint8_t *__restrict__ sb,
+                                               float *__restrict__ sg) {
   const int lane = threadIdx.x & 63;
   const uint32_t nblk = C / 16;
-  const uint32_t row = row_begin + blockIdx.x * 4u + (threadIdx.x >> 6);
-  if (row >= row_end) return;  // whole wave exits together
   const uint16_t *xr = x + (int64_t)row * ld;
   uint32_t w[NB][8];
 #pragma unroll
@@ -240,21 +239,27 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
   }
 }
 
-// Group maximum: each workgroup reduces rows_per_wg rows of one group (wave
-// w takes rows w, w+4, ...; 16-byte loads, packed 16-bit max) and folds the
-// result with one atomicMax into slot blockIdx % AMAX_SLOTS of its group
-// (bf16 magnitude bits: integer order equals value order for non-negative
-// finite values).
+// Per-token scope: workgroup b quantizes rows 4b .. 4b+3, one per wave.
 template <int NB>
-__global__ __launch_bounds__(256) void k_group_amax(
-    const uint16_t *__restrict__ x, int64_t C, int64_t ld, int64_t row_begin,
-    int64_t row_end, int64_t rows_per_scale, int64_t rows_per_wg,
-    uint32_t *__restrict__ amax_ws) {
+__global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(
+    const uint16_t *__restrict__ x, uint32_t C, int64_t ld, uint32_t rows,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ sb, float *__restrict__ sg) {
+  const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave exits together
+  nvfp4_row_wave<NB>(x, C, ld, row, 1u, nullptr, q, sb, sg);
+}
+
+// Group maximum of rows [r0, r1) (all in one group; wave w takes rows w,
+// w+4, ...; 16-byte loads, packed 16-bit max), folded with one atomicMax
+// into slot `slot` of the group (bf16 magnitude bits: integer order equals
+// value order for non-negative finite values).  Whole workgroup.
+template <int NB>
+__device__ __forceinline__ void group_amax_wg(const uint16_t *__restrict__ x, int64_t C,
+                                              int64_t ld, int64_t r0, int64_t r1,
+                                              int64_t rows_per_scale, int slot,
+                                              uint32_t *__restrict__ amax_ws) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nblk = C / 16;
-  const int64_t r0 = row_begin + (int64_t)blockIdx.x * rows_per_wg;
-  int64_t r1 = r0 + rows_per_wg;
-  if (r1 > row_end) r1 = row_end;
   uint32_t m = 0;
 #pragma unroll 4
   for (int64_t r = r0 + wave; r < r1; r += 4) {
@@ -280,9 +285,43 @@ __global__ __launch_bounds__(256) void k_group_amax(
   __syncthreads();
   if (threadIdx.x == 0) {
     m = max(max(red[0], red[1]), max(red[2], red[3]));
-    atomicMax(&amax_ws[((r0 / rows_per_scale) * AMAX_SLOTS + blockIdx.x % AMAX_SLOTS) *
-                       AMAX_STRIDE],
-              m);
+    atomicMax(&amax_ws[((r0 / rows_per_scale) * AMAX_SLOTS + slot) * AMAX_STRIDE], m);
+  }
+}
+
+// One step of the group-scope pipeline: quantize rows [qb, qe) (whose group
+// maxima are complete) and reduce the group maxima of rows [ab, ae), in one
+// launch.  Workgroups alternate between the two roles while both have work,
+// so the reduction's HBM reads overlap the quantization's cache-served
+// re-reads.  nq / na: workgroups of each role (4 rows, resp. rpw rows each).
+struct Nvfp4Step {
+  int64_t qb, qe, ab, ae, rpw;
+  uint32_t nq, na;
+};
+
+template <int NB>
+__global__ __launch_bounds__(256) void k_nvfp4_group_step(
+    const uint16_t *__restrict__ x, uint32_t C, int64_t ld, uint32_t rows_per_scale,
+    Nvfp4Step p, uint32_t *__restrict__ amax_ws, uint8_t *__restrict__ q,
+    uint8_t *__restrict__ sb, float *__restrict__ sg) {
+  const uint32_t b = blockIdx.x, both = min(p.nq, p.na);
+  bool quant;
+  uint32_t idx;
+  if (b < 2u * both) {
+    quant = (b & 1u) == 0u;
+    idx = b >> 1;
+  } else {
+    quant = p.nq > p.na;
+    idx = b - both;
+  }
+  if (quant) {
+    const int64_t row = p.qb + (int64_t)idx * 4 + (threadIdx.x >> 6);
+    if (row >= p.qe) return;  // whole wave exits together
+    nvfp4_row_wave<NB>(x, C, ld, (uint32_t)row, rows_per_scale, amax_ws, q, sb, sg);
+  } else {
+    const int64_t r0 = p.ab + (int64_t)idx * p.rpw;
+    const int64_t r1 = r0 + p.rpw < p.ae ? r0 + p.rpw : p.ae;
+    group_amax_wg<NB>(x, C, ld, r0, r1, rows_per_scale, (int)(idx % AMAX_SLOTS), amax_ws);
   }
 }
 
@@ -292,24 +331,30 @@ __global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
 }
 
 template <int NB>
-static void launch_rows(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int64_t rb,
-                        int64_t re, int64_t rps, const uint32_t *ws, uint8_t *q,
-                        uint8_t *sb, float *sg, hipStream_t st) {
-  (void)R;
-  const unsigned grid = (unsigned)((re - rb + 3) / 4);
-  hipLaunchKernelGGL((k_quantize_nvfp4_rows<NB>), dim3(grid), dim3(256), 0, st, x, (uint32_t)C,
-                     ld, (uint32_t)rb, (uint32_t)re, (uint32_t)rps, ws, q, sb, sg);
+static void launch_nb(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int64_t rps,
+                      const Nvfp4Step *step, uint32_t *ws, uint8_t *q, uint8_t *sb, float *sg,
+                      hipStream_t st) {
+  if (!step) {
+    const unsigned grid = (unsigned)((R + 3) / 4);
+    hipLaunchKernelGGL((k_quantize_nvfp4_rows<NB>), dim3(grid), dim3(256), 0, st, x,
+                       (uint32_t)C, ld, (uint32_t)R, q, sb, sg);
+  } else {
+    const unsigned grid = step->nq + step->na;
+    hipLaunchKernelGGL((k_nvfp4_group_step<NB>), dim3(grid), dim3(256), 0, st, x, (uint32_t)C,
+                       ld, (uint32_t)rps, *step, ws, q, sb, sg);
+  }
 }
 
-static void dispatch_rows(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int64_t rb,
-                          int64_t re, int64_t rps, const uint32_t *ws, uint8_t *q,
-                          uint8_t *sb, float *sg, hipStream_t st) {
+// step == nullptr: the per-token kernel over all R rows.
+static void dispatch_nb(const uint16_t *x, int64_t R, int64_t C, int64_t ld, int64_t rps,
+                        const Nvfp4Step *step, uint32_t *ws, uint8_t *q, uint8_t *sb,
+                        float *sg, hipStream_t st) {
   const int64_t per_lane = (C / 16 + 63) / 64;
-  if (per_lane <= 1) launch_rows<1>(x, R, C, ld, rb, re, rps, ws, q, sb, sg, st);
-  else if (per_lane <= 2) launch_rows<2>(x, R, C, ld, rb, re, rps, ws, q, sb, sg, st);
-  else if (per_lane <= 4) launch_rows<4>(x, R, C, ld, rb, re, rps, ws, q, sb, sg, st);
-  else if (per_lane <= 8) launch_rows<8>(x, R, C, ld, rb, re, rps, ws, q, sb, sg, st);
-  else launch_rows<16>(x, R, C, ld, rb, re, rps, ws, q, sb, sg, st);
+  if (per_lane <= 1) launch_nb<1>(x, R, C, ld, rps, step, ws, q, sb, sg, st);
+  else if (per_lane <= 2) launch_nb<2>(x, R, C, ld, rps, step, ws, q, sb, sg, st);
+  else if (per_lane <= 4) launch_nb<4>(x, R, C, ld, rps, step, ws, q, sb, sg, st);
+  else if (per_lane <= 8) launch_nb<8>(x, R, C, ld, rps, step, ws, q, sb, sg, st);
+  else launch_nb<16>(x, R, C, ld, rps, step, ws, q, sb, sg, st);
 }
 
 int64_t nvfp4_max_cols() { return 16 * 1024; }
@@ -319,45 +364,54 @@ size_t nvfp4_workspace_bytes(int64_t R, int64_t rows_per_scale) {
   return (size_t)(R / rows_per_scale) * AMAX_SLOTS * AMAX_STRIDE * sizeof(uint32_t);
 }
 
-hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
-                                 int64_t rows_per_scale, uint8_t *q, uint8_t *sb, float *sg,
-                                 void *workspace, hipStream_t st) {
-  if (R == 0 || C == 0) return hipSuccess;
-  if (rows_per_scale == 1) {
-    dispatch_rows(x, R, C, ld, 0, R, 1, nullptr, q, sb, sg, st);
-    return hipGetLastError();
-  }
+// Group scope in chunks of whole groups of about chunk_bytes of input:
+// launch j quantizes chunk j-1 and reduces the maxima of chunk j.
+hipError_t launch_quantize_nvfp4_chunked(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
+                                         int64_t rows_per_scale, uint8_t *q, uint8_t *sb,
+                                         float *sg, void *workspace, int64_t chunk_bytes,
+                                         hipStream_t st) {
   uint32_t *ws = static_cast<uint32_t *>(workspace);
   const int64_t G = R / rows_per_scale;
   const int64_t nws = G * AMAX_SLOTS * AMAX_STRIDE;
   hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nws + 255) / 256)), dim3(256), 0, st, ws, nws,
                      0u);
   const int64_t group_bytes = rows_per_scale * C * 2;
-  int64_t groups_per_chunk = ((int64_t)64 << 20) / (group_bytes > 0 ? group_bytes : 1);
-  if (groups_per_chunk < 1) groups_per_chunk = 1;
-  // rows per amax workgroup: about 16 KB of input each (at least one row
-  // per wave), within one group
+  int64_t gpc = chunk_bytes / (group_bytes > 0 ? group_bytes : 1);  // groups per chunk
+  if (gpc < 1) gpc = 1;
+  // rows per reducing workgroup: about 16 KB of input (at least one row per
+  // wave), dividing rows_per_scale so that a workgroup stays in one group
   int64_t rpw = 16384 / (C * 2);
   if (rpw < 4) rpw = 4;
   while (rows_per_scale % rpw) --rpw;
-  const int64_t per_lane = (C / 16 + 63) / 64;
-  for (int64_t g0 = 0; g0 < G; g0 += groups_per_chunk) {
-    const int64_t g1 = (g0 + groups_per_chunk < G) ? g0 + groups_per_chunk : G;
-    const int64_t rb = g0 * rows_per_scale, re = g1 * rows_per_scale;
-    const dim3 ga((unsigned)((re - rb) / rpw));
-    if (per_lane <= 1)
-      hipLaunchKernelGGL(k_group_amax<1>, ga, dim3(256), 0, st, x, C, ld, rb, re, rows_per_scale, rpw, ws);
-    else if (per_lane <= 2)
-      hipLaunchKernelGGL(k_group_amax<2>, ga, dim3(256), 0, st, x, C, ld, rb, re, rows_per_scale, rpw, ws);
-    else if (per_lane <= 4)
-      hipLaunchKernelGGL(k_group_amax<4>, ga, dim3(256), 0, st, x, C, ld, rb, re, rows_per_scale, rpw, ws);
-    else if (per_lane <= 8)
-      hipLaunchKernelGGL(k_group_amax<8>, ga, dim3(256), 0, st, x, C, ld, rb, re, rows_per_scale, rpw, ws);
-    else
-      hipLaunchKernelGGL(k_group_amax<16>, ga, dim3(256), 0, st, x, C, ld, rb, re, rows_per_scale, rpw, ws);
-    dispatch_rows(x, R, C, ld, rb, re, rows_per_scale, ws, q, sb, sg, st);
+  const int64_t rows_per_chunk = gpc * rows_per_scale;
+  const int64_t nchunk = (G + gpc - 1) / gpc;
+  for (int64_t j = 0; j <= nchunk; ++j) {
+    Nvfp4Step p{0, 0, 0, 0, rpw, 0u, 0u};
+    if (j > 0) {
+      p.qb = (j - 1) * rows_per_chunk;
+      p.qe = p.qb + rows_per_chunk < R ? p.qb + rows_per_chunk : R;
+      p.nq = (uint32_t)((p.qe - p.qb + 3) / 4);
+    }
+    if (j < nchunk) {
+      p.ab = j * rows_per_chunk;
+      p.ae = p.ab + rows_per_chunk < R ? p.ab + rows_per_chunk : R;
+      p.na = (uint32_t)((p.ae - p.ab) / rpw);
+    }
+    dispatch_nb(x, R, C, ld, rows_per_scale, &p, ws, q, sb, sg, st);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
+                                 int64_t rows_per_scale, uint8_t *q, uint8_t *sb, float *sg,
+                                 void *workspace, hipStream_t st) {
+  if (R == 0 || C == 0) return hipSuccess;
+  if (rows_per_scale == 1) {
+    dispatch_nb(x, R, C, ld, 1, nullptr, nullptr, q, sb, sg, st);
+    return hipGetLastError();
+  }
+  return launch_quantize_nvfp4_chunked(x, R, C, ld, rows_per_scale, q, sb, sg, workspace,
+                                       (int64_t)64 << 20, st);
 }
 
 }  // namespace pqm
