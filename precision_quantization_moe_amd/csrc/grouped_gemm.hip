@@ -482,18 +482,16 @@ __device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds
   mx3_mma<TM>(cur, acc);
 }
 
+// One TM x 256 output tile (rows ti.row0 .. min(ti.row0 + TM, ti.row_end)).
 template <bool OUT_F32, int TM>
-__global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
-    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
-    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    void *__restrict__ out) {
+__device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
+                                         const uint8_t *__restrict__ As,
+                                         const uint8_t *__restrict__ B,
+                                         const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
+                                         const TileInfo &ti, uint8_t *lds,
+                                         void *__restrict__ out) {
   using C = Mx3<TM>;
   constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
-  __shared__ int64_t sh[4];
-  TileInfo ti;
-  if (!lookup_row_tile<TN, TM>(offsets, G, ntn, ti, sh)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
   const uint32_t KS = (uint32_t)(K / 32), Ku = (uint32_t)K;
@@ -579,6 +577,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
     for (int j = 0; j < FJ; ++j)
       mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (TM / 2) + 32 * i,
                          wn * 128 + 32 * j);
+}
+
+// Row tiles of 256 tokens; an expert's last tile holding 128 rows or fewer
+// (the remainder of a ragged expert, or a whole small one) runs as a
+// 128 x 256 tile, which halves its MFMA and operand traffic.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    void *__restrict__ out) {
+  static_assert(Mx3<128>::LDS <= Mx3<256>::LDS, "LDS of the half tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Mx3<256>::LDS];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
+  if (ti.row_end - ti.row0 <= 128)
+    mx3_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ti, lds, out);
+  else
+    mx3_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ti, lds, out);
 }
 
 // ------------------------------------------------------------------- BF16
@@ -906,11 +924,6 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-#ifndef PQM_MX_PIPE_TM
-#define PQM_MX_PIPE_TM 256
-#endif
-constexpr int MX_PIPE_TM = PQM_MX_PIPE_TM;  // row tile of the pipelined MXFP8 kernel
-
 hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *a_scale,
                                const float *a_outer, const void *b, const uint8_t *b_scale,
                                const float *b_outer, int64_t b_rows_per_scale,
@@ -935,16 +948,15 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
   int64_t tiles = (cdiv(M, GT_M) + G) * ntn;
   tiles = cdiv(tiles, 8) * 8;
   const dim3 grid((unsigned)tiles);
-  if (fmt == 1 && K % 128 == 0 && K / 32 <= Mx3<MX_PIPE_TM>::MAX_KS) {
-    constexpr int TM = MX_PIPE_TM;
+  if (fmt == 1 && K % 128 == 0 && K / 32 <= Mx3<256>::MAX_KS && K / 32 <= Mx3<128>::MAX_KS) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
-    const int64_t ntn_b = cdiv(N, Mx3<TM>::TN);
-    const dim3 grid_b((unsigned)(cdiv((cdiv(M, TM) + G) * ntn_b, 8) * 8));
+    const int64_t ntn_b = cdiv(N, Mx3<256>::TN);
+    const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
     if (out_fp32)
-      hipLaunchKernelGGL((k_gemm_mxfp8_pipe<true, TM>), grid_b, dim3(256), 0, st, A, a_scale, B,
+      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, B,
                          b_scale, offsets, G, N, K, ntn_b, out);
     else
-      hipLaunchKernelGGL((k_gemm_mxfp8_pipe<false, TM>), grid_b, dim3(256), 0, st, A, a_scale, B,
+      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, B,
                          b_scale, offsets, G, N, K, ntn_b, out);
     return hipGetLastError();
   }

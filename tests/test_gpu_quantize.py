@@ -155,7 +155,7 @@ def test_nvfp4_per_token_widths(cols):
 
 def test_nvfp4_per_group_scopes():
     x = np.concatenate([wl.activations(64, 256, seed=12), wl.boundary_tensor(cols=256)])
-    for rps in (2, 8, 32, 96):
+    for rps in (2, 3, 6, 8, 32, 48, 96):
         _check_nvfp4(x, "group", rps=rps)
 
 
