@@ -11,9 +11,10 @@
 //
 // MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 consumes E4M3 operands with one
 // E8M0 scale per 32 K-values per row, which is the MXFP8 block layout, so
-// the scales go to the matrix core unchanged.  K % 128 == 0 (K <= 3072) runs
-// the pipelined 128 x 256 kernel (k_gemm_mxfp8_pipe); other K the simpler
-// 128 x 128 kernel with register-staged tiles.  Lane layout (verified on the
+// the scales go to the matrix core unchanged.  K % 128 == 0 (K <= 2048) runs
+// the pipelined 256 x 256 kernel (k_gemm_mxfp8_pipe, an expert's last tile
+// of at most 128 rows as 128 x 256); other K the simpler 128 x 128 kernel
+// with register-staged tiles.  Lane layout (verified on the
 // hardware): a lane holds row (lane % 32); its bytes 0-15 are K
 // 16*(lane/32) .. +15 of the first 32-block and bytes 16-31 the same offsets
 // in the second block; lane 32*b + r supplies the scale of row r, block b.
