@@ -777,6 +777,333 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_wgrad(
       store_acc<OUT_F32>(acc[i][j], o, K, n0, N, k0, K, wm * 64 + 32 * i, wn * 64 + 32 * j);
 }
 
+// ---------------------------------------------- BF16, pipelined large tiles
+//
+// The MXFP8 pipeline above (3-slot ring of direct global->LDS loads, operands
+// read one step ahead, 256 x 256 tiles with 128 x 128 per wave in AGPRs,
+// transposed accumulators with 16-byte stores) carrying bf16 operands: a step
+// is 32 contraction values, i.e. two v_mfma_f32_32x32x16_bf16 per fragment
+// pair.  An operand is staged in one of two layouts of TM x 64 bytes:
+//  * KL, contraction contiguous in memory (FPROP operands, DGRAD's tokens):
+//    TM rows of 64 bytes, the MXFP8 ring's swizzle, 16-byte LDS reads;
+//  * ML, contraction strided (DGRAD's weight, both WGRAD operands): 32
+//    contraction rows of 256 outputs (512 bytes, 32 chunks of 16 bytes, chunk
+//    x of row r stored at x ^ 4 f(r), f(r) = (r & 3) | ((r >> 3) & 1) << 2),
+//    read with the gfx950 transposing LDS read ds_read_b64_tr_b16.  Within
+//    each group of 16 lanes that read gives lane i, as its element e, element
+//    i % 4 of the 8 bytes addressed by lane 4 e + i / 4 (measured); so lanes
+//    4 r + c addressing row r, outputs 4 c .. 4 c + 3 of a 4-row x 16-output
+//    block leave lane i with the 4 contraction values of output i.  Lanes
+//    16 q + j read rows 8 (q / 2) + j / 4 (+ 4, + 16) and outputs
+//    16 (q % 2) + 4 (j % 4): the 8 rows of one read have 8 different f, so
+//    its 64 lanes touch 32 distinct chunks.
+// WGRAD contracts over a group's rows, any number of them: steps past the
+// group's end load a zero line instead, and the step count is rounded up
+// to even.
+enum { BP_FPROP = 0, BP_DGRAD = 1, BP_WGRAD = 2 };
+
+template <int TM>
+struct Bp {
+  static constexpr int TN = 256;
+  static constexpr int SLOT = (TM + TN) * 64;
+  static constexpr int NSLOT = 3;
+  static constexpr int LDS = NSLOT * SLOT;
+  static constexpr int CA = TM / 64, CB = TN / 64, OPS = CA + CB;
+  static constexpr int FI = TM / 64, FJ = 4;
+};
+
+// 1 KB of zeros: the load source of contraction rows past a group's end.
+__device__ uint4 g_bp_zero[64];
+
+template <int TM>
+struct BpSrc {
+  const uint8_t *Ab, *Bb;                      // panel bases
+  uint32_t oa[Bp<TM>::CA], ob[Bp<TM>::CB];     // per-lane offsets of step 0
+  uint32_t sa, sb;                             // bytes per step
+  uint32_t dst;                                // LDS address of slot 0, this wave
+};
+
+__device__ __forceinline__ int bp_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+
+// Per-lane byte offset (within a step) of the chunks of a KL operand of
+// `rows` valid rows and row stride `ld` bytes.
+template <int C>
+__device__ __forceinline__ void bp_offsets_kl(uint32_t (&o)[C], int rows, uint32_t ld) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    o[i] = (uint32_t)min(r, rows - 1) * ld + 16u * k;
+  }
+}
+
+// ... of an ML operand with `cols` valid outputs (a multiple of 8) and
+// contraction-row stride `ld` bytes.
+template <int C>
+__device__ __forceinline__ void bp_offsets_ml(uint32_t (&o)[C], int cols, uint32_t ld) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int c = tid + 256 * i, r = c >> 5, x = (c & 31) ^ (4 * bp_swz(r));
+    o[i] = (uint32_t)r * ld + 16u * (uint32_t)min(x, cols / 8 - 1);
+  }
+}
+
+// Request step kt into `slot`.  WGRAD: contraction rows at or past `len`
+// read zeros.
+template <int TM, int KIND>
+__device__ __forceinline__ void bp_issue(const BpSrc<TM> &L, int kt, int slot, int len) {
+  using C = Bp<TM>;
+  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT;
+  const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_bp_zero) + 16 * (threadIdx.x & 63);
+  const int r0 = kt * 32 + ((int)threadIdx.x >> 5);  // contraction row of chunk 0 (ML)
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) {
+    const uint8_t *src = L.Ab + (L.oa[i] + (uint32_t)kt * L.sa);
+    if (KIND == BP_WGRAD && r0 + 8 * i >= len) src = zero;
+    dma16(src, base + i * 4096);
+  }
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const uint8_t *src = L.Bb + (L.ob[i] + (uint32_t)kt * L.sb);
+    if (KIND == BP_WGRAD && r0 + 8 * i >= len) src = zero;
+    dma16(src, base + TM * 64 + i * 4096);
+  }
+}
+
+template <int TM>
+struct BpFrags {
+  uint4 a[Bp<TM>::FI][2], b[Bp<TM>::FJ][2];  // [fragment][16-K sub-step]
+};
+
+typedef short pqm_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) pqm_v4s pqm_lds_v4s;
+
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t *p) {
+  const pqm_v4s v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((pqm_lds_v4s *)(const_cast<uint8_t *>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Fragments of one operand (F fragments of 32 outputs) from the ring region
+// `reg`.  KL: off[0] / off[1] = the lane's chunk-h / chunk-(2+h) offsets of
+// fragment 0, fragments 2048 bytes apart.  ML: off[f] = the lane's offset for
+// fragment f; sub-step s, read r at + (16 s + 4 r) * 512.
+template <int F, bool ML>
+__device__ __forceinline__ void bp_read_op(const uint8_t *reg, const int *off, uint4 (&fr)[F][2]) {
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    if (ML) {
+      const uint8_t *p = reg + off[f];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint2 r0 = lds_read_tr16(p + (16 * s) * 512);
+        const uint2 r1 = lds_read_tr16(p + (16 * s + 4) * 512);
+        fr[f][s] = make_uint4(r0.x, r0.y, r1.x, r1.y);
+      }
+    } else {
+      fr[f][0] = *reinterpret_cast<const uint4 *>(reg + off[0] + 2048 * f);
+      fr[f][1] = *reinterpret_cast<const uint4 *>(reg + off[1] + 2048 * f);
+    }
+  }
+}
+
+template <int KIND, int TM>
+__device__ __forceinline__ void bp_read(const uint8_t *lds, int slot, const int *offA,
+                                        const int *offB, BpFrags<TM> &F) {
+  const uint8_t *reg = lds + slot * Bp<TM>::SLOT;
+  bp_read_op<Bp<TM>::FI, KIND == BP_WGRAD>(reg, offA, F.a);
+  bp_read_op<Bp<TM>::FJ, KIND != BP_FPROP>(reg, offB, F.b);
+}
+
+// Weights (B) are the first operand, tokens (A) the second: transposed
+// accumulators as in the MXFP8 pipeline.
+template <int TM>
+__device__ __forceinline__ void bp_mma(const BpFrags<TM> &F,
+                                       v16f (&acc)[Bp<TM>::FI][Bp<TM>::FJ]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < Bp<TM>::FJ; ++j)
+#pragma unroll
+      for (int i = 0; i < Bp<TM>::FI; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(v8bf, F.b[j][s]), __builtin_bit_cast(v8bf, F.a[i][s]), acc[i][j],
+            0, 0, 0);
+}
+
+// Step kt from `slot` (operands in `cur`): as mx3_step.
+template <int KIND, int TM>
+__device__ __forceinline__ void bp_step(const BpSrc<TM> &L, const uint8_t *lds, const int *offA,
+                                        const int *offB, int kt, int nk, int slot, int len,
+                                        v16f (&acc)[Bp<TM>::FI][Bp<TM>::FJ],
+                                        const BpFrags<TM> &cur, BpFrags<TM> &next) {
+  vm_wait<Bp<TM>::OPS>();
+  lgkm_wait0();
+  __builtin_amdgcn_s_barrier();
+  bp_issue<TM, KIND>(L, min(kt + 3, nk - 1), slot, len);
+  __builtin_amdgcn_sched_barrier(0);
+  bp_read<KIND, TM>(lds, slot == 2 ? 0 : slot + 1, offA, offB, next);
+  __builtin_amdgcn_sched_barrier(0);
+  bp_mma<TM>(cur, acc);
+}
+
+// One output tile.  Operand panels start at Ab / Bb (bytes); a_lim / b_lim
+// are the valid rows (KL) or outputs (ML) of each; lda / ldb their row
+// strides in bytes (KL: token / weight rows; ML: contraction rows).  len is
+// the contraction length (WGRAD: the group's rows; otherwise K); the output
+// rows row0 .. row_end-1, columns col0 .., row stride ldo.
+struct BpArgs {
+  const uint8_t *Ab, *Bb;
+  int a_lim, b_lim;
+  uint32_t lda, ldb;
+  int len;
+  void *out;
+  int64_t ldo, row0, row_end, col0;
+};
+
+template <int KIND, bool OUT_F32, int TM>
+__device__ __forceinline__ void bp_tile(const BpArgs &p, uint8_t *lds) {
+  static_assert(KIND != BP_WGRAD || TM == 256, "the ML layout is 256 outputs wide");
+  using C = Bp<TM>;
+  constexpr int FI = C::FI, FJ = C::FJ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
+  BpSrc<TM> L;
+  L.Ab = p.Ab;
+  L.Bb = p.Bb;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+  if (KIND == BP_WGRAD) {
+    bp_offsets_ml<C::CA>(L.oa, p.a_lim, p.lda);
+    L.sa = 32u * p.lda;
+  } else {
+    bp_offsets_kl<C::CA>(L.oa, p.a_lim, p.lda);
+    L.sa = 64u;
+  }
+  if (KIND == BP_FPROP) {
+    bp_offsets_kl<C::CB>(L.ob, p.b_lim, p.ldb);
+    L.sb = 64u;
+  } else {
+    bp_offsets_ml<C::CB>(L.ob, p.b_lim, p.ldb);
+    L.sb = 32u * p.ldb;
+  }
+  // lane 16 q + j of an ML read: rows 8 (q / 2) + j / 4 (+ 4 r + 16 s),
+  // outputs 16 (q % 2) + 4 (j % 4) of the fragment; XOR of the row's swizzle
+  const int q = lane >> 4, jj = lane & 15;
+  const int rb0 = (8 * (q >> 1) + (jj >> 2)) * 512 + (2 * (q & 1) + ((jj >> 1) & 1)) * 16 +
+                  8 * (jj & 1);
+  const int xs = 64 * ((jj >> 2) | ((q >> 1) << 2));
+  int offA[FI > 2 ? FI : 2], offB[FJ];
+  if (KIND == BP_WGRAD) {
+#pragma unroll
+    for (int f = 0; f < FI; ++f) offA[f] = rb0 + ((2 * (wm * (TM / 2) + 32 * f)) ^ xs);
+  } else {
+    const int ra = wm * (TM / 2) + r32;
+    offA[0] = mx3_off(ra, h);
+    offA[1] = mx3_off(ra, 2 + h);
+  }
+  if (KIND == BP_FPROP) {
+    const int rb = wn * 128 + r32;
+    offB[0] = TM * 64 + mx3_off(rb, h);
+    offB[1] = TM * 64 + mx3_off(rb, 2 + h);
+  } else {
+#pragma unroll
+    for (int f = 0; f < FJ; ++f) offB[f] = TM * 64 + rb0 + ((2 * (wn * 128 + 32 * f)) ^ xs);
+  }
+
+  v16f acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = 2 * ((p.len + 63) / 64);  // steps of 32, rounded up to even
+  if (nk > 0) {
+    bp_issue<TM, KIND>(L, 0, 0, p.len);
+    bp_issue<TM, KIND>(L, 1, 1, p.len);
+    bp_issue<TM, KIND>(L, min(2, nk - 1), 2, p.len);
+    vm_wait<2 * C::OPS>();  // step 0
+    __builtin_amdgcn_s_barrier();
+    BpFrags<TM> F0, F1;
+    bp_read<KIND, TM>(lds, 0, offA, offB, F0);
+    int slot = 0;
+    for (int kt = 0; kt < nk; kt += 2) {
+      bp_step<KIND, TM>(L, lds, offA, offB, kt, nk, slot, p.len, acc, F0, F1);
+      slot = slot == 2 ? 0 : slot + 1;
+      bp_step<KIND, TM>(L, lds, offA, offB, kt + 1, nk, slot, p.len, acc, F1, F0);
+      slot = slot == 2 ? 0 : slot + 1;
+    }
+    vm_wait<0>();  // no load may still target this workgroup's LDS at exit
+  }
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+      mx3_store<OUT_F32>(acc[i][j], p.out, p.ldo, p.row0, p.row_end, p.col0,
+                         wm * (TM / 2) + 32 * i, wn * 128 + 32 * j);
+}
+
+// FPROP / DGRAD: row tiles of 256 tokens over the groups (an expert's last
+// tile of <= 128 rows as 128 x 256), 256 output columns; K % 64 == 0.
+// WGRAD: tile (g, 256 rows n, 256 columns k) of Y_g, contraction over the
+// group's rows.
+template <int KIND, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_pipe(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    int64_t ntk, void *__restrict__ out) {
+  static_assert(Bp<128>::LDS <= Bp<256>::LDS, "LDS of the half tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Bp<256>::LDS];
+  __shared__ int64_t sh[4];
+  BpArgs p;
+  if constexpr (KIND == BP_WGRAD) {
+    const int64_t t = blockIdx.x;
+    const int64_t g = t / (ntn * ntk);
+    const int64_t n0 = ((t / ntk) % ntn) * 256, k0 = (t % ntk) * 256;
+    const int64_t m0 = offsets[g], m1 = offsets[g + 1];
+    p.Ab = reinterpret_cast<const uint8_t *>(A + m0 * N + n0);
+    p.Bb = reinterpret_cast<const uint8_t *>(B + m0 * K + k0);
+    p.a_lim = (int)min(N - n0, (int64_t)256);
+    p.b_lim = (int)min(K - k0, (int64_t)256);
+    p.lda = (uint32_t)(N * 2);
+    p.ldb = (uint32_t)(K * 2);
+    p.len = (int)(m1 - m0);
+    p.out = OUT_F32 ? (void *)(static_cast<float *>(out) + g * N * K)
+                    : (void *)(static_cast<uint16_t *>(out) + g * N * K);
+    p.ldo = K;
+    p.row0 = n0;
+    p.row_end = N;
+    p.col0 = k0;
+    bp_tile<KIND, OUT_F32, 256>(p, lds);
+  } else {
+  TileInfo ti;
+  if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
+  p.Ab = reinterpret_cast<const uint8_t *>(A + ti.row0 * K);
+  p.a_lim = (int)min(ti.row_end - ti.row0, (int64_t)256);
+  p.lda = (uint32_t)(K * 2);
+  if (KIND == BP_FPROP) {
+    p.Bb = reinterpret_cast<const uint8_t *>(B + (ti.g * N + ti.n0) * K);
+    p.ldb = (uint32_t)(K * 2);
+  } else {
+    p.Bb = reinterpret_cast<const uint8_t *>(B + ti.g * K * N + ti.n0);
+    p.ldb = (uint32_t)(N * 2);
+  }
+  p.b_lim = (int)min(N - ti.n0, (int64_t)256);
+  p.len = (int)K;
+  p.out = out;
+  p.ldo = N;
+  p.row0 = ti.row0;
+  p.row_end = ti.row_end;
+  p.col0 = ti.n0;
+  if (ti.row_end - ti.row0 <= 128)
+    bp_tile<KIND, OUT_F32, 128>(p, lds);
+  else
+    bp_tile<KIND, OUT_F32, 256>(p, lds);
+  }
+}
+
 // ------------------------------------------------------------------ NVFP4
 //
 // E2M1 x E4M3 (q * s_b) has at most 2 + 4 significant bits and lies in
@@ -931,6 +1258,19 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
                                const int64_t *offsets, int64_t G, int64_t M, int64_t N,
                                int64_t K, void *out, int out_fp32, hipStream_t st) {
   if (G == 0 || N == 0) return hipSuccess;
+  const int64_t U32 = (int64_t)1 << 32;  // the pipelined kernels' per-panel byte offsets
+  if (kind == 2 && K > 0 && M * N * 2 < U32 && M * K * 2 < U32) {  // WGRAD (bf16), pipelined
+    const int64_t ntn = cdiv(N, 256), ntk = cdiv(K, 256);
+    const dim3 grid((unsigned)(G * ntn * ntk));
+    const uint16_t *A = static_cast<const uint16_t *>(a), *B = static_cast<const uint16_t *>(b);
+    if (out_fp32)
+      hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_WGRAD, true>), grid, dim3(256), 0, st, A, B,
+                         offsets, G, N, K, ntn, ntk, out);
+    else
+      hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_WGRAD, false>), grid, dim3(256), 0, st, A, B,
+                         offsets, G, N, K, ntn, ntk, out);
+    return hipGetLastError();
+  }
   if (kind == 2) {  // WGRAD (bf16)
     if (K == 0) return hipSuccess;
     const int64_t ntn = cdiv(N, GT_M), ntk = cdiv(K, GT_N);
@@ -969,6 +1309,27 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     else
       hipLaunchKernelGGL(k_gemm_mxfp8<false>, grid, dim3(256), 0, st, A, a_scale, B, b_scale,
                          offsets, G, N, K, ntn, out);
+    return hipGetLastError();
+  }
+  if (fmt == 0 && K % 64 == 0 && (kind == 0 || K * N * 2 < U32)) {
+    const uint16_t *A = static_cast<const uint16_t *>(a), *B = static_cast<const uint16_t *>(b);
+    const int64_t ntn_b = cdiv(N, 256);
+    const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
+    if (kind == 0) {
+      if (out_fp32)
+        hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_FPROP, true>), grid_b, dim3(256), 0, st, A, B,
+                           offsets, G, N, K, ntn_b, (int64_t)0, out);
+      else
+        hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_FPROP, false>), grid_b, dim3(256), 0, st, A, B,
+                           offsets, G, N, K, ntn_b, (int64_t)0, out);
+    } else {
+      if (out_fp32)
+        hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_DGRAD, true>), grid_b, dim3(256), 0, st, A, B,
+                           offsets, G, N, K, ntn_b, (int64_t)0, out);
+      else
+        hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_DGRAD, false>), grid_b, dim3(256), 0, st, A, B,
+                           offsets, G, N, K, ntn_b, (int64_t)0, out);
+    }
     return hipGetLastError();
   }
   if (fmt == 0) {

@@ -150,7 +150,8 @@ def _bf16_operands(M, N, K, G, seed):
     return a, b
 
 
-@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([200], 256, 64)])
+@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([200], 256, 64),
+                                         ([300, 0, 513, 129, 64], 520, 384)])
 def test_bf16_fprop(sizes, N, K):
     G = len(sizes)
     M = int(sum(sizes))
@@ -163,7 +164,8 @@ def test_bf16_fprop(sizes, N, K):
     check_rows(host(y), want, f"bf16 fprop {sizes}")
 
 
-@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([64, 64], 136, 72)])
+@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([64, 64], 136, 72),
+                                         ([300, 0, 513, 129, 64], 520, 384)])
 def test_bf16_dgrad(sizes, N, K):
     """dX[m, n] = sum_k dY[m, k] W_g[k, n]: W stored [G, K, N] (the forward
     weight [out, in] with the contraction over its rows)."""
@@ -180,7 +182,26 @@ def test_bf16_dgrad(sizes, N, K):
     check_rows(host(y), want, f"bf16 dgrad {sizes}")
 
 
-@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([700], 64, 136)])
+def test_bf16_dgrad_bf16_out():
+    """bf16 output: the GEMM bar plus one bf16 rounding (2^-9 relative)."""
+    sizes, N, K = [300, 0, 129, 64], 264, 192
+    G, M = len(sizes), sum(sizes)
+    dy = wl.normal_bf16((M, K), seed=13)
+    w = wl.normal_bf16((G, K, N), std=0.05, seed=14)
+    off = _offsets(sizes)
+    y = pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_DGRAD, dev_bf16(dy),
+                             dev_bf16(w.reshape(G * K, N)), dev(off), N, K,
+                             out_dtype=pqm.OUT_BF16)
+    wt = np.ascontiguousarray(np.transpose(oracle.bf16_to_f64(w.reshape(-1, N)).reshape(G, K, N),
+                                           (0, 2, 1)))
+    want = oracle.grouped_gemm(oracle.bf16_to_f64(dy), wt, off)
+    r = rel_l2_rows(oracle.bf16_to_f64(host_u16(y)), want)
+    print(f"[gemm] bf16 dgrad bf16 out: max row rel-L2 {r.max():.3e}", flush=True)
+    assert r.max() <= TOL + 2.0 ** -9
+
+
+@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([700], 64, 136),
+                                         ([1000, 0, 33, 257], 520, 264)])
 def test_bf16_wgrad(sizes, N, K):
     G = len(sizes)
     M = int(sum(sizes))
