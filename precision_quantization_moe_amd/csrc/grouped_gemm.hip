@@ -1248,6 +1248,333 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(
   }
 }
 
+// --------------------------------------------- NVFP4, pipelined large tiles
+//
+// The same ring and tiles as the MXFP8 / BF16 pipelines, carrying the packed
+// operands: a step is 128 K, i.e. 64 bytes of E2M1 and 8 E4M3 block scales
+// per row, both loaded straight into LDS (slot: A data, B data, A scales,
+// B scales).  The fp16 operand values are produced while the fragments are
+// read: lane half h takes bytes 32 h .. 32 h + 31 of each row (two 16-byte
+// reads) and the 4 scale bytes of the blocks they cover (one 4-byte read);
+// sub-step s (0..7) contracts the 8 elements 64 h + 8 s .. of each lane (the
+// same K permutation for both operands, and each group of 8 lies in one
+// 16-element block).  A block scale s_b = M 2^E (M in [1, 2), 4 significant
+// bits) is applied in two exact steps: the scaled FP4 -> f16 pair conversion
+// (v_cvt_scalef32_pk_f16_fp4, which scales by the power of two 2^E; checked
+// exhaustively on gfx950) and one packed f16 multiply by M; q s_b has at most
+// 6 significant bits in [2^-10, 2688], exact in f16.  The outer scales
+// multiply the binary32 accumulator in the epilogue as in k_gemm_nvfp4.
+template <int TM>
+struct Np {
+  static constexpr int TN = 256, ROWS = TM + TN;
+  static constexpr int SC = ROWS * 64;        // scale area offset in a slot
+  static constexpr int SLOT = ROWS * 72;
+  static constexpr int NSLOT = 3;
+  static constexpr int LDS = NSLOT * SLOT;
+  static constexpr int CA = TM / 64, CB = TN / 64;  // 16-byte data chunks per lane
+  static constexpr int NS = ROWS / 128;             // 4-byte scale loads per lane
+  static constexpr int OPS = CA + CB + NS;
+  static constexpr int FI = TM / 64, FJ = 4;
+};
+
+template <int TM>
+struct NpSrc {
+  const uint8_t *Ab, *Bb, *Asb, *Bsb;
+  uint32_t oa[Np<TM>::CA], ob[Np<TM>::CB], os[Np<TM>::NS];  // step-0 offsets
+  uint32_t dst, sdst;  // LDS addresses of slot 0's data and scales, this wave
+};
+
+template <int TM>
+__device__ __forceinline__ void np_issue(const NpSrc<TM> &L, int kt, int slot) {
+  using C = Np<TM>;
+  const uint32_t kb = (uint32_t)kt * 64u, ks = (uint32_t)kt * 8u;
+  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT, sbase = L.sdst + (uint32_t)slot * C::SLOT;
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) dma16(L.Ab + (L.oa[i] + kb), base + i * 4096);
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) dma16(L.Bb + (L.ob[i] + kb), base + TM * 64 + i * 4096);
+#pragma unroll
+  for (int i = 0; i < C::NS; ++i)  // dwords 256 i + tid: rows 128 i .. (A rows first)
+    dma4((128 * i < TM ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
+}
+
+// Raw operands of one step: per fragment 8 words (one per sub-step) and the
+// 4 scale bytes of the lane's blocks.
+template <int TM>
+struct NpFrags {
+  uint4 a[Np<TM>::FI][2], b[Np<TM>::FJ][2];
+  uint32_t sa[Np<TM>::FI], sb[Np<TM>::FJ];
+};
+
+struct NpLane {
+  int a0, a1, b0, b1;  // chunk offsets (2h, 2h+1) of the first A / B row
+  int sa, sb;          // scale-word offsets of the first A / B row
+};
+
+template <int TM>
+__device__ __forceinline__ void np_read(const uint8_t *lds, int slot, const NpLane &o,
+                                        NpFrags<TM> &F) {
+  using C = Np<TM>;
+  const uint8_t *cur = lds + slot * C::SLOT;
+#pragma unroll
+  for (int i = 0; i < C::FI; ++i) {
+    F.a[i][0] = *reinterpret_cast<const uint4 *>(cur + o.a0 + 2048 * i);
+    F.a[i][1] = *reinterpret_cast<const uint4 *>(cur + o.a1 + 2048 * i);
+    F.sa[i] = *reinterpret_cast<const uint32_t *>(cur + o.sa + 256 * i);
+  }
+#pragma unroll
+  for (int j = 0; j < C::FJ; ++j) {
+    F.b[j][0] = *reinterpret_cast<const uint4 *>(cur + o.b0 + 2048 * j);
+    F.b[j][1] = *reinterpret_cast<const uint4 *>(cur + o.b1 + 2048 * j);
+    F.sb[j] = *reinterpret_cast<const uint32_t *>(cur + o.sb + 256 * j);
+  }
+}
+
+// Block scale byte `byte` (0..3) of `sw` as 2^E (binary32) and M (f16 pair).
+struct NpScale {
+  float p2;
+  uint32_t m2;
+};
+
+template <int BYTE>
+__device__ __forceinline__ NpScale np_scale(uint32_t sw) {
+  // E4M3 -> binary32 exactly (every E4M3 value is a normal binary32)
+  const uint32_t f = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8((int)sw, BYTE));
+  NpScale r;
+  r.p2 = __uint_as_float(f & 0x7F800000u);
+  const uint32_t m16 = ((f >> 13) & 0x380u) | 0x3C00u;  // 1.mmm in f16
+  r.m2 = m16 | (m16 << 16);
+  return r;
+}
+
+// 8 fp16 operand values of word w (sub-step) under block scale sc.
+__device__ __forceinline__ v8h np_decode(uint32_t w, const NpScale &sc) {
+  const pqm_v2h m = __builtin_bit_cast(pqm_v2h, sc.m2);
+  const pqm_v2h x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.p2, 0) * m;
+  const pqm_v2h x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.p2, 1) * m;
+  const pqm_v2h x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.p2, 2) * m;
+  const pqm_v2h x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc.p2, 3) * m;
+  return v8h{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
+}
+
+__device__ __forceinline__ uint32_t u4_word(const uint4 (&v)[2], int s) {
+  const uint4 &u = v[s >> 2];
+  const int k = s & 3;
+  return k == 0 ? u.x : (k == 1 ? u.y : (k == 2 ? u.z : u.w));
+}
+
+// Sub-steps 2 BLK and 2 BLK + 1 (block BLK of each lane's half).
+template <int TM, int BLK>
+__device__ __forceinline__ void np_mma_blk(const NpFrags<TM> &F,
+                                           v16f (&acc)[Np<TM>::FI][Np<TM>::FJ]) {
+  using C = Np<TM>;
+  {
+    NpScale sa[C::FI], sb[C::FJ];
+#pragma unroll
+    for (int i = 0; i < C::FI; ++i) sa[i] = np_scale<BLK>(F.sa[i]);
+#pragma unroll
+    for (int j = 0; j < C::FJ; ++j) sb[j] = np_scale<BLK>(F.sb[j]);
+#pragma unroll
+    for (int s = 2 * BLK; s < 2 * BLK + 2; ++s) {
+      v8h xa[C::FI], xb[C::FJ];
+#pragma unroll
+      for (int i = 0; i < C::FI; ++i) xa[i] = np_decode(u4_word(F.a[i], s), sa[i]);
+#pragma unroll
+      for (int j = 0; j < C::FJ; ++j) xb[j] = np_decode(u4_word(F.b[j], s), sb[j]);
+#pragma unroll
+      for (int j = 0; j < C::FJ; ++j)
+#pragma unroll
+        for (int i = 0; i < C::FI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[j], xa[i], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+template <int TM>
+__device__ __forceinline__ void np_mma(const NpFrags<TM> &F,
+                                       v16f (&acc)[Np<TM>::FI][Np<TM>::FJ]) {
+  np_mma_blk<TM, 0>(F, acc);
+  np_mma_blk<TM, 1>(F, acc);
+  np_mma_blk<TM, 2>(F, acc);
+  np_mma_blk<TM, 3>(F, acc);
+}
+
+template <int TM>
+__device__ __forceinline__ void np_step(const NpSrc<TM> &L, const uint8_t *lds, const NpLane &o,
+                                        int kt, int nk, int slot,
+                                        v16f (&acc)[Np<TM>::FI][Np<TM>::FJ],
+                                        const NpFrags<TM> &cur, NpFrags<TM> &next) {
+  vm_wait<Np<TM>::OPS>();
+  lgkm_wait0();
+  __builtin_amdgcn_s_barrier();
+  np_issue<TM>(L, min(kt + 3, nk - 1), slot);
+  __builtin_amdgcn_sched_barrier(0);
+  np_read<TM>(lds, slot == 2 ? 0 : slot + 1, o, next);
+  __builtin_amdgcn_sched_barrier(0);
+  np_mma<TM>(cur, acc);
+}
+
+// Store one transposed accumulator with the outer scales: as mx3_store, each
+// value times alpha_a[row] * alpha_b(column) (the product exact in
+// binary64, one rounding to binary32, then to bf16 for bf16 output).
+// ab: the tile's 256 column scales in LDS.
+template <bool OUT_F32>
+__device__ __forceinline__ void np_store(const v16f &acc, void *out, int64_t N, int64_t row0,
+                                         int64_t row_end, int64_t n0, int rbase, int cbase,
+                                         const float *__restrict__ Ao, const float *ab) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int64_t row = row0 + rbase + (lane & 31);
+  const double aa = row < row_end ? (double)Ao[row] : 0.0;
+  const bool vec = (N & 7) == 0;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    float lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = acc[8 * p + e], b = acc[8 * p + 4 + e];
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h ? a : b),
+                                                       __float_as_uint(h ? a : b), false, false);
+      const float got = __uint_as_float(h ? sw[0] : sw[1]);
+      lo[e] = h ? got : a;
+      hi[e] = h ? b : got;
+    }
+    const int c0 = cbase + 16 * p + 8 * h;  // column within the tile
+    const int64_t col = n0 + c0;
+    if (row >= row_end) continue;
+    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)((double)v[e] * (aa * (double)ab[c0 + e]));
+    if (vec && col + 7 < N) {
+      if (OUT_F32) {
+        float *dst = static_cast<float *>(out) + row * N + col;
+        *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        const uint4 w = make_uint4(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                   f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16),
+                                   f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16),
+                                   f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16));
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + row * N + col) = w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (col + e < N) {
+          if (OUT_F32)
+            static_cast<float *>(out)[row * N + col + e] = v[e];
+          else
+            static_cast<uint16_t *>(out)[row * N + col + e] = (uint16_t)f32_to_bf16_rne(v[e]);
+        }
+      }
+    }
+  }
+}
+
+template <bool OUT_F32, int TM>
+__device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
+                                        const uint8_t *__restrict__ As,
+                                        const float *__restrict__ Ao,
+                                        const uint8_t *__restrict__ B,
+                                        const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
+                                        const TileInfo &ti, uint8_t *lds, const float *ab,
+                                        void *__restrict__ out) {
+  using C = Np<TM>;
+  constexpr int FI = C::FI, FJ = C::FJ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
+  const uint32_t KD = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);  // row bytes of data / scales
+  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)TM);
+  const int rows_b = (int)min(N - ti.n0, (int64_t)C::TN);
+  NpSrc<TM> L;
+  L.Ab = A + ti.row0 * (int64_t)KD;
+  L.Bb = B + (ti.g * N + ti.n0) * (int64_t)KD;
+  L.Asb = As + ti.row0 * (int64_t)KS;
+  L.Bsb = Bs + (ti.g * N + ti.n0) * (int64_t)KS;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+  L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + C::SC + (uint32_t)wave * 256u);
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.oa[i] = (uint32_t)min(r, rows_a - 1) * KD + 16u * k;
+  }
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.ob[i] = (uint32_t)min(r, rows_b - 1) * KD + 16u * k;
+  }
+#pragma unroll
+  for (int i = 0; i < C::NS; ++i) {
+    const int d = tid + 256 * i, r = d >> 1, half = d & 1;
+    L.os[i] = r < TM ? (uint32_t)min(r, rows_a - 1) * KS + 4u * half
+                     : (uint32_t)min(r - TM, rows_b - 1) * KS + 4u * half;
+  }
+  NpLane o;
+  {
+    const int ra = wm * (TM / 2) + r32, rb = wn * 128 + r32;
+    o.a0 = mx3_off(ra, 2 * h);
+    o.a1 = mx3_off(ra, 2 * h + 1);
+    o.b0 = TM * 64 + mx3_off(rb, 2 * h);
+    o.b1 = TM * 64 + mx3_off(rb, 2 * h + 1);
+    o.sa = C::SC + ra * 8 + 4 * h;
+    o.sb = C::SC + (TM + rb) * 8 + 4 * h;
+  }
+  v16f acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (int)(K / 128);  // even, >= 2
+  np_issue<TM>(L, 0, 0);
+  np_issue<TM>(L, 1, 1);
+  np_issue<TM>(L, min(2, nk - 1), 2);
+  vm_wait<2 * C::OPS>();  // step 0
+  __builtin_amdgcn_s_barrier();
+  NpFrags<TM> F0, F1;
+  np_read<TM>(lds, 0, o, F0);
+  int slot = 0;
+  for (int kt = 0; kt < nk; kt += 2) {
+    np_step<TM>(L, lds, o, kt, nk, slot, acc, F0, F1);
+    slot = slot == 2 ? 0 : slot + 1;
+    np_step<TM>(L, lds, o, kt + 1, nk, slot, acc, F1, F0);
+    slot = slot == 2 ? 0 : slot + 1;
+  }
+  vm_wait<0>();
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+      np_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (TM / 2) + 32 * i,
+                        wn * 128 + 32 * j, Ao, ab);
+}
+
+// Tiles as k_gemm_mxfp8_pipe; K % 256 == 0.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_pipe(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const float *__restrict__ Ao, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    void *__restrict__ out) {
+  static_assert(Np<128>::LDS <= Np<256>::LDS, "LDS of the half tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Np<256>::LDS];
+  __shared__ float ab[256];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
+  {  // the tile's column scales alpha_b(n) = Bo[(g N + n) / b_rps]
+    const int64_t col = ti.n0 + threadIdx.x;
+    ab[threadIdx.x] = col < N ? Bo[(ti.g * N + col) / b_rps] : 0.0f;
+  }
+  __syncthreads();
+  if (ti.row_end - ti.row0 <= 128)
+    np_tile<OUT_F32, 128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+  else
+    np_tile<OUT_F32, 256>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+}
+
 // ------------------------------------------------------------------ launch
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1349,6 +1676,18 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
         hipLaunchKernelGGL((k_gemm_bf16_rows<true, false>), grid, dim3(256), 0, st, A, B,
                            offsets, G, N, K, ntn, out);
     }
+    return hipGetLastError();
+  }
+  if (fmt == 2 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0) {
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    const int64_t ntn_b = cdiv(N, 256);
+    const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_nvfp4_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, a_outer,
+                         B, b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_b, out);
+    else
+      hipLaunchKernelGGL(k_gemm_nvfp4_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, a_outer,
+                         B, b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_b, out);
     return hipGetLastError();
   }
   if (fmt == 2) {

@@ -248,6 +248,8 @@ def _nvfp4_case(sizes, N, K, seed, brps=None):
     ([0, 37, 128, 1, 300], 192, 320, None),
     ([64, 0, 200], 128, 336, None),           # K % 64 == 16: remainder step
     ([100, 60], 256, 512, 128),               # gate and up scaled separately
+    ([300, 0, 513, 129, 64], 520, 768, None),  # 256- and 128-row tiles, ragged N
+    ([300, 0, 513, 129, 64], 520, 512, 260),   # scale boundaries inside 8-column runs
 ])
 def test_nvfp4_fprop_ragged(case):
     sizes, N, K, brps = case
