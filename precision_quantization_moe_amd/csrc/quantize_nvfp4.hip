@@ -232,7 +232,8 @@ __device__ __forceinline__ void nvfp4_row_wave(const uint16_t *__restrict__ x, u
       uint32_t code;
       const uint2 packed = nvfp4_block(w[b], rc, &code);
       if (blk < nblk) {
-        *reinterpret_cast<uint2 *>(qr + blk * 8) = packed;
+        typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u2v{packed.x, packed.y}, reinterpret_cast<u2v *>(qr + blk * 8));
         sbr[blk] = (uint8_t)code;
       }
     }
