@@ -69,9 +69,9 @@ REPEAT_ROWS = ("mxfp8_quant", "nvfp4_token")
 TRAFFIC = {
     "kernel": "k_quantize_mxfp8<true,true,true,1>",
     "fetch_kib": 32803.4, "fetch_scale": 2.0,
-    "write_kib": 75039.5, "write_scale": 1.0,
+    "write_kib": 74810.4, "write_scale": 1.0,
     "sources": {
-        "precision_quantization_moe_amd/csrc/quantize_mxfp8.hip": "34bf758c10b3f4c5e458489ce37ec08bf8b048500a2588c125481f92e5af9ae5",
+        "precision_quantization_moe_amd/csrc/quantize_mxfp8.hip": "a727c5bb5e20ea240bf590cd8cc6e5b4291706f59a371d3780213255d131a389",
         "precision_quantization_moe_amd/csrc/pqm_device.hpp": "31b5f7b4eee420f65ae5f7298be72b468c3cabb6c27caf16563e64fd805b0b08",
     },
 }
