@@ -54,7 +54,65 @@ template <int TN = GT_N, int TM = GT_M>
 __device__ bool lookup_row_tile(const int64_t *__restrict__ offsets, int64_t G, int64_t ntn,
                                 TileInfo &ti, int64_t *sh) {
   const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) {
+  constexpr int NC = 4;  // up to 64 NC groups: all offsets in one round of loads
+  if (threadIdx.x < 64 && G <= 64 * NC) {
+    int64_t lo[NC], hi[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {  // clamped, so every load is in bounds
+      const int64_t g = min((int64_t)(64 * c + lane), G);
+      lo[c] = offsets[g];
+      hi[c] = offsets[min(g + 1, G)];
+    }
+    const int nch = (int)((G + 63) / 64);
+    int cnt[NC], total = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      cnt[c] = 64 * c + lane < G ? (int)((hi[c] - lo[c] + TM - 1) / TM) : 0;
+      if (c < nch) {
+        int t = cnt[c];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+        total += t;
+      }
+    }
+    const int64_t real = (int64_t)total * ntn;
+    const int64_t per_xcd = (real + 7) / 8;
+    const int64_t b = blockIdx.x;
+    const int64_t T = (b % 8) * per_xcd + b / 8;
+    int64_t found_g = -1, row0 = 0, row_end = 0;
+    if (b < 8 * per_xcd && T < real) {
+      const int mt = (int)(T / ntn);
+      int base = 0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c >= nch || found_g >= 0) break;
+        int incl = cnt[c];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        const bool hit = cnt[c] > 0 && mt >= base + incl - cnt[c] && mt < base + incl;
+        const unsigned long long m = __ballot(hit);
+        if (m) {
+          const int src = __ffsll((long long)m) - 1;
+          found_g = 64 * c + src;
+          row0 = __shfl(lo[c], src, 64) +
+                 (int64_t)(mt - base - __shfl(incl - cnt[c], src, 64)) * TM;
+          row_end = __shfl(hi[c], src, 64);
+        }
+        base += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) {
+        sh[0] = found_g;
+        sh[1] = row0;
+        sh[2] = row_end;
+        sh[3] = (T % ntn) * TN;
+      }
+    } else if (lane == 0) {
+      sh[0] = -1;
+    }
+  } else if (threadIdx.x < 64) {
     // pass 1: total row tiles
     int64_t total = 0;
     for (int64_t c0 = 0; c0 < G; c0 += 64) {
