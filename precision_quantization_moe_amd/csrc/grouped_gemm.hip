@@ -54,7 +54,7 @@ template <int TN = GT_N, int TM = GT_M>
 __device__ bool lookup_row_tile(const int64_t *__restrict__ offsets, int64_t G, int64_t ntn,
                                 TileInfo &ti, int64_t *sh) {
   const int lane = threadIdx.x & 63;
-  constexpr int NC = 4;  // up to 64 NC groups: all offsets in one round of loads
+  constexpr int NC = 8;  // up to 64 NC groups: all offsets in one round of loads
   if (threadIdx.x < 64 && G <= 64 * NC) {
     int64_t lo[NC], hi[NC];
 #pragma unroll
