@@ -11,7 +11,8 @@ seeded input, with all inputs resident in HBM:
   q3_wquant         Qwen3-30B-A3B experts: MXFP8 quantize of W1 and W2
   q3_fwd            MXFP8 MoE expert layer forward: 8192 tokens, top-8 of 128
                     experts (Zipf 1.1): route, token quantize, gather,
-                    gate_up GEMM, SwiGLU x prob, quantize, down GEMM, combine
+                    gate_up GEMM, SwiGLU x prob fused with the FC2 operand's
+                    MXFP8 quantize, down GEMM, combine
   q3_gemm           the two MXFP8 grouped GEMMs of q3_fwd alone
   q3_dequant        dequantize of the forward operands (dequantized backward)
   q3_bwd            BF16 dgrad + wgrad of both expert GEMMs on them
@@ -200,7 +201,7 @@ def main():
 
     def r_q3_fwd(s):
         st["q3"] = moe_layer.mxfp8_moe_forward(st["x4"], st["ids4"], st["prob4"], *st["q3w"], E,
-                                               I4)
+                                               I4, keep_d=False)
 
     def r_q3_gemm(s):
         o, (w1q, w1s, w2q, w2s) = st["q3"], st["q3w"]

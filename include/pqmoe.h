@@ -271,6 +271,22 @@ pqm_status pqm_swiglu_prob(const uint16_t *c, const float *prob, const int32_t *
                            int64_t rows, int64_t inter, uint16_t *d, hipStream_t stream);
 
 /*
+ * The weighted SwiGLU above fused with the row-wise MXFP8 quantization of
+ * its output, the FC2 operand ([MT] 5.3-5.4: the activation of the FC1
+ * output, times the router probability, is quantized for the down GEMM
+ * without a separate pass over D; [BW] Format background: MXFP8).
+ *   q [rows, inter] E4M3 and s [rows, inter / 32] E8M0 equal
+ *   pqm_quantize_mxfp8 (row-wise) of the d that pqm_swiglu_prob returns;
+ *   d (bf16 [rows, inter]) is also written when non-NULL.
+ * Requires inter % 32 == 0 (PQM_ERR_SHAPE), c and d 16-byte aligned, q
+ * 8-byte aligned (PQM_ERR_ALIGN); c, prob, q, s non-NULL (PQM_ERR_NULL).
+ */
+pqm_status pqm_swiglu_prob_quantize_mxfp8(const uint16_t *c, const float *prob,
+                                          const int32_t *src, int64_t rows, int64_t inter,
+                                          uint16_t *d, uint8_t *q, uint8_t *s,
+                                          hipStream_t stream);
+
+/*
  * Combine: out[t, n] = bf16( sum_j y_rows[slot[t, j], n] + shared[t, n] ),
  * summed in binary32 in j order (shared may be NULL).  y_rows, shared, out
  * bf16 with N contiguous; N % 8 == 0.

@@ -41,6 +41,7 @@ SIGNATURES = {
     "pqm_moe_route_workspace": ([I64, I64, I64], SZ),
     "pqm_moe_gather_rows": ([P, I64, I64, P, I64, I64, P, P], I32),
     "pqm_swiglu_prob": ([P, P, P, I64, I64, P, P], I32),
+    "pqm_swiglu_prob_quantize_mxfp8": ([P, P, P, I64, I64, P, P, P, P], I32),
     "pqm_moe_combine": ([P, P, P, I64, I64, I64, P, P], I32),
 }
 
@@ -210,6 +211,21 @@ def swiglu_prob(c: torch.Tensor, prob: torch.Tensor, src: torch.Tensor | None = 
     _check(lib().pqm_swiglu_prob(_ptr(c), _ptr(prob), _ptr(src), M, N2 // 2, _ptr(d),
                                  _stream(c.device)), "pqm_swiglu_prob")
     return d
+
+
+def swiglu_prob_quantize_mxfp8(c: torch.Tensor, prob: torch.Tensor,
+                               src: torch.Tensor | None = None, keep_d: bool = False):
+    """swiglu_prob fused with the row-wise MXFP8 quantization of its output.
+    Returns (q, s, d) with d None unless keep_d."""
+    M, N2 = c.shape
+    inter = N2 // 2
+    q = torch.empty((M, inter), dtype=torch.uint8, device=c.device)
+    s = torch.empty((M, inter // 32), dtype=torch.uint8, device=c.device)
+    d = torch.empty((M, inter), dtype=torch.bfloat16, device=c.device) if keep_d else None
+    _check(lib().pqm_swiglu_prob_quantize_mxfp8(_ptr(c), _ptr(prob), _ptr(src), M, inter,
+                                                _ptr(d), _ptr(q), _ptr(s), _stream(c.device)),
+           "pqm_swiglu_prob_quantize_mxfp8")
+    return q, s, d
 
 
 def moe_combine(y_rows: torch.Tensor, slot: torch.Tensor, shared: torch.Tensor | None = None):

@@ -176,23 +176,17 @@ hipError_t launch_gather(const void *src, int64_t row_bytes, const int32_t *inde
   return hipGetLastError();
 }
 
-// d[m, j] = bf16( silu(g) * u * p ), g = c[m, j], u = c[m, I + j], p = the
-// router probability of the assignment stored at row m.  Eight outputs per
-// lane (16-byte bf16 loads and stores).
-__global__ __launch_bounds__(256) void k_swiglu_prob(const uint16_t *__restrict__ c,
-                                                     const float *__restrict__ prob,
-                                                     const int32_t *__restrict__ src,
-                                                     int64_t M, int64_t I,
-                                                     uint16_t *__restrict__ d) {
-  const int64_t per_row = I / 8;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= M * per_row) return;
-  const int64_t m = i / per_row, j = (i % per_row) * 8;
+// Eight outputs d[m, j .. j+7] = bf16( silu(g) * u * p ), g = c[m, j..],
+// u = c[m, I + j..], p = the router probability of the assignment stored at
+// row m, as 4 words of bf16 pairs.
+__device__ __forceinline__ void swiglu8(const uint16_t *__restrict__ c,
+                                        const float *__restrict__ prob,
+                                        const int32_t *__restrict__ src, int64_t I, int64_t m,
+                                        int64_t j, uint32_t (&o)[4]) {
   const float p = prob[src ? src[m] : m];
   const uint4 gv = *reinterpret_cast<const uint4 *>(c + m * 2 * I + j);
   const uint4 uv = *reinterpret_cast<const uint4 *>(c + m * 2 * I + I + j);
   const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
-  uint32_t o[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     uint32_t h[2];
@@ -205,7 +199,59 @@ __global__ __launch_bounds__(256) void k_swiglu_prob(const uint16_t *__restrict_
     }
     o[k] = h[0] | (h[1] << 16);
   }
+}
+
+// d = swiglu8 per lane (16-byte bf16 loads and stores).
+__global__ __launch_bounds__(256) void k_swiglu_prob(const uint16_t *__restrict__ c,
+                                                     const float *__restrict__ prob,
+                                                     const int32_t *__restrict__ src,
+                                                     int64_t M, int64_t I,
+                                                     uint16_t *__restrict__ d) {
+  const int64_t per_row = I / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * per_row) return;
+  const int64_t m = i / per_row, j = (i % per_row) * 8;
+  uint32_t o[4];
+  swiglu8(c, prob, src, I, m, j, o);
   *reinterpret_cast<uint4 *>(d + m * I + j) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The same d, quantized in place to MXFP8 row-wise (1 x 32 blocks along j):
+// the 4 lanes of a block (consecutive lanes, I % 32 == 0) reduce its
+// maximum with two quad permutes; the E8M0 byte and the E4M3 codes follow
+// the quantizer's rules, so q and s equal pqm_quantize_mxfp8 of d.  d is
+// written too when non-null.
+__global__ __launch_bounds__(256) void k_swiglu_quant_mxfp8(
+    const uint16_t *__restrict__ c, const float *__restrict__ prob,
+    const int32_t *__restrict__ src, int64_t M, int64_t I, uint16_t *__restrict__ d,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ s) {
+  const int64_t per_row = I / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * per_row) return;  // whole quads: M * per_row is a multiple of 4
+  const int64_t m = i / per_row, j = (i % per_row) * 8;
+  uint32_t o[4];
+  swiglu8(c, prob, src, I, m, j, o);
+  if (d) *reinterpret_cast<uint4 *>(d + m * I + j) = make_uint4(o[0], o[1], o[2], o[3]);
+  uint32_t mm = pk_max_u16(pk_max_u16(o[0] & 0x7FFF7FFFu, o[1] & 0x7FFF7FFFu),
+                           pk_max_u16(o[2] & 0x7FFF7FFFu, o[3] & 0x7FFF7FFFu));
+  mm = max(mm & 0xFFFFu, mm >> 16);
+  mm = max(mm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mm, 0xB1, 0xF, 0xF, false));
+  mm = max(mm, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mm, 0x4E, 0xF, 0xF, false));
+  const uint32_t b = mx_scale_byte(mm);
+  const float scale = __uint_as_float(b << 23);  // the E8M0 byte as the conversion's scale
+  *reinterpret_cast<uint2 *>(q + m * I + j) =
+      make_uint2(cvt4_e4m3_bf16(o[0], o[1], scale), cvt4_e4m3_bf16(o[2], o[3], scale));
+  if ((threadIdx.x & 3) == 0) s[m * (I / 32) + j / 32] = (uint8_t)b;
+}
+
+hipError_t launch_swiglu_quant_mxfp8(const uint16_t *c, const float *prob, const int32_t *src,
+                                     int64_t M, int64_t I, uint16_t *d, uint8_t *q, uint8_t *s,
+                                     hipStream_t st) {
+  const int64_t tot = M * (I / 8);
+  if (tot == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_swiglu_quant_mxfp8, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
+                     c, prob, src, M, I, d, q, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_swiglu(const uint16_t *c, const float *prob, const int32_t *src, int64_t M,
@@ -312,6 +358,17 @@ pqm_status pqm_swiglu_prob(const uint16_t *c, const float *prob, const int32_t *
   if (!c || !prob || !d) return PQM_ERR_NULL;
   if (!al(c, 16) || !al(d, 16)) return PQM_ERR_ALIGN;
   return st_of(pqm::launch_swiglu(c, prob, src, rows, inter, d, stream));
+}
+
+pqm_status pqm_swiglu_prob_quantize_mxfp8(const uint16_t *c, const float *prob,
+                                          const int32_t *src, int64_t rows, int64_t inter,
+                                          uint16_t *d, uint8_t *q, uint8_t *s,
+                                          hipStream_t stream) {
+  if (rows < 0 || inter < 0 || inter % 32) return PQM_ERR_SHAPE;
+  if (rows == 0 || inter == 0) return PQM_OK;
+  if (!c || !prob || !q || !s) return PQM_ERR_NULL;
+  if (!al(c, 16) || (d && !al(d, 16)) || !al(q, 8)) return PQM_ERR_ALIGN;
+  return st_of(pqm::launch_swiglu_quant_mxfp8(c, prob, src, rows, inter, d, q, s, stream));
 }
 
 pqm_status pqm_moe_combine(const uint16_t *y_rows, const int32_t *slot, const uint16_t *shared,

@@ -119,5 +119,12 @@ def test_glue_validation():
     assert L.pqm_moe_gather_rows(A16, 4, 16, A16, 4, 0, A16, None) == 2
     assert L.pqm_swiglu_prob(A16, A16, None, 4, 12, A16, None) == 2
     assert L.pqm_swiglu_prob(BAD, A16, None, 4, 16, A16, None) == 3
+    f = L.pqm_swiglu_prob_quantize_mxfp8
+    assert f(A16, A16, None, 4, 48, None, A16, A16, None) == 2       # inter % 32
+    assert f(A16, A16, None, 4, 64, None, None, A16, None) == 1      # q
+    assert f(A16, None, None, 4, 64, None, A16, A16, None) == 1      # prob
+    assert f(BAD, A16, None, 4, 64, None, A16, A16, None) == 3
+    assert f(A16, A16, None, 4, 64, BAD, A16, A16, None) == 3        # d misaligned
+    assert f(A16, A16, None, 0, 64, None, None, None, None) == 0     # empty
     assert L.pqm_moe_combine(A16, A16, None, 4, 0, 16, A16, None) == 2
     assert L.pqm_moe_combine(A16, None, None, 4, 2, 16, A16, None) == 1

@@ -76,6 +76,32 @@ def _run_mxfp8(x, ids, prob, w1, w2, E, I):
     return moe_layer.mxfp8_moe_forward(dev_bf16(x), dev(ids), dev(prob), *wq, E, I)
 
 
+def test_swiglu_quantize_fused_pass():
+    """The fused SwiGLU x prob + row-wise MXFP8 pass: its d equals
+    pqm_swiglu_prob's, and its q / s are the oracle's MXFP8 encoding of that
+    d byte for byte (zero rows and a ragged row count included)."""
+    M, I = 1003, 768
+    rng = np.random.Generator(np.random.PCG64(77))
+    c = wl.normal_bf16((M, 2 * I), std=2.0, seed=78)
+    c[5] = 0
+    c[6, :I] = 0
+    prob = rng.random(M).astype(np.float32)
+    src = rng.permutation(M).astype(np.int32)
+    cd, pd, sd_ = dev_bf16(c), dev(prob), dev(src)
+    d_ref = pqm.swiglu_prob(cd, pd, sd_)
+    q, s, d = pqm.swiglu_prob_quantize_mxfp8(cd, pd, sd_, keep_d=True)
+    q2, s2, none = pqm.swiglu_prob_quantize_mxfp8(cd, pd, sd_)
+    torch.cuda.synchronize()
+    assert none is None
+    dh = host_u16(d)
+    assert_bytes_equal(dh, host_u16(d_ref), "fused d")
+    rq, rs = oracle.quantize_mxfp8_rowwise(dh)
+    assert_bytes_equal(host(q), rq, "fused q")
+    assert_bytes_equal(host(s), rs, "fused s")
+    assert_bytes_equal(host(q2), rq, "fused q without d")
+    assert_bytes_equal(host(s2), rs, "fused s without d")
+
+
 def test_mxfp8_layer_small_all_stages():
     T, E, k, H, I = 256, 16, 4, 256, 128
     x, ids, prob, w1, w2 = _mxfp8_inputs(T, E, k, H, I, seed=40)
