@@ -11,8 +11,8 @@ seeded input, with all inputs resident in HBM:
   q3_wquant         Qwen3-30B-A3B experts: MXFP8 quantize of W1 and W2
   q3_fwd            MXFP8 MoE expert layer forward: 8192 tokens, top-8 of 128
                     experts (Zipf 1.1): route, token quantize, gather,
-                    gate_up GEMM, SwiGLU x prob fused with the FC2 operand's
-                    MXFP8 quantize, down GEMM, combine
+                    gate_up GEMM with SwiGLU x prob and the FC2 operand's
+                    MXFP8 quantize in its epilogue, down GEMM, combine
   q3_gemm           the two MXFP8 grouped GEMMs of q3_fwd alone
   q3_dequant        dequantize of the forward operands (dequantized backward)
   q3_bwd            BF16 dgrad + wgrad of both expert GEMMs on them
@@ -155,6 +155,7 @@ def main():
         st["W2"] = to_dev(wl.expert_weights(E, H, I4, 0.02, tag=1).reshape(E * H, I4))
         st["dY"] = to_dev(wl.output_grad(M4, H))
         st["dC"] = to_dev(wl.output_grad(M4, 2 * I4, seed=5))
+        st["c4"] = torch.empty((M4, 2 * I4), dtype=torch.bfloat16, device=dev)  # q3_gemm's C
     # DeepSeek-V3 expert layer (weights drawn on the GPU from a seeded stream)
     T5, K5, E5, H5, I5 = 4096, 8, 256, 7168, 2048
     M5 = T5 * K5 + T5
@@ -201,12 +202,12 @@ def main():
 
     def r_q3_fwd(s):
         st["q3"] = moe_layer.mxfp8_moe_forward(st["x4"], st["ids4"], st["prob4"], *st["q3w"], E,
-                                               I4, keep_d=False)
+                                               I4, keep_intermediates=False)
 
     def r_q3_gemm(s):
         o, (w1q, w1s, w2q, w2s) = st["q3"], st["q3w"]
         pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, o["qa"], w1q, o["off"], 2 * I4, H,
-                             a_scale=o["sa"], b_scale=w1s, out_dtype=pqm.OUT_BF16, out=o["c"])
+                             a_scale=o["sa"], b_scale=w1s, out_dtype=pqm.OUT_BF16, out=st["c4"])
         pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, o["qd"], w2q, o["off"], H, I4,
                              a_scale=o["sd"], b_scale=w2s, out_dtype=pqm.OUT_BF16, out=o["y"])
 

@@ -215,6 +215,26 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,
                                 hipStream_t stream);
 
 /*
+ * The MXFP8 gate_up grouped GEMM with its activation fused into the
+ * epilogue ([MT] 5.3-5.4: D = act(gate, up) x prob is produced where C is,
+ * and quantized for the down GEMM without another pass; C is not written):
+ *   C_g = A . B_g^T as pqm_moe_grouped_gemm FPROP (MXFP8, bf16 output),
+ *   D   = pqm_swiglu_prob(C, prob, src),  (q, s) = row-wise MXFP8 of D,
+ * with the same bytes as those three calls.  A [M_total, K] E4M3 + a_scale
+ * [M_total, K/32]; B [G, 2 inter, K] E4M3 (rows 0..inter-1 gate, then up)
+ * + b_scale [G, 2 inter, K/32]; prob / src as pqm_swiglu_prob; q [M_total,
+ * inter] E4M3 and s [M_total, inter/32] E8M0 (device).
+ * Requires inter % 128 == 0, K % 128 == 0, K <= 2048 (PQM_ERR_SHAPE); a, b,
+ * q 16-byte aligned, the scale arrays 4-byte aligned (PQM_ERR_ALIGN).
+ */
+pqm_status pqm_moe_gemm_swiglu_quantize_mxfp8(const uint8_t *a, const uint8_t *a_scale,
+                                              const uint8_t *b, const uint8_t *b_scale,
+                                              const int64_t *offsets, int64_t G,
+                                              int64_t M_total, int64_t inter, int64_t K,
+                                              const float *prob, const int32_t *src,
+                                              uint8_t *q, uint8_t *s, hipStream_t stream);
+
+/*
  * MoE glue around the grouped GEMM ([MT] 5.2: quantized rows are placed in
  * one contiguous buffer with offsets marking the expert boundaries, built
  * on the device; [MT] 5.4: D = act(gate, up) x prob; [BW] Fine-grained
@@ -264,7 +284,8 @@ pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_by
  * silu(z) = z / (1 + exp(-z)), p = prob[src[m]] (prob binary32 indexed by
  * assignment, i.e. src_row from pqm_moe_route; with a shared expert prob
  * holds tokens*k + tokens entries, the last tokens of them 1.0; src may be
- * NULL to index prob by m).  Binary32 math.
+ * NULL to index prob by m).  Binary32 math with the hardware exponential
+ * and reciprocal (about 1 ulp each before the bf16 rounding).
  * d bf16 [rows, inter]; inter % 8 == 0.
  */
 pqm_status pqm_swiglu_prob(const uint16_t *c, const float *prob, const int32_t *src,

@@ -37,6 +37,8 @@ SIGNATURES = {
     "pqm_dequantize": ([I32, P, P, P, I64, I64, I64, P, P], I32),
     "pqm_moe_grouped_gemm": ([I32, I32, P, P, P, P, P, P, I64, P, I64, I64, I64, I64,
                               P, I32, P, SZ, P], I32),
+    "pqm_moe_gemm_swiglu_quantize_mxfp8": ([P, P, P, P, P, I64, I64, I64, I64, P, P, P, P, P],
+                                           I32),
     "pqm_moe_route": ([P, I64, I64, I64, I32, P, P, P, P, P, SZ, P], I32),
     "pqm_moe_route_workspace": ([I64, I64, I64], SZ),
     "pqm_moe_gather_rows": ([P, I64, I64, P, I64, I64, P, P], I32),
@@ -226,6 +228,20 @@ def swiglu_prob_quantize_mxfp8(c: torch.Tensor, prob: torch.Tensor,
                                                 _ptr(d), _ptr(q), _ptr(s), _stream(c.device)),
            "pqm_swiglu_prob_quantize_mxfp8")
     return q, s, d
+
+
+def moe_gemm_swiglu_quantize_mxfp8(qa, sa, w1q, w1s, offsets: torch.Tensor, inter: int,
+                                   prob: torch.Tensor, src: torch.Tensor | None = None):
+    """MXFP8 gate_up grouped GEMM with SwiGLU x prob and the row-wise MXFP8
+    quantization of D fused into its epilogue.  Returns (qd, sd)."""
+    G = offsets.numel() - 1
+    M, K = qa.shape
+    q = torch.empty((M, inter), dtype=torch.uint8, device=qa.device)
+    s = torch.empty((M, inter // 32), dtype=torch.uint8, device=qa.device)
+    _check(lib().pqm_moe_gemm_swiglu_quantize_mxfp8(
+        _ptr(qa), _ptr(sa), _ptr(w1q), _ptr(w1s), _ptr(offsets), G, M, inter, K, _ptr(prob),
+        _ptr(src), _ptr(q), _ptr(s), _stream(qa.device)), "pqm_moe_gemm_swiglu_quantize_mxfp8")
+    return q, s
 
 
 def moe_combine(y_rows: torch.Tensor, slot: torch.Tensor, shared: torch.Tensor | None = None):

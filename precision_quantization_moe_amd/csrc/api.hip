@@ -156,4 +156,22 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
                                            K, out, out_dtype == PQM_OUT_FP32, stream));
 }
 
+pqm_status pqm_moe_gemm_swiglu_quantize_mxfp8(const uint8_t *a, const uint8_t *a_scale,
+                                              const uint8_t *b, const uint8_t *b_scale,
+                                              const int64_t *offsets, int64_t G, int64_t M_total,
+                                              int64_t inter, int64_t K, const float *prob,
+                                              const int32_t *src, uint8_t *q, uint8_t *s,
+                                              hipStream_t stream) {
+  if (G < 0 || M_total < 0 || inter < 0 || K < 0) return PQM_ERR_SHAPE;
+  if (inter % 128 || K % 128 || K / 32 > 64) return PQM_ERR_SHAPE;
+  if (G == 0 || M_total == 0 || inter == 0) return PQM_OK;
+  if (K == 0) return PQM_ERR_SHAPE;
+  if (!a || !a_scale || !b || !b_scale || !offsets || !prob || !q || !s) return PQM_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(q, 16) || !aligned(offsets, 8) ||
+      !aligned(a_scale, 4) || !aligned(b_scale, 4))
+    return PQM_ERR_ALIGN;
+  return from_hip(pqm::launch_gemm_swiglu_mxfp8(a, a_scale, b, b_scale, offsets, G, M_total,
+                                                inter, K, prob, src, q, s, stream));
+}
+
 }  // extern "C"

@@ -541,14 +541,97 @@ __device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds
   mx3_mma<TM>(cur, acc);
 }
 
+// Fused gate_up epilogue (SwiGLU x prob, then the row-wise MXFP8 encoding
+// of D, the FC2 operand).  The gate_up weight W_g [2I, K] is read with its
+// rows permuted per 256-column tile tn so that each lane's 8-column run of
+// the transposed accumulator holds 4 gate columns and the 4 matching up
+// columns, and the 16 D values a lane half ends with are 16 consecutive D
+// columns: tile column c = 128 wn + 32 j + 16 p + 8 hh + e (the layout of
+// mx3_store after its lane swap) computes D column
+//   dcol = 128 tn + 64 wn + 32 (j / 2) + 16 hh + 8 (j % 2) + 4 p + e % 4
+// from W row dcol (e < 4, gate) or I + dcol (e >= 4, up).
+struct SwigluEpi {
+  const float *prob;    // router probability, indexed by src[row] (or row)
+  const int32_t *src;
+  int64_t I;            // D columns; I % 128 == 0
+  uint8_t *q, *s;       // D in MXFP8: q [M, I] E4M3, s [M, I / 32] E8M0
+};
+
+__device__ __forceinline__ int64_t swiglu_w_row(int c, int64_t tn, int64_t I) {
+  const int wn = c >> 7, j = (c >> 5) & 3, p = (c >> 4) & 1, hh = (c >> 3) & 1, e = c & 7;
+  const int64_t dcol =
+      128 * tn + 64 * wn + 32 * (j >> 1) + 16 * hh + 8 * (j & 1) + 4 * p + (e & 3);
+  return e < 4 ? dcol : I + dcol;
+}
+
+// D for one fragment-pair block of one wave: acc[i][2 jj], acc[i][2 jj + 1]
+// (token rows row0 + rbase + 0..31, D columns dbase + 0..31).
+__device__ __forceinline__ void swiglu_store(const v16f &a0, const v16f &a1,
+                                             const SwigluEpi &ep, int64_t row0, int64_t row_end,
+                                             int rbase, int64_t dbase) {
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int64_t row = row0 + rbase + (lane & 31);
+  const bool ok = row < row_end;
+  const float pr = ok ? ep.prob[ep.src ? ep.src[row] : row] : 0.0f;
+  uint32_t dw[8];  // 16 D values (bf16 pairs): columns dbase + 16 h + 0..15
+#pragma unroll
+  for (int jo = 0; jo < 2; ++jo) {
+    const v16f &acc = jo ? a1 : a0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      float gate[4], up[4];  // as mx3_store: this lane's 8 columns after the swap
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = acc[8 * p + e], b = acc[8 * p + 4 + e];
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h ? a : b),
+                                                         __float_as_uint(h ? a : b), false, false);
+        const float got = __uint_as_float(h ? sw[0] : sw[1]);
+        gate[e] = h ? got : a;
+        up[e] = h ? b : got;
+      }
+      uint32_t hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // the gate_up output rounded to bf16 first, then the weighted SwiGLU
+        // exactly as pqm_swiglu_prob computes it
+        const float g = __uint_as_float(f32_to_bf16_rne(gate[e]) << 16);
+        const float u = __uint_as_float(f32_to_bf16_rne(up[e]) << 16);
+        const float sg = silu_f32(g);
+        hv[e] = f32_to_bf16_rne(sg * u * pr);
+      }
+      dw[4 * jo + 2 * p] = hv[0] | (hv[1] << 16);
+      dw[4 * jo + 2 * p + 1] = hv[2] | (hv[3] << 16);
+    }
+  }
+  // block maximum over the 32 D columns: this lane's 16, then the other half
+  uint32_t mm = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) mm = pk_max_u16(mm, dw[k] & 0x7FFF7FFFu);
+  mm = max(mm & 0xFFFFu, mm >> 16);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(mm, mm, false, false);
+    mm = max(sw[0], sw[1]);
+  }
+  const uint32_t b = mx_scale_byte(mm);
+  const float scale = __uint_as_float(b << 23);
+  if (ok) {
+    const uint4 qv = make_uint4(cvt4_e4m3_bf16(dw[0], dw[1], scale), cvt4_e4m3_bf16(dw[2], dw[3], scale),
+                                cvt4_e4m3_bf16(dw[4], dw[5], scale), cvt4_e4m3_bf16(dw[6], dw[7], scale));
+    *reinterpret_cast<uint4 *>(ep.q + row * ep.I + dbase + 16 * h) = qv;
+    if (h == 0) ep.s[row * (ep.I / 32) + dbase / 32] = (uint8_t)b;
+  }
+}
+
 // One TM x 256 output tile (rows ti.row0 .. min(ti.row0 + TM, ti.row_end)).
-template <bool OUT_F32, int TM>
+// EPI: false = the plain store of the product, true = the fused gate_up
+// epilogue (B rows permuted as swiglu_w_row describes; `out` unused).
+template <bool OUT_F32, int TM, bool EPI = false>
 __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
                                          const uint8_t *__restrict__ As,
                                          const uint8_t *__restrict__ B,
                                          const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
                                          const TileInfo &ti, uint8_t *lds,
-                                         void *__restrict__ out) {
+                                         void *__restrict__ out, const SwigluEpi *ep = nullptr) {
   using C = Mx3<TM>;
   constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -567,10 +650,12 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
     const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
     L.oa[i] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * k;
   }
+  if (EPI) L.Bb = B + ti.g * N * K;  // whole expert: rows picked by swiglu_w_row
 #pragma unroll
   for (int i = 0; i < C::CB; ++i) {
     const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
-    L.ob[i] = (uint32_t)min(r, rows_b - 1) * Ku + 16u * k;
+    const int64_t wr = EPI ? swiglu_w_row(r, ti.n0 / TN, N / 2) : (int64_t)min(r, rows_b - 1);
+    L.ob[i] = (uint32_t)wr * Ku + 16u * k;
   }
   Mx3Lane o;
   {
@@ -600,8 +685,10 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
       const int d = 256 * q + tid;
       const int g = d / (16 * dpr), rem = d - g * 16 * dpr;
       const int row = min(16 * g + (rem & 15), C::ROWS - 1), dw = rem >> 4;
+      const int64_t brow = EPI ? swiglu_w_row(row - TM, ti.n0 / TN, N / 2) - ti.n0
+                               : (int64_t)min(row - TM, rows_b - 1);
       const uint8_t *src = row < TM ? Asb + (int64_t)min(row, rows_a - 1) * KS + 4 * dw
-                                    : Bsb + (int64_t)min(row - TM, rows_b - 1) * KS + 4 * dw;
+                                    : Bsb + brow * KS + 4 * dw;
       dma4(src, sbase + 1024u * (uint32_t)q);
     }
   }
@@ -630,12 +717,21 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
     slot = slot == 2 ? 0 : slot + 1;
   }
   vm_wait<0>();  // no load may still target this workgroup's LDS at exit
+  if (EPI) {
 #pragma unroll
-  for (int i = 0; i < FI; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < FJ; ++j)
-      mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (TM / 2) + 32 * i,
-                         wn * 128 + 32 * j);
+      for (int jj = 0; jj < FJ / 2; ++jj)
+        swiglu_store(acc[i][2 * jj], acc[i][2 * jj + 1], *ep, ti.row0, ti.row_end,
+                     wm * (TM / 2) + 32 * i, ti.n0 / 2 + 64 * wn + 32 * jj);
+  } else {
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+        mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0,
+                           wm * (TM / 2) + 32 * i, wn * 128 + 32 * j);
+  }
 }
 
 // Row tiles of 256 tokens; an expert's last tile holding 128 rows or fewer
@@ -656,6 +752,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
     mx3_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ti, lds, out);
   else
     mx3_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ti, lds, out);
+}
+
+// The gate_up grouped GEMM with the fused epilogue: D = SwiGLU(C) x prob
+// encoded as MXFP8 (C itself is never written).  N = 2 I, I % 128 == 0.
+__global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_swiglu(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    SwigluEpi ep) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Mx3<256>::LDS];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
+  if (ti.row_end - ti.row0 <= 128)
+    mx3_tile<false, 128, true>(A, As, B, Bs, N, K, ti, lds, nullptr, &ep);
+  else
+    mx3_tile<false, 256, true>(A, As, B, Bs, N, K, ti, lds, nullptr, &ep);
 }
 
 // ------------------------------------------------------------------- BF16
@@ -1759,6 +1872,18 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     return hipGetLastError();
   }
   return hipErrorNotSupported;
+}
+
+hipError_t launch_gemm_swiglu_mxfp8(const uint8_t *a, const uint8_t *a_scale, const uint8_t *b,
+                                    const uint8_t *b_scale, const int64_t *offsets, int64_t G,
+                                    int64_t M, int64_t I, int64_t K, const float *prob,
+                                    const int32_t *src, uint8_t *q, uint8_t *s, hipStream_t st) {
+  if (G == 0 || M == 0 || I == 0) return hipSuccess;
+  const int64_t N = 2 * I, ntn = N / 256;
+  const dim3 grid((unsigned)(cdiv((cdiv(M, 256) + G) * ntn, 8) * 8));
+  hipLaunchKernelGGL(k_gemm_mxfp8_swiglu, grid, dim3(256), 0, st, a, a_scale, b, b_scale,
+                     offsets, G, N, K, ntn, SwigluEpi{prob, src, I, q, s});
+  return hipGetLastError();
 }
 
 }  // namespace pqm

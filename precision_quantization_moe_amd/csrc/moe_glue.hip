@@ -194,7 +194,7 @@ __device__ __forceinline__ void swiglu8(const uint16_t *__restrict__ c,
     for (int t = 0; t < 2; ++t) {
       const float g = t ? bf16_hi_f32(gw[k]) : bf16_lo_f32(gw[k]);
       const float u = t ? bf16_hi_f32(uw[k]) : bf16_lo_f32(uw[k]);
-      const float s = g / (1.0f + expf(-g));
+      const float s = silu_f32(g);
       h[t] = f32_to_bf16_rne(s * u * p);
     }
     o[k] = h[0] | (h[1] << 16);

@@ -21,6 +21,13 @@ __device__ __forceinline__ float bf16_hi_f32(uint32_t w) {
   return __uint_as_float(w & 0xFFFF0000u);
 }
 
+// silu(g) = g / (1 + e^-g) with the hardware exponential and reciprocal
+// (about 1 ulp each): the SwiGLU activation of every kernel that computes it,
+// so that the fused and the separate passes produce the same bits.
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
 // Round a binary32 value to bf16 bits, nearest even (finite or inf input).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -34,19 +34,25 @@ def quantize_expert_weights_nvfp4(w1: torch.Tensor, w2: torch.Tensor, inter: int
 
 
 def mxfp8_moe_forward(x, topk_ids, prob_flat, w1q, w1s, w2q, w2s, num_experts: int,
-                      inter: int, keep_d: bool = True):
+                      inter: int, keep_intermediates: bool = True):
     """x [T, H] bf16; topk_ids [T, k] int32; prob_flat [T*k] float32.
-    Returns a dict of every stage's output (out = [T, H] bf16).  The weighted
-    SwiGLU and the FC2 operand's quantization run as one fused pass; its bf16
-    output d is kept only when keep_d (None otherwise)."""
+    Returns a dict of every stage's output (out = [T, H] bf16).  With
+    keep_intermediates the gate_up output c and d = SwiGLU(c) x prob are
+    materialised (bf16; d and its MXFP8 encoding in one fused pass);
+    without, the gate_up GEMM's epilogue produces the MXFP8 encoding of d
+    directly and c, d are None (same bytes)."""
     T, H = x.shape
     off, src, tok, slot = b.moe_route(topk_ids, num_experts)
     qx, sx, _, _ = b.quantize_mxfp8(x, colwise=False)
     qa = b.moe_gather_rows(qx, tok)
     sa = b.moe_gather_rows(sx, tok)
-    c = b.moe_grouped_gemm(b.FMT_MXFP8, b.GEMM_FPROP, qa, w1q, off, 2 * inter, H,
-                           a_scale=sa, b_scale=w1s, out_dtype=b.OUT_BF16)
-    qd, sd, d = b.swiglu_prob_quantize_mxfp8(c, prob_flat, src, keep_d=keep_d)
+    if keep_intermediates or inter % 128 or H % 128 or H > 2048:
+        c = b.moe_grouped_gemm(b.FMT_MXFP8, b.GEMM_FPROP, qa, w1q, off, 2 * inter, H,
+                               a_scale=sa, b_scale=w1s, out_dtype=b.OUT_BF16)
+        qd, sd, d = b.swiglu_prob_quantize_mxfp8(c, prob_flat, src, keep_d=keep_intermediates)
+    else:
+        c = d = None
+        qd, sd = b.moe_gemm_swiglu_quantize_mxfp8(qa, sa, w1q, w1s, off, inter, prob_flat, src)
     y = b.moe_grouped_gemm(b.FMT_MXFP8, b.GEMM_FPROP, qd, w2q, off, H, inter,
                            a_scale=sd, b_scale=w2s, out_dtype=b.OUT_BF16)
     out = b.moe_combine(y, slot)

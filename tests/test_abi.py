@@ -126,5 +126,13 @@ def test_glue_validation():
     assert f(BAD, A16, None, 4, 64, None, A16, A16, None) == 3
     assert f(A16, A16, None, 4, 64, BAD, A16, A16, None) == 3        # d misaligned
     assert f(A16, A16, None, 0, 64, None, None, None, None) == 0     # empty
+    g = L.pqm_moe_gemm_swiglu_quantize_mxfp8
+    ok = (A16, A16, A16, A16, A16, 4, 64, 128, 256, A16, None, A16, A16, None)
+    assert g(*ok[:7], 96, *ok[8:]) == 2                               # inter % 128
+    assert g(*ok[:8], 4096, *ok[9:]) == 2                             # K > 2048
+    assert g(*ok[:8], 200, *ok[9:]) == 2                              # K % 128
+    assert g(*ok[:11], None, *ok[12:]) == 1                           # q
+    assert g(*ok[:11], BAD, *ok[12:]) == 3                            # q misaligned
+    assert g(BAD, *ok[1:]) == 3
     assert L.pqm_moe_combine(A16, A16, None, 4, 0, 16, A16, None) == 2
     assert L.pqm_moe_combine(A16, None, None, 4, 2, 16, A16, None) == 1

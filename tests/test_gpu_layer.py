@@ -69,11 +69,12 @@ def _mxfp8_inputs(T, E, k, H, I, seed):
     return x, ids, prob, w1, w2
 
 
-def _run_mxfp8(x, ids, prob, w1, w2, E, I):
+def _run_mxfp8(x, ids, prob, w1, w2, E, I, keep=True):
     H = x.shape[1]
     wq = moe_layer.quantize_expert_weights_mxfp8(dev_bf16(w1.reshape(-1, H)),
                                                  dev_bf16(w2.reshape(-1, I)))
-    return moe_layer.mxfp8_moe_forward(dev_bf16(x), dev(ids), dev(prob), *wq, E, I)
+    return moe_layer.mxfp8_moe_forward(dev_bf16(x), dev(ids), dev(prob), *wq, E, I,
+                                       keep_intermediates=keep)
 
 
 def test_swiglu_quantize_fused_pass():
@@ -100,6 +101,30 @@ def test_swiglu_quantize_fused_pass():
     assert_bytes_equal(host(s), rs, "fused s")
     assert_bytes_equal(host(q2), rq, "fused q without d")
     assert_bytes_equal(host(s2), rs, "fused s without d")
+
+
+def test_gate_up_gemm_with_fused_epilogue():
+    """The gate_up GEMM whose epilogue emits the MXFP8 encoding of
+    SwiGLU(C) x prob gives the same bytes as the GEMM, pqm_swiglu_prob and
+    the quantizer run one after the other (ragged experts, an empty one,
+    256- and 128-row tiles, two column tiles of D)."""
+    sizes, I, K = [300, 0, 513, 129, 64], 256, 256
+    G, M = len(sizes), sum(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    x = wl.activations(M, K, seed=81)
+    w = wl.normal_bf16((G * 2 * I, K), std=0.05, seed=82)
+    rng = np.random.Generator(np.random.PCG64(83))
+    prob = rng.random(M).astype(np.float32)
+    src = rng.permutation(M).astype(np.int32)
+    qa, sa, _, _ = pqm.quantize_mxfp8(dev_bf16(x), colwise=False)
+    qw, sw, _, _ = pqm.quantize_mxfp8(dev_bf16(w), colwise=False)
+    c = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, qw, dev(off), 2 * I, K,
+                             a_scale=sa, b_scale=sw, out_dtype=pqm.OUT_BF16)
+    rq, rs, _ = pqm.swiglu_prob_quantize_mxfp8(c, dev(prob), dev(src))
+    q, s = pqm.moe_gemm_swiglu_quantize_mxfp8(qa, sa, qw, sw, dev(off), I, dev(prob), dev(src))
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(q), host(rq), "fused epilogue q")
+    assert_bytes_equal(host(s), host(rs), "fused epilogue s")
 
 
 def test_mxfp8_layer_small_all_stages():
@@ -134,6 +159,13 @@ def test_mxfp8_layer_qwen3_full_sampled_tokens():
     check(host_u16(g["c"])[rows], o["c"], "C")
     check(host_u16(g["y"])[rows], o["y"], "Y")
     check(host_u16(g["out"])[toks], o["out"], "out")
+    # the production path: gate_up epilogue emits D's MXFP8 encoding, same bytes
+    f = _run_mxfp8(x, ids, prob, w1, w2, E, I, keep=False)
+    assert f["c"] is None and f["d"] is None
+    for name in ("qd", "sd"):
+        assert_bytes_equal(host(f[name]), host(g[name]), "fused forward " + name)
+    for name in ("y", "out"):
+        assert_bytes_equal(host_u16(f[name]), host_u16(g[name]), "fused forward " + name)
 
 
 def _nvfp4_inputs(T, E, k, H, I, seed):
