@@ -543,13 +543,14 @@ __device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds
 
 // Fused gate_up epilogue (SwiGLU x prob, then the row-wise MXFP8 encoding
 // of D, the FC2 operand).  The gate_up weight W_g [2I, K] is read with its
-// rows permuted per 256-column tile tn so that each lane's 8-column run of
-// the transposed accumulator holds 4 gate columns and the 4 matching up
-// columns, and the 16 D values a lane half ends with are 16 consecutive D
-// columns: tile column c = 128 wn + 32 j + 16 p + 8 hh + e (the layout of
-// mx3_store after its lane swap) computes D column
-//   dcol = 128 tn + 64 wn + 32 (j / 2) + 16 hh + 8 (j % 2) + 4 p + e % 4
-// from W row dcol (e < 4, gate) or I + dcol (e >= 4, up).
+// rows permuted per 256-column tile tn so that every lane finds matching
+// gate and up columns in its own accumulator registers: a transposed 32 x 32
+// accumulator gives lane h * 32 + r the columns 8 g + 4 h + e (g, e = 0..3)
+// of its fragment as registers 4 g + e, and tile column
+// c = 128 wn + 32 j + 8 g + 4 h + e is made gate (g even) or up (g odd) of
+//   dcol = 128 tn + 64 wn + 32 (j / 2) + 16 h + 8 (j % 2) + 4 (g / 2) + e,
+// i.e. W row dcol or I + dcol.  A lane half then holds 16 consecutive D
+// columns of each 32-column block (fragments j, j + 1).
 struct SwigluEpi {
   const float *prob;    // router probability, indexed by src[row] (or row)
   const int32_t *src;
@@ -558,10 +559,10 @@ struct SwigluEpi {
 };
 
 __device__ __forceinline__ int64_t swiglu_w_row(int c, int64_t tn, int64_t I) {
-  const int wn = c >> 7, j = (c >> 5) & 3, p = (c >> 4) & 1, hh = (c >> 3) & 1, e = c & 7;
+  const int wn = c >> 7, j = (c >> 5) & 3, g = (c >> 3) & 3, hh = (c >> 2) & 1, e = c & 3;
   const int64_t dcol =
-      128 * tn + 64 * wn + 32 * (j >> 1) + 16 * hh + 8 * (j & 1) + 4 * p + (e & 3);
-  return e < 4 ? dcol : I + dcol;
+      128 * tn + 64 * wn + 32 * (j >> 1) + 16 * hh + 8 * (j & 1) + 4 * (g >> 1) + e;
+  return (g & 1) ? I + dcol : dcol;
 }
 
 // D for one fragment-pair block of one wave: acc[i][2 jj], acc[i][2 jj + 1]
@@ -578,30 +579,19 @@ __device__ __forceinline__ void swiglu_store(const v16f &a0, const v16f &a1,
   for (int jo = 0; jo < 2; ++jo) {
     const v16f &acc = jo ? a1 : a0;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      float gate[4], up[4];  // as mx3_store: this lane's 8 columns after the swap
+    for (int gp = 0; gp < 2; ++gp)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a = acc[8 * p + e], b = acc[8 * p + 4 + e];
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h ? a : b),
-                                                         __float_as_uint(h ? a : b), false, false);
-        const float got = __uint_as_float(h ? sw[0] : sw[1]);
-        gate[e] = h ? got : a;
-        up[e] = h ? b : got;
+      for (int e2 = 0; e2 < 2; ++e2) {
+        // gate (register 8 gp + e) and up (8 gp + 4 + e) of D column
+        // 8 jo + 4 gp + e, rounded to bf16 as the GEMM's output would be,
+        // then the weighted SwiGLU exactly as pqm_swiglu_prob computes it
+        const int e = 2 * e2;
+        const uint32_t gw = pk_bf16_rne(acc[8 * gp + e], acc[8 * gp + e + 1]);
+        const uint32_t uw = pk_bf16_rne(acc[8 * gp + 4 + e], acc[8 * gp + 4 + e + 1]);
+        dw[4 * jo + 2 * gp + e2] =
+            pk_bf16_rne(silu_f32(bf16_lo_f32(gw)) * bf16_lo_f32(uw) * pr,
+                        silu_f32(bf16_hi_f32(gw)) * bf16_hi_f32(uw) * pr);
       }
-      uint32_t hv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // the gate_up output rounded to bf16 first, then the weighted SwiGLU
-        // exactly as pqm_swiglu_prob computes it
-        const float g = __uint_as_float(f32_to_bf16_rne(gate[e]) << 16);
-        const float u = __uint_as_float(f32_to_bf16_rne(up[e]) << 16);
-        const float sg = silu_f32(g);
-        hv[e] = f32_to_bf16_rne(sg * u * pr);
-      }
-      dw[4 * jo + 2 * p] = hv[0] | (hv[1] << 16);
-      dw[4 * jo + 2 * p + 1] = hv[2] | (hv[3] << 16);
-    }
   }
   // block maximum over the 32 D columns: this lane's 16, then the other half
   uint32_t mm = 0;

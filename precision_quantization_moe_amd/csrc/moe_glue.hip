@@ -188,17 +188,9 @@ __device__ __forceinline__ void swiglu8(const uint16_t *__restrict__ c,
   const uint4 uv = *reinterpret_cast<const uint4 *>(c + m * 2 * I + I + j);
   const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t h[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float g = t ? bf16_hi_f32(gw[k]) : bf16_lo_f32(gw[k]);
-      const float u = t ? bf16_hi_f32(uw[k]) : bf16_lo_f32(uw[k]);
-      const float s = silu_f32(g);
-      h[t] = f32_to_bf16_rne(s * u * p);
-    }
-    o[k] = h[0] | (h[1] << 16);
-  }
+  for (int k = 0; k < 4; ++k)
+    o[k] = pk_bf16_rne(silu_f32(bf16_lo_f32(gw[k])) * bf16_lo_f32(uw[k]) * p,
+                       silu_f32(bf16_hi_f32(gw[k])) * bf16_hi_f32(uw[k]) * p);
 }
 
 // d = swiglu8 per lane (16-byte bf16 loads and stores).

@@ -21,6 +21,15 @@ __device__ __forceinline__ float bf16_hi_f32(uint32_t w) {
   return __uint_as_float(w & 0xFFFF0000u);
 }
 
+// Two binary32 values rounded to a bf16 pair (first in the low half) by the
+// hardware conversion: nearest even, as f32_to_bf16_rne, for finite values
+// and infinities.
+__device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
+  typedef __bf16 pqm_bf2 __attribute__((ext_vector_type(2)));
+  const pqm_bf2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // silu(g) = g / (1 + e^-g) with the hardware exponential and reciprocal
 // (about 1 ulp each): the SwiGLU activation of every kernel that computes it,
 // so that the fused and the separate passes produce the same bits.
