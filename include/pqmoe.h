@@ -185,6 +185,20 @@ pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q,
  *       A [M_total, K], B [G, K, N] (N contiguous); Y [M_total, N].
  *   PQM_GEMM_WGRAD (PQM_FMT_BF16):  Y_g[n, k] = sum_{m in g} A[m, n] B[m, k]
  *       A [M_total, N], B [M_total, K]; Y [G, N, K] (zero for empty g).
+ *   PQM_GEMM_DGRAD (PQM_FMT_MXFP8): the same Y, with the contraction
+ *       blocks of B_g running along k ([BW] MXFP8 training: backward GEMMs
+ *       read the column-wise copies): a = row-wise MXFP8 of A [M_total, K];
+ *       b / b_scale = the column-wise copy (q_colT [N, G*K], s_colT
+ *       [N, G*K/32]) that pqm_quantize_mxfp8 makes of the stacked B [G*K, N];
+ *       expert g uses its columns g*K .. g*K+K-1.  K % 128 == 0, K <= 2048,
+ *       G*K*256 + K < 2^32.
+ *   PQM_GEMM_WGRAD (PQM_FMT_MXFP8): the same Y_g from the column-wise
+ *       copies of both operands: a / a_scale = q_colT [N, M_total] /
+ *       s_colT [N, M_total/32] of A, b / b_scale = q_colT [K, M_total] /
+ *       s_colT [K, M_total/32] of B.  Every offsets[g] must be a multiple
+ *       of 32 (each expert's rows padded to whole 32-row blocks, padding
+ *       rows zero), else the result is undefined (reads stay in bounds).
+ *       M_total % 32 == 0, M_total*256 + 4096 < 2^32; any N, K.
  *
  * Operand encodings (all device):
  *   PQM_FMT_BF16:  a, b bf16; scales and outer scales unused (NULL).
@@ -196,11 +210,14 @@ pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q,
  *                  [G, N, K/16], b_outer = binary32 [(G*N) /
  *                  b_rows_per_scale] (b_rows_per_scale = N: one scale per
  *                  expert, e.g. joint gate/up).
+ * a, b and out 16-byte aligned, offsets 8-byte aligned, MXFP8 scale arrays
+ * 4-byte aligned (PQM_ERR_ALIGN otherwise).
  * The products use the exact operand values; accumulation is binary32 and
  * the outer scales are applied to the binary32 accumulator.
  * out: Y in bf16 (rounded once) or binary32 per out_dtype.
- * K % 32 == 0 (MXFP8), K % 16 == 0 (NVFP4), K % 8 and N % 8 == 0 (BF16);
- * WGRAD needs N % 8 == 0 and K % 8 == 0.  No workspace is needed today:
+ * K % 32 == 0 (MXFP8 FPROP / DGRAD), K % 16 == 0 (NVFP4), K % 8 and
+ * N % 8 == 0 (BF16); BF16 WGRAD needs N % 8 == 0 and K % 8 == 0; NVFP4 is
+ * FPROP only (PQM_ERR_ENUM otherwise).  No workspace is needed today:
  * pass NULL / 0 (the arguments keep the ABI stable).
  */
 pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,

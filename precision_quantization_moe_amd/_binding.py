@@ -157,7 +157,8 @@ def moe_grouped_gemm(fmt: int, kind: int, a, b, offsets: torch.Tensor, N: int, K
     """Grouped GEMM over experts; see pqm_moe_grouped_gemm in pqmoe.h for the
     operand layouts.  offsets: int64 [G+1] on the device."""
     G = offsets.numel() - 1
-    M = a.shape[0]
+    # the MXFP8 weight gradient takes the transposed column-wise copies
+    M = a.shape[1] if (fmt == FMT_MXFP8 and kind == GEMM_WGRAD) else a.shape[0]
     dev = offsets.device
     odt = torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16
     if out is None:

@@ -137,9 +137,15 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
   if (kind != PQM_GEMM_FPROP && kind != PQM_GEMM_DGRAD && kind != PQM_GEMM_WGRAD)
     return PQM_ERR_ENUM;
   if (out_dtype != PQM_OUT_BF16 && out_dtype != PQM_OUT_FP32) return PQM_ERR_ENUM;
-  if (fmt != PQM_FMT_BF16 && kind != PQM_GEMM_FPROP) return PQM_ERR_ENUM;
+  if (fmt == PQM_FMT_NVFP4 && kind != PQM_GEMM_FPROP) return PQM_ERR_ENUM;
   if (G < 0 || M_total < 0 || N < 0 || K < 0) return PQM_ERR_SHAPE;
-  if (fmt == PQM_FMT_MXFP8 && K % 32) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_MXFP8 && kind != PQM_GEMM_WGRAD && K % 32) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_MXFP8 && kind == PQM_GEMM_DGRAD &&
+      (K % 128 || K > 2048 || G * K * 256 + K >= ((int64_t)1 << 32)))
+    return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_MXFP8 && kind == PQM_GEMM_WGRAD &&
+      (M_total % 32 || M_total * 256 + 4096 >= ((int64_t)1 << 32)))
+    return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_NVFP4 && K % 16) return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_BF16 && (K % 8 || N % 8)) return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_NVFP4 && (b_rows_per_scale < 1 || (G * N) % b_rows_per_scale))
@@ -150,6 +156,8 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
   if (fmt != PQM_FMT_BF16 && (!a_scale || !b_scale)) return PQM_ERR_NULL;
   if (fmt == PQM_FMT_NVFP4 && (!a_outer || !b_outer)) return PQM_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(offsets, 8))
+    return PQM_ERR_ALIGN;
+  if (fmt == PQM_FMT_MXFP8 && (!aligned(a_scale, 4) || !aligned(b_scale, 4)))
     return PQM_ERR_ALIGN;
   return from_hip(pqm::launch_grouped_gemm((int)fmt, (int)kind, a, a_scale, a_outer, b, b_scale,
                                            b_outer, b_rows_per_scale, offsets, G, M_total, N,

@@ -613,6 +613,10 @@ __device__ __forceinline__ void swiglu_store(const v16f &a0, const v16f &a1,
 }
 
 // One TM x 256 output tile (rows ti.row0 .. min(ti.row0 + TM, ti.row_end)).
+// Row n of B_g starts at B + g * bexp + n * ldb (bytes; its scale bytes at
+// Bs + (g * bexp + n * ldb) / 32): ldb = K, bexp = N K for B [G, N, K], and
+// ldb = G K, bexp = K for the transposed column-wise copy of a stacked
+// [G K, N] weight (the data-gradient operand).
 // EPI: false = the plain store of the product, true = the fused gate_up
 // epilogue (B rows permuted as swiglu_w_row describes; `out` unused).
 template <bool OUT_F32, int TM, bool EPI = false>
@@ -620,8 +624,9 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
                                          const uint8_t *__restrict__ As,
                                          const uint8_t *__restrict__ B,
                                          const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
-                                         const TileInfo &ti, uint8_t *lds,
-                                         void *__restrict__ out, const SwigluEpi *ep = nullptr) {
+                                         int64_t ldb, int64_t bexp, const TileInfo &ti,
+                                         uint8_t *lds, void *__restrict__ out,
+                                         const SwigluEpi *ep = nullptr) {
   using C = Mx3<TM>;
   constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -631,7 +636,7 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
   const int rows_b = (int)min(N - ti.n0, (int64_t)TN);
   Mx3Src<TM> L;
   L.Ab = A + ti.row0 * K;
-  L.Bb = B + (ti.g * N + ti.n0) * K;
+  L.Bb = B + ti.g * bexp + ti.n0 * ldb;
   L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
   // ring chunk c = 256 i + tid: row c / 4, physical chunk c % 4, which holds
   // logical chunk (c % 4) ^ ((row / 4) % 4)
@@ -640,12 +645,12 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
     const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
     L.oa[i] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * k;
   }
-  if (EPI) L.Bb = B + ti.g * N * K;  // whole expert: rows picked by swiglu_w_row
+  if (EPI) L.Bb = B + ti.g * bexp;  // whole expert: rows picked by swiglu_w_row
 #pragma unroll
   for (int i = 0; i < C::CB; ++i) {
     const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
     const int64_t wr = EPI ? swiglu_w_row(r, ti.n0 / TN, N / 2) : (int64_t)min(r, rows_b - 1);
-    L.ob[i] = (uint32_t)wr * Ku + 16u * k;
+    L.ob[i] = (uint32_t)wr * (uint32_t)ldb + 16u * k;
   }
   Mx3Lane o;
   {
@@ -666,7 +671,8 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
   // block of 32 rows hit two runs of 16 consecutive dwords.
   {
     const uint8_t *Asb = As + ti.row0 * (int64_t)KS;
-    const uint8_t *Bsb = Bs + (ti.g * N + ti.n0) * (int64_t)KS;
+    const uint8_t *Bsb = Bs + (ti.g * bexp + ti.n0 * ldb) / 32;
+    const int64_t ldbs = ldb / 32;
     const uint32_t sbase =
         __builtin_amdgcn_readfirstlane(lds_addr(lds) + C::NSLOT * C::SLOT + (uint32_t)wave * 256u);
     const int dpr = (int)(KS / 4);                  // dwords per row
@@ -678,7 +684,7 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
       const int64_t brow = EPI ? swiglu_w_row(row - TM, ti.n0 / TN, N / 2) - ti.n0
                                : (int64_t)min(row - TM, rows_b - 1);
       const uint8_t *src = row < TM ? Asb + (int64_t)min(row, rows_a - 1) * KS + 4 * dw
-                                    : Bsb + brow * KS + 4 * dw;
+                                    : Bsb + brow * ldbs + 4 * dw;
       dma4(src, sbase + 1024u * (uint32_t)q);
     }
   }
@@ -732,16 +738,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    void *__restrict__ out) {
+    int64_t ldb, int64_t bexp, void *__restrict__ out) {
   static_assert(Mx3<128>::LDS <= Mx3<256>::LDS, "LDS of the half tile");
   __shared__ __attribute__((aligned(16))) uint8_t lds[Mx3<256>::LDS];
   __shared__ int64_t sh[4];
   TileInfo ti;
   if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
   if (ti.row_end - ti.row0 <= 128)
-    mx3_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ti, lds, out);
+    mx3_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
   else
-    mx3_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ti, lds, out);
+    mx3_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
 }
 
 // The gate_up grouped GEMM with the fused epilogue: D = SwiGLU(C) x prob
@@ -756,9 +762,190 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_swiglu(
   TileInfo ti;
   if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
   if (ti.row_end - ti.row0 <= 128)
-    mx3_tile<false, 128, true>(A, As, B, Bs, N, K, ti, lds, nullptr, &ep);
+    mx3_tile<false, 128, true>(A, As, B, Bs, N, K, K, N * K, ti, lds, nullptr, &ep);
   else
-    mx3_tile<false, 256, true>(A, As, B, Bs, N, K, ti, lds, nullptr, &ep);
+    mx3_tile<false, 256, true>(A, As, B, Bs, N, K, K, N * K, ti, lds, nullptr, &ep);
+}
+
+// ------------------------------------------------------- MXFP8 weight grad
+// Y_g[n, k] = sum over the group's tokens m of A[m, n] B[m, k], from the
+// column-wise (32 x 1 block) MXFP8 copies stored transposed: At [N, M] with
+// scale bytes Ats [N, M / 32], Bt [K, M] with Bts [K, M / 32] ([BW] MXFP8
+// training: the backward GEMMs take the column-wise copies).  Each group's
+// token range starts on a 32-token block boundary (per-expert padding), so
+// blocks never straddle two experts.  One workgroup computes one 256 x 256
+// tile of one Y_g with the forward's three-slot pipeline, in passes of up to
+// 2048 tokens (the scale area holds 64 bytes per row): per pass the scale
+// bytes are gathered through registers (the pass may start on any block, so
+// the dword loads are realigned with a byte shift), chunks of 16 tokens past
+// the group's end read zeros, and their blocks get the scale byte 127 (1.0)
+// so that the zeros stay zeros.
+
+__device__ uint4 g_mx_zero[1];
+
+// Request step kt of a pass; `lim` = tokens in the pass.  Only the last two
+// steps of a pass can reach past it (passes are padded to 128 tokens).
+template <int TM>
+__device__ __forceinline__ void mx3w_issue(const Mx3Src<TM> &L, const uint32_t (&lim_a)[Mx3<TM>::CA],
+                                           const uint32_t (&lim_b)[Mx3<TM>::CB], int kt, int nk,
+                                           int slot) {
+  using C = Mx3<TM>;
+  if (kt < nk - 2) {
+    mx3_issue<TM>(L, kt, slot);
+    return;
+  }
+  const uint32_t kb = (uint32_t)kt * 64u;
+  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT;
+  const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_mx_zero);
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i)
+    dma16(kb < lim_a[i] ? L.Ab + (L.oa[i] + kb) : zero, base + i * 4096);
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i)
+    dma16(kb < lim_b[i] ? L.Bb + (L.ob[i] + kb) : zero, base + TM * 64 + i * 4096);
+}
+
+// Scale bytes of one staged row for a pass: nb valid blocks starting at
+// byte p (any alignment) of an array whose last byte is at `last`; blocks
+// nb .. 4 dpr - 1 get 127.  Written dword-major as mx3_read expects.
+__device__ __forceinline__ void mx3w_scales_row(const uint8_t *p, const uint8_t *last, int nb,
+                                                int dpr, uint8_t *area, int row) {
+  const uintptr_t a0 = (uintptr_t)p & ~(uintptr_t)3, amax = (uintptr_t)last & ~(uintptr_t)3;
+  const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+  uint32_t w[17];
+#pragma unroll
+  for (int j = 0; j < 17; ++j) {
+    const uintptr_t aj = a0 + 4 * (uintptr_t)min(j, dpr);
+    w[j] = *reinterpret_cast<const uint32_t *>(aj < amax ? aj : amax);
+  }
+  uint32_t *dst = reinterpret_cast<uint32_t *>(area) + (row >> 4) * dpr * 16 + (row & 15);
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
+    if (d < dpr) {
+      uint32_t v = __builtin_amdgcn_alignbyte(w[d + 1], w[d], sh);
+      const int vb = nb - 4 * d;  // valid bytes of this dword (may be <= 0 or >= 4)
+      if (vb < 4) {
+        const uint32_t keep = vb <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - vb)));
+        v = (v & keep) | (0x7F7F7F7Fu & ~keep);
+      }
+      dst[d * 16] = v;
+    }
+  }
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_wgrad(
+    const uint8_t *__restrict__ At, const uint8_t *__restrict__ Ats,
+    const uint8_t *__restrict__ Bt, const uint8_t *__restrict__ Bts,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t M, int64_t N, int64_t K,
+    int64_t ntm, int64_t ntn, void *__restrict__ out) {
+  constexpr int TM = 256;
+  using C = Mx3<TM>;
+  constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN, PASS = 32 * C::MAX_KS;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+  // tiles of one expert are consecutive; workgroup b runs on XCD b % 8, and
+  // each XCD takes a contiguous range of tiles
+  const int64_t total = G * ntm * ntn, per_xcd = (int64_t)gridDim.x / 8;
+  const int64_t T = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (T >= total) return;
+  const int64_t g = T / (ntm * ntn), rem = T - g * ntm * ntn;
+  const int64_t n0 = (rem / ntn) * TM, k0 = (rem % ntn) * TN;
+  const int64_t m0 = offsets[g], m1 = offsets[g + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
+  const int rows_a = (int)min(N - n0, (int64_t)TM), rows_b = (int)min(K - k0, (int64_t)TN);
+  const uint32_t Mu = (uint32_t)M;
+  const int64_t MS = M / 32;
+
+  v16f acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  Mx3Src<TM> L;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+  int ka[C::CA], kb4[C::CB];  // logical 16-token chunk of each requested chunk
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.oa[i] = (uint32_t)min(r, rows_a - 1) * Mu + 16u * k;
+    ka[i] = 16 * k;
+  }
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.ob[i] = (uint32_t)min(r, rows_b - 1) * Mu + 16u * k;
+    kb4[i] = 16 * k;
+  }
+  const uint8_t *lastA = Ats + N * MS - 1, *lastB = Bts + K * MS - 1;
+  uint8_t *area = lds + C::NSLOT * C::SLOT;
+
+  for (int64_t c0 = m0; c0 < m1; c0 += PASS) {
+    const int len = (int)min((int64_t)PASS, m1 - c0);
+    const int nk = 2 * ((len + 127) / 128);  // even, >= 2
+    const int KS = 2 * nk, dpr = KS / 4;
+    if (c0 != m0) __syncthreads();  // every wave is done with the last pass's LDS
+    L.Ab = At + n0 * M + c0;
+    L.Bb = Bt + k0 * M + c0;
+    uint32_t lim_a[C::CA], lim_b[C::CB];
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) lim_a[i] = (uint32_t)max(len - ka[i], 0);
+#pragma unroll
+    for (int i = 0; i < C::CB; ++i) lim_b[i] = (uint32_t)max(len - kb4[i], 0);
+    {
+      const int nb = len / 32;
+      const int64_t blk0 = c0 / 32;
+      mx3w_scales_row(Ats + (n0 + min(tid, rows_a - 1)) * MS + blk0, lastA, nb, dpr, area, tid);
+      mx3w_scales_row(Bts + (k0 + min(tid, rows_b - 1)) * MS + blk0, lastB, nb, dpr, area,
+                      TM + tid);
+    }
+    Mx3Lane o;
+    {
+      const int ra = wm * (TM / 2) + r32, rb = wn * 128 + r32;
+      o.a_lo = mx3_off(ra, h);
+      o.a_hi = mx3_off(ra, 2 + h);
+      o.b_lo = TM * 64 + mx3_off(rb, h);
+      o.b_hi = TM * 64 + mx3_off(rb, 2 + h);
+      o.sa = (ra >> 4) * KS * 16 + (ra & 15) * 4;
+      o.sb = ((TM + rb) >> 4) * KS * 16 + ((TM + rb) & 15) * 4;
+      o.ks = KS;
+    }
+    mx3w_issue<TM>(L, lim_a, lim_b, 0, nk, 0);
+    mx3w_issue<TM>(L, lim_a, lim_b, 1, nk, 1);
+    mx3w_issue<TM>(L, lim_a, lim_b, min(2, nk - 1), nk, 2);
+    vm_wait<2 * C::OPS>();  // step 0
+    lgkm_wait0();           // this wave's scale bytes are in LDS
+    __builtin_amdgcn_s_barrier();
+    Mx3Frags<TM> F0, F1;
+    mx3_read<TM>(lds, 0, 0, o, F0);
+    int slot = 0;
+    for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int k = kt + half;
+        vm_wait<C::OPS>();
+        lgkm_wait0();
+        __builtin_amdgcn_s_barrier();
+        mx3w_issue<TM>(L, lim_a, lim_b, min(k + 3, nk - 1), nk, slot);
+        __builtin_amdgcn_sched_barrier(0);
+        mx3_read<TM>(lds, k + 1, slot == 2 ? 0 : slot + 1, o, half ? F0 : F1);
+        __builtin_amdgcn_sched_barrier(0);
+        mx3_mma<TM>(half ? F1 : F0, acc);
+        slot = slot == 2 ? 0 : slot + 1;
+      }
+    }
+    vm_wait<0>();  // no load may still target this workgroup's LDS
+  }
+  const int64_t esz = OUT_F32 ? 4 : 2;
+  void *og = static_cast<uint8_t *>(out) + g * N * K * esz;
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+      mx3_store<OUT_F32>(acc[i][j], og, K, n0, N, k0, wm * (TM / 2) + 32 * i, wn * 128 + 32 * j);
 }
 
 // ------------------------------------------------------------------- BF16
@@ -1747,6 +1934,35 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
                                int64_t K, void *out, int out_fp32, hipStream_t st) {
   if (G == 0 || N == 0) return hipSuccess;
   const int64_t U32 = (int64_t)1 << 32;  // the pipelined kernels' per-panel byte offsets
+  if (fmt == 1 && kind == 2) {  // WGRAD (MXFP8, column-wise copies)
+    if (K == 0) return hipSuccess;
+    if (M % 32 || M * 256 + 4096 >= U32) return hipErrorNotSupported;
+    const int64_t ntm = cdiv(N, 256), ntn = cdiv(K, 256);
+    const dim3 grid((unsigned)(cdiv(G * ntm * ntn, 8) * 8));
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_mxfp8_wgrad<true>, grid, dim3(256), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, M, N, K, ntm, ntn, out);
+    else
+      hipLaunchKernelGGL(k_gemm_mxfp8_wgrad<false>, grid, dim3(256), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, M, N, K, ntm, ntn, out);
+    return hipGetLastError();
+  }
+  if (fmt == 1 && kind == 1) {  // DGRAD (MXFP8): B = column-wise copy of the stacked weight
+    if (M == 0) return hipSuccess;
+    if (K % 128 || K / 32 > Mx3<256>::MAX_KS || G * K * 256 + K >= U32)
+      return hipErrorNotSupported;
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    const int64_t ntn_b = cdiv(N, Mx3<256>::TN);
+    const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_b, G * K, K, out);
+    else
+      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_b, G * K, K, out);
+    return hipGetLastError();
+  }
   if (kind == 2 && K > 0 && M * N * 2 < U32 && M * K * 2 < U32) {  // WGRAD (bf16), pipelined
     const int64_t ntn = cdiv(N, 256), ntk = cdiv(K, 256);
     const dim3 grid((unsigned)(G * ntn * ntk));
@@ -1783,10 +1999,10 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
     if (out_fp32)
       hipLaunchKernelGGL(k_gemm_mxfp8_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_b, out);
+                         b_scale, offsets, G, N, K, ntn_b, K, N * K, out);
     else
       hipLaunchKernelGGL(k_gemm_mxfp8_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_b, out);
+                         b_scale, offsets, G, N, K, ntn_b, K, N * K, out);
     return hipGetLastError();
   }
   if (fmt == 1) {

@@ -96,7 +96,15 @@ def test_grouped_gemm_validation():
     assert f(*args(fmt=5)) == 4
     assert f(*args(kind=9)) == 4
     assert f(*args(out=3)) == 4
-    assert f(*args(kind=1)) == 4                    # MXFP8 dgrad not offered
+    assert f(*args(fmt=2, kind=1)) == 4             # NVFP4: forward only
+    assert f(*args(fmt=2, kind=2)) == 4
+    assert f(*args(kind=1)) == 2                    # MXFP8 dgrad: K % 128
+    assert f(*args(kind=1, K=4096)) == 2            # MXFP8 dgrad: K <= 2048
+    assert f(*args(kind=2, M=48)) == 2              # MXFP8 wgrad: M_total % 32
+    assert f(*args(kind=2, M=1 << 24)) == 2         # MXFP8 wgrad: 32-bit panel offsets
+    a = args()
+    a[3] = BAD                                      # MXFP8 scales 4-byte aligned
+    assert f(*a) == 3
     assert f(*args(K=48)) == 2
     assert f(*args(fmt=2, K=40)) == 2
     assert f(*args(fmt=2, brps=3)) == 2

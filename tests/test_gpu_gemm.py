@@ -142,6 +142,97 @@ def test_mxfp8_qwen3_gate_up_full_sampled():
     assert M == T * k
 
 
+# ------------------------------------------------- MXFP8 backward GEMMs
+
+def _colwise_b_groups(qT, sT, G, K):
+    """Exact values of the column-wise copy of a stacked [G*K, N] weight as
+    per-expert B_g[n, k] = W_g[k, n]: [G, N, K]."""
+    v = oracle.decode_mxfp8(qT, sT)                  # [N, G*K]
+    N = v.shape[0]
+    return np.ascontiguousarray(v.reshape(N, G, K).transpose(1, 0, 2))
+
+
+@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 384), ([260, 0, 3], 160, 128),
+                                         ([513], 224, 2048), ([70, 330], 288, 1536)])
+def test_mxfp8_dgrad(sizes, N, K):
+    """dX[m, n] = sum_k dY[m, k] W_g[k, n] with dY row-wise (blocks along k)
+    and W from its column-wise copy (blocks along k, down W's columns)."""
+    G, M = len(sizes), int(sum(sizes))
+    dy = wl.activations(max(M, 1), K, seed=21)[:M]
+    w = wl.normal_bf16((G * K, N), std=0.02, seed=22)
+    off = _offsets(sizes)
+    qa, sa, _, _ = pqm.quantize_mxfp8(dev_bf16(dy), colwise=False)
+    _, _, qT, sT = pqm.quantize_mxfp8(dev_bf16(w), rowwise=False)
+    y = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_DGRAD, qa, qT, dev(off), N, K,
+                             a_scale=sa, b_scale=sT)
+    torch.cuda.synchronize()
+    ra, rsa = oracle.quantize_mxfp8_rowwise(dy)
+    rT, rsT = oracle.quantize_mxfp8_colwise(w)
+    want = oracle.grouped_gemm(oracle.decode_mxfp8(ra, rsa), _colwise_b_groups(rT, rsT, G, K), off)
+    check_rows(host(y), want, f"mxfp8 dgrad {sizes} N={N} K={K}")
+
+
+def _padded(sizes, align=32):
+    return [-(-s // align) * align for s in sizes]
+
+
+def _pad_rows(x, sizes, align=32):
+    """Each group's rows followed by zero rows up to a multiple of align."""
+    out, lo = [], 0
+    for s in sizes:
+        blk = np.zeros((-(-s // align) * align, x.shape[1]), x.dtype)
+        blk[:s] = x[lo:lo + s]
+        out.append(blk)
+        lo += s
+    return np.concatenate(out) if out else x[:0]
+
+
+def _mxfp8_wgrad_case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32):
+    G, M = len(sizes), int(sum(sizes))
+    dy = _pad_rows(wl.activations(max(M, 1), N, seed=seed)[:M], sizes)
+    x = _pad_rows(wl.activations(max(M, 1), K, seed=seed + 1)[:M], sizes)
+    off = _offsets(_padded(sizes))
+    _, _, aT, asT = pqm.quantize_mxfp8(dev_bf16(dy), rowwise=False)
+    _, _, bT, bsT = pqm.quantize_mxfp8(dev_bf16(x), rowwise=False)
+    y = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_WGRAD, aT, bT, dev(off), N, K,
+                             a_scale=asT, b_scale=bsT, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    rA, rsA = oracle.quantize_mxfp8_colwise(dy)
+    rB, rsB = oracle.quantize_mxfp8_colwise(x)
+    want = oracle.grouped_gemm_wgrad(oracle.decode_mxfp8(rA, rsA).T,
+                                     oracle.decode_mxfp8(rB, rsB).T, off)
+    return y, want
+
+
+@pytest.mark.parametrize("sizes,N,K", [
+    ([0, 37, 128, 1, 300], 192, 320),   # empty, one-row and ragged experts
+    ([2500, 3, 70], 256, 160),           # a 2048-token pass plus a tail
+    ([100, 0, 33, 257], 544, 288),       # output edges inside a tile
+    ([4200], 64, 512),                   # three passes
+])
+def test_mxfp8_wgrad(sizes, N, K):
+    """dW_g = dY_g^T X_g from the column-wise copies, each expert's rows
+    padded with zero rows to whole 32-row blocks."""
+    y, want = _mxfp8_wgrad_case(sizes, N, K, seed=23)
+    got = host(y)
+    assert got.shape == (len(sizes), N, K)
+    for g, s in enumerate(sizes):
+        if s == 0:
+            assert not got[g].any()
+        else:
+            check_rows(got[g], want[g], f"mxfp8 wgrad {sizes} group {g}")
+
+
+def test_mxfp8_wgrad_bf16_out():
+    y, want = _mxfp8_wgrad_case([300, 0, 129], 288, 192, seed=25, out_dtype=pqm.OUT_BF16)
+    got = host_u16(y)
+    for g in (0, 2):
+        r = rel_l2_rows(oracle.bf16_to_f64(got[g]), want[g])
+        print(f"[gemm] mxfp8 wgrad bf16 out group {g}: max row rel-L2 {r.max():.3e}", flush=True)
+        assert r.max() <= TOL + 2.0 ** -9
+    assert not got[1].any()
+
+
 # ------------------------------------------------------------------- BF16
 
 def _bf16_operands(M, N, K, G, seed):
