@@ -16,6 +16,12 @@ seeded input, with all inputs resident in HBM:
   q3_gemm           the two MXFP8 grouped GEMMs of q3_fwd alone
   q3_dequant        dequantize of the forward operands (dequantized backward)
   q3_bwd            BF16 dgrad + wgrad of both expert GEMMs on them
+  q3_bwd_mx         MXFP8 low-precision backward of both expert GEMMs: the
+                    two output gradients padded per expert to 32-row blocks
+                    and quantized (row-wise + column-wise, one pass each),
+                    then dgrad on the weights' column-wise copies and wgrad
+                    on the column-wise copies of gradient and saved input
+                    (those forward-side copies are made outside the step)
   ds_wquant         DeepSeek-V3 experts (256 routed + 1 shared, hidden 7168,
                     intermediate 2048): NVFP4 weights, gate/up jointly scaled
   ds_fwd            NVFP4 MoE expert layer forward, 4096 tokens top-8 + shared
@@ -55,7 +61,7 @@ FP8_PEAK_TFLOPS = 5000.0       # dense MFMA FP8
 BF16_PEAK_TFLOPS = 2500.0      # dense MFMA BF16 / FP16
 
 ALL_ROWS = ["mxfp8_quant", "nvfp4_token", "nvfp4_joint_w", "q3_wquant", "q3_fwd", "q3_gemm",
-            "q3_dequant", "q3_bwd", "ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"]
+            "q3_dequant", "q3_bwd", "q3_bwd_mx", "ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"]
 EXTRA_ROWS = ["hbm_copy"]
 COPY_BYTES = 512 << 20
 REPEAT_ROWS = ("mxfp8_quant", "nvfp4_token")
@@ -147,7 +153,7 @@ def main():
     # Qwen3-30B-A3B expert layer
     T4, K4, I4 = 8192, 8, 768
     M4 = T4 * K4
-    if need("q3_wquant", "q3_fwd", "q3_gemm", "q3_dequant", "q3_bwd"):
+    if need("q3_wquant", "q3_fwd", "q3_gemm", "q3_dequant", "q3_bwd", "q3_bwd_mx"):
         st["x4"] = to_dev(wl.activations(T4, H, seed=4))
         st["ids4"] = torch.from_numpy(wl.zipf_routing(T4, E, K4)).to(dev)
         st["prob4"] = torch.from_numpy(wl.router_probs(T4, K4).reshape(-1)).to(dev)
@@ -156,6 +162,17 @@ def main():
         st["dY"] = to_dev(wl.output_grad(M4, H))
         st["dC"] = to_dev(wl.output_grad(M4, 2 * I4, seed=5))
         st["c4"] = torch.empty((M4, 2 * I4), dtype=torch.bfloat16, device=dev)  # q3_gemm's C
+    if need("q3_bwd_mx"):
+        # forward-side operands of the low-precision backward: the weights'
+        # column-wise copies and those of the padded FC1 input X (the
+        # routed token rows) and FC2 input D
+        off4, _, tok4, _ = pqm.moe_route(st["ids4"], E)
+        xr = pqm.moe_gather_rows(st["x4"], tok4)
+        st["bwmx"] = dict(
+            off=off4, wcol=moe_layer.column_copies_mxfp8(st["W1"], st["W2"]),
+            sx=moe_layer.saved_activation_mxfp8(xr, off4),
+            sd=moe_layer.saved_activation_mxfp8(to_dev(wl.activations(M4, I4, seed=8)), off4))
+        del xr
     # DeepSeek-V3 expert layer (weights drawn on the GPU from a seeded stream)
     T5, K5, E5, H5, I5 = 4096, 8, 256, 7168, 2048
     M5 = T5 * K5 + T5
@@ -232,6 +249,11 @@ def main():
         pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_WGRAD, st["dC"], d["a"], off, 2 * I4, H,
                              out_dtype=pqm.OUT_FP32)
 
+    def r_q3_bwd_mx(s):
+        m = st["bwmx"]
+        st["q3_bwd_mx_out"] = moe_layer.mxfp8_expert_backward(st["dY"], st["dC"], m["sx"], m["sd"],
+                                                              m["wcol"], m["off"], I4)
+
     def r_ds_wquant(s):
         st["dsw"] = moe_layer.quantize_expert_weights_nvfp4(st["W1d"], st["W2d"], I5, H5)
 
@@ -263,7 +285,8 @@ def main():
 
     fns = {"hbm_copy": r_copy, "mxfp8_quant": r_mxfp8, "nvfp4_token": r_nvfp4, "nvfp4_joint_w": r_joint,
            "q3_wquant": r_q3_wquant, "q3_fwd": r_q3_fwd, "q3_gemm": r_q3_gemm,
-           "q3_dequant": r_q3_dequant, "q3_bwd": r_q3_bwd, "ds_wquant": r_ds_wquant,
+           "q3_dequant": r_q3_dequant, "q3_bwd": r_q3_bwd, "q3_bwd_mx": r_q3_bwd_mx,
+           "ds_wquant": r_ds_wquant,
            "ds_fwd": r_ds_fwd, "ds_gemm": r_ds_gemm, "ds_reconstruct": r_ds_reconstruct}
     deps = {"q3_fwd": ["q3_wquant"], "q3_gemm": ["q3_wquant", "q3_fwd"],
             "q3_dequant": ["q3_wquant", "q3_fwd"], "q3_bwd": ["q3_wquant", "q3_fwd", "q3_dequant"],
@@ -329,6 +352,9 @@ def main():
         elif n == "q3_bwd":
             fl = 2 * fl_q3
             c.update(flop=fl, tflops=fl / t / 1e12, frac_bf16=fl / t / 1e12 / BF16_PEAK_TFLOPS)
+        elif n == "q3_bwd_mx":
+            fl = 2 * fl_q3  # algorithmic: routed rows only, padding rows not counted
+            c.update(flop=fl, tflops=fl / t / 1e12, frac_fp8=fl / t / 1e12 / FP8_PEAK_TFLOPS)
         elif n == "ds_wquant":
             hbm(c, ((E5 + 1) * (2 * I5 * H5 + H5 * I5)) * (2 + 0.5 + 1 / 16), t)
         elif n in ("ds_fwd", "ds_gemm"):

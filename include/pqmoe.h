@@ -174,9 +174,9 @@ pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q,
  * ACC *= alpha_a[m] (* alpha_b)).
  *
  * offsets [G+1] int64 (device): group g owns rows offsets[g] ..
- * offsets[g+1]-1 of A; offsets[0] = 0, non-decreasing, offsets[G] =
- * M_total.  Empty groups are legal.  Values outside this contract are
- * undefined behaviour.
+ * offsets[g+1]-1 of A; offsets[0] = 0, non-decreasing, offsets[G] <=
+ * M_total (rows from offsets[G] on are neither read nor written).  Empty
+ * groups are legal.  Values outside this contract are undefined behaviour.
  *
  *   PQM_GEMM_FPROP (all formats):   Y[m, n] = sum_k A[m, k] B_g[n, k]
  *       A [M_total, K] and B [G, N, K], both with K contiguous;
@@ -294,6 +294,29 @@ pqm_status pqm_moe_route(const int32_t *topk_ids, int64_t tokens, int64_t k,
 pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_bytes,
                                const int32_t *index, int64_t n, int64_t divisor,
                                void *out, hipStream_t stream);
+
+/*
+ * Per-expert padding to whole blocks of `align` rows ([MT] 5.3: the
+ * permuted FC1 activation is padded before it is quantized; [BW] MXFP8
+ * training: the column-wise copies have 32 x 1 blocks down each column, so
+ * with align = 32 no block holds two experts' tokens):
+ *   padded_offsets[0] = 0, padded_offsets[g+1] = padded_offsets[g] +
+ *       ceil(n_g / align) * align,  n_g = offsets[g+1] - offsets[g];
+ *   out row padded_offsets[g] + j = src row offsets[g] + j for j < n_g;
+ *   every other row of out (the padding, and rows from padded_offsets[G]
+ *   to out_rows) is zero.
+ *   src [src_rows, row_bytes], out [out_rows, row_bytes]        (device)
+ *   offsets, padded_offsets [G+1] int64                         (device)
+ * Requires align >= 1, row_bytes % 16 == 0, out_rows >= src_rows + G *
+ * (align - 1) (room for any offsets; PQM_ERR_SHAPE otherwise); src and out
+ * 16-byte aligned, the offset arrays 8-byte aligned (PQM_ERR_ALIGN).
+ * offsets must satisfy the pqm_moe_grouped_gemm contract with offsets[G]
+ * <= src_rows.
+ */
+pqm_status pqm_moe_pad_rows(const void *src, int64_t src_rows, int64_t row_bytes,
+                            const int64_t *offsets, int64_t G, int64_t align,
+                            int64_t *padded_offsets, void *out, int64_t out_rows,
+                            hipStream_t stream);
 
 /*
  * Weighted SwiGLU: d[m, j] = bf16( silu(g) * u * p ) with g = c[m, j],

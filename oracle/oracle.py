@@ -296,6 +296,26 @@ def route_token(src_row: np.ndarray, T: int, k: int) -> np.ndarray:
     return np.where(src_row < T * k, src_row // k, src_row - T * k)
 
 
+def pad_rows(x: np.ndarray, offsets: np.ndarray, align: int):
+    """Per-expert padding ([MT] 5.3 pads the permuted activation before it
+    is quantized; [BW] MXFP8 training: a column-wise 32 x 1 block must hold
+    one expert's tokens only).  Group g's rows are moved to start at the sum
+    of the earlier groups' sizes rounded up to multiples of `align`; the
+    rows in between are zero.  Returns (padded x, padded offsets [G+1])."""
+    offsets = np.asarray(offsets, np.int64)
+    G = offsets.size - 1
+    sizes = offsets[1:] - offsets[:-1]
+    padded = [int(-(-int(n) // align) * align) for n in sizes]
+    poff = np.zeros(G + 1, np.int64)
+    for g in range(G):
+        poff[g + 1] = poff[g] + padded[g]
+    out = np.zeros((int(poff[-1]),) + x.shape[1:], x.dtype)
+    for g in range(G):
+        n = int(sizes[g])
+        out[poff[g]:poff[g] + n] = x[offsets[g]:offsets[g] + n]
+    return out, poff
+
+
 def silu(z: np.ndarray) -> np.ndarray:
     """silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), in binary64."""
     z = np.asarray(z, np.float64)

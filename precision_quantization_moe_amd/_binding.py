@@ -42,6 +42,7 @@ SIGNATURES = {
     "pqm_moe_route": ([P, I64, I64, I64, I32, P, P, P, P, P, SZ, P], I32),
     "pqm_moe_route_workspace": ([I64, I64, I64], SZ),
     "pqm_moe_gather_rows": ([P, I64, I64, P, I64, I64, P, P], I32),
+    "pqm_moe_pad_rows": ([P, I64, I64, P, I64, I64, P, P, I64, P], I32),
     "pqm_swiglu_prob": ([P, P, P, I64, I64, P, P], I32),
     "pqm_swiglu_prob_quantize_mxfp8": ([P, P, P, I64, I64, P, P, P, P], I32),
     "pqm_moe_combine": ([P, P, P, I64, I64, I64, P, P], I32),
@@ -204,6 +205,32 @@ def moe_gather_rows(src: torch.Tensor, index: torch.Tensor, divisor: int = 1):
                                      divisor, _ptr(out), _stream(src.device)),
            "pqm_moe_gather_rows")
     return out
+
+
+def pad_rows_bound(rows: int, groups: int, align: int = 32) -> int:
+    """Rows that any per-expert padding of `rows` rows in `groups` groups
+    fits in, rounded up to a whole block."""
+    n = rows + groups * (align - 1)
+    return -(-n // align) * align
+
+
+def moe_pad_rows(src: torch.Tensor, offsets: torch.Tensor, align: int = 32, out=None,
+                 padded_offsets=None):
+    """Each group's rows of a 2-D tensor moved to a start that is a multiple
+    of `align`, padding rows zero.  Returns (out [pad_rows_bound(...), ...],
+    padded_offsets int64 [G+1] on the device)."""
+    G = offsets.numel() - 1
+    rows = src.shape[0]
+    if out is None:
+        out = torch.empty((pad_rows_bound(rows, G, align),) + tuple(src.shape[1:]),
+                          dtype=src.dtype, device=src.device)
+    if padded_offsets is None:
+        padded_offsets = torch.empty(G + 1, dtype=torch.int64, device=src.device)
+    row_bytes = src.stride(0) * src.element_size()
+    _check(lib().pqm_moe_pad_rows(_ptr(src), rows, row_bytes, _ptr(offsets), G, align,
+                                  _ptr(padded_offsets), _ptr(out), out.shape[0],
+                                  _stream(src.device)), "pqm_moe_pad_rows")
+    return out, padded_offsets
 
 
 def swiglu_prob(c: torch.Tensor, prob: torch.Tensor, src: torch.Tensor | None = None):

@@ -464,15 +464,34 @@ __device__ __forceinline__ void mx3_mma(const Mx3Frags<TM> &F,
 
 // Write one transposed accumulator (token rows row0 + rbase + 0..31, output
 // columns n0 + cbase + 0..31).  Lane l holds columns 8 g + 4 (l / 32) + 0..3
-// of its row; the gfx950 lane swap between lanes l and l + 32 trades run
-// g = 1 (3) of the low half for run 0 (2) of the high half, after which lane
-// l holds columns 16 p + 8 (l / 32) + 0..7, p = 0, 1: two 16-byte (bf16) or
-// 32-byte (binary32) stores per lane.
+// of its row.  binary32: one 16-byte store per run, so the two lanes of a
+// row fill a whole 32-byte sector per instruction.  bf16: the gfx950 lane
+// swap between lanes l and l + 32 trades run g = 1 (3) of the low half for
+// run 0 (2) of the high half, after which lane l holds columns
+// 16 p + 8 (l / 32) + 0..7, p = 0, 1: two 16-byte stores per lane.
 template <bool OUT_F32>
 __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N, int64_t row0,
                                           int64_t row_end, int64_t n0, int rbase, int cbase) {
   const int lane = threadIdx.x & 63, h = lane >> 5;
   const int64_t row = row0 + rbase + (lane & 31);
+  if (OUT_F32) {
+    // run g = registers 4 g .. 4 g + 3 = columns 8 g + 4 h + 0..3
+    if (row >= row_end) return;
+    float *orow = static_cast<float *>(out) + row * N;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t col = n0 + cbase + 8 * g + 4 * h;
+      if ((N & 3) == 0 && col + 3 < N) {
+        *reinterpret_cast<float4 *>(orow + col) =
+            make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < N) orow[col + e] = acc[4 * g + e];
+      }
+    }
+    return;
+  }
   const bool vec = (N & 7) == 0;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -495,28 +514,17 @@ __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N,
     const int64_t col = n0 + cbase + 16 * p + 8 * h;
     if (row >= row_end) continue;
     if (vec && col + 7 < N) {
-      if (OUT_F32) {
-        float *dst = static_cast<float *>(out) + row * N + col;
-        *reinterpret_cast<float4 *>(dst) = make_float4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<float4 *>(dst + 4) = make_float4(hi[0], hi[1], hi[2], hi[3]);
-      } else {
-        const uint4 w = make_uint4(f32_to_bf16_rne(lo[0]) | (f32_to_bf16_rne(lo[1]) << 16),
-                                   f32_to_bf16_rne(lo[2]) | (f32_to_bf16_rne(lo[3]) << 16),
-                                   f32_to_bf16_rne(hi[0]) | (f32_to_bf16_rne(hi[1]) << 16),
-                                   f32_to_bf16_rne(hi[2]) | (f32_to_bf16_rne(hi[3]) << 16));
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + row * N + col) = w;
-      }
+      const uint4 w = make_uint4(f32_to_bf16_rne(lo[0]) | (f32_to_bf16_rne(lo[1]) << 16),
+                                 f32_to_bf16_rne(lo[2]) | (f32_to_bf16_rne(lo[3]) << 16),
+                                 f32_to_bf16_rne(hi[0]) | (f32_to_bf16_rne(hi[1]) << 16),
+                                 f32_to_bf16_rne(hi[2]) | (f32_to_bf16_rne(hi[3]) << 16));
+      *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + row * N + col) = w;
     } else {
       const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (col + e < N) {
-          if (OUT_F32)
-            static_cast<float *>(out)[row * N + col + e] = v[e];
-          else
-            static_cast<uint16_t *>(out)[row * N + col + e] = (uint16_t)f32_to_bf16_rne(v[e]);
-        }
-      }
+      for (int e = 0; e < 8; ++e)
+        if (col + e < N)
+          static_cast<uint16_t *>(out)[row * N + col + e] = (uint16_t)f32_to_bf16_rne(v[e]);
     }
   }
 }
@@ -807,7 +815,9 @@ __device__ __forceinline__ void mx3w_issue(const Mx3Src<TM> &L, const uint32_t (
 
 // Scale bytes of one staged row for a pass: nb valid blocks starting at
 // byte p (any alignment) of an array whose last byte is at `last`; blocks
-// nb .. 4 dpr - 1 get 127.  Written dword-major as mx3_read expects.
+// nb .. 4 dpr - 1 get 127.  Loaded as the 17 aligned dwords that cover them
+// (clamped to the array), realigned by a byte shift, written dword-major as
+// mx3_read expects.
 __device__ __forceinline__ void mx3w_scales_row(const uint8_t *p, const uint8_t *last, int nb,
                                                 int dpr, uint8_t *area, int row) {
   const uintptr_t a0 = (uintptr_t)p & ~(uintptr_t)3, amax = (uintptr_t)last & ~(uintptr_t)3;
@@ -843,10 +853,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_wgrad(
   using C = Mx3<TM>;
   constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN, PASS = 32 * C::MAX_KS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
-  // tiles of one expert are consecutive; workgroup b runs on XCD b % 8, and
-  // each XCD takes a contiguous range of tiles
-  const int64_t total = G * ntm * ntn, per_xcd = (int64_t)gridDim.x / 8;
-  const int64_t T = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  // tiles of one expert are consecutive; workgroup b runs on XCD b % 8, so
+  // an expert's tiles spread over all XCDs (expert loads are skewed)
+  const int64_t total = G * ntm * ntn;
+  const int64_t T = blockIdx.x;
   if (T >= total) return;
   const int64_t g = T / (ntm * ntn), rem = T - g * ntm * ntn;
   const int64_t n0 = (rem / ntn) * TM, k0 = (rem % ntn) * TN;

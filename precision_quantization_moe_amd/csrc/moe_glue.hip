@@ -302,6 +302,73 @@ hipError_t launch_combine(const uint16_t *y, const int32_t *slot, const uint16_t
   return hipGetLastError();
 }
 
+// Per-expert padding to whole blocks of `align` rows, so that column-wise
+// (32 x 1) blocks never hold two experts' tokens.  One workgroup scans the
+// padded counts: poff[g] = sum over e < g of ceil(n_e / align) * align.
+__global__ __launch_bounds__(1024) void k_pad_offsets(const int64_t *__restrict__ off, int64_t G,
+                                                      int64_t align, int64_t *__restrict__ poff) {
+  __shared__ int64_t part[1024];
+  int64_t carry = 0;
+  for (int64_t c0 = 0; c0 < G; c0 += 1024) {
+    const int64_t g = c0 + threadIdx.x;
+    int64_t v = 0;
+    if (g < G) v = (off[g + 1] - off[g] + align - 1) / align * align;
+    part[threadIdx.x] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan
+      const int64_t t = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+      __syncthreads();
+      part[threadIdx.x] += t;
+      __syncthreads();
+    }
+    if (g < G) poff[g + 1] = carry + part[threadIdx.x];
+    carry += part[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) poff[0] = 0;
+}
+
+// One wave per output row: find its group in poff (binary search), then
+// copy the source row or write zeros, 16 bytes per lane.
+__global__ __launch_bounds__(256) void k_pad_rows(const uint8_t *__restrict__ src,
+                                                  int64_t row_bytes,
+                                                  const int64_t *__restrict__ off,
+                                                  const int64_t *__restrict__ poff, int64_t G,
+                                                  uint8_t *__restrict__ out, int64_t out_rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= out_rows) return;
+  int64_t srow = -1;
+  if (p < poff[G]) {
+    int64_t lo = 0, hi = G;  // largest g with poff[g] <= p
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) / 2;
+      if (poff[mid] <= p) lo = mid; else hi = mid;
+    }
+    const int64_t j = p - poff[lo];
+    if (j < off[lo + 1] - off[lo]) srow = off[lo] + j;
+  }
+  uint4 *o = reinterpret_cast<uint4 *>(out + p * row_bytes);
+  const int64_t nv = row_bytes / 16;
+  if (srow >= 0) {
+    const uint4 *s = reinterpret_cast<const uint4 *>(src + srow * row_bytes);
+    for (int64_t c = lane; c < nv; c += 64) o[c] = s[c];
+  } else {
+    for (int64_t c = lane; c < nv; c += 64) o[c] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+hipError_t launch_pad_rows(const void *src, int64_t row_bytes, const int64_t *off, int64_t G,
+                           int64_t align, int64_t *poff, void *out, int64_t out_rows,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(k_pad_offsets, dim3(1), dim3(1024), 0, st, off, G, align, poff);
+  if (out_rows > 0 && row_bytes > 0)
+    hipLaunchKernelGGL(k_pad_rows, dim3((unsigned)((out_rows + 3) / 4)), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(src), row_bytes, off, poff, G,
+                       static_cast<uint8_t *>(out), out_rows);
+  return hipGetLastError();
+}
+
 }  // namespace pqm
 
 namespace {
@@ -341,6 +408,21 @@ pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_by
   if (n == 0 || row_bytes == 0) return PQM_OK;
   if (!src || !index || !out) return PQM_ERR_NULL;
   return st_of(pqm::launch_gather(src, row_bytes, index, n, divisor, out, stream));
+}
+
+pqm_status pqm_moe_pad_rows(const void *src, int64_t src_rows, int64_t row_bytes,
+                            const int64_t *offsets, int64_t G, int64_t align,
+                            int64_t *padded_offsets, void *out, int64_t out_rows,
+                            hipStream_t stream) {
+  if (src_rows < 0 || row_bytes < 0 || G < 0 || align < 1 || out_rows < 0) return PQM_ERR_SHAPE;
+  if (row_bytes % 16 || out_rows < src_rows + G * (align - 1) || out_rows >= ((int64_t)1 << 40))
+    return PQM_ERR_SHAPE;
+  if (!offsets || !padded_offsets) return PQM_ERR_NULL;
+  if (out_rows > 0 && row_bytes > 0 && (!out || (src_rows > 0 && !src))) return PQM_ERR_NULL;
+  if (!al(offsets, 8) || !al(padded_offsets, 8) || !al(src, 16) || !al(out, 16))
+    return PQM_ERR_ALIGN;
+  return st_of(pqm::launch_pad_rows(src, row_bytes, offsets, G, align, padded_offsets, out,
+                                    out_rows, stream));
 }
 
 pqm_status pqm_swiglu_prob(const uint16_t *c, const float *prob, const int32_t *src,

@@ -25,6 +25,58 @@ def quantize_expert_weights_mxfp8(w1: torch.Tensor, w2: torch.Tensor):
     return w1q, w1s, w2q, w2s
 
 
+def column_copies_mxfp8(w1: torch.Tensor, w2: torch.Tensor):
+    """Column-wise MXFP8 copies (32 x 1 blocks, stored transposed) of the
+    stacked expert weights, the data-gradient operands of the low-precision
+    backward: w1 [E*2I, H] -> ([H, E*2I], [H, E*2I/32]); w2 [E*H, I] ->
+    ([I, E*H], [I, E*H/32])."""
+    _, _, w1T, w1sT = b.quantize_mxfp8(w1, rowwise=False)
+    _, _, w2T, w2sT = b.quantize_mxfp8(w2, rowwise=False)
+    return w1T, w1sT, w2T, w2sT
+
+
+def saved_activation_mxfp8(rows: torch.Tensor, off: torch.Tensor):
+    """The forward-side column-wise MXFP8 copy of an expert-sorted
+    activation (FC1 input X or FC2 input D) for the weight gradient: each
+    expert's rows padded to whole 32-row blocks, then quantized down the
+    columns.  Returns (qT [C, Mp], sT [C, Mp/32], padded offsets)."""
+    xp, poff = b.moe_pad_rows(rows, off)
+    _, _, qT, sT = b.quantize_mxfp8(xp, rowwise=False)
+    return qT, sT, poff
+
+
+def mxfp8_expert_backward(dy, dc, saved_x, saved_d, w_col, off, inter: int):
+    """MXFP8 low-precision backward of the two expert GEMMs ([BW] MXFP8
+    training: the data- and weight-gradient GEMMs run in MXFP8 on the
+    column-wise copies).
+      dy [M, H] bf16   gradient of the down-projection output rows
+      dc [M, 2I] bf16  gradient of the gate_up output rows
+      saved_x, saved_d (qT, sT, padded offsets) from saved_activation_mxfp8
+      w_col            column_copies_mxfp8(W1, W2)
+    Both gradients are padded per expert (pqm_moe_pad_rows) and quantized
+    once into their row-wise (data gradient) and column-wise (weight
+    gradient) copies.  Returns dict(dd [Mp, I] bf16, dx [Mp, H] bf16,
+    dw2 [E, H, I] fp32, dw1 [E, 2I, H] fp32, poff): dd and dx are in the
+    padded row order (row poff[e] + j of expert e is routed row off[e] + j)."""
+    H = dy.shape[1]
+    w1T, w1sT, w2T, w2sT = w_col
+    xT, xsT, _ = saved_x
+    dT, dsT, _ = saved_d
+    dyp, poff = b.moe_pad_rows(dy, off)
+    dcp, _ = b.moe_pad_rows(dc, off)
+    qy, sy, qyT, syT = b.quantize_mxfp8(dyp)
+    qc, sc, qcT, scT = b.quantize_mxfp8(dcp)
+    dd = b.moe_grouped_gemm(b.FMT_MXFP8, b.GEMM_DGRAD, qy, w2T, poff, inter, H,
+                            a_scale=sy, b_scale=w2sT, out_dtype=b.OUT_BF16)
+    dw2 = b.moe_grouped_gemm(b.FMT_MXFP8, b.GEMM_WGRAD, qyT, dT, poff, H, inter,
+                             a_scale=syT, b_scale=dsT, out_dtype=b.OUT_FP32)
+    dx = b.moe_grouped_gemm(b.FMT_MXFP8, b.GEMM_DGRAD, qc, w1T, poff, H, 2 * inter,
+                            a_scale=sc, b_scale=w1sT, out_dtype=b.OUT_BF16)
+    dw1 = b.moe_grouped_gemm(b.FMT_MXFP8, b.GEMM_WGRAD, qcT, xT, poff, 2 * inter, H,
+                             a_scale=scT, b_scale=xsT, out_dtype=b.OUT_FP32)
+    return dict(dd=dd, dx=dx, dw2=dw2, dw1=dw1, poff=poff)
+
+
 def quantize_expert_weights_nvfp4(w1: torch.Tensor, w2: torch.Tensor, inter: int, hidden: int):
     """NVFP4 weights with one FP32 outer scale per expert tensor; gate and up
     of an expert share one scale (joint)."""

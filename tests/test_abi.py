@@ -125,6 +125,14 @@ def test_glue_validation():
     assert L.pqm_moe_route(A16, 8, 2, 4, 1, A16, A16, None, A16, A16, 1 << 20, None) == 1
     assert L.pqm_moe_route_workspace(8192, 8, 128) == 64 * 128 * 4
     assert L.pqm_moe_gather_rows(A16, 4, 16, A16, 4, 0, A16, None) == 2
+    f = L.pqm_moe_pad_rows
+    assert f(A16, 64, 128, A16, 4, 0, A16, A16, 200, None) == 2      # align >= 1
+    assert f(A16, 64, 24, A16, 4, 32, A16, A16, 200, None) == 2      # row_bytes % 16
+    assert f(A16, 64, 128, A16, 4, 32, A16, A16, 187, None) == 2     # < 64 + 4 * 31 rows
+    assert f(A16, 64, 128, None, 4, 32, A16, A16, 188, None) == 1
+    assert f(A16, 64, 128, A16, 4, 32, None, A16, 188, None) == 1
+    assert f(BAD, 64, 128, A16, 4, 32, A16, A16, 188, None) == 3
+    assert f(A16, 64, 128, A16, 4, 32, BAD, A16, 188, None) == 3
     assert L.pqm_swiglu_prob(A16, A16, None, 4, 12, A16, None) == 2
     assert L.pqm_swiglu_prob(BAD, A16, None, 4, 16, A16, None) == 3
     f = L.pqm_swiglu_prob_quantize_mxfp8

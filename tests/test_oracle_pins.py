@@ -462,6 +462,41 @@ def test_route_counting_sort():
     assert all(len(set(r)) == 4 for r in ids.tolist())
 
 
+def test_pad_rows_worked_example():
+    """Per-expert padding to 32-row blocks, written out for a small case."""
+    x = np.arange(41 * 2, dtype=np.float64).reshape(41, 2) + 1.0
+    out, poff = oracle.pad_rows(x, np.array([0, 3, 3, 40, 41]), 32)
+    assert poff.tolist() == [0, 32, 32, 96, 128]
+    assert out.shape == (128, 2)
+    assert np.array_equal(out[0:3], x[0:3]) and not out[3:32].any()
+    assert np.array_equal(out[32:69], x[3:40]) and not out[69:96].any()
+    assert np.array_equal(out[96], x[40]) and not out[97:].any()
+    same, poff1 = oracle.pad_rows(x, np.array([0, 3, 3, 40, 41]), 1)
+    assert np.array_equal(same, x) and poff1.tolist() == [0, 3, 3, 40, 41]
+
+
+def test_pad_rows_keeps_wgrad_and_column_blocks_per_expert():
+    """Zero padding rows change no weight gradient, and after padding every
+    column-wise block lies inside one expert: quantizing the whole padded
+    buffer gives the bytes of quantizing each expert's padded rows alone."""
+    g = np.random.Generator(np.random.PCG64(31))
+    off = np.array([0, 5, 5, 70, 101])
+    dy = wl.f32_to_bf16_bits(g.standard_normal((101, 64), dtype=np.float32))
+    x = wl.f32_to_bf16_bits(g.standard_normal((101, 32), dtype=np.float32))
+    dyp, poff = oracle.pad_rows(dy, off, 32)
+    xp, _ = oracle.pad_rows(x, off, 32)
+    w = oracle.grouped_gemm_wgrad(oracle.bf16_to_f64(dy), oracle.bf16_to_f64(x), off)
+    wp = oracle.grouped_gemm_wgrad(oracle.bf16_to_f64(dyp), oracle.bf16_to_f64(xp), poff)
+    assert np.allclose(w, wp, rtol=1e-13, atol=1e-13)
+    qT, sT = oracle.quantize_mxfp8_colwise(dyp)
+    for e in range(4):
+        lo, hi = int(poff[e]), int(poff[e + 1])
+        if hi > lo:
+            qe, se = oracle.quantize_mxfp8_colwise(dyp[lo:hi])
+            assert np.array_equal(qT[:, lo:hi], qe)
+            assert np.array_equal(sT[:, lo // 32:hi // 32], se)
+
+
 def test_silu_and_swiglu_identities():
     z = np.linspace(-30, 30, 601)
     s = oracle.silu(z)
