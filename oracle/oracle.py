@@ -14,6 +14,7 @@ Page titles cited:
   [BW] "Towards Blackwell-Native 8-bit and 4-bit RL"
   [MT] "miniTE technical report: stable training and efficient
        implementation of native NVFP4 RL"
+  [PR] "PR #2396 report: docs: refresh MXFP8 and NVFP4 RL guide"
 """
 from __future__ import annotations
 
@@ -58,6 +59,8 @@ def lib():
         L.pqo_dequantize_nvfp4.argtypes = [P, P, P, Lg, Lg, Lg, P]
         L.pqo_decode_mxfp8.argtypes = [P, P, Lg, Lg, P]
         L.pqo_decode_nvfp4.argtypes = [P, P, P, Lg, Lg, Lg, P]
+        L.pqo_quantize_fp8_block.argtypes = [P, Lg, Lg, Lg, Lg, P, P]
+        L.pqo_decode_fp8_block.argtypes = [P, P, Lg, Lg, Lg, P]
         L.pqo_e4m3_encode.argtypes = [ctypes.c_double, ctypes.c_double]
         L.pqo_e4m3_encode.restype = ctypes.c_uint8
         L.pqo_e2m1_encode.argtypes = [ctypes.c_double, ctypes.c_double]
@@ -138,6 +141,30 @@ def quantize_nvfp4(x: np.ndarray, rows_per_group: int = 1):
     lib().pqo_quantize_nvfp4(_ptr(x), R, C, C, rows_per_group,
                              _ptr(q), _ptr(sb), _ptr(sg))
     return q, sb, sg
+
+
+def quantize_fp8_block(x: np.ndarray, block_rows: int):
+    """DeepSeek-V3-style block FP8: blocks of block_rows x 128 (1 for
+    activation tiles, 128 for weight blocks), s = A/448 in binary32, q =
+    nearest E4M3 of x/s.  Returns (q[R, C] u8, s[R/block_rows, C/128] f32)."""
+    x = _bf16(x)
+    R, C = x.shape
+    assert C % 128 == 0 and block_rows >= 1 and R % block_rows == 0
+    q = np.empty((R, C), np.uint8)
+    s = np.empty((R // block_rows, C // 128), np.float32)
+    lib().pqo_quantize_fp8_block(_ptr(x), R, C, C, block_rows, _ptr(q), _ptr(s))
+    return q, s
+
+
+def decode_fp8_block(q: np.ndarray, s: np.ndarray, block_rows: int) -> np.ndarray:
+    """Exact binary64 values q * s."""
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.float32)
+    R, C = q.shape
+    assert s.shape == (R // block_rows, C // 128)
+    out = np.empty((R, C), np.float64)
+    lib().pqo_decode_fp8_block(_ptr(q), _ptr(s), R, C, block_rows, _ptr(out))
+    return out
 
 
 def dequantize_mxfp8(q: np.ndarray, s: np.ndarray) -> np.ndarray:

@@ -290,6 +290,64 @@ void pqo_quantize_nvfp4(const uint16_t *x, long R, long C, long ld,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Block-scaled FP8, the DeepSeek-V3 style ([BW] Why Blackwell-native       */
+/* recipes: 128x128 weight blocks and 1x128 activation tiles, each with an  */
+/* FP32 scale computed online and applied around the matrix core; [PR]      */
+/* Choose a precision: FP8 block-wise, 128x128, FP32 scales).               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Blocks of br rows x 128 columns (br = 1: activation tiles; br = 128:
+ * weight blocks).  For a block with absolute maximum A:
+ *   s = A / 448 rounded once to binary32 (reading: the block maximum maps
+ *       to the E4M3 maximum; the pages give the block shapes and FP32
+ *       scales, not the formula);
+ *   q = nearest E4M3 to x / s, ties to even, saturating at 448; A = 0
+ *       gives s = 0 and q = +-0.
+ * s [R/br, C/128] binary32, q [R, C] bytes.
+ */
+void pqo_quantize_fp8_block(const uint16_t *x, long R, long C, long ld, long br,
+                            uint8_t *q, float *s)
+{
+    init_grids();
+    long RB = R / br, CB = C / 128;
+#pragma omp parallel for schedule(dynamic)
+    for (long blk = 0; blk < RB * CB; ++blk) {
+        long rb = blk / CB, cb = blk % CB;
+        float A = 0.0f;
+        for (long r = rb * br; r < (rb + 1) * br; ++r)
+            for (long c = cb * 128; c < cb * 128 + 128; ++c) {
+                float v = (float)fabs(bf16_value(x[r * ld + c]));
+                if (v > A)
+                    A = v;
+            }
+        volatile float d = 448.0f; /* keep the division in binary32 */
+        float sc = A / d;
+        s[blk] = sc;
+        for (long r = rb * br; r < (rb + 1) * br; ++r)
+            for (long c = cb * 128; c < cb * 128 + 128; ++c) {
+                double v = bf16_value(x[r * ld + c]);
+                q[r * C + c] = sc == 0.0f ? (uint8_t)(signbit(v) ? 0x80 : 0x00)
+                                          : e4m3_encode(v, (double)sc);
+            }
+    }
+}
+
+/* Exact binary64 values q * s of a block-scaled FP8 tensor. */
+void pqo_decode_fp8_block(const uint8_t *q, const float *s, long R, long C, long br,
+                          double *out)
+{
+    long CB = C / 128;
+#pragma omp parallel for
+    for (long r = 0; r < R; ++r)
+        for (long c = 0; c < C; ++c) {
+            uint8_t b = q[r * C + c];
+            double v = e4m3_magnitude(b & 0x7F) * (double)s[(r / br) * CB + c / 128];
+            out[r * C + c] = (b & 0x80) ? -v : v;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantize ([BW] High-precision and dequantized backward: the backward   */
 /* GEMMs read the BF16 dequantization of the exact forward operands).       */
 /* ------------------------------------------------------------------------ */

@@ -133,3 +133,25 @@ def nvfp4(xbits: np.ndarray, rows_per_group: int = 1):
                 for j in range(8):
                     q[r, blk * 8 + j] = nib[2 * j] | (nib[2 * j + 1] << 4)
     return q, sb, sg
+
+
+def fp8_block(xbits: np.ndarray, block_rows: int):
+    """Block-scaled FP8 in Fractions: s = binary32(A / 448) per block of
+    block_rows x 128, codes = nearest E4M3 of x / s (sign kept, s = 0 gives
+    signed zeros).  Returns (q bytes, s float32)."""
+    R, C = xbits.shape
+    q = np.zeros((R, C), np.uint8)
+    s = np.zeros((R // block_rows, C // 128), np.float32)
+    for rb in range(R // block_rows):
+        for cb in range(C // 128):
+            rows = range(rb * block_rows, (rb + 1) * block_rows)
+            cols = range(cb * 128, (cb + 1) * 128)
+            A = max(abs(bf16_value(int(xbits[r, c]))) for r in rows for c in cols)
+            sc = round_fp32(A / 448)
+            s[rb, cb] = np.float32(float(sc))
+            for r in rows:
+                for c in cols:
+                    b = int(xbits[r, c])
+                    sign = 0x80 if b & 0x8000 else 0
+                    q[r, c] = sign if sc == 0 else sign | nearest(E4M3, bf16_value(b) / sc)
+    return q, s

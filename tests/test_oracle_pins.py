@@ -445,6 +445,94 @@ def test_grouped_gemm_nvfp4_operands_factor():
     assert np.allclose(Y, ref, rtol=1e-13, atol=0)
 
 
+# ------------------------------------------------------ block-scaled FP8
+
+def test_fp8_block_worked_example():
+    """1 x 128 activation tile with maximum 1.0 ([BW] Why Blackwell-native
+    recipes: 1x128 activation tiles with an FP32 scale; reading: s = A/448):
+    s = binary32(1/448); 1.0 -> 448 (0x7E), -1.0 -> 0xFE, 0.5 -> 224 (0x76),
+    0 -> 0x00; an all-zero tile has s = 0 and keeps the signs of its zeros."""
+    row = np.zeros(128, np.float32)
+    row[:4] = [1.0, -1.0, 0.5, 0.0]
+    x = np.stack([row, np.zeros(128, np.float32)])
+    bits = wl.f32_to_bf16_bits(x)
+    bits[1, 5] = 0x8000                                 # -0.0
+    q, sc = oracle.quantize_fp8_block(bits, 1)
+    assert sc[0, 0] == np.float32(1.0) / np.float32(448.0) and sc[1, 0] == 0.0
+    assert q[0, :4].tolist() == [0x7E, 0xFE, 0x76, 0x00]
+    assert not q[0, 4:].any() and q[1, 5] == 0x80 and not np.delete(q[1], 5).any()
+
+
+@pytest.mark.parametrize("block_rows", [1, 128])
+def test_fp8_block_vs_bruteforce(block_rows):
+    """Scales of every block and the codes of sampled elements against the
+    exact argmin over all E4M3 values."""
+    if block_rows == 1:
+        x = np.concatenate([wl.activations(6, 256, seed=12), wl.boundary_tensor(256)[:2]])
+        idx = [(r, c) for r in range(x.shape[0]) for c in range(256)]
+    else:
+        x = wl.normal_bf16((256, 256), std=0.02, seed=13)
+        g = np.random.Generator(np.random.PCG64(14))
+        idx = [tuple(v) for v in g.integers(0, 256, (600, 2))]
+    q, sc = oracle.quantize_fp8_block(x, block_rows)
+    R, C = x.shape
+    for rb in range(R // block_rows):
+        for cb in range(C // 128):
+            blk = x[rb * block_rows:(rb + 1) * block_rows, cb * 128:(cb + 1) * 128]
+            A = max(abs(bf.bf16_value(int(b))) for b in blk.reshape(-1))
+            assert Fr(float(sc[rb, cb])) == bf.round_fp32(A / 448)
+    for r, c in idx:
+        b = int(x[r, c])
+        s_ = Fr(float(sc[r // block_rows, c // 128]))
+        want = (0x80 if b & 0x8000 else 0)
+        if s_ != 0:
+            want |= bf.nearest(bf.E4M3, bf.bf16_value(b) / s_)
+        assert q[r, c] == want, (r, c, hex(b))
+
+
+def test_fp8_block_max_maps_to_448_and_error_bound():
+    """Every non-zero block's largest element encodes to +-448, and every
+    decoded value is within half an E4M3 step of x (2^-4 relative for
+    normal codes, 2^-10 s below the smallest normal)."""
+    x = wl.activations(64, 512, seed=15)
+    q, sc = oracle.quantize_fp8_block(x, 1)
+    xv = oracle.bf16_to_f64(x)
+    dec = oracle.decode_fp8_block(q, sc, 1)
+    for r in range(64):
+        for cb in range(4):
+            seg = slice(cb * 128, cb * 128 + 128)
+            j = int(np.argmax(np.abs(xv[r, seg])))
+            assert q[r, cb * 128 + j] & 0x7F == 0x7E
+    s_full = np.repeat(sc.astype(np.float64), 128, axis=1)
+    err = np.abs(dec - xv)
+    normal = np.abs(dec) >= 2.0 ** -6 * s_full
+    assert (err[normal] <= 2.0 ** -4 * np.abs(dec[normal]) * (1 + 1e-12)).all()
+    assert (err[~normal] <= 2.0 ** -10 * s_full[~normal] * (1 + 1e-12)).all()
+
+
+def test_fp8_block_gemm_scales_around_the_product():
+    """Y = sum over 128-K blocks of sa[m, kb] sb[nb, kb] (sum of q_a q_b):
+    the per-block scaled sum in Fractions equals the oracle's product of the
+    decoded operands."""
+    g = np.random.Generator(np.random.PCG64(16))
+    M, N, K = 3, 128, 256
+    xa = wl.f32_to_bf16_bits(g.standard_normal((M, K), dtype=np.float32))
+    xb = wl.f32_to_bf16_bits(g.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    qa, sa = oracle.quantize_fp8_block(xa, 1)
+    qb, sb = oracle.quantize_fp8_block(xb, 128)
+    Y = oracle.grouped_gemm(oracle.decode_fp8_block(qa, sa, 1),
+                            oracle.decode_fp8_block(qb, sb, 128)[None], np.array([0, M]))
+    code = lambda b: (-1 if b & 0x80 else 1) * bf.E4M3[b & 0x7F]
+    for m in range(M):
+        for n in (0, 77, 127):
+            tot = Fr(0)
+            for kb in range(K // 128):
+                part = sum(code(int(qa[m, k])) * code(int(qb[n, k]))
+                           for k in range(kb * 128, kb * 128 + 128))
+                tot += part * Fr(float(sa[m, kb])) * Fr(float(sb[n // 128, kb]))
+            assert abs(Fr(Y[m, n]) - tot) <= abs(tot) * Fr(1, 2 ** 45) + Fr(1, 2 ** 200)
+
+
 # ---------------------------------------------------------------- glue
 
 def test_route_counting_sort():
