@@ -14,6 +14,10 @@ seeded input, with all inputs resident in HBM:
                     gate_up GEMM with SwiGLU x prob and the FC2 operand's
                     MXFP8 quantize in its epilogue, down GEMM, combine
   q3_gemm           the two MXFP8 grouped GEMMs of q3_fwd alone
+  q3_gemm_fp8b      the same two grouped GEMMs in DeepSeek-style block FP8
+                    (1x128 activation tiles, 128x128 weight blocks, FP32
+                    scales applied around the matrix core); operands
+                    quantized outside the step
   q3_dequant        dequantize of the forward operands (dequantized backward)
   q3_bwd            BF16 dgrad + wgrad of both expert GEMMs on them
   q3_bwd_mx         MXFP8 low-precision backward of both expert GEMMs: the
@@ -61,6 +65,7 @@ FP8_PEAK_TFLOPS = 5000.0       # dense MFMA FP8
 BF16_PEAK_TFLOPS = 2500.0      # dense MFMA BF16 / FP16
 
 ALL_ROWS = ["mxfp8_quant", "nvfp4_token", "nvfp4_joint_w", "q3_wquant", "q3_fwd", "q3_gemm",
+            "q3_gemm_fp8b",
             "q3_dequant", "q3_bwd", "q3_bwd_mx", "ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"]
 EXTRA_ROWS = ["hbm_copy"]
 COPY_BYTES = 512 << 20
@@ -153,7 +158,7 @@ def main():
     # Qwen3-30B-A3B expert layer
     T4, K4, I4 = 8192, 8, 768
     M4 = T4 * K4
-    if need("q3_wquant", "q3_fwd", "q3_gemm", "q3_dequant", "q3_bwd", "q3_bwd_mx"):
+    if need("q3_wquant", "q3_fwd", "q3_gemm", "q3_gemm_fp8b", "q3_dequant", "q3_bwd", "q3_bwd_mx"):
         st["x4"] = to_dev(wl.activations(T4, H, seed=4))
         st["ids4"] = torch.from_numpy(wl.zipf_routing(T4, E, K4)).to(dev)
         st["prob4"] = torch.from_numpy(wl.router_probs(T4, K4).reshape(-1)).to(dev)
@@ -162,6 +167,16 @@ def main():
         st["dY"] = to_dev(wl.output_grad(M4, H))
         st["dC"] = to_dev(wl.output_grad(M4, 2 * I4, seed=5))
         st["c4"] = torch.empty((M4, 2 * I4), dtype=torch.bfloat16, device=dev)  # q3_gemm's C
+    if need("q3_gemm_fp8b"):
+        off4, _, tok4, _ = pqm.moe_route(st["ids4"], E)
+        xr = pqm.moe_gather_rows(st["x4"], tok4)
+        st["fp8b"] = dict(
+            off=off4, x=pqm.quantize_fp8_block(xr, 1),
+            d=pqm.quantize_fp8_block(to_dev(wl.activations(M4, I4, seed=9)), 1),
+            w1=pqm.quantize_fp8_block(st["W1"], 128), w2=pqm.quantize_fp8_block(st["W2"], 128),
+            c=torch.empty((M4, 2 * I4), dtype=torch.bfloat16, device=dev),
+            y=torch.empty((M4, H), dtype=torch.bfloat16, device=dev))
+        del xr
     if need("q3_bwd_mx"):
         # forward-side operands of the low-precision backward: the weights'
         # column-wise copies and those of the padded FC1 input X (the
@@ -228,6 +243,15 @@ def main():
         pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, o["qd"], w2q, o["off"], H, I4,
                              a_scale=o["sd"], b_scale=w2s, out_dtype=pqm.OUT_BF16, out=o["y"])
 
+    def r_q3_gemm_fp8b(s):
+        f = st["fp8b"]
+        pqm.moe_grouped_gemm(pqm.FMT_FP8_BLOCK, pqm.GEMM_FPROP, f["x"][0], f["w1"][0], f["off"],
+                             2 * I4, H, a_outer=f["x"][1], b_outer=f["w1"][1],
+                             out_dtype=pqm.OUT_BF16, out=f["c"])
+        pqm.moe_grouped_gemm(pqm.FMT_FP8_BLOCK, pqm.GEMM_FPROP, f["d"][0], f["w2"][0], f["off"],
+                             H, I4, a_outer=f["d"][1], b_outer=f["w2"][1],
+                             out_dtype=pqm.OUT_BF16, out=f["y"])
+
     def r_q3_dequant(s):
         o, (w1q, w1s, w2q, w2s) = st["q3"], st["q3w"]
         prev = st.get("deq", {})
@@ -285,6 +309,7 @@ def main():
 
     fns = {"hbm_copy": r_copy, "mxfp8_quant": r_mxfp8, "nvfp4_token": r_nvfp4, "nvfp4_joint_w": r_joint,
            "q3_wquant": r_q3_wquant, "q3_fwd": r_q3_fwd, "q3_gemm": r_q3_gemm,
+           "q3_gemm_fp8b": r_q3_gemm_fp8b,
            "q3_dequant": r_q3_dequant, "q3_bwd": r_q3_bwd, "q3_bwd_mx": r_q3_bwd_mx,
            "ds_wquant": r_ds_wquant,
            "ds_fwd": r_ds_fwd, "ds_gemm": r_ds_gemm, "ds_reconstruct": r_ds_reconstruct}
@@ -344,7 +369,7 @@ def main():
             hbm(c, E * I2 * H * (2 + 0.5 + 1 / 16) + E * 4, t)
         elif n == "q3_wquant":
             hbm(c, (E * 2 * I4 * H + E * H * I4) * (2 + 1 + 1 / 32), t)
-        elif n in ("q3_fwd", "q3_gemm"):
+        elif n in ("q3_fwd", "q3_gemm", "q3_gemm_fp8b"):
             c.update(flop=fl_q3, tflops=fl_q3 / t / 1e12, frac_fp8=fl_q3 / t / 1e12 / FP8_PEAK_TFLOPS)
         elif n == "q3_dequant":
             el = E * 2 * I4 * H + E * H * I4 + M4 * H + M4 * I4

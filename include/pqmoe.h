@@ -55,7 +55,8 @@ typedef enum pqm_status {
 typedef enum pqm_format {
     PQM_FMT_BF16 = 0,  /* plain bf16 operands */
     PQM_FMT_MXFP8 = 1, /* E4M3 data, one E8M0 scale per 32 along the row */
-    PQM_FMT_NVFP4 = 2  /* packed E2M1, one E4M3 scale per 16, FP32 outer */
+    PQM_FMT_NVFP4 = 2, /* packed E2M1, one E4M3 scale per 16, FP32 outer */
+    PQM_FMT_FP8_BLOCK = 3 /* E4M3, FP32 scale per 1x128 tile / 128x128 block */
 } pqm_format;
 
 typedef enum pqm_gemm_kind {
@@ -147,6 +148,29 @@ size_t pqm_quantize_nvfp4_workspace(int64_t rows, int64_t cols,
                                     int64_t rows_per_scale);
 
 /*
+ * Block-scaled FP8 in the DeepSeek-V3 style ([BW] Why Blackwell-native
+ * recipes: 128x128 weight blocks and 1x128 activation tiles, an FP32 scale
+ * per block computed online and applied around the matrix core; [PR] Choose
+ * a precision: FP8 block-wise, 128x128, FP32 scales).
+ *
+ * Blocks of block_rows x 128 (block_rows = 1: activation tiles; 128: weight
+ * blocks).  For a block with absolute maximum A:
+ *   s = A / 448 rounded once to binary32;
+ *   q = nearest E4M3 to the exact quotient x / s, ties to even, saturating
+ *       at 448 (the block maximum encodes to +-448); A = 0 gives s = 0 and
+ *       q = +-0 (a negative input keeps its sign: 0x80).
+ *   x [rows, cols] bf16, row stride ld elements                  (device)
+ *   q [rows, cols] E4M3 bytes                                    (device)
+ *   s [rows / block_rows, cols / 128] binary32                   (device)
+ * Requires block_rows 1 or 128, cols % 128 == 0, rows % block_rows == 0,
+ * fewer than 2^31 workgroups (PQM_ERR_SHAPE); x and ld 16-byte aligned,
+ * q 8-byte and s 4-byte aligned (PQM_ERR_ALIGN).
+ */
+pqm_status pqm_quantize_fp8_block(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
+                                  int64_t block_rows, uint8_t *q, float *s,
+                                  hipStream_t stream);
+
+/*
  * Dequantize to bf16 for the dequantized-backward mode ([BW]
  * High-precision and dequantized backward: the backward GEMMs run in BF16
  * on the BF16 dequantization of the exact forward operands).
@@ -210,14 +234,24 @@ pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q,
  *                  [G, N, K/16], b_outer = binary32 [(G*N) /
  *                  b_rows_per_scale] (b_rows_per_scale = N: one scale per
  *                  expert, e.g. joint gate/up).
+ *   PQM_FMT_FP8_BLOCK (FPROP only; [BW] Why Blackwell-native recipes: the
+ *                  DeepSeek-V3 design, FP32 scales applied around the
+ *                  matrix core): a = E4M3 [M_total, K] with a_outer =
+ *                  binary32 [M_total, K/128] (1x128 tiles); b = E4M3
+ *                  [G, N, K] with b_outer = binary32 [G*N/128, K/128]
+ *                  (128x128 blocks), as pqm_quantize_fp8_block makes them;
+ *                  a_scale, b_scale unused.  Y[m, n] = sum over 128-K
+ *                  blocks kb of a_outer[m, kb] b_outer[n/128, kb] times the
+ *                  block's sum of E4M3 products.  K % 128 == 0, K <= 8192,
+ *                  N % 128 == 0.
  * a, b and out 16-byte aligned, offsets 8-byte aligned, MXFP8 scale arrays
- * 4-byte aligned (PQM_ERR_ALIGN otherwise).
+ * and block-FP8 scales 4-byte aligned (PQM_ERR_ALIGN otherwise).
  * The products use the exact operand values; accumulation is binary32 and
  * the outer scales are applied to the binary32 accumulator.
  * out: Y in bf16 (rounded once) or binary32 per out_dtype.
  * K % 32 == 0 (MXFP8 FPROP / DGRAD), K % 16 == 0 (NVFP4), K % 8 and
- * N % 8 == 0 (BF16); BF16 WGRAD needs N % 8 == 0 and K % 8 == 0; NVFP4 is
- * FPROP only (PQM_ERR_ENUM otherwise).  No workspace is needed today:
+ * N % 8 == 0 (BF16); BF16 WGRAD needs N % 8 == 0 and K % 8 == 0; NVFP4 and
+ * block FP8 are FPROP only (PQM_ERR_ENUM otherwise).  No workspace is needed today:
  * pass NULL / 0 (the arguments keep the ABI stable).
  */
 pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,

@@ -9,7 +9,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpqmoe.so")
 
-FMT_BF16, FMT_MXFP8, FMT_NVFP4 = 0, 1, 2
+FMT_BF16, FMT_MXFP8, FMT_NVFP4, FMT_FP8_BLOCK = 0, 1, 2, 3
 GEMM_FPROP, GEMM_DGRAD, GEMM_WGRAD = 0, 1, 2
 OUT_BF16, OUT_FP32 = 0, 1
 
@@ -32,6 +32,7 @@ SIGNATURES = {
     "pqm_status_string": ([I32], ctypes.c_char_p),
     "pqm_abi_version": ([], I32),
     "pqm_quantize_mxfp8": ([P, I64, I64, I64, P, P, P, P, P], I32),
+    "pqm_quantize_fp8_block": ([P, I64, I64, I64, I64, P, P, P], I32),
     "pqm_quantize_nvfp4_per_token": ([P, I64, I64, I64, I64, P, P, P, P, SZ, P], I32),
     "pqm_quantize_nvfp4_workspace": ([I64, I64, I64], SZ),
     "pqm_dequantize": ([I32, P, P, P, I64, I64, I64, P, P], I32),
@@ -111,6 +112,24 @@ def quantize_mxfp8(x: torch.Tensor, rowwise: bool = True, colwise: bool = True, 
                                     _ptr(qT), _ptr(sT), _stream(dev)),
            "pqm_quantize_mxfp8")
     return q, s, qT, sT
+
+
+def quantize_fp8_block(x: torch.Tensor, block_rows: int = 1, out=None):
+    """DeepSeek-style block FP8 of a bf16 [R, C] tensor: blocks of
+    block_rows x 128 (1: activation tiles, 128: weight blocks).  Returns
+    (q [R, C] uint8, s [R/block_rows, C/128] float32); `out` may pass them
+    preallocated."""
+    x = _bf16_2d(x)
+    R, C = x.shape
+    dev = x.device
+    if out is not None:
+        q, s = out
+    else:
+        q = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        s = torch.empty((R // block_rows, C // 128), dtype=torch.float32, device=dev)
+    _check(lib().pqm_quantize_fp8_block(_ptr(x), R, C, x.stride(0), block_rows, _ptr(q),
+                                        _ptr(s), _stream(dev)), "pqm_quantize_fp8_block")
+    return q, s
 
 
 def quantize_nvfp4_per_token(x: torch.Tensor, rows_per_scale: int = 1, out=None):

@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpqmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "quantize_mxfp8.hip", "quantize_nvfp4.hip", "dequantize.hip",
+SOURCES = ["api.hip", "quantize_mxfp8.hip", "quantize_nvfp4.hip", "quantize_fp8_block.hip",
+           "dequantize.hip",
            "grouped_gemm.hip", "moe_glue.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

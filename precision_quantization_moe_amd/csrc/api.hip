@@ -78,6 +78,20 @@ pqm_status pqm_quantize_mxfp8(const uint16_t *x, int64_t rows, int64_t cols, int
                                              col ? q_colT : nullptr, s_colT, stream));
 }
 
+pqm_status pqm_quantize_fp8_block(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
+                                  int64_t block_rows, uint8_t *q, float *s,
+                                  hipStream_t stream) {
+  if (block_rows != 1 && block_rows != 128) return PQM_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || ld < cols || cols % 128 || rows % block_rows) return PQM_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return PQM_OK;
+  const int64_t units = block_rows == 1 ? (rows * ((cols + 511) / 512) + 3) / 4
+                                        : (rows / 128) * (cols / 128);
+  if (units >= ((int64_t)1 << 31)) return PQM_ERR_SHAPE;
+  if (!x || !q || !s) return PQM_ERR_NULL;
+  if (!aligned(x, 16) || ld % 8 || !aligned(q, 8) || !aligned(s, 4)) return PQM_ERR_ALIGN;
+  return from_hip(pqm::launch_quantize_fp8_block(x, rows, cols, ld, block_rows, q, s, stream));
+}
+
 size_t pqm_quantize_nvfp4_workspace(int64_t rows, int64_t cols, int64_t rows_per_scale) {
   (void)cols;
   if (rows <= 0 || rows_per_scale <= 0) return 0;
@@ -133,11 +147,14 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
                                 hipStream_t stream) {
   (void)workspace;
   (void)workspace_bytes;
-  if (fmt != PQM_FMT_BF16 && fmt != PQM_FMT_MXFP8 && fmt != PQM_FMT_NVFP4) return PQM_ERR_ENUM;
+  if (fmt != PQM_FMT_BF16 && fmt != PQM_FMT_MXFP8 && fmt != PQM_FMT_NVFP4 &&
+      fmt != PQM_FMT_FP8_BLOCK)
+    return PQM_ERR_ENUM;
   if (kind != PQM_GEMM_FPROP && kind != PQM_GEMM_DGRAD && kind != PQM_GEMM_WGRAD)
     return PQM_ERR_ENUM;
   if (out_dtype != PQM_OUT_BF16 && out_dtype != PQM_OUT_FP32) return PQM_ERR_ENUM;
-  if (fmt == PQM_FMT_NVFP4 && kind != PQM_GEMM_FPROP) return PQM_ERR_ENUM;
+  if ((fmt == PQM_FMT_NVFP4 || fmt == PQM_FMT_FP8_BLOCK) && kind != PQM_GEMM_FPROP)
+    return PQM_ERR_ENUM;
   if (G < 0 || M_total < 0 || N < 0 || K < 0) return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_MXFP8 && kind != PQM_GEMM_WGRAD && K % 32) return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_MXFP8 && kind == PQM_GEMM_DGRAD &&
@@ -147,17 +164,22 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
       (M_total % 32 || M_total * 256 + 4096 >= ((int64_t)1 << 32)))
     return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_NVFP4 && K % 16) return PQM_ERR_SHAPE;
+  if (fmt == PQM_FMT_FP8_BLOCK && (K % 128 || K > 8192 || N % 128)) return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_BF16 && (K % 8 || N % 8)) return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_NVFP4 && (b_rows_per_scale < 1 || (G * N) % b_rows_per_scale))
     return PQM_ERR_SHAPE;
   if (G == 0) return PQM_OK;
   if (!offsets || !out) return PQM_ERR_NULL;
   if (M_total > 0 && (!a || !b)) return PQM_ERR_NULL;
-  if (fmt != PQM_FMT_BF16 && (!a_scale || !b_scale)) return PQM_ERR_NULL;
-  if (fmt == PQM_FMT_NVFP4 && (!a_outer || !b_outer)) return PQM_ERR_NULL;
+  if ((fmt == PQM_FMT_MXFP8 || fmt == PQM_FMT_NVFP4) && (!a_scale || !b_scale))
+    return PQM_ERR_NULL;
+  if ((fmt == PQM_FMT_NVFP4 || fmt == PQM_FMT_FP8_BLOCK) && (!a_outer || !b_outer))
+    return PQM_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(offsets, 8))
     return PQM_ERR_ALIGN;
   if (fmt == PQM_FMT_MXFP8 && (!aligned(a_scale, 4) || !aligned(b_scale, 4)))
+    return PQM_ERR_ALIGN;
+  if (fmt == PQM_FMT_FP8_BLOCK && (!aligned(a_outer, 4) || !aligned(b_outer, 4)))
     return PQM_ERR_ALIGN;
   return from_hip(pqm::launch_grouped_gemm((int)fmt, (int)kind, a, a_scale, a_outer, b, b_scale,
                                            b_outer, b_rows_per_scale, offsets, G, M_total, N,

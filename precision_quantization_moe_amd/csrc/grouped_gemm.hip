@@ -958,6 +958,172 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_wgrad(
       mx3_store<OUT_F32>(acc[i][j], og, K, n0, N, k0, wm * (TM / 2) + 32 * i, wn * 128 + 32 * j);
 }
 
+// ----------------------------------------------------- block-scaled FP8
+// DeepSeek-V3-style operands ("Towards Blackwell-Native 8-bit and 4-bit RL",
+// Why Blackwell-native recipes: 1 x 128 activation tiles and 128 x 128 weight
+// blocks with FP32 scales, applied in software around the matrix core):
+//   Y[m, n] = sum over 128-K blocks kb of sa[m, kb] sb[n / 128, kb]
+//             (sum over k in kb of qa[m, k] qb[n, k]).
+// The forward's ring and 128 x 256 tiles; each 128-K block's products go
+// into a fresh accumulator through the FP8 matrix core (hardware scales
+// fixed at 2^0), which is then added into the result times the product of
+// the two binary32 scales.  All scales of the tile are preloaded to LDS:
+// sa as [kb][row], sb as [column block][kb].
+
+constexpr int FB_MAX_KB = 64;  // K <= 8192
+constexpr int FB_TM = 128;
+constexpr int FB_AREA = 256 * ((FB_TM * FB_MAX_KB + 2 * FB_MAX_KB + 255) / 256);  // dwords
+
+__device__ __forceinline__ void fb_read(const uint8_t *lds, int slot, const Mx3Lane &o,
+                                        Mx3Frags<FB_TM> &F) {
+  using C = Mx3<FB_TM>;
+  const uint8_t *cur = lds + slot * C::SLOT;
+#pragma unroll
+  for (int i = 0; i < C::FI; ++i) {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(cur + o.a_lo + 2048 * i);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(cur + o.a_hi + 2048 * i);
+    F.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+#pragma unroll
+  for (int j = 0; j < C::FJ; ++j) {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(cur + o.b_lo + 2048 * j);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(cur + o.b_hi + 2048 * j);
+    F.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+}
+
+template <bool FIRST>
+__device__ __forceinline__ void fb_mma(const Mx3Frags<FB_TM> &F,
+                                       v16f (&part)[Mx3<FB_TM>::FI][Mx3<FB_TM>::FJ]) {
+  const v16f zero = {};
+#pragma unroll
+  for (int j = 0; j < Mx3<FB_TM>::FJ; ++j)
+#pragma unroll
+    for (int i = 0; i < Mx3<FB_TM>::FI; ++i)
+      part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          F.b[j], F.a[i], FIRST ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
+}
+
+template <bool FIRST>
+__device__ __forceinline__ void fb_step(const Mx3Src<FB_TM> &L, const uint8_t *lds,
+                                        const Mx3Lane &o, int kt, int nk, int slot,
+                                        v16f (&part)[Mx3<FB_TM>::FI][Mx3<FB_TM>::FJ],
+                                        const Mx3Frags<FB_TM> &cur, Mx3Frags<FB_TM> &next) {
+  vm_wait<Mx3<FB_TM>::OPS>();
+  lgkm_wait0();
+  __builtin_amdgcn_s_barrier();
+  mx3_issue<FB_TM>(L, min(kt + 3, nk - 1), slot);
+  __builtin_amdgcn_sched_barrier(0);
+  fb_read(lds, slot == 2 ? 0 : slot + 1, o, next);
+  __builtin_amdgcn_sched_barrier(0);
+  fb_mma<FIRST>(cur, part);
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_fp8_block(
+    const uint8_t *__restrict__ A, const float *__restrict__ As, const uint8_t *__restrict__ B,
+    const float *__restrict__ Bs, const int64_t *__restrict__ offsets, int64_t G, int64_t N,
+    int64_t K, int64_t ntn, void *__restrict__ out) {
+  constexpr int TM = FB_TM;
+  using C = Mx3<TM>;
+  constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::NSLOT * C::SLOT + 4 * FB_AREA];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<256, TM>(offsets, G, ntn, ti, sh)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
+  const int KB = (int)(K / 128);
+  const uint32_t Ku = (uint32_t)K;
+  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)TM);
+  const int rows_b = (int)min(N - ti.n0, (int64_t)TN);
+  Mx3Src<TM> L;
+  L.Ab = A + ti.row0 * K;
+  L.Bb = B + (ti.g * N + ti.n0) * K;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.oa[i] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * k;
+  }
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.ob[i] = (uint32_t)min(r, rows_b - 1) * Ku + 16u * k;
+  }
+  Mx3Lane o;
+  {
+    const int ra = wm * (TM / 2) + r32, rb = wn * 128 + r32;
+    o.a_lo = mx3_off(ra, h);
+    o.a_hi = mx3_off(ra, 2 + h);
+    o.b_lo = TM * 64 + mx3_off(rb, h);
+    o.b_hi = TM * 64 + mx3_off(rb, 2 + h);
+    o.sa = o.sb = o.ks = 0;
+  }
+  // scales: dword d < TM KB is sa of row d % TM, block d / TM; the next 2 KB
+  // are sb of the tile's two 128-column blocks (a block past N repeats the
+  // first; its results are not stored)
+  const float *sa_l = reinterpret_cast<const float *>(lds + C::NSLOT * C::SLOT);
+  const float *sb_l = sa_l + TM * KB;
+  {
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(sa_l) + (uint32_t)wave * 256u);
+    const int total = TM * KB + 2 * KB, nq = (total + 255) / 256;
+    const int64_t nb0 = (ti.g * N + ti.n0) / 128;
+    for (int q = 0; q < nq; ++q) {
+      const int d = min(256 * q + tid, total - 1);
+      const float *src;
+      if (d < TM * KB) {
+        src = As + (ti.row0 + min(d % TM, rows_a - 1)) * (int64_t)KB + d / TM;
+      } else {
+        const int e = d - TM * KB, blk = e / KB;
+        src = Bs + (nb0 + (ti.n0 + 128 * blk < N ? blk : 0)) * (int64_t)KB + e % KB;
+      }
+      dma4(src, sbase + 1024u * (uint32_t)q);
+    }
+  }
+
+  v16f acc[FI][FJ], part[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (int)(K / 64);  // even, >= 2
+  mx3_issue<TM>(L, 0, 0);
+  mx3_issue<TM>(L, 1, 1);
+  mx3_issue<TM>(L, min(2, nk - 1), 2);
+  vm_wait<2 * C::OPS>();  // the scales and step 0
+  __builtin_amdgcn_s_barrier();
+  Mx3Frags<TM> F0, F1;
+  fb_read(lds, 0, o, F0);
+  int slot = 0;
+  for (int kb = 0; kb < KB; ++kb) {
+    const int kt = 2 * kb;
+    fb_step<true>(L, lds, o, kt, nk, slot, part, F0, F1);
+    slot = slot == 2 ? 0 : slot + 1;
+    fb_step<false>(L, lds, o, kt + 1, nk, slot, part, F1, F0);
+    slot = slot == 2 ? 0 : slot + 1;
+    const float sbv = sb_l[wn * KB + kb];
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const float sc = sa_l[kb * TM + wm * (TM / 2) + 32 * i + r32] * sbv;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(part[i][j][r], sc, acc[i][j][r]);
+    }
+  }
+  vm_wait<0>();  // no load may still target this workgroup's LDS at exit
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+      mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (TM / 2) + 32 * i,
+                         wn * 128 + 32 * j);
+}
+
 // ------------------------------------------------------------------- BF16
 
 // Stage a tile whose rows are contiguous in memory and whose contraction
@@ -1944,6 +2110,20 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
                                int64_t K, void *out, int out_fp32, hipStream_t st) {
   if (G == 0 || N == 0) return hipSuccess;
   const int64_t U32 = (int64_t)1 << 32;  // the pipelined kernels' per-panel byte offsets
+  if (fmt == 3) {  // block-scaled FP8 forward
+    if (M == 0) return hipSuccess;
+    if (K % 128 || K / 128 > FB_MAX_KB || N % 128) return hipErrorNotSupported;
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    const int64_t ntn_b = cdiv(N, 256);
+    const dim3 grid_b((unsigned)(cdiv((cdiv(M, FB_TM) + G) * ntn_b, 8) * 8));
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_fp8_block<true>, grid_b, dim3(256), 0, st, A, a_outer, B,
+                         b_outer, offsets, G, N, K, ntn_b, out);
+    else
+      hipLaunchKernelGGL(k_gemm_fp8_block<false>, grid_b, dim3(256), 0, st, A, a_outer, B,
+                         b_outer, offsets, G, N, K, ntn_b, out);
+    return hipGetLastError();
+  }
   if (fmt == 1 && kind == 2) {  // WGRAD (MXFP8, column-wise copies)
     if (K == 0) return hipSuccess;
     if (M % 32 || M * 256 + 4096 >= U32) return hipErrorNotSupported;

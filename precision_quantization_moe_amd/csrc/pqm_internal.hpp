@@ -37,6 +37,8 @@ hipError_t launch_gemm_swiglu_mxfp8(const uint8_t *a, const uint8_t *a_scale, co
                                     const uint8_t *b_scale, const int64_t *offsets, int64_t G,
                                     int64_t M, int64_t I, int64_t K, const float *prob,
                                     const int32_t *src, uint8_t *q, uint8_t *s, hipStream_t st);
+hipError_t launch_quantize_fp8_block(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
+                                     int64_t br, uint8_t *q, float *s, hipStream_t st);
 hipError_t launch_pad_rows(const void *src, int64_t row_bytes, const int64_t *off, int64_t G,
                            int64_t align, int64_t *poff, void *out, int64_t out_rows,
                            hipStream_t st);

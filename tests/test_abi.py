@@ -87,6 +87,20 @@ def test_dequantize_validation():
     assert f(1, A16, A16, None, 0, 32, 1, None, None) == 0         # empty: no-op
 
 
+def test_quantize_fp8_block_validation():
+    L = pqm.lib()
+    f = L.pqm_quantize_fp8_block
+    assert f(A16, 64, 256, 256, 2, A16, A16, None) == 2        # block rows 1 or 128
+    assert f(A16, 64, 192, 192, 1, A16, A16, None) == 2        # cols % 128
+    assert f(A16, 64, 256, 256, 128, A16, A16, None) == 2      # rows % 128
+    assert f(A16, 64, 256, 128, 1, A16, A16, None) == 2        # ld < cols
+    assert f(None, 64, 256, 256, 1, A16, A16, None) == 1
+    assert f(A16, 64, 256, 256, 1, A16, None, None) == 1
+    assert f(BAD, 64, 256, 256, 1, A16, A16, None) == 3
+    assert f(A16, 64, 256, 256, 1, A16, BAD, None) == 3
+    assert f(A16, 0, 256, 256, 1, None, None, None) == 0       # empty: no-op
+
+
 def test_grouped_gemm_validation():
     L = pqm.lib()
     f = L.pqm_moe_grouped_gemm
@@ -96,6 +110,9 @@ def test_grouped_gemm_validation():
     assert f(*args(fmt=5)) == 4
     assert f(*args(kind=9)) == 4
     assert f(*args(out=3)) == 4
+    assert f(*args(fmt=3, kind=1)) == 4             # block FP8: forward only
+    assert f(*args(fmt=3, K=64)) == 2               # block FP8: K % 128
+    assert f(*args(fmt=3, K=128)) == 2              # block FP8: N % 128 (N = 64)
     assert f(*args(fmt=2, kind=1)) == 4             # NVFP4: forward only
     assert f(*args(fmt=2, kind=2)) == 4
     assert f(*args(kind=1)) == 2                    # MXFP8 dgrad: K % 128

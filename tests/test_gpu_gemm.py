@@ -233,6 +233,82 @@ def test_mxfp8_wgrad_bf16_out():
     assert not got[1].any()
 
 
+# ------------------------------------------------------ block-scaled FP8
+
+def _fp8b_case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32):
+    G, M = len(sizes), int(sum(sizes))
+    x = wl.activations(max(M, 1), K, seed=seed)[:M]
+    w = wl.normal_bf16((G * N, K), std=0.02, seed=seed + 1)
+    off = _offsets(sizes)
+    qa, sa = pqm.quantize_fp8_block(dev_bf16(x), 1)
+    qb, sb = pqm.quantize_fp8_block(dev_bf16(w), 128)
+    y = pqm.moe_grouped_gemm(pqm.FMT_FP8_BLOCK, pqm.GEMM_FPROP, qa, qb, dev(off), N, K,
+                             a_outer=sa, b_outer=sb, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ra, rsa = oracle.quantize_fp8_block(x, 1)
+    rb, rsb = oracle.quantize_fp8_block(w, 128)
+    want = oracle.grouped_gemm(oracle.decode_fp8_block(ra, rsa, 1),
+                               oracle.decode_fp8_block(rb, rsb, 128).reshape(G, N, K), off)
+    return y, want
+
+
+@pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 256, 384),
+                                         ([260, 0, 3], 384, 128),
+                                         ([513], 128, 7168),
+                                         ([70, 330], 1536, 2048)])
+def test_fp8_block_fprop(sizes, N, K):
+    """Y = sum over 128-K blocks of sa sb (block sum of E4M3 products)
+    against the oracle's binary64 product of the decoded operands."""
+    y, want = _fp8b_case(sizes, N, K, seed=61)
+    check_rows(host(y), want, f"fp8 block {sizes} N={N} K={K}")
+
+
+def test_fp8_block_fprop_bf16_out_and_contract_tensor():
+    y, want = _fp8b_case([64, 0, 100], 256, 256, seed=62, out_dtype=pqm.OUT_BF16)
+    r = rel_l2_rows(oracle.bf16_to_f64(host_u16(y)), want)
+    assert r.max() <= TOL + 2.0 ** -9
+    x = wl.tiny_contract_tensor()
+    w = wl.normal_bf16((256, 256), std=0.02, seed=63)
+    off = np.array([0, 128], np.int64)
+    qa, sa = pqm.quantize_fp8_block(dev_bf16(x), 1)
+    qb, sb = pqm.quantize_fp8_block(dev_bf16(w), 128)
+    y = pqm.moe_grouped_gemm(pqm.FMT_FP8_BLOCK, pqm.GEMM_FPROP, qa, qb, dev(off), 256, 256,
+                             a_outer=sa, b_outer=sb)
+    ra, rsa = oracle.quantize_fp8_block(x, 1)
+    rb, rsb = oracle.quantize_fp8_block(w, 128)
+    want = oracle.grouped_gemm(oracle.decode_fp8_block(ra, rsa, 1),
+                               oracle.decode_fp8_block(rb, rsb, 128)[None], off)
+    got = host(y)
+    assert not got[1].any()
+    check_rows(got, want, "fp8 block tiny contract")
+
+
+def test_fp8_block_qwen3_gate_up_full_sampled():
+    """The Qwen3-30B-A3B FC1 shape in block FP8 (65536 routed rows, Zipf
+    loads, N = 1536, K = 2048), all rows on the GPU, sampled rows of sampled
+    experts against the oracle."""
+    T, E, k, H, N = 8192, 128, 8, 2048, 1536
+    ids = wl.zipf_routing(T, E, k)
+    off, src, _ = oracle.route(ids, E)
+    x = wl.activations(T, H)
+    xg = x[src // k]
+    w = wl.expert_weights(E, N, H, 0.02)
+    qa, sa = pqm.quantize_fp8_block(dev_bf16(xg), 1)
+    qb, sb = pqm.quantize_fp8_block(dev_bf16(w.reshape(E * N, H)), 128)
+    y = pqm.moe_grouped_gemm(pqm.FMT_FP8_BLOCK, pqm.GEMM_FPROP, qa, qb, dev(off), N, H,
+                             a_outer=sa, b_outer=sb)
+    torch.cuda.synchronize()
+    yh = host(y)
+    rng = np.random.Generator(np.random.PCG64(64))
+    for e in sorted(set(rng.choice(E, 8, replace=False).tolist()) | {0, E - 1}):
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 6)]))
+        ra, rsa = oracle.quantize_fp8_block(xg[rows], 1)
+        rb, rsb = oracle.quantize_fp8_block(w[e], 128)
+        want = oracle.decode_fp8_block(ra, rsa, 1) @ oracle.decode_fp8_block(rb, rsb, 128).T
+        check_rows(yh[rows], want, f"fp8 block qwen3 fc1 expert {e} ({hi - lo} rows)")
+
+
 # ------------------------------------------------------------------- BF16
 
 def _bf16_operands(M, N, K, G, seed):

@@ -231,3 +231,29 @@ def test_dequantize_nvfp4_double_rounding_cases():
     y = pqm.dequantize(pqm.FMT_NVFP4, dev(q), dev(sb), dev(sg))
     want = oracle.dequantize_nvfp4(q, sb, sg)
     assert_bytes_equal(host_u16(y), want, "double rounding")
+
+
+# ------------------------------------------------------ block-scaled FP8
+
+@pytest.mark.parametrize("block_rows,shape", [(1, (64, 384)), (1, (300, 2048)), (128, (256, 384)),
+                                              (128, (128, 2048))])
+def test_fp8_block_bytes(block_rows, shape):
+    """DeepSeek-style block FP8 (1x128 tiles / 128x128 blocks): bytes and
+    binary32 scales equal the oracle's, boundary values and zero blocks
+    included."""
+    R, C = shape
+    x = wl.activations(R, C, seed=51)
+    if block_rows == 1:
+        b = wl.boundary_tensor(C)
+        x[:b.shape[0]] = b[:R]
+        x[-1] = 0
+        x[-2, :128] = 0x8000                          # a tile of -0.0
+    else:
+        x = wl.normal_bf16((R, C), std=0.02, seed=52)
+        x[:128, :128] = 0                              # a zero block
+    q, s = pqm.quantize_fp8_block(dev_bf16(x), block_rows)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_fp8_block(x, block_rows)
+    print(f"[fp8b] block_rows={block_rows} shape={shape}", flush=True)
+    assert_bytes_equal(host(s).view(np.uint32), rs.view(np.uint32), "scales")
+    assert_bytes_equal(host(q), rq, "E4M3 bytes")
