@@ -356,6 +356,22 @@ def main():
     def hbm(c, byt, t):
         c.update(bytes=byt, gbs=byt / t / 1e9, frac_hbm=byt / t / 1e9 / HBM_PEAK_GBS)
 
+    # algorithmic HBM bytes of the two expert GEMMs of a layer (operands and
+    # their scales read once, output written once) per encoded byte/element
+    def gemm_bytes(M, E_, I_, H_, a_el, w_el, a_row=0.0):
+        fc1 = M * H_ * a_el + M * a_row + E_ * 2 * I_ * H_ * w_el + M * 2 * I_ * 2
+        fc2 = M * I_ * a_el + M * a_row + E_ * H_ * I_ * w_el + M * H_ * 2
+        return fc1 + fc2
+
+    by_q3 = {"q3_gemm": gemm_bytes(M4, E, I4, H, 1 + 1 / 32, 1 + 1 / 32),
+             "q3_gemm_fp8b": gemm_bytes(M4, E, I4, H, 1 + 4 / 128, 1 + 4 / 128 ** 2)}
+    by_ds = gemm_bytes(M5, E5 + 1, I5, H5, 0.5 + 1 / 16, 0.5 + 1 / 16, a_row=4)
+
+    def floor(c, flop, byt, peak_tflops, t):
+        # the larger of the compute and the HBM time at peak: the attainable bound
+        fl = max(flop / peak_tflops / 1e12, byt / HBM_PEAK_GBS / 1e9)
+        c.update(bytes=byt, floor_us=fl * 1e6, frac_floor=fl / t)
+
     for n, ts in timings.items():
         if n not in sel:
             continue
@@ -371,6 +387,8 @@ def main():
             hbm(c, (E * 2 * I4 * H + E * H * I4) * (2 + 1 + 1 / 32), t)
         elif n in ("q3_fwd", "q3_gemm", "q3_gemm_fp8b"):
             c.update(flop=fl_q3, tflops=fl_q3 / t / 1e12, frac_fp8=fl_q3 / t / 1e12 / FP8_PEAK_TFLOPS)
+            if n in by_q3:
+                floor(c, fl_q3, by_q3[n], FP8_PEAK_TFLOPS, t)
         elif n == "q3_dequant":
             el = E * 2 * I4 * H + E * H * I4 + M4 * H + M4 * I4
             hbm(c, el * (1 + 1 / 32 + 2), t)
@@ -385,6 +403,8 @@ def main():
         elif n in ("ds_fwd", "ds_gemm"):
             c.update(flop=fl_ds, tflops=fl_ds / t / 1e12,
                      frac_bf16=fl_ds / t / 1e12 / BF16_PEAK_TFLOPS)
+            if n == "ds_gemm":
+                floor(c, fl_ds, by_ds, BF16_PEAK_TFLOPS, t)
         elif n == "ds_reconstruct":
             el = M5 * H5 + (E5 + 1) * (2 * I5 * H5 + H5 * I5)
             hbm(c, el * (0.5 + 1 / 16 + 2), t)

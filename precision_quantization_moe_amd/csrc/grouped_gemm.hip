@@ -758,6 +758,165 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
     mx3_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
 }
 
+#ifndef PQM_MX_OCC2_KMAX
+#define PQM_MX_OCC2_KMAX 1024
+#endif
+
+// ------------------------------------------- MXFP8, two workgroups per CU
+// 128 x 256 tiles whose whole state fits twice in one CU (78 KB of LDS, at
+// most 256 registers per lane), so that one workgroup's prologue and output
+// store overlap the other's matrix-core work: with one 256 x 256 tile per
+// CU those phases run serially with the MFMAs.  Waves 2 x 2, each 64 x 128
+// (2 x 4 fragments).  A 3-slot ring of 64-K steps as in the forward kernel
+// above, but each slot also carries the step's scale bytes (two E8M0 bytes
+// per tile row, one 4-byte entry per row; entries 0..127 A rows, 128..383
+// B rows, 384..511 never read), so no scale area is preloaded and any
+// K % 128 == 0 fits.  Operands of step kt are read from LDS during step kt
+// (one fragment set; the other workgroup's MFMAs cover the read latency).
+struct Mo2 {
+  static constexpr int TM = 128, TN = 256, ROWS = TM + TN;
+  static constexpr int OPB = ROWS * 64;    // operand bytes per slot
+  static constexpr int SCB = 512 * 4;      // scale entries per slot
+  static constexpr int SLOT = OPB + SCB;
+  static constexpr int NSLOT = 3;
+  static constexpr int LDS = NSLOT * SLOT;  // 79872 bytes
+  static constexpr int CA = 2, CB = 4, CS = 2, OPS = CA + CB + CS;
+  static constexpr int FI = 2, FJ = 4;
+};
+static_assert(2 * (Mo2::LDS + 64) <= 160 * 1024, "two workgroups per CU");
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 2 bytes per lane from global `src` into the 4-byte LDS entry m0 + 4 * lane.
+__device__ __forceinline__ void dma2(const void *src, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+struct Mo2Src {
+  const uint8_t *Ab, *Bb;
+  uint32_t oa[Mo2::CA], ob[Mo2::CB];  // per-lane operand chunk offsets at step 0
+  const uint8_t *sc[Mo2::CS];         // per-lane scale-byte sources at step 0
+  uint32_t dst;                       // LDS address of slot 0, this wave's operand chunks
+  uint32_t sdst;                      // LDS address of slot 0, this wave's scale entries
+};
+
+__device__ __forceinline__ void mo2_issue(const Mo2Src &L, int kt, int slot) {
+  const uint32_t kb = (uint32_t)kt * 64u, so = (uint32_t)slot * Mo2::SLOT;
+#pragma unroll
+  for (int i = 0; i < Mo2::CA; ++i) dma16(L.Ab + (L.oa[i] + kb), L.dst + so + i * 4096);
+#pragma unroll
+  for (int i = 0; i < Mo2::CB; ++i)
+    dma16(L.Bb + (L.ob[i] + kb), L.dst + so + Mo2::TM * 64 + i * 4096);
+#pragma unroll
+  for (int s = 0; s < Mo2::CS; ++s) dma2(L.sc[s] + 2 * kt, L.sdst + so + s * 1024);
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void k_gemm_mxfp8_occ2(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    int64_t ldb, int64_t bexp, void *__restrict__ out) {
+  constexpr int TM = Mo2::TM, FI = Mo2::FI, FJ = Mo2::FJ;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Mo2::LDS];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<256, 128>(offsets, G, ntn, ti, sh)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
+  const uint32_t KS = (uint32_t)(K / 32), Ku = (uint32_t)K;
+  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)TM);
+  const int rows_b = (int)min(N - ti.n0, (int64_t)Mo2::TN);
+  Mo2Src L;
+  L.Ab = A + ti.row0 * K;
+  L.Bb = B + ti.g * bexp + ti.n0 * ldb;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+  L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + Mo2::OPB + (uint32_t)wave * 256u);
+  // chunk c = 256 i + tid: row c / 4, physical chunk c % 4 holding logical
+  // chunk (c % 4) ^ ((row / 4) % 4); rows past the expert's end or past N
+  // load a clamped valid row whose results are never stored
+#pragma unroll
+  for (int i = 0; i < Mo2::CA; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.oa[i] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * k;
+  }
+#pragma unroll
+  for (int i = 0; i < Mo2::CB; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.ob[i] = (uint32_t)min(r, rows_b - 1) * (uint32_t)ldb + 16u * k;
+  }
+  {
+    const uint8_t *Asb = As + ti.row0 * (int64_t)KS;
+    const uint8_t *Bsb = Bs + (ti.g * bexp + ti.n0 * ldb) / 32;
+    const int64_t ldbs = ldb / 32;
+#pragma unroll
+    for (int s = 0; s < Mo2::CS; ++s) {
+      const int e = 256 * s + tid;  // scale entry; >= 384: padding, reads A row 0
+      L.sc[s] = e < TM ? Asb + (int64_t)min(e, rows_a - 1) * KS
+                : e < Mo2::ROWS ? Bsb + (int64_t)min(e - TM, rows_b - 1) * ldbs
+                                : Asb;
+    }
+  }
+  const int ra = wm * 64 + r32, rb = wn * 128 + r32;
+  const int a_lo = mx3_off(ra, h), a_hi = mx3_off(ra, 2 + h);
+  const int b_lo = TM * 64 + mx3_off(rb, h), b_hi = TM * 64 + mx3_off(rb, 2 + h);
+  const int s_a = Mo2::OPB + 4 * ra + h, s_b = Mo2::OPB + 4 * (TM + rb) + h;
+
+  v16f acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (int)(K / 64);  // even, >= 2
+  mo2_issue(L, 0, 0);
+  mo2_issue(L, 1, 1);
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    vm_wait<Mo2::OPS>();  // own loads of step kt done; step kt + 1 may be pending
+    lgkm_wait0();         // own reads of the slot refilled below are done
+    __builtin_amdgcn_s_barrier();
+    const int fill = slot == 0 ? 2 : slot - 1;  // (kt + 2) % 3, read at step kt - 1
+    mo2_issue(L, min(kt + 2, nk - 1), fill);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t *cur = lds + slot * Mo2::SLOT;
+    v8i fa[FI], fb[FJ];
+    int sa[FI], sb[FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const uint4 lo = *reinterpret_cast<const uint4 *>(cur + a_lo + 2048 * i);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(cur + a_hi + 2048 * i);
+      fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      sa[i] = cur[s_a + 4 * 32 * i];
+    }
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const uint4 lo = *reinterpret_cast<const uint4 *>(cur + b_lo + 2048 * j);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(cur + b_hi + 2048 * j);
+      fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      sb[j] = cur[s_b + 4 * 32 * j];
+    }
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0,
+                                                                     0, sb[j], 0, sa[i]);
+    slot = slot == 2 ? 0 : slot + 1;
+  }
+  vm_wait<0>();  // no load may still target this workgroup's LDS at exit
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+      mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * 64 + 32 * i,
+                         wn * 128 + 32 * j);
+}
+
 // The gate_up grouped GEMM with the fused epilogue: D = SwiGLU(C) x prob
 // encoded as MXFP8 (C itself is never written).  N = 2 I, I % 128 == 0.
 __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_swiglu(
@@ -1793,7 +1952,7 @@ struct Np {
   static constexpr int TN = 256, ROWS = TM + TN;
   static constexpr int SC = ROWS * 64;        // scale area offset in a slot
   static constexpr int SLOT = ROWS * 72;
-  static constexpr int NSLOT = 3;
+  static constexpr int NSLOT = 3;  // 4 slots measured no faster
   static constexpr int LDS = NSLOT * SLOT;
   static constexpr int CA = TM / 64, CB = TN / 64;  // 16-byte data chunks per lane
   static constexpr int NS = ROWS / 128;             // 4-byte scale loads per lane
@@ -1928,12 +2087,13 @@ __device__ __forceinline__ void np_step(const NpSrc<TM> &L, const uint8_t *lds, 
                                         int kt, int nk, int slot,
                                         v16f (&acc)[Np<TM>::FI][Np<TM>::FJ],
                                         const NpFrags<TM> &cur, NpFrags<TM> &next) {
-  vm_wait<Np<TM>::OPS>();
+  constexpr int S = Np<TM>::NSLOT;
+  vm_wait<(S - 2) * Np<TM>::OPS>();  // own loads of step kt+1 done; later steps may be pending
   lgkm_wait0();
   __builtin_amdgcn_s_barrier();
-  np_issue<TM>(L, min(kt + 3, nk - 1), slot);
+  np_issue<TM>(L, min(kt + S, nk - 1), slot);
   __builtin_amdgcn_sched_barrier(0);
-  np_read<TM>(lds, slot == 2 ? 0 : slot + 1, o, next);
+  np_read<TM>(lds, slot == S - 1 ? 0 : slot + 1, o, next);
   __builtin_amdgcn_sched_barrier(0);
   np_mma<TM>(cur, acc);
 }
@@ -2051,19 +2211,18 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = (int)(K / 128);  // even, >= 2
-  np_issue<TM>(L, 0, 0);
-  np_issue<TM>(L, 1, 1);
-  np_issue<TM>(L, min(2, nk - 1), 2);
-  vm_wait<2 * C::OPS>();  // step 0
+#pragma unroll
+  for (int s = 0; s < C::NSLOT; ++s) np_issue<TM>(L, min(s, nk - 1), s);
+  vm_wait<(C::NSLOT - 1) * C::OPS>();  // step 0
   __builtin_amdgcn_s_barrier();
   NpFrags<TM> F0, F1;
   np_read<TM>(lds, 0, o, F0);
   int slot = 0;
   for (int kt = 0; kt < nk; kt += 2) {
     np_step<TM>(L, lds, o, kt, nk, slot, acc, F0, F1);
-    slot = slot == 2 ? 0 : slot + 1;
+    slot = slot == C::NSLOT - 1 ? 0 : slot + 1;
     np_step<TM>(L, lds, o, kt + 1, nk, slot, acc, F1, F0);
-    slot = slot == 2 ? 0 : slot + 1;
+    slot = slot == C::NSLOT - 1 ? 0 : slot + 1;
   }
   vm_wait<0>();
 #pragma unroll
@@ -2183,7 +2342,20 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
   int64_t tiles = (cdiv(M, GT_M) + G) * ntn;
   tiles = cdiv(tiles, 8) * 8;
   const dim3 grid((unsigned)tiles);
-  if (fmt == 1 && K % 128 == 0 && K / 32 <= Mx3<256>::MAX_KS && K / 32 <= Mx3<128>::MAX_KS) {
+  if (fmt == 1 && K > 0 && K % 128 == 0 && K <= PQM_MX_OCC2_KMAX) {
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    const int64_t ntn_o = cdiv(N, Mo2::TN);
+    const dim3 grid_o((unsigned)(cdiv((cdiv(M, Mo2::TM) + G) * ntn_o, 8) * 8));
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_mxfp8_occ2<true>, grid_o, dim3(256), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_o, K, N * K, out);
+    else
+      hipLaunchKernelGGL(k_gemm_mxfp8_occ2<false>, grid_o, dim3(256), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_o, K, N * K, out);
+    return hipGetLastError();
+  }
+  if (fmt == 1 && K > 0 && K % 128 == 0 && K / 32 <= Mx3<256>::MAX_KS &&
+      K / 32 <= Mx3<128>::MAX_KS) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_b = cdiv(N, Mx3<256>::TN);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
