@@ -1981,36 +1981,46 @@ __device__ __forceinline__ void np_issue(const NpSrc<TM> &L, int kt, int slot) {
     dma4((128 * i < TM ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
 }
 
-// Raw operands of one step: per fragment 8 words (one per sub-step) and the
-// 4 scale bytes of the lane's blocks.
-template <int TM>
-struct NpFrags {
-  uint4 a[Np<TM>::FI][2], b[Np<TM>::FJ][2];
-  uint32_t sa[Np<TM>::FI], sb[Np<TM>::FJ];
-};
-
 struct NpLane {
   int a0, a1, b0, b1;  // chunk offsets (2h, 2h+1) of the first A / B row
   int sa, sb;          // scale-word offsets of the first A / B row
 };
 
+// A lane's raw operands of one step, per fragment 32 bytes in two halves:
+// half 0 (chunk 2h: words 0..3 = sub-steps 0..3 = blocks 0, 1) and half 1
+// (chunk 2h + 1: sub-steps 4..7 = blocks 2, 3), plus one word holding the
+// 4 scale bytes of the lane's blocks.
 template <int TM>
-__device__ __forceinline__ void np_read(const uint8_t *lds, int slot, const NpLane &o,
-                                        NpFrags<TM> &F) {
+struct NpHalf {
+  uint4 a[Np<TM>::FI], b[Np<TM>::FJ];
+};
+template <int TM>
+struct NpWords {
+  uint32_t a[Np<TM>::FI], b[Np<TM>::FJ];
+};
+
+template <int TM, int HALF>
+__device__ __forceinline__ void np_read_half(const uint8_t *lds, int slot, const NpLane &o,
+                                             NpHalf<TM> &R) {
   using C = Np<TM>;
   const uint8_t *cur = lds + slot * C::SLOT;
 #pragma unroll
-  for (int i = 0; i < C::FI; ++i) {
-    F.a[i][0] = *reinterpret_cast<const uint4 *>(cur + o.a0 + 2048 * i);
-    F.a[i][1] = *reinterpret_cast<const uint4 *>(cur + o.a1 + 2048 * i);
-    F.sa[i] = *reinterpret_cast<const uint32_t *>(cur + o.sa + 256 * i);
-  }
+  for (int i = 0; i < C::FI; ++i)
+    R.a[i] = *reinterpret_cast<const uint4 *>(cur + (HALF ? o.a1 : o.a0) + 2048 * i);
 #pragma unroll
-  for (int j = 0; j < C::FJ; ++j) {
-    F.b[j][0] = *reinterpret_cast<const uint4 *>(cur + o.b0 + 2048 * j);
-    F.b[j][1] = *reinterpret_cast<const uint4 *>(cur + o.b1 + 2048 * j);
-    F.sb[j] = *reinterpret_cast<const uint32_t *>(cur + o.sb + 256 * j);
-  }
+  for (int j = 0; j < C::FJ; ++j)
+    R.b[j] = *reinterpret_cast<const uint4 *>(cur + (HALF ? o.b1 : o.b0) + 2048 * j);
+}
+
+template <int TM>
+__device__ __forceinline__ void np_read_words(const uint8_t *lds, int slot, const NpLane &o,
+                                              NpWords<TM> &W) {
+  using C = Np<TM>;
+  const uint8_t *cur = lds + slot * C::SLOT;
+#pragma unroll
+  for (int i = 0; i < C::FI; ++i) W.a[i] = *reinterpret_cast<const uint32_t *>(cur + o.sa + 256 * i);
+#pragma unroll
+  for (int j = 0; j < C::FJ; ++j) W.b[j] = *reinterpret_cast<const uint32_t *>(cur + o.sb + 256 * j);
 }
 
 // Block scale byte `byte` (0..3) of `sw` as 2^E (binary32) and M (f16 pair).
@@ -2040,62 +2050,98 @@ __device__ __forceinline__ v8h np_decode(uint32_t w, const NpScale &sc) {
   return v8h{x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
 }
 
-__device__ __forceinline__ uint32_t u4_word(const uint4 (&v)[2], int s) {
-  const uint4 &u = v[s >> 2];
-  const int k = s & 3;
-  return k == 0 ? u.x : (k == 1 ? u.y : (k == 2 ? u.z : u.w));
+template <int WORD>
+__device__ __forceinline__ uint32_t u4_word(const uint4 &u) {
+  return WORD == 0 ? u.x : (WORD == 1 ? u.y : (WORD == 2 ? u.z : u.w));
 }
 
-// Sub-steps 2 BLK and 2 BLK + 1 (block BLK of each lane's half).
+// Block scales of one block of every fragment, and the fp16 operands of one
+// sub-step.
+template <int TM>
+struct NpScales {
+  NpScale a[Np<TM>::FI], b[Np<TM>::FJ];
+};
+template <int TM>
+struct NpDec {
+  v8h a[Np<TM>::FI], b[Np<TM>::FJ];
+};
+
 template <int TM, int BLK>
-__device__ __forceinline__ void np_mma_blk(const NpFrags<TM> &F,
-                                           v16f (&acc)[Np<TM>::FI][Np<TM>::FJ]) {
-  using C = Np<TM>;
-  {
-    NpScale sa[C::FI], sb[C::FJ];
+__device__ __forceinline__ void np_scales(const NpWords<TM> &W, NpScales<TM> &S) {
 #pragma unroll
-    for (int i = 0; i < C::FI; ++i) sa[i] = np_scale<BLK>(F.sa[i]);
+  for (int i = 0; i < Np<TM>::FI; ++i) S.a[i] = np_scale<BLK>(W.a[i]);
 #pragma unroll
-    for (int j = 0; j < C::FJ; ++j) sb[j] = np_scale<BLK>(F.sb[j]);
+  for (int j = 0; j < Np<TM>::FJ; ++j) S.b[j] = np_scale<BLK>(W.b[j]);
+}
+
+template <int TM, int WORD>
+__device__ __forceinline__ void np_dec(const NpHalf<TM> &R, const NpScales<TM> &S, NpDec<TM> &X) {
 #pragma unroll
-    for (int s = 2 * BLK; s < 2 * BLK + 2; ++s) {
-      v8h xa[C::FI], xb[C::FJ];
+  for (int i = 0; i < Np<TM>::FI; ++i) X.a[i] = np_decode(u4_word<WORD>(R.a[i]), S.a[i]);
 #pragma unroll
-      for (int i = 0; i < C::FI; ++i) xa[i] = np_decode(u4_word(F.a[i], s), sa[i]);
+  for (int j = 0; j < Np<TM>::FJ; ++j) X.b[j] = np_decode(u4_word<WORD>(R.b[j]), S.b[j]);
+}
+
+// The MFMAs of one decoded sub-step; the instructions placed before them in
+// the same scheduling region (the next sub-step's decode) are spread between
+// them: each MFMA keeps the matrix core busy for 32 cycles while the wave
+// issues up to 6 VALU instructions.
+template <int TM>
+__device__ __forceinline__ void np_mfmas(const NpDec<TM> &X,
+                                         v16f (&acc)[Np<TM>::FI][Np<TM>::FJ]) {
 #pragma unroll
-      for (int j = 0; j < C::FJ; ++j) xb[j] = np_decode(u4_word(F.b[j], s), sb[j]);
+  for (int j = 0; j < Np<TM>::FJ; ++j)
 #pragma unroll
-      for (int j = 0; j < C::FJ; ++j)
+    for (int i = 0; i < Np<TM>::FI; ++i)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(X.b[j], X.a[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < C::FI; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xb[j], xa[i], acc[i][j], 0, 0, 0);
-    }
+  for (int m = 0; m < Np<TM>::FI * Np<TM>::FJ; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then VALU
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
+// One 128-K step, software-pipelined over its 8 sub-steps.  On entry R0 / R1
+// hold this step's raw halves, W its scale words and X its decoded sub-step
+// 0.  Sub-step s + 1 is decoded while the MFMAs of s run.  Once sub-step 3
+// is decoded (half 0 dead) half 0 and the scale words of step kt + 1 are
+// read from slot `nslot` into R0 / W; once sub-step 7 is, half 1 into R1;
+// and the last sub-step's MFMAs cover the decode of step kt + 1's sub-step
+// 0.  So one set of raw registers serves two steps, and the registers saved
+// hold the second decoded sub-step.
 template <int TM>
-__device__ __forceinline__ void np_mma(const NpFrags<TM> &F,
-                                       v16f (&acc)[Np<TM>::FI][Np<TM>::FJ]) {
-  np_mma_blk<TM, 0>(F, acc);
-  np_mma_blk<TM, 1>(F, acc);
-  np_mma_blk<TM, 2>(F, acc);
-  np_mma_blk<TM, 3>(F, acc);
-}
-
-template <int TM>
-__device__ __forceinline__ void np_step(const NpSrc<TM> &L, const uint8_t *lds, const NpLane &o,
-                                        int kt, int nk, int slot,
-                                        v16f (&acc)[Np<TM>::FI][Np<TM>::FJ],
-                                        const NpFrags<TM> &cur, NpFrags<TM> &next) {
-  constexpr int S = Np<TM>::NSLOT;
-  vm_wait<(S - 2) * Np<TM>::OPS>();  // own loads of step kt+1 done; later steps may be pending
-  lgkm_wait0();
-  __builtin_amdgcn_s_barrier();
-  np_issue<TM>(L, min(kt + S, nk - 1), slot);
+__device__ __forceinline__ void np_step(const uint8_t *lds, const NpLane &o, int nslot,
+                                        v16f (&acc)[Np<TM>::FI][Np<TM>::FJ], NpHalf<TM> &R0,
+                                        NpHalf<TM> &R1, NpWords<TM> &W, NpScales<TM> &S,
+                                        NpDec<TM> &X, NpDec<TM> &Y) {
+  np_dec<TM, 1>(R0, S, Y);                 // s = 1 (block 0)
+  np_mfmas<TM>(X, acc);                    // s = 0
+  np_scales<TM, 1>(W, S);
+  np_dec<TM, 2>(R0, S, X);                 // s = 2 (block 1)
+  np_mfmas<TM>(Y, acc);                    // s = 1
+  np_dec<TM, 3>(R0, S, Y);                 // s = 3
+  np_mfmas<TM>(X, acc);                    // s = 2
+  np_scales<TM, 2>(W, S);
+  np_dec<TM, 0>(R1, S, X);                 // s = 4 (block 2)
+  np_mfmas<TM>(Y, acc);                    // s = 3
+  np_read_half<TM, 0>(lds, nslot, o, R0);  // step kt + 1, half 0
+  NpWords<TM> Wn;
+  np_read_words<TM>(lds, nslot, o, Wn);
   __builtin_amdgcn_sched_barrier(0);
-  np_read<TM>(lds, slot == S - 1 ? 0 : slot + 1, o, next);
+  np_dec<TM, 1>(R1, S, Y);                 // s = 5
+  np_mfmas<TM>(X, acc);                    // s = 4
+  np_scales<TM, 3>(W, S);
+  np_dec<TM, 2>(R1, S, X);                 // s = 6 (block 3)
+  np_mfmas<TM>(Y, acc);                    // s = 5
+  np_dec<TM, 3>(R1, S, Y);                 // s = 7
+  np_mfmas<TM>(X, acc);                    // s = 6
+  np_read_half<TM, 1>(lds, nslot, o, R1);  // step kt + 1, half 1
   __builtin_amdgcn_sched_barrier(0);
-  np_mma<TM>(cur, acc);
+  W = Wn;
+  np_scales<TM, 0>(W, S);
+  np_dec<TM, 0>(R0, S, X);                 // step kt + 1, s = 0
+  np_mfmas<TM>(Y, acc);                    // s = 7
 }
 
 // Store one transposed accumulator with the outer scales: as mx3_store, each
@@ -2215,14 +2261,31 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
   for (int s = 0; s < C::NSLOT; ++s) np_issue<TM>(L, min(s, nk - 1), s);
   vm_wait<(C::NSLOT - 1) * C::OPS>();  // step 0
   __builtin_amdgcn_s_barrier();
-  NpFrags<TM> F0, F1;
-  np_read<TM>(lds, 0, o, F0);
+  NpHalf<TM> R0, R1;
+  NpWords<TM> W;
+  NpScales<TM> S;
+  NpDec<TM> X, Y;
+  np_read_half<TM, 0>(lds, 0, o, R0);
+  np_read_half<TM, 1>(lds, 0, o, R1);
+  np_read_words<TM>(lds, 0, o, W);
+  np_scales<TM, 0>(W, S);
+  np_dec<TM, 0>(R0, S, X);
   int slot = 0;
-  for (int kt = 0; kt < nk; kt += 2) {
-    np_step<TM>(L, lds, o, kt, nk, slot, acc, F0, F1);
-    slot = slot == C::NSLOT - 1 ? 0 : slot + 1;
-    np_step<TM>(L, lds, o, kt + 1, nk, slot, acc, F1, F0);
-    slot = slot == C::NSLOT - 1 ? 0 : slot + 1;
+  for (int kt = 0; kt < nk; ++kt) {
+    // own loads of step kt + 1 done (step kt + 2 may be pending), own reads
+    // of slot kt % 3 (issued during step kt - 1) done; after the barrier
+    // every wave's are, so step kt + 3 may refill the slot and step kt + 1
+    // may be read
+    vm_wait<C::OPS>();
+    lgkm_wait0();
+    __builtin_amdgcn_s_barrier();
+    np_issue<TM>(L, min(kt + C::NSLOT, nk - 1), slot);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;
+    // past the last step the reads take the slot's repeated last step (in
+    // bounds; decoded, never multiplied)
+    np_step<TM>(lds, o, nslot, acc, R0, R1, W, S, X, Y);
+    slot = nslot;
   }
   vm_wait<0>();
 #pragma unroll
