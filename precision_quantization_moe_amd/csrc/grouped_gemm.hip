@@ -537,16 +537,62 @@ __device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds
                                          const Mx3Lane &o, int kt, int nk, int slot,
                                          v16f (&acc)[Mx3<TM>::FI][Mx3<TM>::FJ],
                                          const Mx3Frags<TM> &cur, Mx3Frags<TM> &next) {
-  vm_wait<Mx3<TM>::OPS>();  // own loads of step kt+1 done; step kt+2 may be pending
-  lgkm_wait0();             // own reads of `slot` done before it is refilled
+  using C = Mx3<TM>;
+  vm_wait<C::OPS>();  // own loads of step kt+1 done; step kt+2 may be pending
+  lgkm_wait0();       // own reads of `slot` done before it is refilled
   __builtin_amdgcn_s_barrier();
-  // keep the order: loads out first, then the operand reads, then the MFMAs
-  // (which need none of them)
-  mx3_issue<TM>(L, min(kt + 3, nk - 1), slot);
-  __builtin_amdgcn_sched_barrier(0);
-  mx3_read<TM>(lds, kt + 1, slot == 2 ? 0 : slot + 1, o, next);
-  __builtin_amdgcn_sched_barrier(0);
-  mx3_mma<TM>(cur, acc);
+  // One wave per SIMD: while an MFMA occupies the matrix core (64 cycles) the
+  // wave can issue other instructions, but the next MFMA waits.  So each
+  // MFMA is followed by a slice of the step's other work: two of the refill
+  // loads of step kt+3, then one fragment's operand reads of step kt+1.
+  const uint8_t *rd = lds + (slot == 2 ? 0 : slot + 1) * C::SLOT;
+  const uint32_t kb = (uint32_t)min(kt + 3, nk - 1) * 64u;
+  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT;
+  const int blk = 2 * (kt + 1) + ((threadIdx.x & 63) >> 5);
+  const uint8_t *sc = lds + C::NSLOT * C::SLOT + (blk >> 2) * 64 + (blk & 3);
+  constexpr int NL = C::CA + C::CB, ND = (NL + 1) / 2;  // loads, MFMAs carrying them
+#pragma unroll
+  for (int m = 0; m < C::FI * C::FJ; ++m) {
+    const int j = m / C::FI, i = m % C::FI;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j], cur.a[i], acc[i][j], 0,
+                                                                 0, 0, cur.sb[j], 0, cur.sa[i]);
+    if (m < ND) {
+#pragma unroll
+      for (int q = 2 * m; q < 2 * m + 2 && q < NL; ++q) {
+        if (q < C::CA) dma16(L.Ab + (L.oa[q] + kb), base + q * 4096);
+        else dma16(L.Bb + (L.ob[q - C::CA] + kb), base + TM * 64 + (q - C::CA) * 4096);
+      }
+    } else if (m - ND < C::FI) {
+      const int f = m - ND;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(rd + o.a_lo + 2048 * f);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(rd + o.a_hi + 2048 * f);
+      next.a[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      next.sa[f] = sc[o.sa + 2 * f * o.ks * 16];
+    } else if (m - ND - C::FI < C::FJ) {
+      const int f = m - ND - C::FI;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(rd + o.b_lo + 2048 * f);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(rd + o.b_hi + 2048 * f);
+      next.b[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      next.sb[f] = sc[o.sb + 2 * f * o.ks * 16];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // fragments left over when there are fewer MFMAs than slices (TM = 128)
+#pragma unroll
+  for (int f = C::FI * C::FJ - ND; f < C::FI + C::FJ; ++f) {
+    if (f < C::FI) {
+      const uint4 lo = *reinterpret_cast<const uint4 *>(rd + o.a_lo + 2048 * f);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(rd + o.a_hi + 2048 * f);
+      next.a[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      next.sa[f] = sc[o.sa + 2 * f * o.ks * 16];
+    } else {
+      const int g = f - C::FI;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(rd + o.b_lo + 2048 * g);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(rd + o.b_hi + 2048 * g);
+      next.b[g] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      next.sb[g] = sc[o.sb + 2 * g * o.ks * 16];
+    }
+  }
 }
 
 // Fused gate_up epilogue (SwiGLU x prob, then the row-wise MXFP8 encoding
