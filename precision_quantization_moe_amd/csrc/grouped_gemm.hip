@@ -514,10 +514,9 @@ __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N,
     const int64_t col = n0 + cbase + 16 * p + 8 * h;
     if (row >= row_end) continue;
     if (vec && col + 7 < N) {
-      const uint4 w = make_uint4(f32_to_bf16_rne(lo[0]) | (f32_to_bf16_rne(lo[1]) << 16),
-                                 f32_to_bf16_rne(lo[2]) | (f32_to_bf16_rne(lo[3]) << 16),
-                                 f32_to_bf16_rne(hi[0]) | (f32_to_bf16_rne(hi[1]) << 16),
-                                 f32_to_bf16_rne(hi[2]) | (f32_to_bf16_rne(hi[3]) << 16));
+      // hardware pair conversion (nearest even, as f32_to_bf16_rne)
+      const uint4 w = make_uint4(pk_bf16_rne(lo[0], lo[1]), pk_bf16_rne(lo[2], lo[3]),
+                                 pk_bf16_rne(hi[0], hi[1]), pk_bf16_rne(hi[2], hi[3]));
       *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + row * N + col) = w;
     } else {
       const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -1197,31 +1196,68 @@ __device__ __forceinline__ void fb_read(const uint8_t *lds, int slot, const Mx3L
   }
 }
 
-template <bool FIRST>
-__device__ __forceinline__ void fb_mma(const Mx3Frags<FB_TM> &F,
-                                       v16f (&part)[Mx3<FB_TM>::FI][Mx3<FB_TM>::FJ]) {
-  const v16f zero = {};
-#pragma unroll
-  for (int j = 0; j < Mx3<FB_TM>::FJ; ++j)
-#pragma unroll
-    for (int i = 0; i < Mx3<FB_TM>::FI; ++i)
-      part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          F.b[j], F.a[i], FIRST ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
-}
-
-template <bool FIRST>
+// Step kt from slot `slot` (operands in `cur`).  FIRST (the first step of
+// a 128-K block): each MFMA starts a fresh partial, and just before it that
+// fragment's partial of the previous block is folded into the result times
+// its scale product (FOLD; sc[i] per row fragment), so the folding runs
+// while the matrix core works instead of after the block.  As mx3_step, the
+// refill loads of step kt+3 and the operand reads of step kt+1 are issued
+// between the MFMAs.
+template <bool FIRST, bool FOLD>
 __device__ __forceinline__ void fb_step(const Mx3Src<FB_TM> &L, const uint8_t *lds,
                                         const Mx3Lane &o, int kt, int nk, int slot,
                                         v16f (&part)[Mx3<FB_TM>::FI][Mx3<FB_TM>::FJ],
+                                        v16f (&acc)[Mx3<FB_TM>::FI][Mx3<FB_TM>::FJ],
+                                        const float (&sc)[Mx3<FB_TM>::FI],
                                         const Mx3Frags<FB_TM> &cur, Mx3Frags<FB_TM> &next) {
-  vm_wait<Mx3<FB_TM>::OPS>();
+  using C = Mx3<FB_TM>;
+  constexpr int TM = FB_TM;
+  vm_wait<C::OPS>();
   lgkm_wait0();
   __builtin_amdgcn_s_barrier();
-  mx3_issue<FB_TM>(L, min(kt + 3, nk - 1), slot);
-  __builtin_amdgcn_sched_barrier(0);
-  fb_read(lds, slot == 2 ? 0 : slot + 1, o, next);
-  __builtin_amdgcn_sched_barrier(0);
-  fb_mma<FIRST>(cur, part);
+  const uint8_t *rd = lds + (slot == 2 ? 0 : slot + 1) * C::SLOT;
+  const uint32_t kb = (uint32_t)min(kt + 3, nk - 1) * 64u;
+  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT;
+  constexpr int NL = C::CA + C::CB, ND = (NL + 1) / 2, NM = C::FI * C::FJ;
+  const v16f zero = {};
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int j = m / C::FI, i = m % C::FI;
+    if (FOLD) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(part[i][j][r], sc[i], acc[i][j][r]);
+    }
+    part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        cur.b[j], cur.a[i], FIRST ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
+    if (m < ND) {
+#pragma unroll
+      for (int q = 2 * m; q < 2 * m + 2 && q < NL; ++q) {
+        if (q < C::CA) dma16(L.Ab + (L.oa[q] + kb), base + q * 4096);
+        else dma16(L.Bb + (L.ob[q - C::CA] + kb), base + TM * 64 + (q - C::CA) * 4096);
+      }
+    } else if (m - ND < C::FI) {
+      const int f = m - ND;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(rd + o.a_lo + 2048 * f);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(rd + o.a_hi + 2048 * f);
+      next.a[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    } else if (m - ND - C::FI < C::FJ) {
+      const int f = m - ND - C::FI;
+      const uint4 lo = *reinterpret_cast<const uint4 *>(rd + o.b_lo + 2048 * f);
+      const uint4 hi = *reinterpret_cast<const uint4 *>(rd + o.b_hi + 2048 * f);
+      next.b[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // fragments left over when there are fewer MFMAs than slices
+#pragma unroll
+  for (int f = NM - ND; f < C::FI + C::FJ; ++f) {
+    const int g = f - C::FI;
+    const uint4 lo = *reinterpret_cast<const uint4 *>(rd + (f < C::FI ? o.a_lo + 2048 * f : o.b_lo + 2048 * g));
+    const uint4 hi = *reinterpret_cast<const uint4 *>(rd + (f < C::FI ? o.a_hi + 2048 * f : o.b_hi + 2048 * g));
+    const v8i v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    if (f < C::FI) next.a[f] = v;
+    else next.b[g] = v;
+  }
 }
 
 template <bool OUT_F32>
@@ -1304,22 +1340,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_block(
   Mx3Frags<TM> F0, F1;
   fb_read(lds, 0, o, F0);
   int slot = 0;
+  float sc[FI];  // scale products of the block whose partial is pending
   for (int kb = 0; kb < KB; ++kb) {
     const int kt = 2 * kb;
-    fb_step<true>(L, lds, o, kt, nk, slot, part, F0, F1);
+    if (kb == 0)
+      fb_step<true, false>(L, lds, o, kt, nk, slot, part, acc, sc, F0, F1);
+    else
+      fb_step<true, true>(L, lds, o, kt, nk, slot, part, acc, sc, F0, F1);
     slot = slot == 2 ? 0 : slot + 1;
-    fb_step<false>(L, lds, o, kt + 1, nk, slot, part, F1, F0);
+    fb_step<false, false>(L, lds, o, kt + 1, nk, slot, part, acc, sc, F1, F0);
     slot = slot == 2 ? 0 : slot + 1;
     const float sbv = sb_l[wn * KB + kb];
 #pragma unroll
-    for (int i = 0; i < FI; ++i) {
-      const float sc = sa_l[kb * TM + wm * (TM / 2) + 32 * i + r32] * sbv;
-#pragma unroll
-      for (int j = 0; j < FJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(part[i][j][r], sc, acc[i][j][r]);
-    }
+    for (int i = 0; i < FI; ++i) sc[i] = sa_l[kb * TM + wm * (TM / 2) + 32 * i + r32] * sbv;
   }
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(part[i][j][r], sc[i], acc[i][j][r]);
   vm_wait<0>();  // no load may still target this workgroup's LDS at exit
 #pragma unroll
   for (int i = 0; i < FI; ++i)
@@ -1618,23 +1658,27 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint8_t *p) {
 // `reg`.  KL: off[0] / off[1] = the lane's chunk-h / chunk-(2+h) offsets of
 // fragment 0, fragments 2048 bytes apart.  ML: off[f] = the lane's offset for
 // fragment f; sub-step s, read r at + (16 s + 4 r) * 512.
+template <bool ML>
+__device__ __forceinline__ void bp_read_frag(const uint8_t *reg, const int *off, int f,
+                                             uint4 (&fr)[2]) {
+  if (ML) {
+    const uint8_t *p = reg + off[f];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint2 r0 = lds_read_tr16(p + (16 * s) * 512);
+      const uint2 r1 = lds_read_tr16(p + (16 * s + 4) * 512);
+      fr[s] = make_uint4(r0.x, r0.y, r1.x, r1.y);
+    }
+  } else {
+    fr[0] = *reinterpret_cast<const uint4 *>(reg + off[0] + 2048 * f);
+    fr[1] = *reinterpret_cast<const uint4 *>(reg + off[1] + 2048 * f);
+  }
+}
+
 template <int F, bool ML>
 __device__ __forceinline__ void bp_read_op(const uint8_t *reg, const int *off, uint4 (&fr)[F][2]) {
 #pragma unroll
-  for (int f = 0; f < F; ++f) {
-    if (ML) {
-      const uint8_t *p = reg + off[f];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint2 r0 = lds_read_tr16(p + (16 * s) * 512);
-        const uint2 r1 = lds_read_tr16(p + (16 * s + 4) * 512);
-        fr[f][s] = make_uint4(r0.x, r0.y, r1.x, r1.y);
-      }
-    } else {
-      fr[f][0] = *reinterpret_cast<const uint4 *>(reg + off[0] + 2048 * f);
-      fr[f][1] = *reinterpret_cast<const uint4 *>(reg + off[1] + 2048 * f);
-    }
-  }
+  for (int f = 0; f < F; ++f) bp_read_frag<ML>(reg, off, f, fr[f]);
 }
 
 template <int KIND, int TM>
@@ -1667,14 +1711,42 @@ __device__ __forceinline__ void bp_step(const BpSrc<TM> &L, const uint8_t *lds, 
                                         const int *offB, int kt, int nk, int slot, int len,
                                         v16f (&acc)[Bp<TM>::FI][Bp<TM>::FJ],
                                         const BpFrags<TM> &cur, BpFrags<TM> &next) {
-  vm_wait<Bp<TM>::OPS>();
+  using C = Bp<TM>;
+  vm_wait<C::OPS>();
   lgkm_wait0();
   __builtin_amdgcn_s_barrier();
-  bp_issue<TM, KIND>(L, min(kt + 3, nk - 1), slot, len);
-  __builtin_amdgcn_sched_barrier(0);
-  bp_read<KIND, TM>(lds, slot == 2 ? 0 : slot + 1, offA, offB, next);
-  __builtin_amdgcn_sched_barrier(0);
-  bp_mma<TM>(cur, acc);
+  // as mx3_step: after each MFMA a slice of the step's other work, two of
+  // the refill loads of step kt+3 or one fragment's reads of step kt+1
+  const int rk = min(kt + 3, nk - 1);
+  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT;
+  const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_bp_zero) + 16 * (threadIdx.x & 63);
+  const int r0 = rk * 32 + ((int)threadIdx.x >> 5);  // contraction row of chunk 0 (ML)
+  const uint8_t *reg = lds + (slot == 2 ? 0 : slot + 1) * C::SLOT;
+  constexpr int NL = C::CA + C::CB, ND = (NL + 1) / 2, NM = 2 * C::FI * C::FJ;
+  static_assert(NM - ND >= C::FI + C::FJ, "a slice for every fragment");
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int sub = m / (C::FI * C::FJ), j = (m / C::FI) % C::FJ, i = m % C::FI;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, cur.b[j][sub]),
+                                                        __builtin_bit_cast(v8bf, cur.a[i][sub]),
+                                                        acc[i][j], 0, 0, 0);
+    if (m < ND) {
+#pragma unroll
+      for (int q = 2 * m; q < 2 * m + 2 && q < NL; ++q) {
+        const bool isa = q < C::CA;
+        const int ii = isa ? q : q - C::CA;
+        const uint8_t *src = isa ? L.Ab + (L.oa[ii] + (uint32_t)rk * L.sa)
+                                 : L.Bb + (L.ob[ii] + (uint32_t)rk * L.sb);
+        if (KIND == BP_WGRAD && r0 + 8 * ii >= len) src = zero;
+        dma16(src, base + (isa ? 0 : TM * 64) + ii * 4096);
+      }
+    } else if (m - ND < C::FI) {
+      bp_read_frag<KIND == BP_WGRAD>(reg, offA, m - ND, next.a[m - ND]);
+    } else if (m - ND - C::FI < C::FJ) {
+      bp_read_frag<KIND != BP_FPROP>(reg, offB, m - ND - C::FI, next.b[m - ND - C::FI]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // One output tile.  Operand panels start at Ab / Bb (bytes); a_lim / b_lim
@@ -2226,10 +2298,8 @@ __device__ __forceinline__ void np_store(const v16f &acc, void *out, int64_t N, 
         *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4 *>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
       } else {
-        const uint4 w = make_uint4(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                   f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16),
-                                   f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16),
-                                   f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16));
+        const uint4 w = make_uint4(pk_bf16_rne(v[0], v[1]), pk_bf16_rne(v[2], v[3]),
+                                   pk_bf16_rne(v[4], v[5]), pk_bf16_rne(v[6], v[7]));
         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + row * N + col) = w;
       }
     } else {

@@ -477,3 +477,46 @@ def test_nvfp4_deepseek_gate_up_full_sampled():
         want = oracle.decode_nvfp4(ra, rsa, rga) @ oracle.decode_nvfp4(rb, rsb, rgb, N).T
         check_rows(yh[rows], want, f"deepseek fc1 expert {e} ({hi - lo} rows)")
     del w, qb
+
+
+# ------------------------------------------------- bf16 output rounding
+
+def _rne_bf16_bits(f32: np.ndarray) -> np.ndarray:
+    """Nearest-even bf16 bits of finite binary32 values (host reference)."""
+    u = f32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt,sizes,N,K", [
+    ("mxfp8", [300, 0, 513, 129, 64], 520, 2048),  # 256 x 256 kernel
+    ("mxfp8", [300, 0, 513, 129, 64], 520, 768),   # 128 x 256 two-per-CU kernel
+    ("nvfp4", [300, 0, 513, 129, 64], 520, 768),
+])
+def test_bf16_output_is_rne_of_binary32_output(fmt, sizes, N, K):
+    """The bf16-output epilogue rounds the same binary32 accumulators the
+    binary32-output epilogue stores: every element must be their nearest-
+    even bf16 (checks the hardware pair conversion on ~0.5 M values)."""
+    G, M = len(sizes), int(sum(sizes))
+    off = dev(_offsets(sizes))
+    x = dev_bf16(wl.activations(M, K, seed=31))
+    w = dev_bf16(wl.normal_bf16((G * N, K), std=0.02, seed=32))
+    if fmt == "mxfp8":
+        qa, sa, _, _ = pqm.quantize_mxfp8(x, colwise=False)
+        qb, sb, _, _ = pqm.quantize_mxfp8(w, colwise=False)
+        kw = dict(a_scale=sa, b_scale=sb)
+        f = pqm.FMT_MXFP8
+    else:
+        qa, sa, ga = pqm.quantize_nvfp4_per_token(x)
+        qb, sb, gb = pqm.quantize_nvfp4_per_token(w, rows_per_scale=N)
+        kw = dict(a_scale=sa, a_outer=ga, b_scale=sb, b_outer=gb, b_rows_per_scale=N)
+        f = pqm.FMT_NVFP4
+    y32 = pqm.moe_grouped_gemm(f, pqm.GEMM_FPROP, qa, qb, off, N, K, out_dtype=pqm.OUT_FP32, **kw)
+    y16 = pqm.moe_grouped_gemm(f, pqm.GEMM_FPROP, qa, qb, off, N, K, out_dtype=pqm.OUT_BF16, **kw)
+    torch.cuda.synchronize()
+    want = _rne_bf16_bits(host(y32))
+    got = host_u16(y16)
+    assert np.isfinite(host(y32)).all()
+    bad = int((got != want).sum())
+    print(f"[gemm] {fmt} K={K} bf16 output vs RNE(binary32 output): {bad} mismatches "
+          f"of {got.size}", flush=True)
+    assert bad == 0
