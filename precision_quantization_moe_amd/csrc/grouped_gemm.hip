@@ -1196,68 +1196,31 @@ __device__ __forceinline__ void fb_read(const uint8_t *lds, int slot, const Mx3L
   }
 }
 
-// Step kt from slot `slot` (operands in `cur`).  FIRST (the first step of
-// a 128-K block): each MFMA starts a fresh partial, and just before it that
-// fragment's partial of the previous block is folded into the result times
-// its scale product (FOLD; sc[i] per row fragment), so the folding runs
-// while the matrix core works instead of after the block.  As mx3_step, the
-// refill loads of step kt+3 and the operand reads of step kt+1 are issued
-// between the MFMAs.
-template <bool FIRST, bool FOLD>
+template <bool FIRST>
+__device__ __forceinline__ void fb_mma(const Mx3Frags<FB_TM> &F,
+                                       v16f (&part)[Mx3<FB_TM>::FI][Mx3<FB_TM>::FJ]) {
+  const v16f zero = {};
+#pragma unroll
+  for (int j = 0; j < Mx3<FB_TM>::FJ; ++j)
+#pragma unroll
+    for (int i = 0; i < Mx3<FB_TM>::FI; ++i)
+      part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          F.b[j], F.a[i], FIRST ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
+}
+
+template <bool FIRST>
 __device__ __forceinline__ void fb_step(const Mx3Src<FB_TM> &L, const uint8_t *lds,
                                         const Mx3Lane &o, int kt, int nk, int slot,
                                         v16f (&part)[Mx3<FB_TM>::FI][Mx3<FB_TM>::FJ],
-                                        v16f (&acc)[Mx3<FB_TM>::FI][Mx3<FB_TM>::FJ],
-                                        const float (&sc)[Mx3<FB_TM>::FI],
                                         const Mx3Frags<FB_TM> &cur, Mx3Frags<FB_TM> &next) {
-  using C = Mx3<FB_TM>;
-  constexpr int TM = FB_TM;
-  vm_wait<C::OPS>();
+  vm_wait<Mx3<FB_TM>::OPS>();
   lgkm_wait0();
   __builtin_amdgcn_s_barrier();
-  const uint8_t *rd = lds + (slot == 2 ? 0 : slot + 1) * C::SLOT;
-  const uint32_t kb = (uint32_t)min(kt + 3, nk - 1) * 64u;
-  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT;
-  constexpr int NL = C::CA + C::CB, ND = (NL + 1) / 2, NM = C::FI * C::FJ;
-  const v16f zero = {};
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const int j = m / C::FI, i = m % C::FI;
-    if (FOLD) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(part[i][j][r], sc[i], acc[i][j][r]);
-    }
-    part[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-        cur.b[j], cur.a[i], FIRST ? zero : part[i][j], 0, 0, 0, 127, 0, 127);
-    if (m < ND) {
-#pragma unroll
-      for (int q = 2 * m; q < 2 * m + 2 && q < NL; ++q) {
-        if (q < C::CA) dma16(L.Ab + (L.oa[q] + kb), base + q * 4096);
-        else dma16(L.Bb + (L.ob[q - C::CA] + kb), base + TM * 64 + (q - C::CA) * 4096);
-      }
-    } else if (m - ND < C::FI) {
-      const int f = m - ND;
-      const uint4 lo = *reinterpret_cast<const uint4 *>(rd + o.a_lo + 2048 * f);
-      const uint4 hi = *reinterpret_cast<const uint4 *>(rd + o.a_hi + 2048 * f);
-      next.a[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    } else if (m - ND - C::FI < C::FJ) {
-      const int f = m - ND - C::FI;
-      const uint4 lo = *reinterpret_cast<const uint4 *>(rd + o.b_lo + 2048 * f);
-      const uint4 hi = *reinterpret_cast<const uint4 *>(rd + o.b_hi + 2048 * f);
-      next.b[f] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // fragments left over when there are fewer MFMAs than slices
-#pragma unroll
-  for (int f = NM - ND; f < C::FI + C::FJ; ++f) {
-    const int g = f - C::FI;
-    const uint4 lo = *reinterpret_cast<const uint4 *>(rd + (f < C::FI ? o.a_lo + 2048 * f : o.b_lo + 2048 * g));
-    const uint4 hi = *reinterpret_cast<const uint4 *>(rd + (f < C::FI ? o.a_hi + 2048 * f : o.b_hi + 2048 * g));
-    const v8i v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    if (f < C::FI) next.a[f] = v;
-    else next.b[g] = v;
-  }
+  mx3_issue<FB_TM>(L, min(kt + 3, nk - 1), slot);
+  __builtin_amdgcn_sched_barrier(0);
+  fb_read(lds, slot == 2 ? 0 : slot + 1, o, next);
+  __builtin_amdgcn_sched_barrier(0);
+  fb_mma<FIRST>(cur, part);
 }
 
 template <bool OUT_F32>
@@ -1340,26 +1303,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_block(
   Mx3Frags<TM> F0, F1;
   fb_read(lds, 0, o, F0);
   int slot = 0;
-  float sc[FI];  // scale products of the block whose partial is pending
   for (int kb = 0; kb < KB; ++kb) {
     const int kt = 2 * kb;
-    if (kb == 0)
-      fb_step<true, false>(L, lds, o, kt, nk, slot, part, acc, sc, F0, F1);
-    else
-      fb_step<true, true>(L, lds, o, kt, nk, slot, part, acc, sc, F0, F1);
+    fb_step<true>(L, lds, o, kt, nk, slot, part, F0, F1);
     slot = slot == 2 ? 0 : slot + 1;
-    fb_step<false, false>(L, lds, o, kt + 1, nk, slot, part, acc, sc, F1, F0);
+    fb_step<false>(L, lds, o, kt + 1, nk, slot, part, F1, F0);
     slot = slot == 2 ? 0 : slot + 1;
     const float sbv = sb_l[wn * KB + kb];
 #pragma unroll
-    for (int i = 0; i < FI; ++i) sc[i] = sa_l[kb * TM + wm * (TM / 2) + 32 * i + r32] * sbv;
+    for (int i = 0; i < FI; ++i) {
+      const float sc = sa_l[kb * TM + wm * (TM / 2) + 32 * i + r32] * sbv;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(part[i][j][r], sc, acc[i][j][r]);
+    }
   }
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < FJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(part[i][j][r], sc[i], acc[i][j][r]);
   vm_wait<0>();  // no load may still target this workgroup's LDS at exit
 #pragma unroll
   for (int i = 0; i < FI; ++i)
