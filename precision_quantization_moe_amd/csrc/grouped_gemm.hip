@@ -530,12 +530,14 @@ __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N,
 
 // Step kt from slot `slot`: operands in `cur` (read during the previous
 // step).  Publish step kt+1, refill `slot` with step kt+3, read step kt+1's
-// operands into `next`, multiply `cur`.
-template <int TM>
-__device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds,
-                                         const Mx3Lane &o, int kt, int nk, int slot,
-                                         v16f (&acc)[Mx3<TM>::FI][Mx3<TM>::FJ],
-                                         const Mx3Frags<TM> &cur, Mx3Frags<TM> &next) {
+// operands into `next`, multiply `cur`.  src(q, kb) gives the global source
+// of refill load q (A chunks 0 .. CA-1, then B chunks) at step byte kb.
+template <int TM, class Src>
+__device__ __forceinline__ void mx3_step_with(const Mx3Src<TM> &L, const uint8_t *lds,
+                                              const Mx3Lane &o, int kt, int nk, int slot,
+                                              v16f (&acc)[Mx3<TM>::FI][Mx3<TM>::FJ],
+                                              const Mx3Frags<TM> &cur, Mx3Frags<TM> &next,
+                                              const Src &src) {
   using C = Mx3<TM>;
   vm_wait<C::OPS>();  // own loads of step kt+1 done; step kt+2 may be pending
   lgkm_wait0();       // own reads of `slot` done before it is refilled
@@ -558,8 +560,7 @@ __device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds
     if (m < ND) {
 #pragma unroll
       for (int q = 2 * m; q < 2 * m + 2 && q < NL; ++q) {
-        if (q < C::CA) dma16(L.Ab + (L.oa[q] + kb), base + q * 4096);
-        else dma16(L.Bb + (L.ob[q - C::CA] + kb), base + TM * 64 + (q - C::CA) * 4096);
+        dma16(src(q, kb), base + (q < C::CA ? q * 4096 : TM * 64 + (q - C::CA) * 4096));
       }
     } else if (m - ND < C::FI) {
       const int f = m - ND;
@@ -592,6 +593,16 @@ __device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds
       next.sb[g] = sc[o.sb + 2 * g * o.ks * 16];
     }
   }
+}
+
+template <int TM>
+__device__ __forceinline__ void mx3_step(const Mx3Src<TM> &L, const uint8_t *lds,
+                                         const Mx3Lane &o, int kt, int nk, int slot,
+                                         v16f (&acc)[Mx3<TM>::FI][Mx3<TM>::FJ],
+                                         const Mx3Frags<TM> &cur, Mx3Frags<TM> &next) {
+  mx3_step_with<TM>(L, lds, o, kt, nk, slot, acc, cur, next, [&](int q, uint32_t kb) {
+    return q < Mx3<TM>::CA ? L.Ab + (L.oa[q] + kb) : L.Bb + (L.ob[q - Mx3<TM>::CA] + kb);
+  });
 }
 
 // Fused gate_up epilogue (SwiGLU x prob, then the row-wise MXFP8 encoding
@@ -1140,14 +1151,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_wgrad(
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int k = kt + half;
-        vm_wait<C::OPS>();
-        lgkm_wait0();
-        __builtin_amdgcn_s_barrier();
-        mx3w_issue<TM>(L, lim_a, lim_b, min(k + 3, nk - 1), nk, slot);
-        __builtin_amdgcn_sched_barrier(0);
-        mx3_read<TM>(lds, k + 1, slot == 2 ? 0 : slot + 1, o, half ? F0 : F1);
-        __builtin_amdgcn_sched_barrier(0);
-        mx3_mma<TM>(half ? F1 : F0, acc);
+        // chunks past the pass read the zero line (only the last two steps
+        // of a pass can reach past it)
+        mx3_step_with<TM>(L, lds, o, k, nk, slot, acc, half ? F1 : F0, half ? F0 : F1,
+                          [&](int q, uint32_t kb) {
+                            const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_mx_zero);
+                            return q < C::CA
+                                       ? (kb < lim_a[q] ? L.Ab + (L.oa[q] + kb) : zero)
+                                       : (kb < lim_b[q - C::CA] ? L.Bb + (L.ob[q - C::CA] + kb)
+                                                                : zero);
+                          });
         slot = slot == 2 ? 0 : slot + 1;
       }
     }
