@@ -34,6 +34,8 @@ seeded input, with all inputs resident in HBM:
                     and all 257 experts' weights) for the dequantized backward
 
 Not part of a step unless named in --rows:
+  q3_gemm_uniform   q3_gemm's two MXFP8 GEMMs with uniform routing (every
+                    expert 512 rows on average): the balanced-load reference
   hbm_copy          torch's device copy of 512 MiB: a plain copy kernel of
                     known size whose FETCH_SIZE / WRITE_SIZE counter readings
                     calibrate the counters read on the other kernels
@@ -67,7 +69,7 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA BF16 / FP16
 ALL_ROWS = ["mxfp8_quant", "nvfp4_token", "nvfp4_joint_w", "q3_wquant", "q3_fwd", "q3_gemm",
             "q3_gemm_fp8b",
             "q3_dequant", "q3_bwd", "q3_bwd_mx", "ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"]
-EXTRA_ROWS = ["hbm_copy"]
+EXTRA_ROWS = ["q3_gemm_uniform", "hbm_copy"]
 COPY_BYTES = 512 << 20
 REPEAT_ROWS = ("mxfp8_quant", "nvfp4_token")
 
@@ -158,7 +160,8 @@ def main():
     # Qwen3-30B-A3B expert layer
     T4, K4, I4 = 8192, 8, 768
     M4 = T4 * K4
-    if need("q3_wquant", "q3_fwd", "q3_gemm", "q3_gemm_fp8b", "q3_dequant", "q3_bwd", "q3_bwd_mx"):
+    if need("q3_wquant", "q3_fwd", "q3_gemm", "q3_gemm_fp8b", "q3_dequant", "q3_bwd", "q3_bwd_mx",
+            "q3_gemm_uniform"):
         st["x4"] = to_dev(wl.activations(T4, H, seed=4))
         st["ids4"] = torch.from_numpy(wl.zipf_routing(T4, E, K4)).to(dev)
         st["prob4"] = torch.from_numpy(wl.router_probs(T4, K4).reshape(-1)).to(dev)
@@ -177,6 +180,15 @@ def main():
             c=torch.empty((M4, 2 * I4), dtype=torch.bfloat16, device=dev),
             y=torch.empty((M4, H), dtype=torch.bfloat16, device=dev))
         del xr
+    if need("q3_gemm_uniform"):
+        ids_u = torch.from_numpy(wl.uniform_routing(T4, E, K4)).to(dev)
+        off_u, _, tok_u, _ = pqm.moe_route(ids_u, E)
+        xu = pqm.moe_gather_rows(st["x4"], tok_u)
+        st["uni"] = dict(off=off_u, x=pqm.quantize_mxfp8(xu, colwise=False),
+                         d=pqm.quantize_mxfp8(to_dev(wl.activations(M4, I4, seed=9)), colwise=False),
+                         c=torch.empty((M4, 2 * I4), dtype=torch.bfloat16, device=dev),
+                         y=torch.empty((M4, H), dtype=torch.bfloat16, device=dev))
+        del xu
     if need("q3_bwd_mx"):
         # forward-side operands of the low-precision backward: the weights'
         # column-wise copies and those of the padded FC1 input X (the
@@ -242,6 +254,13 @@ def main():
                              a_scale=o["sa"], b_scale=w1s, out_dtype=pqm.OUT_BF16, out=st["c4"])
         pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, o["qd"], w2q, o["off"], H, I4,
                              a_scale=o["sd"], b_scale=w2s, out_dtype=pqm.OUT_BF16, out=o["y"])
+
+    def r_q3_gemm_uniform(s):
+        u, (w1q, w1s, w2q, w2s) = st["uni"], st["q3w"]
+        pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, u["x"][0], w1q, u["off"], 2 * I4, H,
+                             a_scale=u["x"][1], b_scale=w1s, out_dtype=pqm.OUT_BF16, out=u["c"])
+        pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, u["d"][0], w2q, u["off"], H, I4,
+                             a_scale=u["d"][1], b_scale=w2s, out_dtype=pqm.OUT_BF16, out=u["y"])
 
     def r_q3_gemm_fp8b(s):
         f = st["fp8b"]
@@ -309,11 +328,12 @@ def main():
 
     fns = {"hbm_copy": r_copy, "mxfp8_quant": r_mxfp8, "nvfp4_token": r_nvfp4, "nvfp4_joint_w": r_joint,
            "q3_wquant": r_q3_wquant, "q3_fwd": r_q3_fwd, "q3_gemm": r_q3_gemm,
-           "q3_gemm_fp8b": r_q3_gemm_fp8b,
+           "q3_gemm_fp8b": r_q3_gemm_fp8b, "q3_gemm_uniform": r_q3_gemm_uniform,
            "q3_dequant": r_q3_dequant, "q3_bwd": r_q3_bwd, "q3_bwd_mx": r_q3_bwd_mx,
            "ds_wquant": r_ds_wquant,
            "ds_fwd": r_ds_fwd, "ds_gemm": r_ds_gemm, "ds_reconstruct": r_ds_reconstruct}
     deps = {"q3_fwd": ["q3_wquant"], "q3_gemm": ["q3_wquant", "q3_fwd"],
+            "q3_gemm_uniform": ["q3_wquant"],
             "q3_dequant": ["q3_wquant", "q3_fwd"], "q3_bwd": ["q3_wquant", "q3_fwd", "q3_dequant"],
             "ds_fwd": ["ds_wquant"], "ds_gemm": ["ds_wquant", "ds_fwd"],
             "ds_reconstruct": ["ds_wquant", "ds_fwd"]}
@@ -364,6 +384,7 @@ def main():
         return fc1 + fc2
 
     by_q3 = {"q3_gemm": gemm_bytes(M4, E, I4, H, 1 + 1 / 32, 1 + 1 / 32),
+             "q3_gemm_uniform": gemm_bytes(M4, E, I4, H, 1 + 1 / 32, 1 + 1 / 32),
              "q3_gemm_fp8b": gemm_bytes(M4, E, I4, H, 1 + 4 / 128, 1 + 4 / 128 ** 2)}
     by_ds = gemm_bytes(M5, E5 + 1, I5, H5, 0.5 + 1 / 16, 0.5 + 1 / 16, a_row=4)
 
@@ -385,7 +406,7 @@ def main():
             hbm(c, E * I2 * H * (2 + 0.5 + 1 / 16) + E * 4, t)
         elif n == "q3_wquant":
             hbm(c, (E * 2 * I4 * H + E * H * I4) * (2 + 1 + 1 / 32), t)
-        elif n in ("q3_fwd", "q3_gemm", "q3_gemm_fp8b"):
+        elif n in ("q3_fwd", "q3_gemm", "q3_gemm_fp8b", "q3_gemm_uniform"):
             c.update(flop=fl_q3, tflops=fl_q3 / t / 1e12, frac_fp8=fl_q3 / t / 1e12 / FP8_PEAK_TFLOPS)
             if n in by_q3:
                 floor(c, fl_q3, by_q3[n], FP8_PEAK_TFLOPS, t)

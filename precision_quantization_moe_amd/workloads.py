@@ -129,6 +129,12 @@ def zipf_routing(tokens: int, num_experts: int, k: int, s: float = 1.1,
     return route_topk(tokens, num_experts, k, zipf_weights(num_experts, s), seed)
 
 
+def uniform_routing(tokens: int, num_experts: int, k: int, seed: int = SEED_ROUTE):
+    """Every expert equally likely (the balanced-load reference case)."""
+    p = np.full(num_experts, 1.0 / num_experts)
+    return route_topk(tokens, num_experts, k, p, seed)
+
+
 def uniform_plus_zipf_routing(tokens: int, num_experts: int, k: int,
                               s: float = 1.1, seed: int = SEED_ROUTE):
     """Half uniform, half Zipf(s) expert load."""
