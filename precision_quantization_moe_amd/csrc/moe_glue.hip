@@ -267,14 +267,26 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ y,
   if (i >= T * per_row) return;
   const int64_t t = i / per_row, n = (i % per_row) * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t j = 0; j < k; ++j) {
-    const int64_t r = slot[t * k + j];
-    const uint4 v = *reinterpret_cast<const uint4 *>(y + r * N + n);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // batches of 8 slots: all index loads, then all row loads in flight
+  // together, then the sums in j order
+  constexpr int KB = 8;
+  for (int64_t j0 = 0; j0 < k; j0 += KB) {
+    int64_t r[KB];
+    uint4 v[KB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += bf16_lo_f32(w[q]);
-      acc[2 * q + 1] += bf16_hi_f32(w[q]);
+    for (int u = 0; u < KB; ++u) r[u] = j0 + u < k ? (int64_t)slot[t * k + j0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      v[u] = r[u] >= 0 ? *reinterpret_cast<const uint4 *>(y + r[u] * N + n) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (r[u] < 0) break;
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_lo_f32(w[q]);
+        acc[2 * q + 1] += bf16_hi_f32(w[q]);
+      }
     }
   }
   if (shared) {
@@ -286,11 +298,9 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ y,
       acc[2 * q + 1] += bf16_hi_f32(w[q]);
     }
   }
-  uint32_t o[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    o[q] = f32_to_bf16_rne(acc[2 * q]) | (f32_to_bf16_rne(acc[2 * q + 1]) << 16);
-  *reinterpret_cast<uint4 *>(out + t * N + n) = make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint4 *>(out + t * N + n) =
+      make_uint4(pk_bf16_rne(acc[0], acc[1]), pk_bf16_rne(acc[2], acc[3]),
+                 pk_bf16_rne(acc[4], acc[5]), pk_bf16_rne(acc[6], acc[7]));
 }
 
 hipError_t launch_combine(const uint16_t *y, const int32_t *slot, const uint16_t *shared,

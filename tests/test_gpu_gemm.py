@@ -142,6 +142,37 @@ def test_mxfp8_qwen3_gate_up_full_sampled():
     assert M == T * k
 
 
+def test_mxfp8_qwen3_down_full_sampled():
+    """Full Qwen3-30B-A3B FC2 shape (the two-workgroups-per-CU kernel that
+    runs K <= 1024): 65536 routed rows of D [.., 768] under Zipf(1.1) load,
+    N = 2048, K = 768, bf16 output as in the layer; sampled rows of every
+    checked expert against the binary64 product (bar + one bf16 rounding)."""
+    T, E, k, H, I = 8192, 128, 8, 2048, 768
+    ids = wl.zipf_routing(T, E, k)
+    off, _, _ = oracle.route(ids, E)
+    M = T * k
+    d = wl.activations(M, I, seed=9)
+    qa, sa, _, _ = pqm.quantize_mxfp8(dev_bf16(d), colwise=False)
+    w = wl.expert_weights(E, H, I, 0.02, tag=1)
+    qb, sb, _, _ = pqm.quantize_mxfp8(dev_bf16(w.reshape(E * H, I)), colwise=False)
+    y = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, qb, dev(off), H, I,
+                             a_scale=sa, b_scale=sb, out_dtype=pqm.OUT_BF16)
+    torch.cuda.synchronize()
+    yh = oracle.bf16_to_f64(host_u16(y))
+    rng = np.random.Generator(np.random.PCG64(18))
+    experts = sorted(set(rng.choice(E, 12, replace=False).tolist()) | {0, E - 1})
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 6)]))
+        ra, rsa = oracle.quantize_mxfp8_rowwise(d[rows])
+        rb, rsb = oracle.quantize_mxfp8_rowwise(w[e])
+        want = oracle.decode_mxfp8(ra, rsa) @ oracle.decode_mxfp8(rb, rsb).T
+        r = rel_l2_rows(yh[rows], want)
+        print(f"[gemm] qwen3 fc2 expert {e} ({hi - lo} rows): max row rel-L2 {r.max():.3e}",
+              flush=True)
+        assert r.max() <= TOL + 2.0 ** -9, (e, float(r.max()))
+
+
 # ------------------------------------------------- MXFP8 backward GEMMs
 
 def _colwise_b_groups(qT, sT, G, K):
