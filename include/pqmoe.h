@@ -307,7 +307,8 @@ pqm_status pqm_moe_gemm_swiglu_quantize_mxfp8(const uint8_t *a, const uint8_t *a
  *             kept                                               (device)
  *   token     [same] int32: the token of each position           (device)
  *   slot      [tokens, k] int32: position of assignment (t, j)   (device)
- *   workspace >= pqm_moe_route_workspace(...) bytes, 4-byte aligned.
+ *   workspace >= pqm_moe_route_workspace(...) bytes (0 when tokens == 0;
+ *             may then be NULL), 8-byte aligned.
  * num_experts <= 4096, tokens * (k + 1) < 2^31.  Ids outside
  * [0, num_experts) are undefined behaviour.
  */

@@ -10,7 +10,7 @@
 
 namespace pqm {
 
-constexpr int ROUTE_CHUNK = 1024;  // assignments per workgroup
+constexpr int ROUTE_CHUNK = 256;  // assignments per workgroup (one per thread)
 
 // Per-chunk histogram of expert ids: counts[chunk * E + e].
 __global__ __launch_bounds__(256) void k_route_hist(const int32_t *__restrict__ ids,
@@ -31,40 +31,61 @@ __global__ __launch_bounds__(256) void k_route_hist(const int32_t *__restrict__ 
   for (int64_t e = threadIdx.x; e < E; e += 256) counts[blockIdx.x * E + e] = h[e];
 }
 
-// One workgroup: offsets (exclusive scan of expert totals) and, in place,
-// the start position of every (chunk, expert) pair.  With a shared expert,
-// offsets[E+1] closes one more group of `shared_rows` rows after the routed
-// ones.
-__global__ __launch_bounds__(256) void k_route_scan(int32_t *__restrict__ counts,
-                                                    int64_t nchunks, int64_t E,
-                                                    int64_t shared_rows,
-                                                    int64_t *__restrict__ offsets) {
-  extern __shared__ int64_t tot[];
-  for (int64_t e = threadIdx.x; e < E; e += 256) {
-    int64_t s = 0;
-    for (int64_t c = 0; c < nchunks; ++c) s += counts[c * E + e];
-    tot[e] = s;
+// Exclusive prefix of v over the 256 threads of the workgroup (thread
+// order) plus `carry`; the 256 values' sum is added to carry.  wsum: 4
+// shared slots.  Every thread must call it.
+__device__ __forceinline__ int64_t block_excl_scan256(int64_t v, int64_t &carry, int64_t *wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
   }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
+  int64_t before = carry;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();  // every thread has read the slots before they are reused
+  return before + incl - v;
+}
+
+// One workgroup per expert e: its column of chunk counts becomes, in place,
+// the exclusive prefix over chunks (the first row of (chunk, e) relative to
+// the expert's first row), and total[e] its sum.
+__global__ __launch_bounds__(256) void k_route_colscan(int32_t *__restrict__ counts,
+                                                       int64_t nchunks, int64_t E,
+                                                       int64_t *__restrict__ total) {
+  __shared__ int64_t wsum[4];
+  const int64_t e = blockIdx.x;
+  int64_t carry = 0;
+  for (int64_t c0 = 0; c0 < nchunks; c0 += 256) {
+    const int64_t c = c0 + threadIdx.x;
+    const int64_t v = c < nchunks ? counts[c * E + e] : 0;
+    const int64_t x = block_excl_scan256(v, carry, wsum);
+    if (c < nchunks) counts[c * E + e] = (int32_t)x;
+  }
+  if (threadIdx.x == 0) total[e] = carry;
+}
+
+// One workgroup: offsets = exclusive scan of the expert totals (all zero
+// when total is NULL).  shared_rows >= 0 (a shared expert, possibly with no
+// tokens): offsets[E+1] closes one more group of that many rows after the
+// routed ones; -1: no such group.
+__global__ __launch_bounds__(256) void k_route_offsets(const int64_t *__restrict__ total,
+                                                       int64_t E, int64_t shared_rows,
+                                                       int64_t *__restrict__ offsets) {
+  __shared__ int64_t wsum[4];
+  int64_t carry = 0;
+  for (int64_t b = 0; b < E; b += 256) {
+    const int64_t e = b + threadIdx.x;
+    const int64_t x = block_excl_scan256(e < E && total ? total[e] : 0, carry, wsum);
+    if (e < E) offsets[e] = x;
+  }
   if (threadIdx.x == 0) {
-    int64_t run = 0;
-    for (int64_t e = 0; e < E; ++e) {
-      const int64_t t = tot[e];
-      tot[e] = run;
-      offsets[e] = run;
-      run += t;
-    }
-    offsets[E] = run;
-    if (shared_rows > 0) offsets[E + 1] = run + shared_rows;
-  }
-  __syncthreads();
-  for (int64_t e = threadIdx.x; e < E; e += 256) {
-    int64_t run = tot[e];
-    for (int64_t c = 0; c < nchunks; ++c) {
-      const int32_t k = counts[c * E + e];
-      counts[c * E + e] = (int32_t)run;
-      run += k;
-    }
+    offsets[E] = carry;
+    if (shared_rows >= 0) offsets[E + 1] = carry + shared_rows;
   }
 }
 
@@ -73,13 +94,15 @@ __global__ __launch_bounds__(256) void k_route_scan(int32_t *__restrict__ counts
 __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict__ ids,
                                                        int64_t n, int64_t E, int64_t k,
                                                        const int32_t *__restrict__ start,
+                                                       const int64_t *__restrict__ offsets,
                                                        int32_t *__restrict__ src_row,
                                                        int32_t *__restrict__ token,
                                                        int32_t *__restrict__ slot) {
   extern __shared__ int32_t sh[];
   int32_t *run = sh;          // [E]
   int32_t *round_ids = sh + E;  // [256]
-  for (int64_t e = threadIdx.x; e < E; e += 256) run[e] = start[blockIdx.x * E + e];
+  for (int64_t e = threadIdx.x; e < E; e += 256)
+    run[e] = start[blockIdx.x * E + e] + (int32_t)offsets[e];
   const int64_t base = (int64_t)blockIdx.x * ROUTE_CHUNK;
   for (int r = 0; r < ROUTE_CHUNK / 256; ++r) {
     const int64_t a = base + r * 256 + threadIdx.x;
@@ -101,10 +124,17 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t *__restrict
   }
 }
 
+// Workspace: the (chunk, expert) counts as int32, then the expert totals as
+// int64 (8-byte aligned).
+static int64_t route_totals_offset(int64_t nchunks, int64_t E) {
+  return (nchunks * E * (int64_t)sizeof(int32_t) + 7) / 8 * 8;
+}
+
 size_t route_workspace_bytes(int64_t T, int64_t k, int64_t E) {
   const int64_t n = T * k;
   const int64_t nchunks = (n + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
-  return (size_t)(nchunks * E) * sizeof(int32_t);
+  if (nchunks == 0) return 0;  // no assignments: the offsets are all zero
+  return (size_t)(route_totals_offset(nchunks, E) + E * (int64_t)sizeof(int64_t));
 }
 
 // The shared expert's rows: row n + t is token t (assignment index n + t).
@@ -122,16 +152,24 @@ hipError_t launch_route(const int32_t *ids, int64_t T, int64_t k, int64_t E, int
                         void *ws, hipStream_t st) {
   const int64_t n = T * k;
   const int64_t nchunks = (n + ROUTE_CHUNK - 1) / ROUTE_CHUNK;
+  // with no assignments the workspace may be absent: no counts, and the
+  // offsets come from zero totals (total == NULL)
   int32_t *counts = static_cast<int32_t *>(ws);
-  if (nchunks > 0)
+  int64_t *total = nchunks > 0 ? reinterpret_cast<int64_t *>(static_cast<uint8_t *>(ws) +
+                                                             route_totals_offset(nchunks, E))
+                               : nullptr;
+  if (nchunks > 0) {
     hipLaunchKernelGGL(k_route_hist, dim3((unsigned)nchunks), dim3(256), E * sizeof(int32_t),
                        st, ids, n, E, counts);
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), E * sizeof(int64_t), st, counts,
-                     nchunks, E, shared ? T : (int64_t)0, offsets);
+    hipLaunchKernelGGL(k_route_colscan, dim3((unsigned)E), dim3(256), 0, st, counts, nchunks, E,
+                       total);
+  }
+  hipLaunchKernelGGL(k_route_offsets, dim3(1), dim3(256), 0, st, total, E,
+                     shared ? T : (int64_t)-1, offsets);
   if (nchunks > 0)
     hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nchunks), dim3(256),
-                       (E + 256) * sizeof(int32_t), st, ids, n, E, k, counts, src_row, token,
-                       slot);
+                       (E + 256) * sizeof(int32_t), st, ids, n, E, k, counts, offsets, src_row,
+                       token, slot);
   if (shared && T > 0)
     hipLaunchKernelGGL(k_route_shared, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, n,
                        T, src_row, token);
@@ -405,7 +443,7 @@ pqm_status pqm_moe_route(const int32_t *topk_ids, int64_t tokens, int64_t k,
     return PQM_ERR_NULL;
   if (workspace_bytes < pqm::route_workspace_bytes(tokens, k, num_experts))
     return PQM_ERR_WORKSPACE;
-  if (!al(offsets, 8) || (workspace && !al(workspace, 4))) return PQM_ERR_ALIGN;
+  if (!al(offsets, 8) || (workspace && !al(workspace, 8))) return PQM_ERR_ALIGN;
   return st_of(pqm::launch_route(topk_ids, tokens, k, num_experts, shared_expert, offsets,
                                  src_row, token, slot, workspace, stream));
 }

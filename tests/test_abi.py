@@ -140,7 +140,9 @@ def test_glue_validation():
     assert L.pqm_moe_route(A16, 8, 2, 4, 0, A16, A16, A16, A16, A16, 0, None) == 5
     assert L.pqm_moe_route(A16, 8, 2, 4, 3, A16, A16, A16, A16, A16, 1 << 20, None) == 4
     assert L.pqm_moe_route(A16, 8, 2, 4, 1, A16, A16, None, A16, A16, 1 << 20, None) == 1
-    assert L.pqm_moe_route_workspace(8192, 8, 128) == 64 * 128 * 4
+    # one int32 count per expert per 256 assignments, then one int64 total per expert
+    assert L.pqm_moe_route_workspace(8192, 8, 128) == 256 * 128 * 4 + 128 * 8
+    assert L.pqm_moe_route_workspace(0, 8, 128) == 0
     assert L.pqm_moe_gather_rows(A16, 4, 16, A16, 4, 0, A16, None) == 2
     f = L.pqm_moe_pad_rows
     assert f(A16, 64, 128, A16, 4, 0, A16, A16, 200, None) == 2      # align >= 1

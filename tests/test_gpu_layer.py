@@ -224,3 +224,23 @@ def test_nvfp4_layer_deepseek_full_sampled_tokens():
     check(host_u16(g["c"])[rows], o["c"], "C", TOL_NVFP4)
     check(host_u16(g["y"])[rows], o["y"], "Y", TOL_NVFP4)
     check(host_u16(g["out"])[toks], o["out"], "out", TOL_NVFP4)
+
+
+@pytest.mark.parametrize("T,E,k", [(0, 16, 8), (1, 4, 2), (300, 260, 3)])
+def test_route_edge_cases(T, E, k):
+    """Routing with no tokens (no workspace needed: all offsets zero), one
+    token, and more than 256 experts (the expert-total scan runs in two
+    passes), with and without the shared-expert group: bit-exact against
+    the oracle's stable counting sort."""
+    rng = np.random.Generator(np.random.PCG64(50 + T))
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32) \
+        if T else np.zeros((0, k), np.int32)
+    for shared in (False, True):
+        off, src, tok, slot = pqm.moe_route(dev(ids), E, shared_expert=shared)
+        torch.cuda.synchronize()
+        w_off, w_src, w_slot = oracle.route(ids, E, shared_expert=shared)
+        assert np.array_equal(host(off), w_off)
+        assert np.array_equal(host(src), w_src)
+        assert np.array_equal(host(tok), w_src // k if not shared else
+                              np.where(w_src < T * k, w_src // k, w_src - T * k))
+        assert np.array_equal(host(slot).reshape(ids.shape), w_slot.reshape(ids.shape))
