@@ -2071,6 +2071,25 @@ __device__ __forceinline__ void np_issue(const NpSrc<TM> &L, int kt, int slot) {
     dma4((128 * i < TM ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
 }
 
+// Loads q0 .. q1-1 of np_issue's sequence (A chunks, B chunks, scale words).
+template <int TM, int Q0, int Q1>
+__device__ __forceinline__ void np_issue_range(const NpSrc<TM> &L, int kt, int slot) {
+  using C = Np<TM>;
+  const uint32_t kb = (uint32_t)kt * 64u, ks = (uint32_t)kt * 8u;
+  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT, sbase = L.sdst + (uint32_t)slot * C::SLOT;
+#pragma unroll
+  for (int q = Q0; q < Q1; ++q) {
+    if (q < C::CA) {
+      dma16(L.Ab + (L.oa[q] + kb), base + q * 4096);
+    } else if (q < C::CA + C::CB) {
+      dma16(L.Bb + (L.ob[q - C::CA] + kb), base + TM * 64 + (q - C::CA) * 4096);
+    } else {
+      const int i = q - C::CA - C::CB;
+      dma4((128 * i < TM ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
+    }
+  }
+}
+
 struct NpLane {
   int a0, a1, b0, b1;  // chunk offsets (2h, 2h+1) of the first A / B row
   int sa, sb;          // scale-word offsets of the first A / B row
@@ -2201,15 +2220,21 @@ __device__ __forceinline__ void np_mfmas(const NpDec<TM> &X,
 // 0.  So one set of raw registers serves two steps, and the registers saved
 // hold the second decoded sub-step.
 template <int TM>
-__device__ __forceinline__ void np_step(const uint8_t *lds, const NpLane &o, int nslot,
+__device__ __forceinline__ void np_step(const NpSrc<TM> &L, int rk, int slot,
+                                        const uint8_t *lds, const NpLane &o, int nslot,
                                         v16f (&acc)[Np<TM>::FI][Np<TM>::FJ], NpHalf<TM> &R0,
                                         NpHalf<TM> &R1, NpWords<TM> &W, NpScales<TM> &S,
                                         NpDec<TM> &X, NpDec<TM> &Y) {
+  constexpr int NQ = Np<TM>::OPS, H1 = (NQ + 1) / 2;
   np_dec<TM, 1>(R0, S, Y);                 // s = 1 (block 0)
   np_mfmas<TM>(X, acc);                    // s = 0
+  // the refill of `slot` with step rk, in two halves issued while the last
+  // MFMAs of sub-steps 0 and 1 run
+  np_issue_range<TM, 0, H1>(L, rk, slot);
   np_scales<TM, 1>(W, S);
   np_dec<TM, 2>(R0, S, X);                 // s = 2 (block 1)
   np_mfmas<TM>(Y, acc);                    // s = 1
+  np_issue_range<TM, H1, NQ>(L, rk, slot);
   np_dec<TM, 3>(R0, S, Y);                 // s = 3
   np_mfmas<TM>(X, acc);                    // s = 2
   np_scales<TM, 2>(W, S);
@@ -2367,12 +2392,10 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
     vm_wait<C::OPS>();
     lgkm_wait0();
     __builtin_amdgcn_s_barrier();
-    np_issue<TM>(L, min(kt + C::NSLOT, nk - 1), slot);
-    __builtin_amdgcn_sched_barrier(0);
     const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;
     // past the last step the reads take the slot's repeated last step (in
     // bounds; decoded, never multiplied)
-    np_step<TM>(lds, o, nslot, acc, R0, R1, W, S, X, Y);
+    np_step<TM>(L, min(kt + C::NSLOT, nk - 1), slot, lds, o, nslot, acc, R0, R1, W, S, X, Y);
     slot = nslot;
   }
   vm_wait<0>();
