@@ -2037,17 +2037,19 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(
 // exhaustively on gfx950) and one packed f16 multiply by M; q s_b has at most
 // 6 significant bits in [2^-10, 2688], exact in f16.  The outer scales
 // multiply the binary32 accumulator in the epilogue as in k_gemm_nvfp4.
+// Tile code TM: 128 or 256 rows by 256 columns, or 1128 = 128 rows by 512
+// columns (waves 64 x 256: fewer fragment decodes per MFMA than 64 x 128).
 template <int TM>
 struct Np {
-  static constexpr int TN = 256, ROWS = TM + TN;
+  static constexpr int TMR = TM % 1000, TN = 256 * (1 + TM / 1000), ROWS = TMR + TN;
   static constexpr int SC = ROWS * 64;        // scale area offset in a slot
   static constexpr int SLOT = ROWS * 72;
   static constexpr int NSLOT = 3;  // 4 slots measured no faster
   static constexpr int LDS = NSLOT * SLOT;
-  static constexpr int CA = TM / 64, CB = TN / 64;  // 16-byte data chunks per lane
-  static constexpr int NS = ROWS / 128;             // 4-byte scale loads per lane
+  static constexpr int CA = TMR / 64, CB = TN / 64;  // 16-byte data chunks per lane
+  static constexpr int NS = ROWS / 128;              // 4-byte scale loads per lane
   static constexpr int OPS = CA + CB + NS;
-  static constexpr int FI = TM / 64, FJ = 4;
+  static constexpr int FI = TMR / 64, FJ = TN / 64;
 };
 
 template <int TM>
@@ -2065,10 +2067,10 @@ __device__ __forceinline__ void np_issue(const NpSrc<TM> &L, int kt, int slot) {
 #pragma unroll
   for (int i = 0; i < C::CA; ++i) dma16(L.Ab + (L.oa[i] + kb), base + i * 4096);
 #pragma unroll
-  for (int i = 0; i < C::CB; ++i) dma16(L.Bb + (L.ob[i] + kb), base + TM * 64 + i * 4096);
+  for (int i = 0; i < C::CB; ++i) dma16(L.Bb + (L.ob[i] + kb), base + C::TMR * 64 + i * 4096);
 #pragma unroll
   for (int i = 0; i < C::NS; ++i)  // dwords 256 i + tid: rows 128 i .. (A rows first)
-    dma4((128 * i < TM ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
+    dma4((128 * i < C::TMR ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
 }
 
 // Loads q0 .. q1-1 of np_issue's sequence (A chunks, B chunks, scale words).
@@ -2082,10 +2084,10 @@ __device__ __forceinline__ void np_issue_range(const NpSrc<TM> &L, int kt, int s
     if (q < C::CA) {
       dma16(L.Ab + (L.oa[q] + kb), base + q * 4096);
     } else if (q < C::CA + C::CB) {
-      dma16(L.Bb + (L.ob[q - C::CA] + kb), base + TM * 64 + (q - C::CA) * 4096);
+      dma16(L.Bb + (L.ob[q - C::CA] + kb), base + C::TMR * 64 + (q - C::CA) * 4096);
     } else {
       const int i = q - C::CA - C::CB;
-      dma4((128 * i < TM ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
+      dma4((128 * i < C::TMR ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
     }
   }
 }
@@ -2326,7 +2328,7 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
   const uint32_t KD = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);  // row bytes of data / scales
-  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)TM);
+  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)C::TMR);
   const int rows_b = (int)min(N - ti.n0, (int64_t)C::TN);
   NpSrc<TM> L;
   L.Ab = A + ti.row0 * (int64_t)KD;
@@ -2348,18 +2350,18 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
 #pragma unroll
   for (int i = 0; i < C::NS; ++i) {
     const int d = tid + 256 * i, r = d >> 1, half = d & 1;
-    L.os[i] = r < TM ? (uint32_t)min(r, rows_a - 1) * KS + 4u * half
-                     : (uint32_t)min(r - TM, rows_b - 1) * KS + 4u * half;
+    L.os[i] = r < C::TMR ? (uint32_t)min(r, rows_a - 1) * KS + 4u * half
+                          : (uint32_t)min(r - C::TMR, rows_b - 1) * KS + 4u * half;
   }
   NpLane o;
   {
-    const int ra = wm * (TM / 2) + r32, rb = wn * 128 + r32;
+    const int ra = wm * (C::TMR / 2) + r32, rb = wn * (C::TN / 2) + r32;
     o.a0 = mx3_off(ra, 2 * h);
     o.a1 = mx3_off(ra, 2 * h + 1);
-    o.b0 = TM * 64 + mx3_off(rb, 2 * h);
-    o.b1 = TM * 64 + mx3_off(rb, 2 * h + 1);
+    o.b0 = C::TMR * 64 + mx3_off(rb, 2 * h);
+    o.b1 = C::TMR * 64 + mx3_off(rb, 2 * h + 1);
     o.sa = C::SC + ra * 8 + 4 * h;
-    o.sb = C::SC + (TM + rb) * 8 + 4 * h;
+    o.sb = C::SC + (C::TMR + rb) * 8 + 4 * h;
   }
   v16f acc[FI][FJ];
 #pragma unroll
@@ -2403,8 +2405,8 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
   for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < FJ; ++j)
-      np_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (TM / 2) + 32 * i,
-                        wn * 128 + 32 * j, Ao, ab);
+      np_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (C::TMR / 2) + 32 * i,
+                        wn * (C::TN / 2) + 32 * j, Ao, ab);
 }
 
 // Tiles as k_gemm_mxfp8_pipe; K % 256 == 0.
@@ -2430,6 +2432,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_pipe(
     np_tile<OUT_F32, 128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
   else
     np_tile<OUT_F32, 256>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+}
+
+// 128 x 512 tiles (tile code 1128) for experts of few rows each: a wave
+// holds 64 x 256 outputs, so a sub-step decodes 2 + 8 fragments for 16 MFMAs
+// instead of 2 + 4 for 8.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const float *__restrict__ Ao, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    void *__restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Np<1128>::LDS];
+  __shared__ float ab[512];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<512, 128>(offsets, G, ntn, ti, sh)) return;
+  for (int c = threadIdx.x; c < 512; c += 256) {  // alpha_b(n) = Bo[(g N + n) / b_rps]
+    const int64_t col = ti.n0 + c;
+    ab[c] = col < N ? Bo[(ti.g * N + col) / b_rps] : 0.0f;
+  }
+  __syncthreads();
+  np_tile<OUT_F32, 1128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
 }
 
 // ------------------------------------------------------------------ launch
@@ -2589,6 +2614,19 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
         hipLaunchKernelGGL((k_gemm_bf16_rows<true, false>), grid, dim3(256), 0, st, A, B,
                            offsets, G, N, K, ntn, out);
     }
+    return hipGetLastError();
+  }
+  if (fmt == 2 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0 &&
+      N >= 512 && M <= 256 * G) {  // experts of 256 rows or fewer on average
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    const int64_t ntn_w = cdiv(N, 512);
+    const dim3 grid_w((unsigned)(cdiv((cdiv(M, 128) + G) * ntn_w, 8) * 8));
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_nvfp4_wide<true>, grid_w, dim3(256), 0, st, A, a_scale, a_outer, B,
+                         b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_w, out);
+    else
+      hipLaunchKernelGGL(k_gemm_nvfp4_wide<false>, grid_w, dim3(256), 0, st, A, a_scale, a_outer,
+                         B, b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_w, out);
     return hipGetLastError();
   }
   if (fmt == 2 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0) {
