@@ -253,6 +253,10 @@ pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q,
  * N % 8 == 0 (BF16); BF16 WGRAD needs N % 8 == 0 and K % 8 == 0; NVFP4 and
  * block FP8 are FPROP only (PQM_ERR_ENUM otherwise).  No workspace is needed today:
  * pass NULL / 0 (the arguments keep the ABI stable).
+ * An empty contraction (K == 0) makes FPROP / DGRAD write zeros to rows
+ * 0 .. offsets[G]-1 and read no operand; operand, scale and outer-scale
+ * pointers are required (non-NULL) only when M_total, N and K are all
+ * positive, and out only when Y has elements.
  */
 pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,
                                 const void *a, const uint8_t *a_scale,
@@ -360,7 +364,9 @@ pqm_status pqm_moe_pad_rows(const void *src, int64_t src_rows, int64_t row_bytes
  * assignment, i.e. src_row from pqm_moe_route; with a shared expert prob
  * holds tokens*k + tokens entries, the last tokens of them 1.0; src may be
  * NULL to index prob by m).  Binary32 math with the hardware exponential
- * and reciprocal (about 1 ulp each before the bf16 rounding).
+ * and reciprocal (about 1 ulp each before the bf16 rounding); for g <= -64
+ * the value is formed as (g u p) e^g with power-of-two range scaling, so
+ * that neither e^-g nor e^g leaves the binary32 normal range.
  * d bf16 [rows, inter]; inter % 8 == 0.
  */
 pqm_status pqm_swiglu_prob(const uint16_t *c, const float *prob, const int32_t *src,

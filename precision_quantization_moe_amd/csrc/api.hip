@@ -169,11 +169,15 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
   if (fmt == PQM_FMT_NVFP4 && (b_rows_per_scale < 1 || (G * N) % b_rows_per_scale))
     return PQM_ERR_SHAPE;
   if (G == 0) return PQM_OK;
-  if (!offsets || !out) return PQM_ERR_NULL;
-  if (M_total > 0 && (!a || !b)) return PQM_ERR_NULL;
-  if ((fmt == PQM_FMT_MXFP8 || fmt == PQM_FMT_NVFP4) && (!a_scale || !b_scale))
+  // operands are read only when the contraction is non-empty; the output is
+  // written only when it has elements (K = 0 clears the routed rows)
+  const bool reads = M_total > 0 && N > 0 && K > 0;
+  const bool writes = kind == PQM_GEMM_WGRAD ? (N > 0 && K > 0) : (M_total > 0 && N > 0);
+  if (!offsets || (writes && !out)) return PQM_ERR_NULL;
+  if (reads && (!a || !b)) return PQM_ERR_NULL;
+  if (reads && (fmt == PQM_FMT_MXFP8 || fmt == PQM_FMT_NVFP4) && (!a_scale || !b_scale))
     return PQM_ERR_NULL;
-  if ((fmt == PQM_FMT_NVFP4 || fmt == PQM_FMT_FP8_BLOCK) && (!a_outer || !b_outer))
+  if (reads && (fmt == PQM_FMT_NVFP4 || fmt == PQM_FMT_FP8_BLOCK) && (!a_outer || !b_outer))
     return PQM_ERR_NULL;
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(offsets, 8))
     return PQM_ERR_ALIGN;

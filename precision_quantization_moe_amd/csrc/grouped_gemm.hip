@@ -653,8 +653,8 @@ __device__ __forceinline__ void swiglu_store(const v16f &a0, const v16f &a1,
         const uint32_t gw = pk_bf16_rne(acc[8 * gp + e], acc[8 * gp + e + 1]);
         const uint32_t uw = pk_bf16_rne(acc[8 * gp + 4 + e], acc[8 * gp + 4 + e + 1]);
         dw[4 * jo + 2 * gp + e2] =
-            pk_bf16_rne(silu_f32(bf16_lo_f32(gw)) * bf16_lo_f32(uw) * pr,
-                        silu_f32(bf16_hi_f32(gw)) * bf16_hi_f32(uw) * pr);
+            pk_bf16_rne(swiglu_f32(bf16_lo_f32(gw), bf16_lo_f32(uw), pr),
+                        swiglu_f32(bf16_hi_f32(gw), bf16_hi_f32(uw), pr));
       }
   }
   // block maximum over the 32 D columns: this lane's 16, then the other half
@@ -2459,6 +2459,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
 
 // ------------------------------------------------------------------ launch
 
+// K = 0: the product over an empty contraction is zero, so rows 0 ..
+// offsets[G]-1 of Y [M, N] (element size esize) are cleared and nothing is
+// read.  The pipelined kernels assume at least one contraction step; this
+// keeps every K = 0 call away from them.
+__global__ __launch_bounds__(256) void k_zero_rows(const int64_t *__restrict__ offsets, int64_t G,
+                                                   int64_t N, int esize, void *__restrict__ out) {
+  const int64_t bytes = offsets[G] * N * esize;  // a multiple of 2; out 16-byte aligned
+  uint16_t *o = static_cast<uint16_t *>(out);
+  const int64_t n = bytes / 2;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    o[i] = 0;
+}
+
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *a_scale,
@@ -2468,6 +2482,14 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
                                int64_t K, void *out, int out_fp32, hipStream_t st) {
   if (G == 0 || N == 0) return hipSuccess;
   const int64_t U32 = (int64_t)1 << 32;  // the pipelined kernels' per-panel byte offsets
+  if (K == 0 && kind != 2) {  // FPROP / DGRAD over an empty contraction: Y = 0
+    if (M == 0) return hipSuccess;
+    const int64_t n = M * N / 2 + 1;
+    const unsigned grid = (unsigned)min(cdiv(n, 256), (int64_t)8192);
+    hipLaunchKernelGGL(k_zero_rows, dim3(grid), dim3(256), 0, st, offsets, G, N,
+                       out_fp32 ? 4 : 2, out);
+    return hipGetLastError();
+  }
   if (fmt == 3) {  // block-scaled FP8 forward
     if (M == 0) return hipSuccess;
     if (K % 128 || K / 128 > FB_MAX_KB || N % 128) return hipErrorNotSupported;
@@ -2616,7 +2638,7 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     }
     return hipGetLastError();
   }
-  if (fmt == 2 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0 &&
+  if (fmt == 2 && K > 0 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0 &&
       N >= 512 && M <= 256 * G) {  // experts of 256 rows or fewer on average
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_w = cdiv(N, 512);
@@ -2629,7 +2651,7 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
                          B, b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_w, out);
     return hipGetLastError();
   }
-  if (fmt == 2 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0) {
+  if (fmt == 2 && K > 0 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_b = cdiv(N, 256);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));

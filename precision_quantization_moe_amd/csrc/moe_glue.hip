@@ -227,8 +227,8 @@ __device__ __forceinline__ void swiglu8(const uint16_t *__restrict__ c,
   const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k)
-    o[k] = pk_bf16_rne(silu_f32(bf16_lo_f32(gw[k])) * bf16_lo_f32(uw[k]) * p,
-                       silu_f32(bf16_hi_f32(gw[k])) * bf16_hi_f32(uw[k]) * p);
+    o[k] = pk_bf16_rne(swiglu_f32(bf16_lo_f32(gw[k]), bf16_lo_f32(uw[k]), p),
+                       swiglu_f32(bf16_hi_f32(gw[k]), bf16_hi_f32(uw[k]), p));
 }
 
 // d = swiglu8 per lane (16-byte bf16 loads and stores).

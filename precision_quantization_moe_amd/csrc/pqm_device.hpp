@@ -30,11 +30,17 @@ __device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// silu(g) = g / (1 + e^-g) with the hardware exponential and reciprocal
-// (about 1 ulp each): the SwiGLU activation of every kernel that computes it,
-// so that the fused and the separate passes produce the same bits.
-__device__ __forceinline__ float silu_f32(float g) {
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+// The weighted SwiGLU value silu(g) u p, silu(g) = g / (1 + e^-g), with the
+// hardware exponential and reciprocal (about 1 ulp each): the activation of
+// every kernel that computes it, so that the fused and the separate passes
+// produce the same bits.  For g <= -64, e^-g would overflow binary32 (and e^g
+// leave its normal range), so there silu(g) u p = (g u p) e^g is formed with
+// e^g = 2^(g log2(e) + 64) 2^-64: both factors stay normal down to g = -131,
+// where the true value is far below the smallest bf16 subnormal.
+__device__ __forceinline__ float swiglu_f32(float g, float u, float p) {
+  if (g > -64.0f) return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u * p;
+  const float t = __builtin_amdgcn_exp2f(g * 1.44269504088896341f + 64.0f);
+  return ((g * u * p) * t) * 0x1p-64f;
 }
 
 // Round a binary32 value to bf16 bits, nearest even (finite or inf input).

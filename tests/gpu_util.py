@@ -40,3 +40,15 @@ def assert_bytes_equal(got: np.ndarray, want: np.ndarray, what: str):
     assert got.shape == want.shape, (what, got.shape, want.shape)
     if not np.array_equal(got, want):
         raise AssertionError(f"{what}: {first_mismatch(got, want)}")
+
+
+def gpu_normal_bf16(rows: int, cols: int, std: float, seed: int) -> torch.Tensor:
+    """bf16 [rows, cols] N(0, std^2) drawn on the GPU from a seeded torch
+    generator (for weight sets too large to draw on the host quickly)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    step = 1 << 16
+    for r in range(0, rows, step):
+        n = min(step, rows - r)
+        out[r:r + n] = (torch.randn(n, cols, generator=g, device="cuda") * std).to(torch.bfloat16)
+    return out

@@ -446,8 +446,10 @@ def _nvfp4_case(sizes, N, K, seed, brps=None):
     ([0, 37, 128, 1, 300], 192, 320, None),
     ([64, 0, 200], 128, 336, None),           # K % 64 == 16: remainder step
     ([100, 60], 256, 512, 128),               # gate and up scaled separately
-    ([300, 0, 513, 129, 64], 520, 768, None),  # 256- and 128-row tiles, ragged N
+    ([300, 0, 513, 129, 64], 520, 768, None),  # 128 x 512 tiles (<= 256 rows per expert on average)
     ([300, 0, 513, 129, 64], 520, 512, 260),   # scale boundaries inside 8-column runs
+    ([600, 0, 513, 129], 520, 768, None),      # > 256 rows per expert on average: 256- and 128-row tiles
+    ([300, 0, 513, 129, 64], 384, 512, None),  # N < 512: 256- and 128-row tiles
 ])
 def test_nvfp4_fprop_ragged(case):
     sizes, N, K, brps = case
@@ -551,3 +553,216 @@ def test_bf16_output_is_rne_of_binary32_output(fmt, sizes, N, K):
     print(f"[gemm] {fmt} K={K} bf16 output vs RNE(binary32 output): {bad} mismatches "
           f"of {got.size}", flush=True)
     assert bad == 0
+
+
+# ------------------------------------------------- degenerate and large-G
+
+_SENTINEL = 0x7F
+
+
+@pytest.mark.parametrize("fmt,kind,N", [
+    (pqm.FMT_MXFP8, pqm.GEMM_FPROP, 520), (pqm.FMT_MXFP8, pqm.GEMM_DGRAD, 520),
+    (pqm.FMT_NVFP4, pqm.GEMM_FPROP, 520), (pqm.FMT_NVFP4, pqm.GEMM_FPROP, 384),
+    (pqm.FMT_FP8_BLOCK, pqm.GEMM_FPROP, 512), (pqm.FMT_BF16, pqm.GEMM_FPROP, 520),
+    (pqm.FMT_BF16, pqm.GEMM_DGRAD, 520)])
+@pytest.mark.parametrize("out_dtype", [pqm.OUT_FP32, pqm.OUT_BF16])
+def test_empty_contraction_writes_zero_rows(fmt, kind, N, out_dtype):
+    """K = 0: the sum over an empty contraction is 0 for every routed row
+    (rows 0 .. offsets[G]-1), rows past offsets[G] are left untouched, and
+    no operand is read (the operands are empty)."""
+    sizes, M = [3, 0, 700], 710                       # rows 703 .. 709 are not routed
+    off = dev(_offsets(sizes))
+    dt = torch.float32 if out_dtype == pqm.OUT_FP32 else torch.bfloat16
+    out = torch.empty((M, N), dtype=dt, device="cuda")
+    out.view(torch.uint8).fill_(_SENTINEL)
+    a = torch.empty((M, 0), dtype=torch.bfloat16 if fmt == pqm.FMT_BF16 else torch.uint8,
+                    device="cuda")
+    b = torch.empty((len(sizes) * N, 0), dtype=a.dtype, device="cuda")
+    print(f"[gemm] K=0 fmt={fmt} kind={kind} N={N} out={out_dtype}", flush=True)
+    pqm.moe_grouped_gemm(fmt, kind, a, b, off, N, 0, b_rows_per_scale=N,
+                         out_dtype=out_dtype, out=out)
+    torch.cuda.synchronize()
+    raw = host(out.view(torch.uint8)).reshape(M, -1)
+    assert not raw[:703].any()
+    assert (raw[703:] == _SENTINEL).all()
+
+
+def _many_small_groups(G, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    sizes = rng.choice([0, 0, 1, 2, 5, 33], size=G).tolist()
+    sizes[G // 2] = 300                                # one expert with several row tiles
+    return sizes
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+def test_more_than_512_groups(fmt):
+    """About 600 mostly empty or tiny experts: the tile lookup's general
+    path (more groups than one round of offset loads covers)."""
+    sizes = _many_small_groups(600, seed=91)
+    if fmt == "mxfp8":
+        y, want = _mxfp8_case(sizes, 256, 256, seed=92)
+    else:
+        y, want = _nvfp4_case(sizes, 512, 256, seed=93)
+    check_rows(host(y), want, f"{fmt} G=600 ({sum(sizes)} rows)")
+
+
+# ------------------------------------------------------------ determinism
+
+def _det_cases():
+    sizes = [300, 0, 513, 129, 64]
+    return [("mxfp8", 1536, 2048), ("mxfp8", 2048, 768), ("mxfp8_dgrad", 768, 2048),
+            ("mxfp8_wgrad", 512, 768), ("nvfp4", 1024, 1024), ("nvfp4", 384, 512),
+            ("bf16", 520, 384), ("bf16_dgrad", 520, 384), ("bf16_wgrad", 520, 384),
+            ("fp8b", 512, 1024)], sizes
+
+
+@pytest.mark.parametrize("case", _det_cases()[0], ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}")
+def test_grouped_gemm_is_deterministic(case):
+    """Two calls on the same operands give bitwise identical outputs (fixed
+    reduction order, no split-K atomics: the deterministic mode of [MT]
+    4.5), for every kernel family the dispatcher picks."""
+    name, N, K = case
+    sizes = _det_cases()[1]
+    G, M = len(sizes), sum(sizes)
+    pad = name == "mxfp8_wgrad"           # column-wise copies: 32-row expert blocks
+    off = dev(_offsets([-(-s // 32) * 32 for s in sizes] if pad else sizes))
+    Mp = int(host(off)[-1])
+    x = dev_bf16(wl.activations(max(M, Mp), max(K, N), seed=95))
+    w = dev_bf16(wl.normal_bf16((G * max(N, K), max(K, N)), std=0.02, seed=96))
+    if name == "mxfp8":
+        qa, sa, _, _ = pqm.quantize_mxfp8(x[:M, :K].contiguous(), colwise=False)
+        qb, sb, _, _ = pqm.quantize_mxfp8(w[:G * N, :K].contiguous(), colwise=False)
+        call = lambda: pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, qb, off, N, K,
+                                            a_scale=sa, b_scale=sb, out_dtype=pqm.OUT_BF16)
+    elif name == "mxfp8_dgrad":
+        qa, sa, _, _ = pqm.quantize_mxfp8(x[:M, :K].contiguous(), colwise=False)
+        _, _, qT, sT = pqm.quantize_mxfp8(w[:G * K, :N].contiguous(), rowwise=False)
+        call = lambda: pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_DGRAD, qa, qT, off, N, K,
+                                            a_scale=sa, b_scale=sT)
+    elif name == "mxfp8_wgrad":
+        _, _, aT, asT = pqm.quantize_mxfp8(x[:Mp, :N].contiguous(), rowwise=False)
+        _, _, bT, bsT = pqm.quantize_mxfp8(x[:Mp, :K].contiguous() * 0.5, rowwise=False)
+        call = lambda: pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_WGRAD, aT, bT, off, N, K,
+                                            a_scale=asT, b_scale=bsT)
+    elif name == "nvfp4":
+        qa, sa, ga = pqm.quantize_nvfp4_per_token(x[:M, :K].contiguous())
+        qb, sb, gb = pqm.quantize_nvfp4_per_token(w[:G * N, :K].contiguous(), rows_per_scale=N)
+        call = lambda: pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, qa, qb, off, N, K,
+                                            a_scale=sa, a_outer=ga, b_scale=sb, b_outer=gb,
+                                            b_rows_per_scale=N, out_dtype=pqm.OUT_BF16)
+    elif name == "fp8b":
+        qa, sa = pqm.quantize_fp8_block(x[:M, :K].contiguous(), 1)
+        qb, sb = pqm.quantize_fp8_block(w[:G * N, :K].contiguous(), 128)
+        call = lambda: pqm.moe_grouped_gemm(pqm.FMT_FP8_BLOCK, pqm.GEMM_FPROP, qa, qb, off, N, K,
+                                            a_outer=sa, b_outer=sb)
+    elif name == "bf16":
+        a, b = x[:M, :K].contiguous(), w[:G * N, :K].contiguous()
+        call = lambda: pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_FPROP, a, b, off, N, K)
+    elif name == "bf16_dgrad":
+        a, b = x[:M, :K].contiguous(), w[:G * K, :N].contiguous()
+        call = lambda: pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_DGRAD, a, b, off, N, K)
+    else:
+        a, b = x[:M, :N].contiguous(), x[:M, :K].contiguous() * 0.5
+        call = lambda: pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_WGRAD, a, b, off, N, K)
+    print(f"[gemm] determinism {name} N={N} K={K}", flush=True)
+    y1 = call()
+    y2 = call()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.uint8), y2.view(torch.uint8)), name
+
+
+# ------------------------------------------- full-size sampled: DeepSeek FC2
+
+def test_nvfp4_deepseek_down_full_sampled():
+    """DeepSeek-V3 down projection at full size: 32768 routed rows (half
+    uniform, half Zipf over 256 experts) plus the shared expert's 4096 rows,
+    N = 7168, K = 2048, weights [257, 7168, 2048] N(0, 0.01) drawn on the
+    GPU, one outer scale per expert tensor (b_rows_per_scale = 7168), bf16
+    output as in the layer.  Sampled rows of sampled experts against the
+    binary64 product (bar + one bf16 rounding)."""
+    T, E, k, H, I = 4096, 256, 8, 7168, 2048
+    ids = wl.uniform_plus_zipf_routing(T, E, k)
+    off_r, _, _ = oracle.route(ids, E)
+    off = np.concatenate([off_r, [T * k + T]]).astype(np.int64)
+    M = T * k + T
+    d = wl.activations(M, I, seed=24)
+    gen = torch.Generator(device="cuda").manual_seed(4321)
+    w = (torch.randn((E + 1) * H, I, generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+    qa, sa, ga = pqm.quantize_nvfp4_per_token(dev_bf16(d))
+    qb, sb, gb = pqm.quantize_nvfp4_per_token(w, rows_per_scale=H)
+    y = pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, qa, qb, dev(off), H, I,
+                             a_scale=sa, a_outer=ga, b_scale=sb, b_outer=gb,
+                             b_rows_per_scale=H, out_dtype=pqm.OUT_BF16)
+    torch.cuda.synchronize()
+    yh = oracle.bf16_to_f64(host_u16(y))
+    rng = np.random.Generator(np.random.PCG64(25))
+    experts = sorted(set(rng.choice(E, 5, replace=False).tolist()) | {0, E - 1, E})
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 4)]))
+        we = host_u16(w[e * H:(e + 1) * H])
+        ra, rsa, rga = oracle.quantize_nvfp4(d[rows])
+        rb, rsb, rgb = oracle.quantize_nvfp4(we, rows_per_group=H)
+        want = oracle.decode_nvfp4(ra, rsa, rga) @ oracle.decode_nvfp4(rb, rsb, rgb, H).T
+        r = rel_l2_rows(yh[rows], want)
+        print(f"[gemm] deepseek fc2 expert {e} ({hi - lo} rows): max row rel-L2 {r.max():.3e}",
+              flush=True)
+        assert r.max() <= TOL + 2.0 ** -9, (e, float(r.max()))
+    del w, qb
+
+
+# ------------------------------- full-size sampled: Qwen3 BF16 backward
+
+def _q3_bwd_setup():
+    T, E, k, H, I = 8192, 128, 8, 2048, 768
+    ids = wl.zipf_routing(T, E, k)
+    off, _, _ = oracle.route(ids, E)
+    M = T * k
+    gen = torch.Generator(device="cuda").manual_seed(555)
+    rnd = lambda *shape, std=1.0: (torch.randn(*shape, generator=gen, device="cuda")
+                                   * std).to(torch.bfloat16)
+    return T, E, k, H, I, off, M, rnd
+
+
+@pytest.mark.parametrize("proj", ["fc2", "fc1"])
+def test_bf16_backward_qwen3_full_sampled(proj):
+    """The BF16 backward GEMMs at the Qwen3-30B-A3B layer shapes the
+    benchmark runs (65536 routed rows, Zipf(1.1) loads, experts up to ~7400
+    rows): dgrad (bf16 output) on sampled rows and wgrad (binary32 output)
+    on sampled output rows of sampled experts, against binary64 sums."""
+    T, E, k, H, I, off, M, rnd = _q3_bwd_setup()
+    if proj == "fc2":      # dD = dY W2 (W2 [E, H, I]); dW2 = dY^T D
+        Nd, Kd = I, H
+    else:                  # dX = dC W1 (W1 [E, 2I, H]); dW1 = dC^T X
+        Nd, Kd = H, 2 * I
+    dy = rnd(M, Kd)
+    w = rnd(E * Kd, Nd, std=0.02)
+    xs = rnd(M, Nd)
+    offd = dev(off)
+    dx = pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_DGRAD, dy, w, offd, Nd, Kd,
+                              out_dtype=pqm.OUT_BF16)
+    dw = pqm.moe_grouped_gemm(pqm.FMT_BF16, pqm.GEMM_WGRAD, dy, xs, offd, Kd, Nd,
+                              out_dtype=pqm.OUT_FP32)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(26))
+    sizes = np.diff(off)
+    experts = sorted({int(np.argmax(sizes)), int(np.argmin(sizes)), 0, E - 1}
+                     | set(rng.choice(E, 3, replace=False).tolist()))
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 4)]))
+        we = oracle.bf16_to_f64(host_u16(w[e * Kd:(e + 1) * Kd]))          # [Kd, Nd]
+        ri = torch.from_numpy(rows).cuda()
+        want = oracle.bf16_to_f64(host_u16(dy[ri])) @ we
+        r = rel_l2_rows(oracle.bf16_to_f64(host_u16(dx[ri])), want)
+        print(f"[gemm] qwen3 {proj} bf16 dgrad expert {e} ({hi - lo} rows): "
+              f"max row rel-L2 {r.max():.3e}", flush=True)
+        assert r.max() <= TOL + 2.0 ** -9, (e, float(r.max()))
+        outs = np.unique(np.concatenate([[0, Kd - 1], rng.integers(0, Kd, 6)]))
+        dyg = oracle.bf16_to_f64(host_u16(dy[lo:hi]))
+        xg = oracle.bf16_to_f64(host_u16(xs[lo:hi]))
+        want_w = dyg[:, outs].T @ xg                                      # [len(outs), Nd]
+        got_w = host(dw[e])[outs]
+        check_rows(got_w, want_w, f"qwen3 {proj} bf16 wgrad expert {e} ({hi - lo} rows)")

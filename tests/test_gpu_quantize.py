@@ -11,7 +11,7 @@ import torch
 import oracle
 import precision_quantization_moe_amd as pqm
 from precision_quantization_moe_amd import workloads as wl
-from gpu_util import (assert_bytes_equal, dev, dev_bf16, host, host_u16,
+from gpu_util import (assert_bytes_equal, dev, dev_bf16, gpu_normal_bf16, host, host_u16,
                       requires_gpu)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -192,6 +192,33 @@ def test_nvfp4_joint_gate_up_weights_full():
     rq, rsb, rsg = oracle.quantize_nvfp4(w[:2].reshape(-1, H), rows_per_group=R2 // 2)
     assert_bytes_equal(host(q2), rq, "separate q")
     assert_bytes_equal(host(sg2).view(np.uint32), rsg.view(np.uint32), "separate sg")
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_nvfp4_deepseek_expert_weights_full(which):
+    """DeepSeek-V3 expert weights at full size, 256 routed + 1 shared expert
+    drawn on the GPU (N(0, 0.01)): fused [gate; up] [4096 x 7168] with one
+    joint outer scale per expert, and down [7168 x 2048] with one scale per
+    expert tensor (the group path with 8 blocks per lane and one or two
+    groups per chunk).  Every expert's s_g = A / 2688 (A = the tensor's
+    exact maximum) and sampled experts' bytes against the oracle."""
+    E, H, I = 257, 7168, 2048
+    rows, cols = (2 * I, H) if which == "gate_up" else (H, I)
+    w = gpu_normal_bf16(E * rows, cols, 0.01, seed=401 if which == "gate_up" else 402)
+    q, sb, sg = pqm.quantize_nvfp4_per_token(w, rows_per_scale=rows)
+    amax = w.view(E, -1).abs().amax(dim=1).float()
+    torch.cuda.synchronize()
+    print(f"[nvfp4] deepseek {which} weights {E} x [{rows} x {cols}]", flush=True)
+    sgh = host(sg)
+    want_sg = host(amax).astype(np.float32) / np.float32(2688.0)
+    assert_bytes_equal(sgh.view(np.uint32), want_sg.view(np.uint32), which + " every s_g")
+    for e in (0, 131, E - 1):
+        we = host_u16(w[e * rows:(e + 1) * rows])
+        rq, rsb, rsg = oracle.quantize_nvfp4(we, rows_per_group=rows)
+        assert_bytes_equal(host(q[e * rows:(e + 1) * rows]), rq, f"{which} expert {e} q")
+        assert_bytes_equal(host(sb[e * rows:(e + 1) * rows]), rsb, f"{which} expert {e} s_b")
+        assert sgh[e].view(np.uint32) == rsg[0].view(np.uint32)
+    del w, q, sb
 
 
 # ----------------------------------------------------------- dequantize
