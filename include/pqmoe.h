@@ -323,6 +323,29 @@ pqm_status pqm_moe_route(const int32_t *topk_ids, int64_t tokens, int64_t k,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pqm_moe_route without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and the same outputs
+ * as pqm_moe_route, with the (chunk, expert) counts and expert totals kept
+ * in a scratch array of PQM_ROUTE_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends.  The call allocates
+ * and frees nothing.  Requires pqm_moe_route_workspace(tokens, k,
+ * num_experts) <= PQM_ROUTE_NOALLOC_SCRATCH_BYTES, i.e. about
+ * ceil(tokens k / 256) num_experts 4 + num_experts 8 bytes (PQM_ERR_WORKSPACE
+ * otherwise; 65536 tokens x top-8 over 256 experts need 2 MiB, 4096 tokens x
+ * top-8 over 256 experts 130 KiB); other arguments and errors as
+ * pqm_moe_route; PQM_ERR_HIP if the scratch address cannot be obtained.
+ * All calls on one GPU share its scratch array: calls that overlap in time
+ * on one GPU (different streams, or host threads) race and must be
+ * serialized by the caller; calls in stream order are safe.
+ */
+#define PQM_ROUTE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+pqm_status pqm_moe_route_noalloc(const int32_t *topk_ids, int64_t tokens, int64_t k,
+                                 int64_t num_experts, int shared_expert, int64_t *offsets,
+                                 int32_t *src_row, int32_t *token, int32_t *slot,
+                                 hipStream_t stream);
+
+/*
  * Row gather: out row i = src row (index[i] / divisor), rows of row_bytes
  * bytes (quantized data, scale bytes or FP32 token scales).  With
  * index = token from pqm_moe_route (divisor 1) this places each token's

@@ -42,6 +42,7 @@ SIGNATURES = {
                                            I32),
     "pqm_moe_route": ([P, I64, I64, I64, I32, P, P, P, P, P, SZ, P], I32),
     "pqm_moe_route_workspace": ([I64, I64, I64], SZ),
+    "pqm_moe_route_noalloc": ([P, I64, I64, I64, I32, P, P, P, P, P], I32),
     "pqm_moe_gather_rows": ([P, I64, I64, P, I64, I64, P, P], I32),
     "pqm_moe_pad_rows": ([P, I64, I64, P, I64, I64, P, P, I64, P], I32),
     "pqm_swiglu_prob": ([P, P, P, I64, I64, P, P], I32),
@@ -212,6 +213,28 @@ def moe_route(topk_ids: torch.Tensor, num_experts: int, shared_expert: bool = Fa
     _check(L.pqm_moe_route(_ptr(topk_ids), T, k, num_experts, sh, _ptr(offsets), _ptr(src),
                            _ptr(tok), _ptr(slot), _ptr(ws), ws_bytes, _stream(dev)),
            "pqm_moe_route")
+    return offsets, src, tok, slot
+
+
+def moe_route_noalloc(topk_ids: torch.Tensor, num_experts: int, shared_expert: bool = False,
+                      out=None):
+    """moe_route through the entry point that allocates nothing on the
+    device: its scratch is the library's per-GPU array.  `out` may pass the
+    (offsets, src_row, token, slot) tensors preallocated, so that the call
+    itself allocates nothing."""
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    sh = 1 if shared_expert else 0
+    M = T * k + sh * T
+    if out is None:
+        out = (torch.empty((num_experts + 1 + sh,), dtype=torch.int64, device=dev),
+               torch.empty((M,), dtype=torch.int32, device=dev),
+               torch.empty((M,), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev))
+    offsets, src, tok, slot = out
+    _check(lib().pqm_moe_route_noalloc(_ptr(topk_ids), T, k, num_experts, sh, _ptr(offsets),
+                                       _ptr(src), _ptr(tok), _ptr(slot), _stream(dev)),
+           "pqm_moe_route_noalloc")
     return offsets, src, tok, slot
 
 

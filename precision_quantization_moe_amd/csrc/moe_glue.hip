@@ -8,6 +8,9 @@
 #include "pqm_internal.hpp"
 #include "pqmoe.h"
 
+#include <map>
+#include <mutex>
+
 namespace pqm {
 
 constexpr int ROUTE_CHUNK = 256;  // assignments per workgroup (one per thread)
@@ -174,6 +177,31 @@ hipError_t launch_route(const int32_t *ids, int64_t T, int64_t k, int64_t E, int
     hipLaunchKernelGGL(k_route_shared, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, st, n,
                        T, src_row, token);
   return hipGetLastError();
+}
+
+// Routing scratch for callers that cannot allocate (pqm_moe_route_noalloc):
+// one file-scope device array per GPU, holding the (chunk, expert) counts
+// and the expert totals exactly as the caller workspace of pqm_moe_route
+// does.  Every entry is written before it is read, so nothing is cleared
+// between calls.  In host code `route_scratch` names a host-side stand-in,
+// not device memory: kernels get the per-device address that
+// hipGetSymbolAddress returns (route_scratch_ptr).
+static __device__ __align__(256) uint8_t route_scratch[PQM_ROUTE_NOALLOC_SCRATCH_BYTES];
+
+// The device address of this device's route_scratch, looked up once per
+// device with that device current; NULL if the lookup failed.
+static void *route_scratch_ptr() {
+  static std::mutex mu;
+  static std::map<int, void *> addr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) return it->second;
+  void *p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(route_scratch)) != hipSuccess) p = nullptr;
+  if (p) addr[dev] = p;
+  return p;
 }
 
 // out[i] = src[index[i] / divisor], rows of row_bytes bytes.
@@ -446,6 +474,27 @@ pqm_status pqm_moe_route(const int32_t *topk_ids, int64_t tokens, int64_t k,
   if (!al(offsets, 8) || (workspace && !al(workspace, 8))) return PQM_ERR_ALIGN;
   return st_of(pqm::launch_route(topk_ids, tokens, k, num_experts, shared_expert, offsets,
                                  src_row, token, slot, workspace, stream));
+}
+
+pqm_status pqm_moe_route_noalloc(const int32_t *topk_ids, int64_t tokens, int64_t k,
+                                 int64_t num_experts, int shared_expert, int64_t *offsets,
+                                 int32_t *src_row, int32_t *token, int32_t *slot,
+                                 hipStream_t stream) {
+  if (tokens < 0 || k < 1 || num_experts < 1 || num_experts > 4096) return PQM_ERR_SHAPE;
+  if (tokens * (k + 1) > (int64_t)0x7FFFFFFF) return PQM_ERR_SHAPE;
+  if (!offsets) return PQM_ERR_NULL;
+  if (shared_expert != 0 && shared_expert != 1) return PQM_ERR_ENUM;
+  if (tokens > 0 && (!topk_ids || !src_row || !token || !slot)) return PQM_ERR_NULL;
+  if (pqm::route_workspace_bytes(tokens, k, num_experts) > PQM_ROUTE_NOALLOC_SCRATCH_BYTES)
+    return PQM_ERR_WORKSPACE;
+  if (!al(offsets, 8)) return PQM_ERR_ALIGN;
+  void *ws = nullptr;
+  if (pqm::route_workspace_bytes(tokens, k, num_experts) > 0) {
+    ws = pqm::route_scratch_ptr();
+    if (!ws) return PQM_ERR_HIP;
+  }
+  return st_of(pqm::launch_route(topk_ids, tokens, k, num_experts, shared_expert, offsets,
+                                 src_row, token, slot, ws, stream));
 }
 
 pqm_status pqm_moe_gather_rows(const void *src, int64_t src_rows, int64_t row_bytes,

@@ -171,3 +171,19 @@ def test_glue_validation():
     assert g(BAD, *ok[1:]) == 3
     assert L.pqm_moe_combine(A16, A16, None, 4, 0, 16, A16, None) == 2
     assert L.pqm_moe_combine(A16, None, None, 4, 2, 16, A16, None) == 1
+
+
+def test_route_noalloc_validation():
+    """The no-allocation routing entry point rejects inputs whose counts do
+    not fit its fixed scratch array before anything is enqueued."""
+    L = pqm.lib()
+    f = L.pqm_moe_route_noalloc
+    limit = 4 << 20
+    assert L.pqm_moe_route_workspace(65536, 8, 256) <= limit
+    assert L.pqm_moe_route_workspace(1 << 20, 8, 4096) > limit
+    assert f(A16, 1 << 20, 8, 4096, 0, A16, A16, A16, A16, None) == 5
+    assert f(A16, 64, 8, 4097, 0, A16, A16, A16, A16, None) == 2
+    assert f(A16, 64, 8, 16, 2, A16, A16, A16, A16, None) == 4
+    assert f(A16, 64, 8, 16, 0, None, A16, A16, A16, None) == 1
+    assert f(None, 64, 8, 16, 0, A16, A16, A16, A16, None) == 1
+    assert f(A16, 64, 8, 16, 0, BAD, A16, A16, A16, None) == 3
