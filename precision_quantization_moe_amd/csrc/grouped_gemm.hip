@@ -11,10 +11,10 @@
 //
 // MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 consumes E4M3 operands with one
 // E8M0 scale per 32 K-values per row, which is the MXFP8 block layout, so
-// the scales go to the matrix core unchanged.  K % 128 == 0 (K <= 2048) runs
-// the pipelined 256 x 256 kernel (k_gemm_mxfp8_pipe, an expert's last tile
-// of at most 128 rows as 128 x 256); other K the simpler 128 x 128 kernel
-// with register-staged tiles.  Lane layout (verified on the
+// the scales go to the matrix core unchanged.  K % 128 == 0 runs the
+// pipelined 256 x 256 kernel (k_gemm_mxfp8_q: eight waves, 128-byte ring
+// steps, an expert's last tile of at most 128 rows as 128 x 256); other K
+// the simpler 128 x 128 kernel with register-staged tiles.  Lane layout (verified on the
 // hardware): a lane holds row (lane % 32); its bytes 0-15 are K
 // 16*(lane/32) .. +15 of the first 32-block and bytes 16-31 the same offsets
 // in the second block; lane 32*b + r supplies the scale of row r, block b.
@@ -794,131 +794,242 @@ __device__ __forceinline__ void mx3_tile(const uint8_t *__restrict__ A,
   }
 }
 
-// Row tiles of 256 tokens; an expert's last tile holding 128 rows or fewer
-// (the remainder of a ragged expert, or a whole small one) runs as a
-// 128 x 256 tile, which halves its MFMA and operand traffic.
-template <bool OUT_F32>
-__global__ __launch_bounds__(256, 1) void k_gemm_mxfp8_pipe(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
-    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
-    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    int64_t ldb, int64_t bexp, void *__restrict__ out) {
-  static_assert(Mx3<128>::LDS <= Mx3<256>::LDS, "LDS of the half tile");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[Mx3<256>::LDS];
-  __shared__ int64_t sh[4];
-  TileInfo ti;
-  if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
-  if (ti.row_end - ti.row0 <= 128)
-    mx3_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
-  else
-    mx3_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
+__device__ __forceinline__ v8i mw_frag(const uint8_t *p_lo, const uint8_t *p_hi) {
+  const uint4 lo = *reinterpret_cast<const uint4 *>(p_lo);
+  const uint4 hi = *reinterpret_cast<const uint4 *>(p_hi);
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-#ifndef PQM_MX_OCC2_KMAX
-#define PQM_MX_OCC2_KMAX 1024
-#endif
-
-// ------------------------------------------- MXFP8, two workgroups per CU
-// 128 x 256 tiles whose whole state fits twice in one CU (78 KB of LDS, at
-// most 256 registers per lane), so that one workgroup's prologue and output
-// store overlap the other's matrix-core work: with one 256 x 256 tile per
-// CU those phases run serially with the MFMAs.  Waves 2 x 2, each 64 x 128
-// (2 x 4 fragments).  A 3-slot ring of 64-K steps as in the forward kernel
-// above, but each slot also carries the step's scale bytes (two E8M0 bytes
-// per tile row, one 4-byte entry per row; entries 0..127 A rows, 128..383
-// B rows, 384..511 never read), so no scale area is preloaded and any
-// K % 128 == 0 fits.  Operands of step kt are read from LDS during step kt
-// (one fragment set; the other workgroup's MFMAs cover the read latency).
-struct Mo2 {
-  static constexpr int TM = 128, TN = 256, ROWS = TM + TN;
-  static constexpr int OPB = ROWS * 64;    // operand bytes per slot
-  static constexpr int SCB = 512 * 4;      // scale entries per slot
-  static constexpr int SLOT = OPB + SCB;
-  static constexpr int NSLOT = 3;
-  static constexpr int LDS = NSLOT * SLOT;  // 79872 bytes
-  static constexpr int CA = 2, CB = 4, CS = 2, OPS = CA + CB + CS;
-  static constexpr int FI = 2, FJ = 4;
+// ------------------------------- MXFP8, eight waves, 128-byte ring steps
+// The 256 x 256 tile with 8 waves (two per SIMD, each 128 x 64 outputs) and
+// a ring of two slots, each holding one 128-K step: 128 bytes of every tile
+// row (A rows, then B rows) plus one 4-byte word per row with the row's four
+// E8M0 scale bytes of the step.  A load instruction then reads whole
+// 128-byte lines (8 lanes per row, 64 rows per instruction): measured, a CU
+// streams ~107 GB/s that way against ~64 GB/s when each row contributes half
+// a line per step, and the tile needs ~64 GB/s at the matrix core's rate.
+// The scales travel with the data, so nothing is preloaded and any
+// K % 128 == 0 fits.  Rows are 8 chunks of 16 bytes, chunk c of row r stored
+// at c ^ (r % 8).
+// Schedule of step k (slot s = k % 2): the first half (64 K) multiplies the
+// fragments read before it and reads the second half's fragments of slot s;
+// then every wave waits for its loads of step k+1 (slot s ^ 1) and for its
+// LDS reads, and meets the others at the barrier (step k+1 published, slot
+// s no longer read); the second half multiplies, requests step k+2 into
+// slot s and reads step k+1's first-half fragments.  So a step's loads have
+// one full step to arrive.  A lane holds one set of fragments, each
+// replaced right after its last use.
+template <int TM>
+struct Mq {
+  static constexpr int TN = 256, ROWS = TM + TN;
+  static constexpr int DATA = ROWS * 128;     // operand bytes of a slot
+  static constexpr int SLOT = DATA + 2048;    // + scale words (512 entries)
+  static constexpr int NSLOT = 2, LDS = NSLOT * SLOT;
+  static constexpr int CA = TM / 64, CB = TN / 64;  // 16-byte loads per lane per step
+  static constexpr int OPS = CA + CB + 1;           // + one scale word per lane
+  static constexpr int FI = TM / 64, FJ = 2;
 };
-static_assert(2 * (Mo2::LDS + 64) <= 160 * 1024, "two workgroups per CU");
 
+// 16 bytes per lane from global `sbase + voff` (sbase wave-uniform, in
+// scalar registers) into LDS at m0 + 16 * lane.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// 2 bytes per lane from global `src` into the 4-byte LDS entry m0 + 4 * lane.
-__device__ __forceinline__ void dma2(const void *src, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(src), "s"(m0)
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(m0)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
-struct Mo2Src {
-  const uint8_t *Ab, *Bb;
-  uint32_t oa[Mo2::CA], ob[Mo2::CB];  // per-lane operand chunk offsets at step 0
-  const uint8_t *sc[Mo2::CS];         // per-lane scale-byte sources at step 0
-  uint32_t dst;                       // LDS address of slot 0, this wave's operand chunks
-  uint32_t sdst;                      // LDS address of slot 0, this wave's scale entries
-};
-
-__device__ __forceinline__ void mo2_issue(const Mo2Src &L, int kt, int slot) {
-  const uint32_t kb = (uint32_t)kt * 64u, so = (uint32_t)slot * Mo2::SLOT;
-#pragma unroll
-  for (int i = 0; i < Mo2::CA; ++i) dma16(L.Ab + (L.oa[i] + kb), L.dst + so + i * 4096);
-#pragma unroll
-  for (int i = 0; i < Mo2::CB; ++i)
-    dma16(L.Bb + (L.ob[i] + kb), L.dst + so + Mo2::TM * 64 + i * 4096);
-#pragma unroll
-  for (int s = 0; s < Mo2::CS; ++s) dma2(L.sc[s] + 2 * kt, L.sdst + so + s * 1024);
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const uint8_t *>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void k_gemm_mxfp8_occ2(
-    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
-    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
-    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    int64_t ldb, int64_t bexp, void *__restrict__ out) {
-  constexpr int TM = Mo2::TM, FI = Mo2::FI, FJ = Mo2::FJ;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[Mo2::LDS];
-  __shared__ int64_t sh[4];
-  TileInfo ti;
-  if (!lookup_row_tile<256, 128>(offsets, G, ntn, ti, sh)) return;
+template <int TM>
+struct MqSrc {
+  const uint8_t *Ab, *Bb;                   // operand panels (wave-uniform)
+  const uint8_t *sa, *sb;                   // this lane's scale-word row (k = 0)
+  uint32_t oa[Mq<TM>::CA], ob[Mq<TM>::CB];  // per-lane chunk sources at k = 0
+  uint32_t dst;                             // LDS address of slot 0, this wave's lanes
+  uint32_t sdst;                            // LDS address of slot 0's scale words, this wave
+  bool sa_row;                              // the lane's scale word is an A row
+};
+
+template <int TM>
+__device__ __forceinline__ void mq_load(const MqSrc<TM> &L, int q, uint32_t kb, int slot) {
+  using C = Mq<TM>;
+  const uint32_t sl = (uint32_t)slot * C::SLOT;
+  if (q < C::CA)
+    dma16s(L.Ab, L.oa[q] + kb, L.dst + sl + q * 8192);
+  else if (q < C::CA + C::CB)
+    dma16s(L.Bb, L.ob[q - C::CA] + kb, L.dst + sl + TM * 128 + (q - C::CA) * 8192);
+  else
+    dma4((L.sa_row ? L.sa : L.sb) + kb / 32, L.sdst + sl);
+}
+
+template <int TM>
+struct MqFrags {
+  v8i a[Mq<TM>::FI], b[Mq<TM>::FJ];
+  int sa[Mq<TM>::FI], sb[Mq<TM>::FJ];
+};
+
+// Per-lane LDS offsets: first A / B row's chunks h and 2 + h of K-half 0
+// (K-half t adds 64 bytes before the swizzle: chunk 4 t + x), fragments 32
+// rows (4096 bytes) apart; scale bytes of the first A / B row, block h.
+struct MqLane {
+  int a0, a1, b0, b1;  // chunk byte offsets for half 0
+  int x;               // row % 8 (the swizzle; the same for every fragment row)
+  int sa, sb;          // scale byte offsets (half 0)
+};
+
+template <int TM>
+__device__ __forceinline__ void mq_read_one(const uint8_t *lds, int slot, int half,
+                                            const MqLane &o, int f, MqFrags<TM> &F) {
+  using C = Mq<TM>;
+  const uint8_t *cur = lds + slot * C::SLOT;
+  // chunk (4 half + h) ^ x = chunk (h ^ x) with bit 2 flipped by half
+  const int hx = half * 64;
+  if (f < C::FI) {
+    F.a[f] = mw_frag(cur + (o.a0 ^ hx) + 4096 * f, cur + (o.a1 ^ hx) + 4096 * f);
+    F.sa[f] = cur[C::DATA + o.sa + 2 * half + 128 * f];
+  } else {
+    const int g = f - C::FI;
+    F.b[g] = mw_frag(cur + (o.b0 ^ hx) + 4096 * g, cur + (o.b1 ^ hx) + 4096 * g);
+    F.sb[g] = cur[C::DATA + o.sb + 2 * half + 128 * g];
+  }
+}
+
+// One K-half: FI x FJ MFMAs on F, in the order (b0, a0..), (b1, a0..); each
+// fragment is replaced by fragment f of (rslot, rhalf) after its last use;
+// load q of `lq` goes out after MFMA q when lq.k >= 0.
+template <int TM>
+__device__ __forceinline__ void mq_half(const MqSrc<TM> &L, const uint8_t *lds, const MqLane &o,
+                                        v16f (&acc)[Mq<TM>::FI][Mq<TM>::FJ], MqFrags<TM> &F,
+                                        int rslot, int rhalf, bool loads, uint32_t kb, int lslot) {
+  using C = Mq<TM>;
+  constexpr int FI = C::FI;
+#pragma unroll
+  for (int m = 0; m < 2 * FI; ++m) {
+    const int j = m / FI, i = m % FI;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0, 0,
+                                                                 0, F.sb[j], 0, F.sa[i]);
+    if (loads) {
+      // OPS loads spread over the 2 FI MFMAs (two per MFMA while needed)
+      constexpr int PER = (C::OPS + 2 * FI - 1) / (2 * FI);
+#pragma unroll
+      for (int q = PER * m; q < PER * m + PER && q < C::OPS; ++q) mq_load<TM>(L, q, kb, lslot);
+    }
+    if (m == FI - 1) mq_read_one<TM>(lds, rslot, rhalf, o, FI, F);          // b0
+    if (m >= FI) mq_read_one<TM>(lds, rslot, rhalf, o, i, F);              // a_i
+    if (m == 2 * FI - 1) mq_read_one<TM>(lds, rslot, rhalf, o, FI + 1, F);  // b1
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// bf16 epilogue through LDS: each wave writes its rounded accumulators into a
+// TM x 256 bf16 tile (row pitch 512 bytes, 16-byte chunk x of row r at
+// x ^ (r % 32)), then every lane stores 16 bytes of a row, so one store
+// instruction writes two whole 512-byte rows (four full 128-byte lines
+// each) instead of 32 bytes of 32 rows.
+template <int TM>
+__device__ __forceinline__ void mq_store_staged(const v16f (&acc)[Mq<TM>::FI][Mq<TM>::FJ],
+                                                uint8_t *lds, const TileInfo &ti, int64_t N,
+                                                void *__restrict__ out) {
+  static_assert(TM * 512 <= Mq<TM>::LDS, "staged tile fits the ring");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
-  const uint32_t KS = (uint32_t)(K / 32), Ku = (uint32_t)K;
-  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)TM);
-  const int rows_b = (int)min(N - ti.n0, (int64_t)Mo2::TN);
-  Mo2Src L;
-  L.Ab = A + ti.row0 * K;
-  L.Bb = B + ti.g * bexp + ti.n0 * ldb;
-  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
-  L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + Mo2::OPB + (uint32_t)wave * 256u);
-  // chunk c = 256 i + tid: row c / 4, physical chunk c % 4 holding logical
-  // chunk (c % 4) ^ ((row / 4) % 4); rows past the expert's end or past N
-  // load a clamped valid row whose results are never stored
+  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
 #pragma unroll
-  for (int i = 0; i < Mo2::CA; ++i) {
-    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
-    L.oa[i] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * k;
+  for (int i = 0; i < Mq<TM>::FI; ++i) {
+    const int R = wm * (TM / 2) + 32 * i + r32;
+#pragma unroll
+    for (int j = 0; j < Mq<TM>::FJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // columns 64 wn + 32 j + 8 g + 4 h + 0..3: chunk 8 wn + 4 j + g, bytes 8 h ..
+        const int x = 8 * wn + 4 * j + g;
+        const uint2 v = make_uint2(pk_bf16_rne(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                                   pk_bf16_rne(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+        *reinterpret_cast<uint2 *>(lds + R * 512 + ((x ^ (R & 31)) * 16) + 8 * h) = v;
+      }
   }
+  __syncthreads();
+  const int rows = (int)min(ti.row_end - ti.row0, (int64_t)TM);
+  const int x = tid & 31;
+  const int64_t col = ti.n0 + 8 * x;
+  const bool vec = (N & 7) == 0 && col + 7 < N;
+#pragma unroll 4
+  for (int it = 0; it < TM / 16; ++it) {
+    const int R = 16 * it + (tid >> 5);
+    const uint4 v = *reinterpret_cast<const uint4 *>(lds + R * 512 + ((x ^ (R & 31)) * 16));
+    if (R >= rows) continue;
+    uint16_t *orow = static_cast<uint16_t *>(out) + (ti.row0 + R) * N;
+    if (vec) {
+      *reinterpret_cast<uint4 *>(orow + col) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int i = 0; i < Mo2::CB; ++i) {
-    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
-    L.ob[i] = (uint32_t)min(r, rows_b - 1) * (uint32_t)ldb + 16u * k;
-  }
-  {
-    const uint8_t *Asb = As + ti.row0 * (int64_t)KS;
-    const uint8_t *Bsb = Bs + (ti.g * bexp + ti.n0 * ldb) / 32;
-    const int64_t ldbs = ldb / 32;
-#pragma unroll
-    for (int s = 0; s < Mo2::CS; ++s) {
-      const int e = 256 * s + tid;  // scale entry; >= 384: padding, reads A row 0
-      L.sc[s] = e < TM ? Asb + (int64_t)min(e, rows_a - 1) * KS
-                : e < Mo2::ROWS ? Bsb + (int64_t)min(e - TM, rows_b - 1) * ldbs
-                                : Asb;
+      for (int e = 0; e < 8; ++e)
+        if (col + e < N) orow[col + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   }
-  const int ra = wm * 64 + r32, rb = wn * 128 + r32;
-  const int a_lo = mx3_off(ra, h), a_hi = mx3_off(ra, 2 + h);
-  const int b_lo = TM * 64 + mx3_off(rb, h), b_hi = TM * 64 + mx3_off(rb, 2 + h);
-  const int s_a = Mo2::OPB + 4 * ra + h, s_b = Mo2::OPB + 4 * (TM + rb) + h;
+}
+
+template <bool OUT_F32, int TM>
+__device__ __forceinline__ void mq_tile(const uint8_t *__restrict__ A,
+                                        const uint8_t *__restrict__ As,
+                                        const uint8_t *__restrict__ B,
+                                        const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
+                                        int64_t ldb, int64_t bexp, const TileInfo &ti,
+                                        uint8_t *lds, void *__restrict__ out) {
+  using C = Mq<TM>;
+  constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
+  const int64_t KS = K / 32;
+  const uint32_t Ku = (uint32_t)K;
+  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)TM);
+  const int rows_b = (int)min(N - ti.n0, (int64_t)TN);
+  MqSrc<TM> L;
+  L.Ab = uniform_ptr(A + ti.row0 * K);
+  L.Bb = uniform_ptr(B + ti.g * bexp + ti.n0 * ldb);
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+  L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + C::DATA + (uint32_t)wave * 256u);
+  // load q, lane tid: row 64 q + tid / 8 of the operand, physical chunk
+  // tid % 8 holding logical chunk (tid % 8) ^ (row % 8); rows past the
+  // expert's end or past N load a clamped valid row
+#pragma unroll
+  for (int q = 0; q < C::CA; ++q) {
+    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
+    L.oa[q] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * c;
+  }
+#pragma unroll
+  for (int q = 0; q < C::CB; ++q) {
+    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
+    L.ob[q] = (uint32_t)min(r, rows_b - 1) * (uint32_t)ldb + 16u * c;
+  }
+  // scale word of lane tid: tile row tid (A rows first; lanes past the
+  // tile's rows fetch a valid row into the unused entries)
+  {
+    const int r = min(tid, C::ROWS - 1);
+    L.sa_row = r < TM;
+    L.sa = As + (ti.row0 + min(r, rows_a - 1)) * KS;
+    L.sb = Bs + (ti.g * bexp + ti.n0 * ldb) / 32 + (int64_t)min(r - TM, rows_b - 1) * (ldb / 32);
+    if (L.sa_row) L.sb = L.sa;  // never dereferenced for A rows
+  }
+  MqLane o;
+  {
+    const int ra = wm * (TM / 2) + r32, rb = wn * 64 + r32;
+    o.x = r32 & 7;
+    o.a0 = ra * 128 + ((h ^ o.x) * 16);
+    o.a1 = ra * 128 + (((2 + h) ^ o.x) * 16);
+    o.b0 = TM * 128 + rb * 128 + ((h ^ o.x) * 16);
+    o.b1 = TM * 128 + rb * 128 + (((2 + h) ^ o.x) * 16);
+    o.sa = ra * 4 + h;
+    o.sb = (TM + rb) * 4 + h;
+  }
 
   v16f acc[FI][FJ];
 #pragma unroll
@@ -928,49 +1039,57 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mxfp8_occ2(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (int)(K / 64);  // even, >= 2
-  mo2_issue(L, 0, 0);
-  mo2_issue(L, 1, 1);
-  int slot = 0;
+  const int nk = (int)(K / 128);  // >= 1
+#pragma unroll
+  for (int q = 0; q < C::OPS; ++q) mq_load<TM>(L, q, 0u, 0);
+#pragma unroll
+  for (int q = 0; q < C::OPS; ++q) mq_load<TM>(L, q, (uint32_t)min(1, nk - 1) * 128u, 1);
+  vm_wait<C::OPS>();  // step 0
+  __builtin_amdgcn_s_barrier();
+  MqFrags<TM> F;
+#pragma unroll
+  for (int f = 0; f < FI + FJ; ++f) mq_read_one<TM>(lds, 0, 0, o, f, F);
   for (int kt = 0; kt < nk; ++kt) {
-    vm_wait<Mo2::OPS>();  // own loads of step kt done; step kt + 1 may be pending
-    lgkm_wait0();         // own reads of the slot refilled below are done
+    const int slot = kt & 1;
+    mq_half<TM>(L, lds, o, acc, F, slot, 1, false, 0u, 0);
+    vm_wait<0>();  // own loads of step kt+1 arrived
+    lgkm_wait0();  // own reads of this slot done
     __builtin_amdgcn_s_barrier();
-    const int fill = slot == 0 ? 2 : slot - 1;  // (kt + 2) % 3, read at step kt - 1
-    mo2_issue(L, min(kt + 2, nk - 1), fill);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint8_t *cur = lds + slot * Mo2::SLOT;
-    v8i fa[FI], fb[FJ];
-    int sa[FI], sb[FJ];
-#pragma unroll
-    for (int i = 0; i < FI; ++i) {
-      const uint4 lo = *reinterpret_cast<const uint4 *>(cur + a_lo + 2048 * i);
-      const uint4 hi = *reinterpret_cast<const uint4 *>(cur + a_hi + 2048 * i);
-      fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sa[i] = cur[s_a + 4 * 32 * i];
-    }
-#pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      const uint4 lo = *reinterpret_cast<const uint4 *>(cur + b_lo + 2048 * j);
-      const uint4 hi = *reinterpret_cast<const uint4 *>(cur + b_hi + 2048 * j);
-      fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      sb[j] = cur[s_b + 4 * 32 * j];
-    }
-#pragma unroll
-    for (int j = 0; j < FJ; ++j)
-#pragma unroll
-      for (int i = 0; i < FI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0,
-                                                                     0, sb[j], 0, sa[i]);
-    slot = slot == 2 ? 0 : slot + 1;
+    // past the last step: requests repeat it and reads take step nk-1's
+    // first half again (in bounds, never used)
+    const uint32_t kb = (uint32_t)min(kt + 2, nk - 1) * 128u;
+    mq_half<TM>(L, lds, o, acc, F, kt + 1 < nk ? slot ^ 1 : slot, 0, true, kb, slot);
   }
   vm_wait<0>();  // no load may still target this workgroup's LDS at exit
+  if (OUT_F32) {
 #pragma unroll
-  for (int i = 0; i < FI; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < FJ; ++j)
-      mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * 64 + 32 * i,
-                         wn * 128 + 32 * j);
+      for (int j = 0; j < FJ; ++j)
+        mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0,
+                           wm * (TM / 2) + 32 * i, wn * 64 + 32 * j);
+  } else {
+    lgkm_wait0();
+    __builtin_amdgcn_s_barrier();  // the ring is no longer read: stage the tile there
+    mq_store_staged<TM>(acc, lds, ti, N, out);
+  }
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_q(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    int64_t ldb, int64_t bexp, void *__restrict__ out) {
+  static_assert(Mq<128>::LDS <= Mq<256>::LDS, "LDS of the half tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Mq<256>::LDS];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
+  if (ti.row_end - ti.row0 <= 128)
+    mq_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
+  else
+    mq_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
 }
 
 // The gate_up grouped GEMM with the fused epilogue: D = SwiGLU(C) x prob
@@ -2409,7 +2528,8 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
                         wn * (C::TN / 2) + 32 * j, Ao, ab);
 }
 
-// Tiles as k_gemm_mxfp8_pipe; K % 256 == 0.
+// 256 x 256 tiles (an expert's last tile of <= 128 rows as 128 x 256);
+// K % 256 == 0.
 template <bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_pipe(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
@@ -2523,13 +2643,13 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     if (K % 128 || K / 32 > Mx3<256>::MAX_KS || G * K * 256 + K >= U32)
       return hipErrorNotSupported;
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
-    const int64_t ntn_b = cdiv(N, Mx3<256>::TN);
+    const int64_t ntn_b = cdiv(N, Mq<256>::TN);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
     if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, B,
+      hipLaunchKernelGGL(k_gemm_mxfp8_q<true>, grid_b, dim3(512), 0, st, A, a_scale, B,
                          b_scale, offsets, G, N, K, ntn_b, G * K, K, out);
     else
-      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, B,
+      hipLaunchKernelGGL(k_gemm_mxfp8_q<false>, grid_b, dim3(512), 0, st, A, a_scale, B,
                          b_scale, offsets, G, N, K, ntn_b, G * K, K, out);
     return hipGetLastError();
   }
@@ -2563,28 +2683,15 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
   int64_t tiles = (cdiv(M, GT_M) + G) * ntn;
   tiles = cdiv(tiles, 8) * 8;
   const dim3 grid((unsigned)tiles);
-  if (fmt == 1 && K > 0 && K % 128 == 0 && K <= PQM_MX_OCC2_KMAX) {
+  if (fmt == 1 && K > 0 && K % 128 == 0 && 256 * K < U32) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
-    const int64_t ntn_o = cdiv(N, Mo2::TN);
-    const dim3 grid_o((unsigned)(cdiv((cdiv(M, Mo2::TM) + G) * ntn_o, 8) * 8));
-    if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_mxfp8_occ2<true>, grid_o, dim3(256), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_o, K, N * K, out);
-    else
-      hipLaunchKernelGGL(k_gemm_mxfp8_occ2<false>, grid_o, dim3(256), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_o, K, N * K, out);
-    return hipGetLastError();
-  }
-  if (fmt == 1 && K > 0 && K % 128 == 0 && K / 32 <= Mx3<256>::MAX_KS &&
-      K / 32 <= Mx3<128>::MAX_KS) {
-    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
-    const int64_t ntn_b = cdiv(N, Mx3<256>::TN);
+    const int64_t ntn_b = cdiv(N, Mq<256>::TN);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
     if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, B,
+      hipLaunchKernelGGL(k_gemm_mxfp8_q<true>, grid_b, dim3(512), 0, st, A, a_scale, B,
                          b_scale, offsets, G, N, K, ntn_b, K, N * K, out);
     else
-      hipLaunchKernelGGL(k_gemm_mxfp8_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, B,
+      hipLaunchKernelGGL(k_gemm_mxfp8_q<false>, grid_b, dim3(512), 0, st, A, a_scale, B,
                          b_scale, offsets, G, N, K, ntn_b, K, N * K, out);
     return hipGetLastError();
   }
