@@ -851,11 +851,10 @@ __device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p) {
 template <int TM>
 struct MqSrc {
   const uint8_t *Ab, *Bb;                   // operand panels (wave-uniform)
-  const uint8_t *sa, *sb;                   // this lane's scale-word row (k = 0)
+  const uint8_t *sp;                        // this lane's scale-word row (k = 0)
   uint32_t oa[Mq<TM>::CA], ob[Mq<TM>::CB];  // per-lane chunk sources at k = 0
   uint32_t dst;                             // LDS address of slot 0, this wave's lanes
   uint32_t sdst;                            // LDS address of slot 0's scale words, this wave
-  bool sa_row;                              // the lane's scale word is an A row
 };
 
 template <int TM>
@@ -867,7 +866,7 @@ __device__ __forceinline__ void mq_load(const MqSrc<TM> &L, int q, uint32_t kb, 
   else if (q < C::CA + C::CB)
     dma16s(L.Bb, L.ob[q - C::CA] + kb, L.dst + sl + TM * 128 + (q - C::CA) * 8192);
   else
-    dma4((L.sa_row ? L.sa : L.sb) + kb / 32, L.sdst + sl);
+    dma4(L.sp + kb / 32, L.sdst + sl);
 }
 
 template <int TM>
@@ -908,14 +907,16 @@ __device__ __forceinline__ void mq_read_one(const uint8_t *lds, int slot, int ha
 template <int TM>
 __device__ __forceinline__ void mq_half(const MqSrc<TM> &L, const uint8_t *lds, const MqLane &o,
                                         v16f (&acc)[Mq<TM>::FI][Mq<TM>::FJ], MqFrags<TM> &F,
-                                        int rslot, int rhalf, bool loads, uint32_t kb, int lslot) {
+                                        int rslot, int rhalf, bool loads, uint32_t kb, int lslot,
+                                        bool MF = true) {
   using C = Mq<TM>;
   constexpr int FI = C::FI;
 #pragma unroll
   for (int m = 0; m < 2 * FI; ++m) {
     const int j = m / FI, i = m % FI;
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0, 0,
-                                                                 0, F.sb[j], 0, F.sa[i]);
+    if (MF)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0,
+                                                                   0, 0, F.sb[j], 0, F.sa[i]);
     if (loads) {
       // OPS loads spread over the 2 FI MFMAs (two per MFMA while needed)
       constexpr int PER = (C::OPS + 2 * FI - 1) / (2 * FI);
@@ -1014,10 +1015,8 @@ __device__ __forceinline__ void mq_tile(const uint8_t *__restrict__ A,
   // tile's rows fetch a valid row into the unused entries)
   {
     const int r = min(tid, C::ROWS - 1);
-    L.sa_row = r < TM;
-    L.sa = As + (ti.row0 + min(r, rows_a - 1)) * KS;
-    L.sb = Bs + (ti.g * bexp + ti.n0 * ldb) / 32 + (int64_t)min(r - TM, rows_b - 1) * (ldb / 32);
-    if (L.sa_row) L.sb = L.sa;  // never dereferenced for A rows
+    L.sp = r < TM ? As + (ti.row0 + min(r, rows_a - 1)) * KS
+                  : Bs + (ti.g * bexp + ti.n0 * ldb) / 32 + (int64_t)min(r - TM, rows_b - 1) * (ldb / 32);
   }
   MqLane o;
   {
@@ -1090,6 +1089,256 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_q(
     mq_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
   else
     mq_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
+}
+
+// ------------------------------------------ MXFP8, persistent eight waves
+// k_gemm_mxfp8_q as a persistent kernel: one workgroup per CU walks its
+// tiles (those of its XCD's contiguous range, 32 apart) with one unbroken
+// stream of ring steps, so the first two steps of tile n+1 are loaded while
+// tile n finishes and no tile starts with an empty ring.  Tile n's output
+// leaves by buffer stores issued right after its last step, the same number
+// of store instructions in every wave (rows past the tile's end get an
+// offset beyond the buffer, which the hardware drops), so that the first
+// step of tile n+1 can wait for its own loads (issued before the stores)
+// with vmcnt <= stores and let the stores drain under its MFMAs.  On an
+// expert's last tile of at most 128 rows the four waves of rows 128..255
+// skip their MFMAs (their rows are beyond the tile).  The tile list is made
+// once at the start: a scan of the per-expert tile counts (in the ring's
+// LDS, before any ring load), then each tile found by binary search.
+constexpr int QP_MAXT = 256;  // tiles per workgroup
+// Store offset of a lane with nothing to store: past the output (which is
+// smaller than 2^31 bytes) without wrapping, so the hardware range check
+// drops it.
+constexpr uint32_t QP_OOB = 0x80000000u;
+
+struct QpTile {
+  int32_t row0, row_end, g, n0;
+};
+
+// Exclusive prefix of v over the 512 threads (thread order) plus `carry`,
+// which then grows by the 512 values' sum.  wsum: 8 shared slots.
+__device__ __forceinline__ int32_t qp_scan512(int32_t v, int32_t &carry, int32_t *wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int32_t before = carry, all = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  carry += all;
+  __syncthreads();
+  return before + incl - v;
+}
+
+template <bool OUT_F32>
+__device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffer_rsrc_t rs,
+                                         const QpTile &t, int64_t N) {
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
+  const uint32_t Nu = (uint32_t)N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = t.row0 + wm * 128 + 32 * i + r32;
+    const bool rok = row < t.row_end;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const v16f &a = acc[i][j];
+      const int cb = t.n0 + wn * 64 + 32 * j;
+      if (OUT_F32) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t col = (uint32_t)(cb + 8 * g + 4 * h);
+          const uint32_t off = rok && col < Nu ? ((uint32_t)row * Nu + col) * 4u : QP_OOB;
+          const u32x4 w = {__float_as_uint(a[4 * g]), __float_as_uint(a[4 * g + 1]),
+                           __float_as_uint(a[4 * g + 2]), __float_as_uint(a[4 * g + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          float lo[4], hi[4];  // as mx3_store: runs 2p, 2p+1 traded between lane halves
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = a[8 * p + e], y = a[8 * p + 4 + e];
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h ? x : y),
+                                                             __float_as_uint(h ? x : y), false, false);
+            const float got = __uint_as_float(h ? sw[0] : sw[1]);
+            lo[e] = h ? got : x;
+            hi[e] = h ? y : got;
+          }
+          const uint32_t col = (uint32_t)(cb + 16 * p + 8 * h);
+          const uint32_t off = rok && col < Nu ? ((uint32_t)row * Nu + col) * 2u : QP_OOB;
+          const u32x4 w = {pk_bf16_rne(lo[0], lo[1]), pk_bf16_rne(lo[2], lo[3]),
+                           pk_bf16_rne(hi[0], hi[1]), pk_bf16_rne(hi[2], hi[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Loader of one 256 x 256 tile (as in mq_tile).
+__device__ __forceinline__ void qp_loader(MqSrc<256> &L, const QpTile &t,
+                                          const uint8_t *__restrict__ A,
+                                          const uint8_t *__restrict__ As,
+                                          const uint8_t *__restrict__ B,
+                                          const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
+                                          int64_t ldb, int64_t bexp) {
+  using C = Mq<256>;
+  const int tid = threadIdx.x;
+  const int64_t KS = K / 32;
+  const uint32_t Ku = (uint32_t)K;
+  const int rows_a = min(t.row_end - t.row0, 256);
+  const int rows_b = (int)min(N - t.n0, (int64_t)256);
+  L.Ab = uniform_ptr(A + (int64_t)t.row0 * K);
+  L.Bb = uniform_ptr(B + t.g * bexp + t.n0 * ldb);
+#pragma unroll
+  for (int q = 0; q < C::CA; ++q) {
+    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
+    L.oa[q] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * c;
+  }
+#pragma unroll
+  for (int q = 0; q < C::CB; ++q) {
+    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
+    L.ob[q] = (uint32_t)min(r, rows_b - 1) * (uint32_t)ldb + 16u * c;
+  }
+  const int r = tid;  // 512 lanes, 512 tile rows
+  L.sp = r < 256 ? As + ((int64_t)t.row0 + min(r, rows_a - 1)) * KS
+                 : Bs + (t.g * bexp + t.n0 * ldb) / 32 + (int64_t)min(r - 256, rows_b - 1) * (ldb / 32);
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes) {
+  using C = Mq<256>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+  __shared__ QpTile tl[QP_MAXT];
+  __shared__ int32_t wsum[8], nt_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
+
+  // ---- tile list: per-expert counts of 256-row tiles, scanned into tpre
+  int32_t *tpre = reinterpret_cast<int32_t *>(lds);  // G + 1 entries (checked on the host)
+  {
+    int32_t carry = 0;
+    for (int64_t b0 = 0; b0 < G; b0 += 512) {
+      const int64_t g = b0 + tid;
+      const int32_t v = g < G ? (int32_t)((offsets[g + 1] - offsets[g] + 255) / 256) : 0;
+      const int32_t x = qp_scan512(v, carry, wsum);
+      if (g < G) tpre[g] = x;
+    }
+    if (tid == 0) tpre[G] = carry;
+  }
+  __syncthreads();
+  {
+    const int64_t real = (int64_t)tpre[G] * ntn;
+    const int64_t per_xcd = (real + 7) / 8, nw = gridDim.x / 8;
+    const int64_t lo = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int64_t hi = min((blockIdx.x % 8 + 1) * per_xcd, real);
+    const int nt = lo < hi ? (int)((hi - lo + nw - 1) / nw) : 0;
+    if (tid == 0) nt_sh = min(nt, QP_MAXT);
+    for (int k = tid; k < nt && k < QP_MAXT; k += 512) {
+      const int64_t T = lo + (int64_t)k * nw;
+      const int32_t mt = (int32_t)(T / ntn);
+      int a = 0, b = (int)G;  // largest g with tpre[g] <= mt (tpre[G] > mt)
+      while (b - a > 1) {
+        const int m = (a + b) >> 1;
+        if (tpre[m] <= mt) a = m; else b = m;
+      }
+      QpTile t;
+      t.g = a;
+      t.row0 = (int32_t)(offsets[a] + (int64_t)(mt - tpre[a]) * 256);
+      t.row_end = (int32_t)offsets[a + 1];
+      t.n0 = (int32_t)((T % ntn) * 256);
+      tl[k] = t;
+    }
+  }
+  __syncthreads();  // the tile list is complete and tpre is no longer read
+  const int nt = nt_sh;
+  if (nt == 0) return;
+  const int nk = (int)(K / 128);
+  const int S = nt * nk;
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(out, (short)0, (int)out_bytes, 0x00020000);
+
+  MqSrc<256> L;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+  L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + C::DATA + (uint32_t)wave * 256u);
+  MqLane o;
+  {
+    const int ra = wm * 128 + r32, rb = wn * 64 + r32;
+    o.x = r32 & 7;
+    o.a0 = ra * 128 + ((h ^ o.x) * 16);
+    o.a1 = ra * 128 + (((2 + h) ^ o.x) * 16);
+    o.b0 = 256 * 128 + rb * 128 + ((h ^ o.x) * 16);
+    o.b1 = 256 * 128 + rb * 128 + (((2 + h) ^ o.x) * 16);
+    o.sa = ra * 4 + h;
+    o.sb = (256 + rb) * 4 + h;
+  }
+  // stream position v = tile v / nk, step v % nk
+  qp_loader(L, tl[0], A, As, B, Bs, N, K, ldb, bexp);
+#pragma unroll
+  for (int q = 0; q < C::OPS; ++q) mq_load<256>(L, q, 0u, 0);
+  if (S > 1) {
+    if (nk == 1) qp_loader(L, tl[1], A, As, B, Bs, N, K, ldb, bexp);
+#pragma unroll
+    for (int q = 0; q < C::OPS; ++q) mq_load<256>(L, q, (uint32_t)(1 % nk) * 128u, 1);
+  }
+  vm_wait<0>();
+  __builtin_amdgcn_s_barrier();
+  MqFrags<256> F;
+#pragma unroll
+  for (int f = 0; f < 6; ++f) mq_read_one<256>(lds, 0, 0, o, f, F);
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  QpTile ct = tl[0];
+  bool active = __builtin_amdgcn_readfirstlane((wm == 0 || ct.row_end - ct.row0 > 128) ? 1 : 0);
+  for (int u = 0; u < S; ++u) {
+    const int slot = u & 1, k = u % nk;
+    mq_half<256>(L, lds, o, acc, F, slot, 1, false, 0u, 0, active);
+    if (k == 0 && u > 0)
+      vm_wait<OUT_F32 ? 32 : 16>();  // loads of step u+1 came before the last tile's stores
+    else
+      vm_wait<0>();
+    lgkm_wait0();
+    __builtin_amdgcn_s_barrier();
+    const int v = u + 2;
+    const bool ld = v < S;
+    if (ld && v % nk == 0) qp_loader(L, tl[v / nk], A, As, B, Bs, N, K, ldb, bexp);
+    const uint32_t kb = (uint32_t)(v % nk) * 128u;
+    const int rslot = u + 1 < S ? slot ^ 1 : slot;
+    mq_half<256>(L, lds, o, acc, F, rslot, 0, ld, kb, slot, active);
+    if (k == nk - 1) {
+      qp_store<OUT_F32>(acc, rs, ct, N);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      if (u + 1 < S) {
+        ct = tl[(u + 1) / nk];
+        active = __builtin_amdgcn_readfirstlane((wm == 0 || ct.row_end - ct.row0 > 128) ? 1 : 0);
+      }
+    }
+  }
+  vm_wait<0>();  // stores done and no load still targets this workgroup's LDS
 }
 
 // The gate_up grouped GEMM with the fused epilogue: D = SwiGLU(C) x prob
@@ -2595,6 +2844,28 @@ __global__ __launch_bounds__(256) void k_zero_rows(const int64_t *__restrict__ o
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Persistent MXFP8 grid: one workgroup per CU (a multiple of 8, one range
+// of tiles per XCD), fewer when there are fewer tiles.
+static int64_t qp_grid(int64_t G, int64_t M, int64_t N) {
+  const int64_t tiles_ub = (cdiv(M, 256) + G) * cdiv(N, 256);
+  const int64_t cus = resident_workgroups((const void *)k_gemm_mxfp8_qp<false>, 512, 0);
+  return max((int64_t)8, min(cdiv(cus, 8) * 8, cdiv(tiles_ub, 8) * 8));
+}
+
+// The persistent kernel's limits: the expert tile counts fit the ring's LDS
+// for the scan, every workgroup's tiles fit its tile list, the output is
+// below 2^31 bytes (its store offsets and the dropped offset), and rows are
+// whole 16-byte store vectors.
+static bool qp_fits(int64_t G, int64_t M, int64_t N, int64_t K, int esize) {
+  (void)K;
+  if ((G + 1) * 4 > Mq<256>::LDS) return false;
+  if ((N * esize) % 16) return false;
+  if (M * N * esize >= (int64_t)QP_OOB) return false;
+  const int64_t tiles_ub = (cdiv(M, 256) + G) * cdiv(N, 256);
+  const int64_t nw = qp_grid(G, M, N) / 8;
+  return cdiv(cdiv(tiles_ub, 8), nw) <= QP_MAXT;
+}
+
 hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *a_scale,
                                const float *a_outer, const void *b, const uint8_t *b_scale,
                                const float *b_outer, int64_t b_rows_per_scale,
@@ -2683,6 +2954,20 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
   int64_t tiles = (cdiv(M, GT_M) + G) * ntn;
   tiles = cdiv(tiles, 8) * 8;
   const dim3 grid((unsigned)tiles);
+  if (fmt == 1 && K > 0 && K % 128 == 0 && 256 * K < U32 &&
+      qp_fits(G, M, N, K, out_fp32 ? 4 : 2)) {
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    const int64_t ntn_b = cdiv(N, 256);
+    const dim3 grid_p((unsigned)qp_grid(G, M, N));
+    const uint32_t ob = (uint32_t)(M * N * (out_fp32 ? 4 : 2));
+    if (out_fp32)
+      hipLaunchKernelGGL(k_gemm_mxfp8_qp<true>, grid_p, dim3(512), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_b, K, N * K, out, ob);
+    else
+      hipLaunchKernelGGL(k_gemm_mxfp8_qp<false>, grid_p, dim3(512), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_b, K, N * K, out, ob);
+    return hipGetLastError();
+  }
   if (fmt == 1 && K > 0 && K % 128 == 0 && 256 * K < U32) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_b = cdiv(N, Mq<256>::TN);

@@ -84,10 +84,13 @@ def test_mxfp8_fprop_ragged(case):
     check_rows(host(y), want, f"mxfp8 {sizes} N={N} K={K}")
 
 
-def test_mxfp8_fprop_bf16_out():
+@pytest.mark.parametrize("N", [128, 100])
+def test_mxfp8_fprop_bf16_out(N):
     """bf16 output vs the binary64 product: the GEMM bar (1e-3) plus one
-    bf16 rounding of the output (at most 2^-9 relative per element)."""
-    y, want = _mxfp8_case([64, 0, 100], 128, 256, seed=4, out_dtype=pqm.OUT_BF16)
+    bf16 rounding of the output (at most 2^-9 relative per element).  N =
+    100 (rows of 200 bytes, not whole 16-byte vectors) runs the
+    non-persistent kernel."""
+    y, want = _mxfp8_case([64, 0, 100, 300], N, 256, seed=4, out_dtype=pqm.OUT_BF16)
     got = oracle.bf16_to_f64(host_u16(y))
     r = rel_l2_rows(got, want)
     print(f"[gemm] mxfp8 bf16 out vs fp64: max row rel-L2 {r.max():.3e}", flush=True)
