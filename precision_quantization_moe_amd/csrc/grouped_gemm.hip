@@ -1186,7 +1186,23 @@ __device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffe
   }
 }
 
-// Loader of one 256 x 256 tile (as in mq_tile).
+// Fused gate_up epilogue on the eight-wave layout: wave (wm, wn) of tile tn
+// holds, per row, gate values in its fragment j = 0 and up values in j = 1
+// for the 32 D columns 128 tn + 32 wn + 0..31 (one MXFP8 block): the
+// transposed accumulator gives lane h * 32 + r the fragment columns
+// 8 g + 4 h + e (g, e = 0..3) as registers 4 g + e, and tile column
+// c = 64 wn + 32 j + 8 g + 4 h + e is made gate (j = 0) or up (j = 1) of
+// D column dcol = 128 tn + 32 wn + 16 h + 4 g + e, i.e. W row dcol or
+// I + dcol.  A lane then holds 16 consecutive D columns.
+__device__ __forceinline__ int64_t qp_swiglu_w_row(int c, int64_t tn, int64_t I) {
+  const int wn = c >> 6, j = (c >> 5) & 1, g = (c >> 3) & 3, hh = (c >> 2) & 1, e = c & 3;
+  const int64_t dcol = 128 * tn + 32 * wn + 16 * hh + 4 * g + e;
+  return j ? I + dcol : dcol;
+}
+
+// Loader of one 256 x 256 tile (as in mq_tile); EPI: B rows permuted as
+// qp_swiglu_w_row describes (N = 2 I, whole tiles).
+template <bool EPI = false>
 __device__ __forceinline__ void qp_loader(MqSrc<256> &L, const QpTile &t,
                                           const uint8_t *__restrict__ A,
                                           const uint8_t *__restrict__ As,
@@ -1199,8 +1215,9 @@ __device__ __forceinline__ void qp_loader(MqSrc<256> &L, const QpTile &t,
   const uint32_t Ku = (uint32_t)K;
   const int rows_a = min(t.row_end - t.row0, 256);
   const int rows_b = (int)min(N - t.n0, (int64_t)256);
+  const int64_t tn = t.n0 / 256;
   L.Ab = uniform_ptr(A + (int64_t)t.row0 * K);
-  L.Bb = uniform_ptr(B + t.g * bexp + t.n0 * ldb);
+  L.Bb = uniform_ptr(B + t.g * bexp + (EPI ? 0 : t.n0 * ldb));
 #pragma unroll
   for (int q = 0; q < C::CA; ++q) {
     const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
@@ -1209,12 +1226,67 @@ __device__ __forceinline__ void qp_loader(MqSrc<256> &L, const QpTile &t,
 #pragma unroll
   for (int q = 0; q < C::CB; ++q) {
     const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
-    L.ob[q] = (uint32_t)min(r, rows_b - 1) * (uint32_t)ldb + 16u * c;
+    const int64_t wr = EPI ? qp_swiglu_w_row(r, tn, N / 2) : (int64_t)min(r, rows_b - 1);
+    L.ob[q] = (uint32_t)wr * (uint32_t)ldb + 16u * c;
   }
   const int r = tid;  // 512 lanes, 512 tile rows
+  const int64_t wr = EPI ? qp_swiglu_w_row(max(r - 256, 0), tn, N / 2) - t.n0
+                         : (int64_t)min(r - 256, rows_b - 1);
   L.sp = r < 256 ? As + ((int64_t)t.row0 + min(r, rows_a - 1)) * KS
-                 : Bs + (t.g * bexp + t.n0 * ldb) / 32 + (int64_t)min(r - 256, rows_b - 1) * (ldb / 32);
+                 : Bs + (t.g * bexp + t.n0 * ldb) / 32 + wr * (ldb / 32);
 }
+
+// The fused epilogue of one tile: D = bf16(silu(bf16 gate) bf16 up p) as
+// pqm_swiglu_prob computes it, then its row-wise MXFP8 block (this lane's
+// 16 columns and the other half's 16), stored with buffer stores whose
+// count is the same in every wave: 4 of 16 bytes (q) and 4 of one byte (s)
+// per lane, lanes without a value getting a dropped offset.
+__device__ __forceinline__ void qp_swiglu_store(const v16f (&acc)[4][2], const float (&pr)[4],
+                                                __amdgpu_buffer_rsrc_t rq,
+                                                __amdgpu_buffer_rsrc_t rs, const QpTile &t,
+                                                int64_t I) {
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
+  const uint32_t dbase = (uint32_t)(t.n0 / 2 + 32 * wn), Iu = (uint32_t)I;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = t.row0 + wm * 128 + 32 * i + r32;
+    const bool ok = row < t.row_end;
+    uint32_t dw[8];  // D columns dbase + 16 h + 2 k, + 1
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int g = k >> 1, e = 2 * (k & 1);
+      const uint32_t gw = pk_bf16_rne(acc[i][0][4 * g + e], acc[i][0][4 * g + e + 1]);
+      const uint32_t uw = pk_bf16_rne(acc[i][1][4 * g + e], acc[i][1][4 * g + e + 1]);
+      dw[k] = pk_bf16_rne(swiglu_f32(bf16_lo_f32(gw), bf16_lo_f32(uw), pr[i]),
+                          swiglu_f32(bf16_hi_f32(gw), bf16_hi_f32(uw), pr[i]));
+    }
+    uint32_t mm = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mm = pk_max_u16(mm, dw[k] & 0x7FFF7FFFu);
+    mm = max(mm & 0xFFFFu, mm >> 16);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(mm, mm, false, false);
+      mm = max(sw[0], sw[1]);
+    }
+    const uint32_t b = mx_scale_byte(mm);
+    const float scale = __uint_as_float(b << 23);
+    const u32x4 qv = {cvt4_e4m3_bf16(dw[0], dw[1], scale), cvt4_e4m3_bf16(dw[2], dw[3], scale),
+                      cvt4_e4m3_bf16(dw[4], dw[5], scale), cvt4_e4m3_bf16(dw[6], dw[7], scale)};
+    const uint32_t qoff = ok ? (uint32_t)row * Iu + dbase + 16u * (uint32_t)h : QP_OOB;
+    const uint32_t soff = ok && h == 0 ? (uint32_t)row * (Iu / 32) + dbase / 32 : QP_OOB;
+    __builtin_amdgcn_raw_buffer_store_b128(qv, rq, (int)qoff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b, rs, (int)soff, 0, 0);
+  }
+}
+
+template <bool OUT_F32, bool EPI>
+__device__ __forceinline__ void k_gemm_mxfp8_qp_body(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes, const SwigluEpi &ep);
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp(
@@ -1222,6 +1294,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp(
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
     int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes) {
+  k_gemm_mxfp8_qp_body<OUT_F32, false>(A, As, B, Bs, offsets, G, N, K, ntn, ldb, bexp, out,
+                                       out_bytes, SwigluEpi{nullptr, nullptr, 0, nullptr, nullptr});
+}
+
+template <bool OUT_F32, bool EPI>
+__device__ __forceinline__ void k_gemm_mxfp8_qp_body(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes, const SwigluEpi &ep) {
   using C = Mq<256>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
   __shared__ QpTile tl[QP_MAXT];
@@ -1270,7 +1352,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp(
   if (nt == 0) return;
   const int nk = (int)(K / 128);
   const int S = nt * nk;
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(out, (short)0, (int)out_bytes, 0x00020000);
+  // EPI: out_bytes = M I (q); the scale array is M I / 32 bytes
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(EPI ? (void *)ep.q : out, (short)0,
+                                                                (int)out_bytes, 0x00020000);
+  __amdgpu_buffer_rsrc_t rss =
+      __builtin_amdgcn_make_buffer_rsrc(ep.s, (short)0, (int)(out_bytes / 32), 0x00020000);
+  float pr[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // EPI: router probability of the lane's rows
+  int32_t pidx[4] = {0, 0, 0, 0};
 
   MqSrc<256> L;
   L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
@@ -1287,11 +1375,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp(
     o.sb = (256 + rb) * 4 + h;
   }
   // stream position v = tile v / nk, step v % nk
-  qp_loader(L, tl[0], A, As, B, Bs, N, K, ldb, bexp);
+  qp_loader<EPI>(L, tl[0], A, As, B, Bs, N, K, ldb, bexp);
 #pragma unroll
   for (int q = 0; q < C::OPS; ++q) mq_load<256>(L, q, 0u, 0);
   if (S > 1) {
-    if (nk == 1) qp_loader(L, tl[1], A, As, B, Bs, N, K, ldb, bexp);
+    if (nk == 1) qp_loader<EPI>(L, tl[1], A, As, B, Bs, N, K, ldb, bexp);
 #pragma unroll
     for (int q = 0; q < C::OPS; ++q) mq_load<256>(L, q, (uint32_t)(1 % nk) * 128u, 1);
   }
@@ -1313,19 +1401,41 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp(
     const int slot = u & 1, k = u % nk;
     mq_half<256>(L, lds, o, acc, F, slot, 1, false, 0u, 0, active);
     if (k == 0 && u > 0)
-      vm_wait<OUT_F32 ? 32 : 16>();  // loads of step u+1 came before the last tile's stores
+      vm_wait<EPI ? 8 : (OUT_F32 ? 32 : 16)>();  // loads of step u+1 came before the last tile's stores
     else
       vm_wait<0>();
     lgkm_wait0();
     __builtin_amdgcn_s_barrier();
     const int v = u + 2;
     const bool ld = v < S;
-    if (ld && v % nk == 0) qp_loader(L, tl[v / nk], A, As, B, Bs, N, K, ldb, bexp);
+    if (ld && v % nk == 0) qp_loader<EPI>(L, tl[v / nk], A, As, B, Bs, N, K, ldb, bexp);
     const uint32_t kb = (uint32_t)(v % nk) * 128u;
     const int rslot = u + 1 < S ? slot ^ 1 : slot;
     mq_half<256>(L, lds, o, acc, F, rslot, 0, ld, kb, slot, active);
+    if (EPI) {
+      // the lane's row indices into prob (src[row], or row) at the tile's
+      // first step, the probabilities at its second (each load waited by
+      // the next step's barrier; with fewer steps, before the epilogue)
+      if (k == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = min(ct.row0 + wm * 128 + 32 * i + r32, ct.row_end - 1);
+          pidx[i] = ep.src ? ep.src[row] : row;
+        }
+        if (nk == 1) vm_wait<0>();
+      }
+      if (k == min(1, nk - 1)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = ep.prob[pidx[i]];
+      }
+    }
     if (k == nk - 1) {
-      qp_store<OUT_F32>(acc, rs, ct, N);
+      if (EPI) {
+        if (nk <= 2) vm_wait<0>();
+        qp_swiglu_store(acc, pr, rs, rss, ct, N / 2);
+      } else {
+        qp_store<OUT_F32>(acc, rs, ct, N);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1339,6 +1449,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp(
     }
   }
   vm_wait<0>();  // stores done and no load still targets this workgroup's LDS
+}
+
+// The gate_up grouped GEMM with the fused epilogue on the persistent kernel
+// (N = 2 I, I % 128 == 0): q [M, I] E4M3, s [M, I / 32] E8M0.
+__global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp_swiglu(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    uint32_t q_bytes, SwigluEpi ep) {
+  k_gemm_mxfp8_qp_body<false, true>(A, As, B, Bs, offsets, G, N, K, ntn, K, N * K, nullptr,
+                                    q_bytes, ep);
 }
 
 // The gate_up grouped GEMM with the fused epilogue: D = SwiGLU(C) x prob
@@ -3074,6 +3195,12 @@ hipError_t launch_gemm_swiglu_mxfp8(const uint8_t *a, const uint8_t *a_scale, co
                                     const int32_t *src, uint8_t *q, uint8_t *s, hipStream_t st) {
   if (G == 0 || M == 0 || I == 0) return hipSuccess;
   const int64_t N = 2 * I, ntn = N / 256;
+  if (qp_fits(G, M, N, K, 2) && M * I < (int64_t)QP_OOB) {
+    hipLaunchKernelGGL(k_gemm_mxfp8_qp_swiglu, dim3((unsigned)qp_grid(G, M, N)), dim3(512), 0, st,
+                       a, a_scale, b, b_scale, offsets, G, N, K, ntn, (uint32_t)(M * I),
+                       SwigluEpi{prob, src, I, q, s});
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(cdiv((cdiv(M, 256) + G) * ntn, 8) * 8));
   hipLaunchKernelGGL(k_gemm_mxfp8_swiglu, grid, dim3(256), 0, st, a, a_scale, b, b_scale,
                      offsets, G, N, K, ntn, SwigluEpi{prob, src, I, q, s});
