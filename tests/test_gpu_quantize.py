@@ -221,6 +221,29 @@ def test_nvfp4_deepseek_expert_weights_full(which):
     del w, q, sb
 
 
+def test_nvfp4_group_chunks_and_row_stride():
+    """The group-scope pipeline over several chunks of whole groups (40
+    groups of 512 rows x 2048 columns, 2 MB each: a full 64 MB chunk and a
+    partial one) on a column slice of a wider tensor (row stride 2560):
+    bytes and every s_g equal the oracle's."""
+    G, rps, C, ld = 40, 512, 2048, 2560
+    wide = gpu_normal_bf16(G * rps, ld, 0.02, seed=405)
+    x = wide[:, :C]
+    q, sb, sg = pqm.quantize_nvfp4_per_token(x, rows_per_scale=rps)
+    amax = x.reshape(G, rps, C).abs().amax(dim=(1, 2)).float()
+    torch.cuda.synchronize()
+    print("[nvfp4] group scope, 40 x [512 x 2048], row stride 2560", flush=True)
+    sgh = host(sg)
+    want_sg = host(amax).astype(np.float32) / np.float32(2688.0)
+    assert_bytes_equal(sgh.view(np.uint32), want_sg.view(np.uint32), "every s_g")
+    for g in (0, 31, 32, G - 1):
+        xg = host_u16(x[g * rps:(g + 1) * rps].contiguous())
+        rq, rsb, rsg = oracle.quantize_nvfp4(xg, rows_per_group=rps)
+        assert_bytes_equal(host(q[g * rps:(g + 1) * rps]), rq, f"group {g} q")
+        assert_bytes_equal(host(sb[g * rps:(g + 1) * rps]), rsb, f"group {g} s_b")
+        assert sgh[g].view(np.uint32) == rsg[0].view(np.uint32)
+
+
 # ----------------------------------------------------------- dequantize
 
 def test_dequantize_mxfp8_both_copies():
