@@ -29,6 +29,8 @@ seeded input, with all inputs resident in HBM:
   ds_wquant         DeepSeek-V3 experts (256 routed + 1 shared, hidden 7168,
                     intermediate 2048): NVFP4 weights, gate/up jointly scaled
   ds_fwd            NVFP4 MoE expert layer forward, 4096 tokens top-8 + shared
+                    (the weighted SwiGLU and the FC2 operand's per-token
+                    NVFP4 quantize in one fused pass)
   ds_gemm           the two NVFP4 grouped GEMMs of ds_fwd alone
   ds_reconstruct    bf16 reconstruction of the forward operands (activations
                     and all 257 experts' weights) for the dequantized backward
@@ -302,7 +304,7 @@ def main():
 
     def r_ds_fwd(s):
         st["ds"] = moe_layer.nvfp4_moe_forward(st["x5"], st["ids5"], st["prob5"], *st["dsw"],
-                                               E5, I5)
+                                               E5, I5, keep_intermediates=False)
 
     def r_ds_gemm(s):
         o, (w1q, w1b, w1g, w2q, w2b, w2g) = st["ds"], st["dsw"]

@@ -412,6 +412,25 @@ pqm_status pqm_swiglu_prob_quantize_mxfp8(const uint16_t *c, const float *prob,
                                           hipStream_t stream);
 
 /*
+ * The weighted SwiGLU above fused with the per-token NVFP4 quantization of
+ * its output, the FC2 operand of the NVFP4 recipe ([MT] 5.3-5.4: the
+ * activation times the router probability is quantized where it is
+ * produced, the per-token amax taken in the same pass, so D is neither
+ * written nor read back; [BW] Recipe 2: per-token activation scaling):
+ *   q [rows, inter / 2] packed E2M1, s_block [rows, inter / 16] E4M3 and
+ *   s_outer [rows] binary32 equal pqm_quantize_nvfp4_per_token (one scale
+ *   per row) of the d that pqm_swiglu_prob returns; d (bf16 [rows, inter])
+ *   is also written when non-NULL.
+ * Requires inter % 16 == 0, inter <= 16384, rows < 2^31 (PQM_ERR_SHAPE);
+ * c and d 16-byte aligned, q 8-byte and s_outer 4-byte aligned
+ * (PQM_ERR_ALIGN); c, prob, q, s_block, s_outer non-NULL (PQM_ERR_NULL).
+ */
+pqm_status pqm_swiglu_prob_quantize_nvfp4(const uint16_t *c, const float *prob,
+                                          const int32_t *src, int64_t rows, int64_t inter,
+                                          uint16_t *d, uint8_t *q, uint8_t *s_block,
+                                          float *s_outer, hipStream_t stream);
+
+/*
  * Combine: out[t, n] = bf16( sum_j y_rows[slot[t, j], n] + shared[t, n] ),
  * summed in binary32 in j order (shared may be NULL).  y_rows, shared, out
  * bf16 with N contiguous; N % 8 == 0.

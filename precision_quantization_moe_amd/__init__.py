@@ -14,5 +14,6 @@ from ._binding import (  # noqa: F401
     OUT_BF16, OUT_FP32, PqmError, dequantize, lib, moe_combine, moe_gather_rows, moe_pad_rows,
     moe_gemm_swiglu_quantize_mxfp8, moe_grouped_gemm, moe_route, moe_route_noalloc, pad_rows_bound, quantize_fp8_block,
     quantize_mxfp8,
-    quantize_nvfp4_per_token, swiglu_prob, swiglu_prob_quantize_mxfp8, LIB_PATH,
+    quantize_nvfp4_per_token, swiglu_prob, swiglu_prob_quantize_mxfp8, swiglu_prob_quantize_nvfp4,
+    LIB_PATH,
 )

@@ -47,6 +47,7 @@ SIGNATURES = {
     "pqm_moe_pad_rows": ([P, I64, I64, P, I64, I64, P, P, I64, P], I32),
     "pqm_swiglu_prob": ([P, P, P, I64, I64, P, P], I32),
     "pqm_swiglu_prob_quantize_mxfp8": ([P, P, P, I64, I64, P, P, P, P], I32),
+    "pqm_swiglu_prob_quantize_nvfp4": ([P, P, P, I64, I64, P, P, P, P, P], I32),
     "pqm_moe_combine": ([P, P, P, I64, I64, I64, P, P], I32),
 }
 
@@ -298,6 +299,23 @@ def swiglu_prob_quantize_mxfp8(c: torch.Tensor, prob: torch.Tensor,
                                                 _ptr(d), _ptr(q), _ptr(s), _stream(c.device)),
            "pqm_swiglu_prob_quantize_mxfp8")
     return q, s, d
+
+
+def swiglu_prob_quantize_nvfp4(c: torch.Tensor, prob: torch.Tensor,
+                               src: torch.Tensor | None = None, keep_d: bool = False):
+    """swiglu_prob fused with the per-token NVFP4 quantization of its output.
+    Returns (q, s_block, s_outer, d) with d None unless keep_d."""
+    M, N2 = c.shape
+    inter = N2 // 2
+    dev = c.device
+    q = torch.empty((M, inter // 2), dtype=torch.uint8, device=dev)
+    sb = torch.empty((M, inter // 16), dtype=torch.uint8, device=dev)
+    sg = torch.empty((M,), dtype=torch.float32, device=dev)
+    d = torch.empty((M, inter), dtype=torch.bfloat16, device=dev) if keep_d else None
+    _check(lib().pqm_swiglu_prob_quantize_nvfp4(_ptr(c), _ptr(prob), _ptr(src), M, inter, _ptr(d),
+                                                _ptr(q), _ptr(sb), _ptr(sg), _stream(dev)),
+           "pqm_swiglu_prob_quantize_nvfp4")
+    return q, sb, sg, d
 
 
 def moe_gemm_swiglu_quantize_mxfp8(qa, sa, w1q, w1s, offsets: torch.Tensor, inter: int,

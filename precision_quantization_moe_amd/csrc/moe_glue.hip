@@ -542,6 +542,20 @@ pqm_status pqm_swiglu_prob_quantize_mxfp8(const uint16_t *c, const float *prob,
   return st_of(pqm::launch_swiglu_quant_mxfp8(c, prob, src, rows, inter, d, q, s, stream));
 }
 
+pqm_status pqm_swiglu_prob_quantize_nvfp4(const uint16_t *c, const float *prob,
+                                          const int32_t *src, int64_t rows, int64_t inter,
+                                          uint16_t *d, uint8_t *q, uint8_t *s_block,
+                                          float *s_outer, hipStream_t stream) {
+  if (rows < 0 || inter < 0 || inter % 16 || inter > pqm::nvfp4_max_cols() ||
+      rows >= ((int64_t)1 << 31))
+    return PQM_ERR_SHAPE;
+  if (rows == 0 || inter == 0) return PQM_OK;
+  if (!c || !prob || !q || !s_block || !s_outer) return PQM_ERR_NULL;
+  if (!al(c, 16) || !al(q, 8) || !al(s_outer, 4) || (d && !al(d, 16))) return PQM_ERR_ALIGN;
+  return st_of(pqm::launch_swiglu_quant_nvfp4(c, prob, src, rows, inter, d, q, s_block, s_outer,
+                                               stream));
+}
+
 pqm_status pqm_moe_combine(const uint16_t *y_rows, const int32_t *slot, const uint16_t *shared,
                            int64_t tokens, int64_t k, int64_t N, uint16_t *out,
                            hipStream_t stream) {

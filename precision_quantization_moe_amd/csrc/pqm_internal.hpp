@@ -27,6 +27,9 @@ hipError_t launch_quantize_nvfp4(const uint16_t *x, int64_t R, int64_t C, int64_
                                  int64_t rows_per_scale, uint8_t *q, uint8_t *sb, float *sg,
                                  void *workspace, hipStream_t st);
 size_t nvfp4_workspace_bytes(int64_t R, int64_t rows_per_scale);
+hipError_t launch_swiglu_quant_nvfp4(const uint16_t *c, const float *prob, const int32_t *src,
+                                     int64_t M, int64_t I, uint16_t *d, uint8_t *q, uint8_t *sb,
+                                     float *sg, hipStream_t st);
 int64_t nvfp4_max_cols();
 
 hipError_t launch_dequantize(int fmt, const uint8_t *q, const uint8_t *s, const float *sg,

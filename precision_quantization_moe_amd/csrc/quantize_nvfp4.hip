@@ -240,6 +240,100 @@ __device__ __forceinline__ void nvfp4_row_wave(const uint16_t *__restrict__ x, u
   }
 }
 
+// D = bf16(silu(gate) up p) (pqm_swiglu_prob) fused with the per-token
+// NVFP4 encoding of D, the FC2 operand ("miniTE technical report", 5.3-5.4:
+// the activation times the router probability is quantized where it is
+// produced, and its per-token amax needs no separate pass).  One wave per
+// row of D: lane l owns the 1x16 D blocks l + 64 b, whose gate and up values
+// are the 16 columns 16 (l + 64 b) .. of C's two halves; the row maximum,
+// s_g and the blocks are then exactly those of the per-token quantizer.
+// The loads are unconditional (blocks past the row re-read its last block
+// and are then zeroed), so that no load waits at a branch join.
+template <int NB>
+__global__ __launch_bounds__(256) void k_swiglu_quant_nvfp4(
+    const uint16_t *__restrict__ c, const float *__restrict__ prob,
+    const int32_t *__restrict__ src, uint32_t rows, uint32_t I, uint16_t *__restrict__ d,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ sb, float *__restrict__ sg) {
+  const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave exits together
+  const int lane = threadIdx.x & 63;
+  const uint32_t nblk = I / 16;
+  const float p = prob[src ? src[row] : (int32_t)row];
+  const uint16_t *cr = c + (int64_t)row * 2 * I;
+  uint4 gv[NB][2], uv[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const uint32_t blk = min(lane + 64u * b, nblk - 1u);
+    gv[b][0] = *reinterpret_cast<const uint4 *>(cr + blk * 16);
+    gv[b][1] = *reinterpret_cast<const uint4 *>(cr + blk * 16 + 8);
+    uv[b][0] = *reinterpret_cast<const uint4 *>(cr + I + blk * 16);
+    uv[b][1] = *reinterpret_cast<const uint4 *>(cr + I + blk * 16 + 8);
+  }
+  uint32_t w[NB][8];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const bool ok = lane + 64u * b < nblk;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t gw[4] = {gv[b][h].x, gv[b][h].y, gv[b][h].z, gv[b][h].w};
+      const uint32_t uw[4] = {uv[b][h].x, uv[b][h].y, uv[b][h].z, uv[b][h].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[b][4 * h + k] = ok ? pk_bf16_rne(swiglu_f32(bf16_lo_f32(gw[k]), bf16_lo_f32(uw[k]), p),
+                                           swiglu_f32(bf16_hi_f32(gw[k]), bf16_hi_f32(uw[k]), p))
+                             : 0u;
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = pk_max_u16(m, w[b][i] & 0x7FFF7FFFu);
+  m = max(m & 0xFFFFu, m >> 16);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  const Nvfp4Row rc = nvfp4_row(__uint_as_float(m << 16));
+  if (lane == 0) sg[row] = rc.s_g;
+  uint8_t *qr = q + (int64_t)row * (I / 2);
+  uint8_t *sbr = sb + (int64_t)row * nblk;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (64u * b < nblk) {  // uniform: the exact path's ballot needs the wave
+      const uint32_t blk = lane + 64u * b;
+      uint32_t code;
+      const uint2 packed = nvfp4_block(w[b], rc, &code);
+      if (blk < nblk) {
+        typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u2v{packed.x, packed.y}, reinterpret_cast<u2v *>(qr + blk * 8));
+        sbr[blk] = (uint8_t)code;
+        if (d) {
+          uint16_t *dr = d + (int64_t)row * I + blk * 16;
+          *reinterpret_cast<uint4 *>(dr) = make_uint4(w[b][0], w[b][1], w[b][2], w[b][3]);
+          *reinterpret_cast<uint4 *>(dr + 8) = make_uint4(w[b][4], w[b][5], w[b][6], w[b][7]);
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_swiglu_quant_nvfp4(const uint16_t *c, const float *prob, const int32_t *src,
+                                     int64_t M, int64_t I, uint16_t *d, uint8_t *q, uint8_t *sb,
+                                     float *sg, hipStream_t st) {
+  if (M == 0 || I == 0) return hipSuccess;
+  const dim3 grid((unsigned)((M + 3) / 4));
+  const int64_t per_lane = (I / 16 + 63) / 64;
+#define PQM_SQ(NB)                                                                        \
+  hipLaunchKernelGGL((k_swiglu_quant_nvfp4<NB>), grid, dim3(256), 0, st, c, prob, src,  \
+                     (uint32_t)M, (uint32_t)I, d, q, sb, sg)
+  if (per_lane <= 1) PQM_SQ(1);
+  else if (per_lane <= 2) PQM_SQ(2);
+  else if (per_lane <= 4) PQM_SQ(4);
+  else if (per_lane <= 8) PQM_SQ(8);
+  else PQM_SQ(16);
+#undef PQM_SQ
+  return hipGetLastError();
+}
+
 // Per-token scope: workgroup b quantizes rows 4b .. 4b+3, one per wave.
 template <int NB>
 __global__ __launch_bounds__(256) void k_quantize_nvfp4_rows(

@@ -113,10 +113,13 @@ def mxfp8_moe_forward(x, topk_ids, prob_flat, w1q, w1s, w2q, w2s, num_experts: i
 
 
 def nvfp4_moe_forward(x, topk_ids, prob_all, w1q, w1b, w1g, w2q, w2b, w2g, num_experts: int,
-                      inter: int):
+                      inter: int, keep_intermediates: bool = True):
     """Routed experts plus one shared expert (group num_experts, every token)
     with per-token NVFP4 activations.  prob_all [T*k + T] float32: router
-    probabilities, then 1.0 for each token's shared-expert row."""
+    probabilities, then 1.0 for each token's shared-expert row.  The weighted
+    SwiGLU and the per-token NVFP4 quantization of its output D run as one
+    fused pass; D is materialised (bf16) only with keep_intermediates (same
+    bytes either way)."""
     T, H = x.shape
     k = topk_ids.shape[1]
     off, src, tok, slot = b.moe_route(topk_ids, num_experts, shared_expert=True)
@@ -127,8 +130,7 @@ def nvfp4_moe_forward(x, topk_ids, prob_all, w1q, w1b, w1g, w2q, w2b, w2g, num_e
     c = b.moe_grouped_gemm(b.FMT_NVFP4, b.GEMM_FPROP, qa, w1q, off, 2 * inter, H,
                            a_scale=sba, a_outer=sga, b_scale=w1b, b_outer=w1g,
                            b_rows_per_scale=2 * inter, out_dtype=b.OUT_BF16)
-    d = b.swiglu_prob(c, prob_all, src)
-    qd, sbd, sgd = b.quantize_nvfp4_per_token(d)
+    qd, sbd, sgd, d = b.swiglu_prob_quantize_nvfp4(c, prob_all, src, keep_d=keep_intermediates)
     y = b.moe_grouped_gemm(b.FMT_NVFP4, b.GEMM_FPROP, qd, w2q, off, H, inter,
                            a_scale=sbd, a_outer=sgd, b_scale=w2b, b_outer=w2g,
                            b_rows_per_scale=H, out_dtype=b.OUT_BF16)

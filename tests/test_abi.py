@@ -187,3 +187,15 @@ def test_route_noalloc_validation():
     assert f(A16, 64, 8, 16, 0, None, A16, A16, A16, None) == 1
     assert f(None, 64, 8, 16, 0, A16, A16, A16, A16, None) == 1
     assert f(A16, 64, 8, 16, 0, BAD, A16, A16, A16, None) == 3
+
+
+def test_swiglu_quantize_nvfp4_validation():
+    L = pqm.lib()
+    f = L.pqm_swiglu_prob_quantize_nvfp4
+    assert f(A16, A16, None, 64, 40, None, A16, A16, A16, None) == 2       # inter % 16
+    assert f(A16, A16, None, 64, 1 << 15, None, A16, A16, A16, None) == 2  # inter > 16384
+    assert f(None, A16, None, 64, 64, None, A16, A16, A16, None) == 1
+    assert f(A16, A16, None, 64, 64, None, A16, None, A16, None) == 1
+    assert f(BAD, A16, None, 64, 64, None, A16, A16, A16, None) == 3
+    assert f(A16, A16, None, 64, 64, BAD, A16, A16, A16, None) == 3
+    assert f(A16, A16, None, 0, 64, None, None, None, None, None) == 0   # nothing to do

@@ -207,6 +207,12 @@ def test_glue_stays_inside_outputs():
     print("[canary] swiglu + mxfp8", flush=True)
     _run(L.pqm_swiglu_prob_quantize_mxfp8(_p(c), _p(prob), _p(srcs), n, I, d.ptr, q.ptr, s.ptr,
                                           _stream()), "swiglu+mxfp8", d, q, s)
+    I2 = 272
+    c2 = dev_bf16(wl.normal_bf16((n, 2 * I2), std=2.0, seed=14))
+    d, q, sbk, sgo = Guarded(n * I2 * 2), Guarded(n * I2 // 2), Guarded(n * I2 // 16), Guarded(4 * n)
+    print("[canary] swiglu + nvfp4", flush=True)
+    _run(L.pqm_swiglu_prob_quantize_nvfp4(_p(c2), _p(prob), _p(srcs), n, I2, d.ptr, q.ptr, sbk.ptr,
+                                          sgo.ptr, _stream()), "swiglu+nvfp4", d, q, sbk, sgo)
     # combine, with and without a shared-expert term
     y = dev_bf16(wl.normal_bf16((n, 136), seed=9))
     shared = dev_bf16(wl.normal_bf16((T, 136), seed=10))

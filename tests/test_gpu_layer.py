@@ -103,6 +103,36 @@ def test_swiglu_quantize_fused_pass():
     assert_bytes_equal(host(s2), rs, "fused s without d")
 
 
+@pytest.mark.parametrize("inter", [2048, 272, 7168])
+def test_swiglu_quantize_nvfp4_fused_pass(inter):
+    """The fused SwiGLU x prob + per-token NVFP4 pass: its d equals
+    pqm_swiglu_prob's, its q / s_block / s_outer equal the oracle's NVFP4 of
+    that d byte for byte and the unfused chain's (zero rows, a zero gate
+    half, a ragged row count and a width that is not a multiple of 1024)."""
+    M = 1003
+    rng = np.random.Generator(np.random.PCG64(79))
+    c = wl.normal_bf16((M, 2 * inter), std=2.0, seed=80)
+    c[5] = 0
+    c[6, :inter] = 0
+    prob = rng.random(M).astype(np.float32)
+    src = rng.permutation(M).astype(np.int32)
+    cd, pd, sd_ = dev_bf16(c), dev(prob), dev(src)
+    d_ref = pqm.swiglu_prob(cd, pd, sd_)
+    q, sb, sg, d = pqm.swiglu_prob_quantize_nvfp4(cd, pd, sd_, keep_d=True)
+    q2, sb2, sg2, none = pqm.swiglu_prob_quantize_nvfp4(cd, pd, sd_)
+    uq, usb, usg = pqm.quantize_nvfp4_per_token(d_ref)
+    torch.cuda.synchronize()
+    assert none is None
+    dh = host_u16(d)
+    assert_bytes_equal(dh, host_u16(d_ref), "fused d")
+    rq, rsb, rsg = oracle.quantize_nvfp4(dh)
+    for tag, (a, b_, g_) in (("with d", (q, sb, sg)), ("without d", (q2, sb2, sg2)),
+                             ("unfused", (uq, usb, usg))):
+        assert_bytes_equal(host(a), rq, f"{tag} q")
+        assert_bytes_equal(host(b_), rsb, f"{tag} s_block")
+        assert_bytes_equal(host(g_).view(np.uint32), rsg.view(np.uint32), f"{tag} s_outer")
+
+
 def test_gate_up_gemm_with_fused_epilogue():
     """The gate_up GEMM whose epilogue emits the MXFP8 encoding of
     SwiGLU(C) x prob gives the same bytes as the GEMM, pqm_swiglu_prob and
