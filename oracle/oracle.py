@@ -55,6 +55,7 @@ def lib():
         L.pqo_quantize_mxfp8_rowwise.argtypes = [P, Lg, Lg, Lg, P, P]
         L.pqo_quantize_mxfp8_colwise.argtypes = [P, Lg, Lg, Lg, P, P]
         L.pqo_quantize_nvfp4.argtypes = [P, Lg, Lg, Lg, Lg, P, P, P]
+        L.pqo_quantize_nvfp4_given_scale.argtypes = [P, Lg, Lg, Lg, P, P, P]
         L.pqo_dequantize_mxfp8.argtypes = [P, P, Lg, Lg, P]
         L.pqo_dequantize_nvfp4.argtypes = [P, P, P, Lg, Lg, Lg, P]
         L.pqo_decode_mxfp8.argtypes = [P, P, Lg, Lg, P]
@@ -141,6 +142,21 @@ def quantize_nvfp4(x: np.ndarray, rows_per_group: int = 1):
     lib().pqo_quantize_nvfp4(_ptr(x), R, C, C, rows_per_group,
                              _ptr(q), _ptr(sb), _ptr(sg))
     return q, sb, sg
+
+
+def quantize_nvfp4_given_scale(x: np.ndarray, sg: np.ndarray):
+    """The NVFP4 block encoding of each row of x under a caller-given FP32
+    outer scale sg[r] (the running-amax scale of [MT] 5.6).  With sg[r] =
+    fp32(max|x[r]| / 2688) this is quantize_nvfp4(x).  Returns
+    (q[R, C/2] u8, sb[R, C/16] u8)."""
+    x = _bf16(x)
+    R, C = x.shape
+    sg = np.ascontiguousarray(sg, np.float32)
+    assert C % 16 == 0 and sg.shape == (R,)
+    q = np.empty((R, C // 2), np.uint8)
+    sb = np.empty((R, C // 16), np.uint8)
+    lib().pqo_quantize_nvfp4_given_scale(_ptr(x), R, C, C, _ptr(sg), _ptr(q), _ptr(sb))
+    return q, sb
 
 
 def quantize_fp8_block(x: np.ndarray, block_rows: int):
@@ -366,3 +382,144 @@ def combine(y_rows: np.ndarray, slot: np.ndarray,
     if shared is not None:
         out = out + np.asarray(shared, np.float64)
     return out
+
+
+# --------------------------------------------------------------------------
+# Online amax compensation for a single-pass SwiGLU-FFN ([MT] 5.6)
+# --------------------------------------------------------------------------
+#
+# The FC2 GEMM consumes the activation P = SwiGLU(gate, up) x prob tile by
+# tile along its contraction dimension, before the row's full maximum (and
+# hence its NVFP4 outer scale) is known.  Each row keeps a running maximum;
+# tile i is encoded under the outer scale gs_i of the maximum so far, its FC2
+# partial product dO_i carries the block scales but not gs_i, and the
+# accumulator is moved to the new scale whenever gs grows:
+#     O <- O * (gs_prev / gs_i) + dO_i,      Y = O * gs_last * gs_W2,
+# so that O * gs_i equals sum_{j <= i} gs_j dO_j at every step.  Rows whose
+# maximum is still zero skip the tile; an all-zero row gives Y = 0.
+#
+# Readings (the pages leave these open):
+#  * P enters as bf16, the activation dtype of the two-pass path (the fused
+#    SwiGLU + NVFP4 pass quantizes a bf16 D), so both paths encode the same
+#    values with the same quantizer.
+#  * gs_i = fp32(gamax_i / 2688), the FP32 outer scale of the per-token
+#    quantizer, so a row whose maximum lies in its first non-zero tile gets
+#    the two-pass encoding exactly.
+#  * The loop runs in binary64 (acc=np.float64).  acc=np.float32 models a
+#    binary32 accumulator: dO_i, the ratio gs_prev / gs_i, the product and the
+#    sum are each rounded to binary32; the report uses it for the compensation
+#    error of such an accumulator.
+#  * W2 is NVFP4 with one outer scale for the whole [N, I] matrix.
+
+
+def _nvfp4_block_values(q: np.ndarray, sb: np.ndarray) -> np.ndarray:
+    """Exact q * s_b (block scale applied, outer scale not)."""
+    return decode_nvfp4(q, sb, np.ones(q.shape[0], np.float32))
+
+
+def online_amax_fc2(p: np.ndarray, tile: int, w2q: np.ndarray, w2sb: np.ndarray,
+                    w2sg: float, acc=np.float64):
+    """The [MT] 5.6 loop over the K-tiles of FC2.
+
+    p: bf16 bits [R, I] (the weighted SwiGLU output, consumed tile by tile);
+    tile: K-tile width, a multiple of 16 dividing I; w2q [N, I/2], w2sb
+    [N, I/16], w2sg: NVFP4 W2 (one outer scale).  Returns (Y [R, N] binary64,
+    rec) with rec = dict(gs [R, n_tiles] fp32, 0 where the tile was skipped;
+    q [R, I/2] and sb [R, I/16]: each tile's encoding under its running scale).
+    """
+    p = _bf16(p)
+    R, I = p.shape
+    N = w2q.shape[0]
+    assert tile % 16 == 0 and I % tile == 0
+    assert w2q.shape == (N, I // 2) and w2sb.shape == (N, I // 16)
+    w2 = _nvfp4_block_values(w2q, w2sb)                  # [N, I], no gs_W2
+    n_tiles = I // tile
+    gamax = np.zeros(R, np.float32)
+    gs_prev = np.zeros(R, np.float32)
+    O = np.zeros((R, N), acc)
+    gs_rec = np.zeros((R, n_tiles), np.float32)
+    q_all = np.zeros((R, I // 2), np.uint8)
+    sb_all = np.zeros((R, I // 16), np.uint8)
+    for i in range(n_tiles):
+        c0, c1 = i * tile, (i + 1) * tile
+        p_i = np.ascontiguousarray(p[:, c0:c1])
+        rowmax = np.abs(bf16_to_f64(p_i)).max(axis=1).astype(np.float32)
+        gamax = np.maximum(gamax, rowmax)
+        live = gamax > 0                                   # else: skip the tile
+        gs = np.array([lib().pqo_fp32_div(float(a), 2688.0) for a in gamax], np.float32)
+        q_i, sb_i = quantize_nvfp4_given_scale(p_i, np.where(live, gs, 0).astype(np.float32))
+        q_all[:, c0 // 2:c1 // 2] = q_i
+        sb_all[:, c0 // 16:c1 // 16] = sb_i
+        dO = _nvfp4_block_values(q_i, sb_i) @ w2[:, c0:c1].T   # binary64
+        for r in np.nonzero(live)[0]:
+            if acc is np.float32:
+                ratio = np.float32(gs_prev[r]) / np.float32(gs[r])
+                O[r] = (O[r] * ratio) + dO[r].astype(np.float32)
+            else:
+                O[r] = O[r] * (float(gs_prev[r]) / float(gs[r])) + dO[r]
+            gs_prev[r] = gs[r]
+            gs_rec[r, i] = gs[r]
+    Y = np.asarray(O, np.float64) * gs_prev.astype(np.float64)[:, None] * float(np.float32(w2sg))
+    return Y, dict(gs=gs_rec, q=q_all, sb=sb_all)
+
+
+def two_pass_fc2(p: np.ndarray, w2q: np.ndarray, w2sb: np.ndarray, w2sg: float):
+    """Two-pass counterpart: the whole row of P is produced first, encoded
+    per token under its full maximum, then FC2.  Returns (Y [R, N] binary64,
+    (q, sb, sg))."""
+    q, sb, sg = quantize_nvfp4(p)
+    N = w2q.shape[0]
+    w2 = decode_nvfp4(w2q, w2sb, np.full(1, w2sg, np.float32), rows_per_group=N)
+    return decode_nvfp4(q, sb, sg) @ w2.T, (q, sb, sg)
+
+
+def online_amax_report(p: np.ndarray, tile: int, w2q, w2sb, w2sg) -> dict:
+    """Compensation error and quantization difference of the online loop
+    ([MT] 5.6 evaluates both separately):
+
+    * comp_rel_fp32: max over rows of ||Y_fp32acc - Y_exact|| / ||Y_exact||,
+      where Y_exact = gs_W2 sum_i gs_i dO_i from the same encodings (the
+      rescaling error of a binary32 accumulator);
+    * comp_rel_fp64: the same for the binary64 loop;
+    * blocks_changed: fraction of 16-blocks whose decoded values differ from
+      the two-pass encoding (early encoding under a smaller outer scale);
+    * rel_vs_two_pass: max and mean over rows of ||Y_online - Y_two_pass|| /
+      ||Y_two_pass|| (zero rows excluded);
+    * rel_two_pass_vs_exact / rel_online_vs_exact: the same against the
+      unquantized product bf16(P) @ W2 (dequantized W2), for scale.
+    """
+    N = w2q.shape[0]
+    y64, rec = online_amax_fc2(p, tile, w2q, w2sb, w2sg, np.float64)
+    y32, _ = online_amax_fc2(p, tile, w2q, w2sb, w2sg, np.float32)
+    y2, (q2, sb2, sg2) = two_pass_fc2(p, w2q, w2sb, w2sg)
+    w2b = _nvfp4_block_values(w2q, w2sb)
+    R, I = p.shape
+    exact = np.zeros((R, N))
+    vals = _nvfp4_block_values(rec["q"], rec["sb"])
+    for i in range(rec["gs"].shape[1]):
+        c0, c1 = i * tile, (i + 1) * tile
+        exact += rec["gs"][:, i:i + 1].astype(np.float64) * (vals[:, c0:c1] @ w2b[:, c0:c1].T)
+    exact *= float(np.float32(w2sg))
+    w2 = w2b * float(np.float32(w2sg))
+    ref = bf16_to_f64(_bf16(p)) @ w2.T
+
+    def rel(a, b):
+        nb = np.linalg.norm(b, axis=1)
+        m = nb > 0
+        return np.linalg.norm(a - b, axis=1)[m] / nb[m]
+
+    # decoded values per block: online tile i under its own gs_i
+    on_v = vals.copy()
+    for i in range(rec["gs"].shape[1]):
+        c0, c1 = i * tile, (i + 1) * tile
+        on_v[:, c0:c1] *= rec["gs"][:, i:i + 1].astype(np.float64)
+    two = decode_nvfp4(q2, sb2, sg2)
+    changed = (on_v != two).reshape(R, -1, 16).any(axis=2)
+    r64, r32, rv = rel(y64, exact), rel(y32, exact), rel(y64, y2)
+    return dict(comp_rel_fp64=float(r64.max(initial=0.0)),
+                comp_rel_fp32=float(r32.max(initial=0.0)),
+                blocks_changed=float(changed.mean()),
+                rel_vs_two_pass_max=float(rv.max(initial=0.0)),
+                rel_vs_two_pass_mean=float(rv.mean()) if rv.size else 0.0,
+                rel_two_pass_vs_exact=float(rel(y2, ref).mean()) if rv.size else 0.0,
+                rel_online_vs_exact=float(rel(y64, ref).mean()) if rv.size else 0.0)

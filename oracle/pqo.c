@@ -237,6 +237,44 @@ void pqo_quantize_mxfp8_colwise(const uint16_t *x, long R, long C, long ld,
  * sb[R, C/16] E4M3 bytes, sg[R / rows_per_group] binary32 decode scales.
  * C must be a multiple of 16 and R a multiple of rows_per_group.
  */
+/*
+ * The 1x16 blocks of one row xr[0..C) under a given outer scale s_g: block
+ * scale s_b, then the E2M1 codes, as described above.  qr gets C/2 bytes and
+ * sbr C/16 bytes.
+ */
+static void nvfp4_encode_row(const uint16_t *xr, long C, float s_g,
+                             uint8_t *qr, uint8_t *sbr)
+{
+    for (long b = 0; b < C / 16; ++b) {
+        const uint16_t *xb = xr + b * 16;
+        uint8_t *qb = qr + b * 8;
+        double ab = 0.0;
+        for (int i = 0; i < 16; ++i) {
+            double v = fabs(bf16_value(xb[i]));
+            if (v > ab)
+                ab = v;
+        }
+        int sbc = 0;
+        if (s_g != 0.0f) /* 6 * s_g: at most 26 significant bits */
+            sbc = rne_grid(ab, 6.0 * (double)s_g, g_e4m3, 127);
+        sbr[b] = (uint8_t)sbc;
+        double dec = g_e4m3[sbc] * (double)s_g; /* <= 28 bits */
+        for (int j = 0; j < 8; ++j) {
+            uint8_t lo, hi;
+            double x0 = bf16_value(xb[2 * j]);
+            double x1 = bf16_value(xb[2 * j + 1]);
+            if (sbc == 0) {
+                lo = signbit(x0) ? 0x8 : 0x0;
+                hi = signbit(x1) ? 0x8 : 0x0;
+            } else {
+                lo = e2m1_encode(x0, dec);
+                hi = e2m1_encode(x1, dec);
+            }
+            qb[j] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
 void pqo_quantize_nvfp4(const uint16_t *x, long R, long C, long ld,
                         long rows_per_group, uint8_t *q, uint8_t *sb,
                         float *sg)
@@ -256,37 +294,27 @@ void pqo_quantize_nvfp4(const uint16_t *x, long R, long C, long ld,
         volatile float denom = 2688.0f; /* keep the division in binary32 */
         float s_g = A / denom;
         sg[g] = s_g;
-        for (long r = r0; r < r0 + rows_per_group; ++r) {
-            for (long b = 0; b < C / 16; ++b) {
-                const uint16_t *xb = x + r * ld + b * 16;
-                uint8_t *qb = q + r * (C / 2) + b * 8;
-                double ab = 0.0;
-                for (int i = 0; i < 16; ++i) {
-                    double v = fabs(bf16_value(xb[i]));
-                    if (v > ab)
-                        ab = v;
-                }
-                int sbc = 0;
-                if (s_g != 0.0f) /* 6 * s_g: at most 26 significant bits */
-                    sbc = rne_grid(ab, 6.0 * (double)s_g, g_e4m3, 127);
-                sb[r * (C / 16) + b] = (uint8_t)sbc;
-                double dec = g_e4m3[sbc] * (double)s_g; /* <= 28 bits */
-                for (int j = 0; j < 8; ++j) {
-                    uint8_t lo, hi;
-                    double x0 = bf16_value(xb[2 * j]);
-                    double x1 = bf16_value(xb[2 * j + 1]);
-                    if (sbc == 0) {
-                        lo = signbit(x0) ? 0x8 : 0x0;
-                        hi = signbit(x1) ? 0x8 : 0x0;
-                    } else {
-                        lo = e2m1_encode(x0, dec);
-                        hi = e2m1_encode(x1, dec);
-                    }
-                    qb[j] = (uint8_t)(lo | (hi << 4));
-                }
-            }
-        }
+        for (long r = r0; r < r0 + rows_per_group; ++r)
+            nvfp4_encode_row(x + r * ld, C, s_g, q + r * (C / 2), sb + r * (C / 16));
     }
+}
+
+/*
+ * The same block encoding of each row r of x[R, C] under an outer scale
+ * sg[r] given by the caller instead of taken from the row's own maximum.
+ * The online amax loop of [MT] 5.6 encodes each activation tile with the
+ * outer scale of the running row maximum, which may exceed the tile's own
+ * maximum; with sg[r] = fp32(max|x[r]| / 2688) this is the per-token
+ * quantizer above.  Every |x| must be at most 2688 sg[r] (not checked:
+ * larger values saturate the block scale at 448).
+ */
+void pqo_quantize_nvfp4_given_scale(const uint16_t *x, long R, long C, long ld,
+                                    const float *sg, uint8_t *q, uint8_t *sb)
+{
+    init_grids();
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < R; ++r)
+        nvfp4_encode_row(x + r * ld, C, sg[r], q + r * (C / 2), sb + r * (C / 16));
 }
 
 /* ------------------------------------------------------------------------ */

@@ -117,22 +117,42 @@ def nvfp4(xbits: np.ndarray, rows_per_group: int = 1):
         s_g = round_fp32(A / 2688)
         sg[g] = np.float32(float(s_g))
         for r in rows:
-            for blk in range(C // 16):
-                bits = [int(b) for b in xbits[r, blk * 16:(blk + 1) * 16]]
-                vals = [bf16_value(b) for b in bits]
-                ab = max(abs(v) for v in vals)
-                c_sb = 0 if s_g == 0 else nearest(E4M3, ab / (6 * s_g))
-                sb[r, blk] = c_sb
-                nib = []
-                for v, b in zip(vals, bits):
-                    sign = 8 if b & 0x8000 else 0
-                    if c_sb == 0:
-                        nib.append(sign)
-                    else:
-                        nib.append(sign | nearest(E2M1, v / (E4M3[c_sb] * s_g)))
-                for j in range(8):
-                    q[r, blk * 8 + j] = nib[2 * j] | (nib[2 * j + 1] << 4)
+            q[r], sb[r] = nvfp4_row_given_scale(xbits[r], s_g)
     return q, sb, sg
+
+
+def nvfp4_row_given_scale(xbits_row, s_g: Fr):
+    """NVFP4 blocks of one row under the outer scale s_g (a Fraction):
+    returns (q bytes [C/2], sb [C/16])."""
+    C = len(xbits_row)
+    q = np.zeros(C // 2, np.uint8)
+    sb = np.zeros(C // 16, np.uint8)
+    for blk in range(C // 16):
+        bits = [int(b) for b in xbits_row[blk * 16:(blk + 1) * 16]]
+        vals = [bf16_value(b) for b in bits]
+        ab = max(abs(v) for v in vals)
+        c_sb = 0 if s_g == 0 else nearest(E4M3, ab / (6 * s_g))
+        sb[blk] = c_sb
+        nib = []
+        for v, b in zip(vals, bits):
+            sign = 8 if b & 0x8000 else 0
+            if c_sb == 0:
+                nib.append(sign)
+            else:
+                nib.append(sign | nearest(E2M1, v / (E4M3[c_sb] * s_g)))
+        for j in range(8):
+            q[blk * 8 + j] = nib[2 * j] | (nib[2 * j + 1] << 4)
+    return q, sb
+
+
+def nvfp4_values(q_row, sb_row, s_g: Fr):
+    """Exact decoded values q * s_b * s_g of one row, as Fractions."""
+    out = []
+    for i in range(2 * len(q_row)):
+        nib = (int(q_row[i // 2]) >> (4 * (i % 2))) & 0xF
+        v = E2M1[nib & 7] * E4M3[int(sb_row[i // 16]) & 0x7F] * s_g
+        out.append(-v if nib & 8 else v)
+    return out
 
 
 def fp8_block(xbits: np.ndarray, block_rows: int):
