@@ -454,9 +454,34 @@ def main():
             reps += 1
         byt = R2 * (2 + 2 * (1 + 1 / 32))
         cpu = {"value": round(byt * reps / t_cpu / 1e9, 4), "unit": "GB/s",
-               "cores": int(oracle.lib().pqo_omp_threads()), "kind": "oracle",
+               "cores": oracle.threads(), "kind": "oracle",
                "sample": f"MXFP8 row+col quantize of the full 16384x2048 activation set, "
                          f"{reps} repetitions ({t_cpu:.1f} s)"}
+        # the same oracle on one thread, over the first 2048 rows
+        n1 = oracle.threads()
+        oracle.set_threads(1)
+        part = np.ascontiguousarray(host[:2048])
+        t1 = time.perf_counter()
+        oracle.quantize_mxfp8(part)
+        t_one = time.perf_counter() - t1
+        oracle.set_threads(n1)
+        cpu["single_thread"] = {"value": round(part.size * (2 + 2 * (1 + 1 / 32)) / t_one / 1e9, 4),
+                                "unit": "GB/s", "cores": 1,
+                                "sample": f"rows 0..2047 of the same set ({t_one:.1f} s)"}
+        # the grouped-GEMM oracle (exact decode, binary64 product) on one
+        # expert of the Qwen3 gate_up shape: 4096 rows x 2048 -> 1536
+        xa = wl.activations(4096, H, seed=31)
+        wb = wl.expert_weights(1, 2 * I4, H, 0.02, tag=31).reshape(2 * I4, H)
+        qa, sa = oracle.quantize_mxfp8_rowwise(xa)
+        qb, sb_ = oracle.quantize_mxfp8_rowwise(wb)
+        t1 = time.perf_counter()
+        a64, b64 = oracle.decode_mxfp8(qa, sa), oracle.decode_mxfp8(qb, sb_)
+        oracle.grouped_gemm(a64, b64[None], np.array([0, 4096]))
+        t_g = time.perf_counter() - t1
+        cpu["gemm"] = {"value": round(2 * 4096 * 2 * I4 * H / t_g / 1e12, 6), "unit": "TFLOP/s",
+                       "cores": oracle.threads(),
+                       "sample": f"MXFP8 grouped GEMM oracle, one expert of the Qwen3 gate_up "
+                                 f"shape (4096 x 2048 @ 2048 x 1536, {t_g:.2f} s), sampled"}
         log("cpu baseline", cpu)
 
     head = comp.get("mxfp8_quant", {})

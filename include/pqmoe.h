@@ -251,8 +251,14 @@ pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q,
  * out: Y in bf16 (rounded once) or binary32 per out_dtype.
  * K % 32 == 0 (MXFP8 FPROP / DGRAD), K % 16 == 0 (NVFP4), K % 8 and
  * N % 8 == 0 (BF16); BF16 WGRAD needs N % 8 == 0 and K % 8 == 0; NVFP4 and
- * block FP8 are FPROP only (PQM_ERR_ENUM otherwise).  No workspace is needed today:
- * pass NULL / 0 (the arguments keep the ABI stable).
+ * block FP8 are FPROP only (PQM_ERR_ENUM otherwise).
+ * workspace (device, optional): pqm_moe_grouped_gemm_workspace_size(fmt,
+ * kind) bytes, 4-byte aligned, contents irrelevant; the call overwrites
+ * them, so calls that may run at the same time need separate workspaces.
+ * Only the MXFP8 weight gradient uses one today (a tile counter: with it the
+ * tiles, heaviest experts first, go to whichever workgroup is free; without
+ * it they are dealt in a fixed order, same results either way).  NULL / 0,
+ * or a buffer that is too small or misaligned, means no workspace.
  * An empty contraction (K == 0) makes FPROP / DGRAD write zeros to rows
  * 0 .. offsets[G]-1 and read no operand; operand, scale and outer-scale
  * pointers are required (non-NULL) only when M_total, N and K are all
@@ -268,6 +274,10 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,
                                 void *out, pqm_dtype out_dtype,
                                 void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/* Workspace bytes pqm_moe_grouped_gemm can use for (fmt, kind): 4 for the
+ * MXFP8 weight gradient, 0 otherwise (host only, no device work). */
+size_t pqm_moe_grouped_gemm_workspace_size(pqm_format fmt, pqm_gemm_kind kind);
 
 /*
  * The MXFP8 gate_up grouped GEMM with its activation fused into the

@@ -77,6 +77,7 @@ def lib():
         L.pqo_bf16_round_array.argtypes = [P, Lg, P]
         L.pqo_inexact_count.restype = ctypes.c_long
         L.pqo_omp_threads.restype = ctypes.c_int
+        L.pqo_set_threads.argtypes = [ctypes.c_int]
         L.pqo_fp32_div.argtypes = [ctypes.c_float, ctypes.c_float]
         L.pqo_fp32_div.restype = ctypes.c_float
         _lib = L
@@ -241,6 +242,15 @@ def f64_to_bf16(v: np.ndarray) -> np.ndarray:
     out = np.empty(v.shape, np.uint16)
     lib().pqo_bf16_round_array(_ptr(v), v.size, _ptr(out))
     return out
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the C oracle's loops (timing only)."""
+    lib().pqo_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(lib().pqo_omp_threads())
 
 
 def inexact_count() -> int:

@@ -486,3 +486,4 @@ void pqo_bf16_round_array(const double *v, long n, uint16_t *out)
 }
 
 int pqo_omp_threads(void) { return omp_get_max_threads(); }
+void pqo_set_threads(int n) { omp_set_num_threads(n); }

@@ -145,8 +145,6 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
                                 int64_t M_total, int64_t N, int64_t K, void *out,
                                 pqm_dtype out_dtype, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (fmt != PQM_FMT_BF16 && fmt != PQM_FMT_MXFP8 && fmt != PQM_FMT_NVFP4 &&
       fmt != PQM_FMT_FP8_BLOCK)
     return PQM_ERR_ENUM;
@@ -185,9 +183,19 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
     return PQM_ERR_ALIGN;
   if (fmt == PQM_FMT_FP8_BLOCK && (!aligned(a_outer, 4) || !aligned(b_outer, 4)))
     return PQM_ERR_ALIGN;
+  // the workspace is optional; one that is too small or misaligned is unused
+  const int64_t ws_need = pqm::grouped_gemm_workspace_bytes((int)fmt, (int)kind);
+  uint32_t *ctr = ws_need > 0 && workspace && (int64_t)workspace_bytes >= ws_need &&
+                          aligned(workspace, 4)
+                      ? static_cast<uint32_t *>(workspace)
+                      : nullptr;
   return from_hip(pqm::launch_grouped_gemm((int)fmt, (int)kind, a, a_scale, a_outer, b, b_scale,
                                            b_outer, b_rows_per_scale, offsets, G, M_total, N,
-                                           K, out, out_dtype == PQM_OUT_FP32, stream));
+                                           K, out, out_dtype == PQM_OUT_FP32, ctr, stream));
+}
+
+size_t pqm_moe_grouped_gemm_workspace_size(pqm_format fmt, pqm_gemm_kind kind) {
+  return (size_t)pqm::grouped_gemm_workspace_bytes((int)fmt, (int)kind);
 }
 
 pqm_status pqm_moe_gemm_swiglu_quantize_mxfp8(const uint8_t *a, const uint8_t *a_scale,

@@ -133,6 +133,17 @@ def test_grouped_gemm_validation():
     assert f(*a) == 3
 
 
+def test_grouped_gemm_workspace_size():
+    """Only the MXFP8 weight gradient takes a workspace (its tile counter);
+    the query is host-only."""
+    ws = pqm.lib().pqm_moe_grouped_gemm_workspace_size
+    assert ws(1, 2) == 4
+    for fmt in (0, 1, 2, 3):
+        for kind in (0, 1, 2):
+            if (fmt, kind) != (1, 2):
+                assert ws(fmt, kind) == 0
+
+
 def test_glue_validation():
     L = pqm.lib()
     assert L.pqm_moe_route(A16, 8, 0, 4, 0, A16, A16, A16, A16, A16, 1 << 20, None) == 2

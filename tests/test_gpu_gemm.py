@@ -257,6 +257,41 @@ def test_mxfp8_wgrad(sizes, N, K):
             check_rows(got[g], want[g], f"mxfp8 wgrad {sizes} group {g}")
 
 
+@pytest.mark.parametrize("sizes,N,K", [
+    ([0, 37, 128, 1, 300], 192, 320),
+    ([5000, 0, 0, 96, 64, 32, 160], 544, 288),
+    ([int(v) for v in np.random.Generator(np.random.PCG64(61)).integers(0, 90, 300)], 64, 96),
+])
+@pytest.mark.parametrize("out_dtype", [pqm.OUT_FP32, pqm.OUT_BF16])
+def test_mxfp8_wgrad_kernels_agree(sizes, N, K, out_dtype):
+    """The persistent weight-gradient kernel against the general one, which
+    runs when an output row is not a whole number of 16-byte vectors (here
+    K - 1 columns of the same operands): the same MFMAs in the same token
+    order, so the same bits (empty experts, tails of 32 to 96 tokens, 300
+    experts over fewer workgroups than tiles); and with the tiles handed out
+    through the workspace counter or dealt in a fixed order."""
+    M = int(sum(sizes))
+    dy = _pad_rows(wl.activations(max(M, 1), N, seed=71)[:M], sizes)
+    x = _pad_rows(wl.activations(max(M, 1), K, seed=72)[:M], sizes)
+    off = dev(_offsets(_padded(sizes)))
+    _, _, aT, asT = pqm.quantize_mxfp8(dev_bf16(dy), rowwise=False)
+    _, _, bT, bsT = pqm.quantize_mxfp8(dev_bf16(x), rowwise=False)
+    y1 = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_WGRAD, aT, bT, off, N, K,
+                              a_scale=asT, b_scale=bsT, out_dtype=out_dtype)
+    y2 = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_WGRAD, aT, bT[:K - 1], off, N, K - 1,
+                              a_scale=asT, b_scale=bsT[:K - 1], out_dtype=out_dtype)
+    y3 = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_WGRAD, aT, bT, off, N, K,
+                              a_scale=asT, b_scale=bsT, out_dtype=out_dtype, workspace=False)
+    torch.cuda.synchronize()
+    it = torch.int32 if out_dtype == pqm.OUT_FP32 else torch.int16
+    a1, a2, a3 = (y.view(it).cpu().numpy() for y in (y1, y2, y3))
+    assert np.array_equal(a1[:, :, :K - 1], a2), f"wgrad kernels differ {sizes[:8]} N={N} K={K}"
+    assert np.array_equal(a1, a3), "handed-out and fixed tile orders differ"
+    for g, s in enumerate(sizes):
+        if s == 0:
+            assert not a1[g].any()
+
+
 def test_mxfp8_wgrad_bf16_out():
     y, want = _mxfp8_wgrad_case([300, 0, 129], 288, 192, seed=25, out_dtype=pqm.OUT_BF16)
     got = host_u16(y)
