@@ -2907,11 +2907,16 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(
 // exhaustively on gfx950) and one packed f16 multiply by M; q s_b has at most
 // 6 significant bits in [2^-10, 2688], exact in f16.  The outer scales
 // multiply the binary32 accumulator in the epilogue as in k_gemm_nvfp4.
-// Tile code TM: 128 or 256 rows by 256 columns, or 1128 = 128 rows by 512
-// columns (waves 64 x 256: fewer fragment decodes per MFMA than 64 x 128).
-template <int TM>
+// Tile configuration: TMR_ rows of A and TN_ rows of B (output columns) in
+// a slot; WM_ waves along M: 2 gives 2 x 2 waves of (TMR/2) x (TN/2)
+// outputs, 1 gives 1 x 4 waves of (32 FI_) x (TN/4) outputs, FI_ A fragments
+// per wave (rows of the slot past 32 FI_ WM_ are loaded but not multiplied,
+// so an expert's last tile of few rows multiplies only whole 32-row groups).
+// With 1 x 4 waves every wave decodes the tile's A fragments and its own
+// quarter of B: 8 decodes per 16 MFMAs at 128 x 512 against 10 with 2 x 2.
+template <int TMR_, int TN_, int WM_, int FI_>
 struct Np {
-  static constexpr int TMR = TM % 1000, TN = 256 * (1 + TM / 1000), ROWS = TMR + TN;
+  static constexpr int TMR = TMR_, TN = TN_, WM = WM_, ROWS = TMR + TN;
   static constexpr int SC = ROWS * 64;        // scale area offset in a slot
   static constexpr int SLOT = ROWS * 72;
   static constexpr int NSLOT = 3;  // 4 slots measured no faster
@@ -2919,19 +2924,22 @@ struct Np {
   static constexpr int CA = TMR / 64, CB = TN / 64;  // 16-byte data chunks per lane
   static constexpr int NS = ROWS / 128;              // 4-byte scale loads per lane
   static constexpr int OPS = CA + CB + NS;
-  static constexpr int FI = TMR / 64, FJ = TN / 64;
+  static constexpr int FI = FI_, FJ = TN * WM / 128;
+  static constexpr int WROWS = TMR / WM, WCOLS = TN * WM / 4;  // a wave's row / column offset step
+  static_assert(FI * 32 <= WROWS && FJ * 32 == WCOLS, "wave tile");
 };
+using NpPipe256 = Np<256, 256, 2, 4>;
+using NpPipe128 = Np<128, 256, 2, 2>;
 
-template <int TM>
+template <class C>
 struct NpSrc {
   const uint8_t *Ab, *Bb, *Asb, *Bsb;
-  uint32_t oa[Np<TM>::CA], ob[Np<TM>::CB], os[Np<TM>::NS];  // step-0 offsets
+  uint32_t oa[C::CA], ob[C::CB], os[C::NS];  // step-0 offsets
   uint32_t dst, sdst;  // LDS addresses of slot 0's data and scales, this wave
 };
 
-template <int TM>
-__device__ __forceinline__ void np_issue(const NpSrc<TM> &L, int kt, int slot) {
-  using C = Np<TM>;
+template <class C>
+__device__ __forceinline__ void np_issue(const NpSrc<C> &L, int kt, int slot) {
   const uint32_t kb = (uint32_t)kt * 64u, ks = (uint32_t)kt * 8u;
   const uint32_t base = L.dst + (uint32_t)slot * C::SLOT, sbase = L.sdst + (uint32_t)slot * C::SLOT;
 #pragma unroll
@@ -2944,9 +2952,8 @@ __device__ __forceinline__ void np_issue(const NpSrc<TM> &L, int kt, int slot) {
 }
 
 // Loads q0 .. q1-1 of np_issue's sequence (A chunks, B chunks, scale words).
-template <int TM, int Q0, int Q1>
-__device__ __forceinline__ void np_issue_range(const NpSrc<TM> &L, int kt, int slot) {
-  using C = Np<TM>;
+template <class C, int Q0, int Q1>
+__device__ __forceinline__ void np_issue_range(const NpSrc<C> &L, int kt, int slot) {
   const uint32_t kb = (uint32_t)kt * 64u, ks = (uint32_t)kt * 8u;
   const uint32_t base = L.dst + (uint32_t)slot * C::SLOT, sbase = L.sdst + (uint32_t)slot * C::SLOT;
 #pragma unroll
@@ -2971,19 +2978,18 @@ struct NpLane {
 // half 0 (chunk 2h: words 0..3 = sub-steps 0..3 = blocks 0, 1) and half 1
 // (chunk 2h + 1: sub-steps 4..7 = blocks 2, 3), plus one word holding the
 // 4 scale bytes of the lane's blocks.
-template <int TM>
+template <class C>
 struct NpHalf {
-  uint4 a[Np<TM>::FI], b[Np<TM>::FJ];
+  uint4 a[C::FI], b[C::FJ];
 };
-template <int TM>
+template <class C>
 struct NpWords {
-  uint32_t a[Np<TM>::FI], b[Np<TM>::FJ];
+  uint32_t a[C::FI], b[C::FJ];
 };
 
-template <int TM, int HALF>
+template <class C, int HALF>
 __device__ __forceinline__ void np_read_half(const uint8_t *lds, int slot, const NpLane &o,
-                                             NpHalf<TM> &R) {
-  using C = Np<TM>;
+                                             NpHalf<C> &R) {
   const uint8_t *cur = lds + slot * C::SLOT;
 #pragma unroll
   for (int i = 0; i < C::FI; ++i)
@@ -2993,10 +2999,9 @@ __device__ __forceinline__ void np_read_half(const uint8_t *lds, int slot, const
     R.b[j] = *reinterpret_cast<const uint4 *>(cur + (HALF ? o.b1 : o.b0) + 2048 * j);
 }
 
-template <int TM>
+template <class C>
 __device__ __forceinline__ void np_read_words(const uint8_t *lds, int slot, const NpLane &o,
-                                              NpWords<TM> &W) {
-  using C = Np<TM>;
+                                              NpWords<C> &W) {
   const uint8_t *cur = lds + slot * C::SLOT;
 #pragma unroll
   for (int i = 0; i < C::FI; ++i) W.a[i] = *reinterpret_cast<const uint32_t *>(cur + o.sa + 256 * i);
@@ -3038,45 +3043,45 @@ __device__ __forceinline__ uint32_t u4_word(const uint4 &u) {
 
 // Block scales of one block of every fragment, and the fp16 operands of one
 // sub-step.
-template <int TM>
+template <class C>
 struct NpScales {
-  NpScale a[Np<TM>::FI], b[Np<TM>::FJ];
+  NpScale a[C::FI], b[C::FJ];
 };
-template <int TM>
+template <class C>
 struct NpDec {
-  v8h a[Np<TM>::FI], b[Np<TM>::FJ];
+  v8h a[C::FI], b[C::FJ];
 };
 
-template <int TM, int BLK>
-__device__ __forceinline__ void np_scales(const NpWords<TM> &W, NpScales<TM> &S) {
+template <class C, int BLK>
+__device__ __forceinline__ void np_scales(const NpWords<C> &W, NpScales<C> &S) {
 #pragma unroll
-  for (int i = 0; i < Np<TM>::FI; ++i) S.a[i] = np_scale<BLK>(W.a[i]);
+  for (int i = 0; i < C::FI; ++i) S.a[i] = np_scale<BLK>(W.a[i]);
 #pragma unroll
-  for (int j = 0; j < Np<TM>::FJ; ++j) S.b[j] = np_scale<BLK>(W.b[j]);
+  for (int j = 0; j < C::FJ; ++j) S.b[j] = np_scale<BLK>(W.b[j]);
 }
 
-template <int TM, int WORD>
-__device__ __forceinline__ void np_dec(const NpHalf<TM> &R, const NpScales<TM> &S, NpDec<TM> &X) {
+template <class C, int WORD>
+__device__ __forceinline__ void np_dec(const NpHalf<C> &R, const NpScales<C> &S, NpDec<C> &X) {
 #pragma unroll
-  for (int i = 0; i < Np<TM>::FI; ++i) X.a[i] = np_decode(u4_word<WORD>(R.a[i]), S.a[i]);
+  for (int i = 0; i < C::FI; ++i) X.a[i] = np_decode(u4_word<WORD>(R.a[i]), S.a[i]);
 #pragma unroll
-  for (int j = 0; j < Np<TM>::FJ; ++j) X.b[j] = np_decode(u4_word<WORD>(R.b[j]), S.b[j]);
+  for (int j = 0; j < C::FJ; ++j) X.b[j] = np_decode(u4_word<WORD>(R.b[j]), S.b[j]);
 }
 
 // The MFMAs of one decoded sub-step; the instructions placed before them in
 // the same scheduling region (the next sub-step's decode) are spread between
 // them: each MFMA keeps the matrix core busy for 32 cycles while the wave
 // issues up to 6 VALU instructions.
-template <int TM>
-__device__ __forceinline__ void np_mfmas(const NpDec<TM> &X,
-                                         v16f (&acc)[Np<TM>::FI][Np<TM>::FJ]) {
+template <class C>
+__device__ __forceinline__ void np_mfmas(const NpDec<C> &X,
+                                         v16f (&acc)[C::FI][C::FJ]) {
 #pragma unroll
-  for (int j = 0; j < Np<TM>::FJ; ++j)
+  for (int j = 0; j < C::FJ; ++j)
 #pragma unroll
-    for (int i = 0; i < Np<TM>::FI; ++i)
+    for (int i = 0; i < C::FI; ++i)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(X.b[j], X.a[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-  for (int m = 0; m < Np<TM>::FI * Np<TM>::FJ; ++m) {
+  for (int m = 0; m < C::FI * C::FJ; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then VALU
   }
@@ -3091,44 +3096,44 @@ __device__ __forceinline__ void np_mfmas(const NpDec<TM> &X,
 // and the last sub-step's MFMAs cover the decode of step kt + 1's sub-step
 // 0.  So one set of raw registers serves two steps, and the registers saved
 // hold the second decoded sub-step.
-template <int TM>
-__device__ __forceinline__ void np_step(const NpSrc<TM> &L, int rk, int slot,
+template <class C>
+__device__ __forceinline__ void np_step(const NpSrc<C> &L, int rk, int slot,
                                         const uint8_t *lds, const NpLane &o, int nslot,
-                                        v16f (&acc)[Np<TM>::FI][Np<TM>::FJ], NpHalf<TM> &R0,
-                                        NpHalf<TM> &R1, NpWords<TM> &W, NpScales<TM> &S,
-                                        NpDec<TM> &X, NpDec<TM> &Y) {
-  constexpr int NQ = Np<TM>::OPS, H1 = (NQ + 1) / 2;
-  np_dec<TM, 1>(R0, S, Y);                 // s = 1 (block 0)
-  np_mfmas<TM>(X, acc);                    // s = 0
+                                        v16f (&acc)[C::FI][C::FJ], NpHalf<C> &R0,
+                                        NpHalf<C> &R1, NpWords<C> &W, NpScales<C> &S,
+                                        NpDec<C> &X, NpDec<C> &Y) {
+  constexpr int NQ = C::OPS, H1 = (NQ + 1) / 2;
+  np_dec<C, 1>(R0, S, Y);                 // s = 1 (block 0)
+  np_mfmas<C>(X, acc);                    // s = 0
   // the refill of `slot` with step rk, in two halves issued while the last
   // MFMAs of sub-steps 0 and 1 run
-  np_issue_range<TM, 0, H1>(L, rk, slot);
-  np_scales<TM, 1>(W, S);
-  np_dec<TM, 2>(R0, S, X);                 // s = 2 (block 1)
-  np_mfmas<TM>(Y, acc);                    // s = 1
-  np_issue_range<TM, H1, NQ>(L, rk, slot);
-  np_dec<TM, 3>(R0, S, Y);                 // s = 3
-  np_mfmas<TM>(X, acc);                    // s = 2
-  np_scales<TM, 2>(W, S);
-  np_dec<TM, 0>(R1, S, X);                 // s = 4 (block 2)
-  np_mfmas<TM>(Y, acc);                    // s = 3
-  np_read_half<TM, 0>(lds, nslot, o, R0);  // step kt + 1, half 0
-  NpWords<TM> Wn;
-  np_read_words<TM>(lds, nslot, o, Wn);
+  np_issue_range<C, 0, H1>(L, rk, slot);
+  np_scales<C, 1>(W, S);
+  np_dec<C, 2>(R0, S, X);                 // s = 2 (block 1)
+  np_mfmas<C>(Y, acc);                    // s = 1
+  np_issue_range<C, H1, NQ>(L, rk, slot);
+  np_dec<C, 3>(R0, S, Y);                 // s = 3
+  np_mfmas<C>(X, acc);                    // s = 2
+  np_scales<C, 2>(W, S);
+  np_dec<C, 0>(R1, S, X);                 // s = 4 (block 2)
+  np_mfmas<C>(Y, acc);                    // s = 3
+  np_read_half<C, 0>(lds, nslot, o, R0);  // step kt + 1, half 0
+  NpWords<C> Wn;
+  np_read_words<C>(lds, nslot, o, Wn);
   __builtin_amdgcn_sched_barrier(0);
-  np_dec<TM, 1>(R1, S, Y);                 // s = 5
-  np_mfmas<TM>(X, acc);                    // s = 4
-  np_scales<TM, 3>(W, S);
-  np_dec<TM, 2>(R1, S, X);                 // s = 6 (block 3)
-  np_mfmas<TM>(Y, acc);                    // s = 5
-  np_dec<TM, 3>(R1, S, Y);                 // s = 7
-  np_mfmas<TM>(X, acc);                    // s = 6
-  np_read_half<TM, 1>(lds, nslot, o, R1);  // step kt + 1, half 1
+  np_dec<C, 1>(R1, S, Y);                 // s = 5
+  np_mfmas<C>(X, acc);                    // s = 4
+  np_scales<C, 3>(W, S);
+  np_dec<C, 2>(R1, S, X);                 // s = 6 (block 3)
+  np_mfmas<C>(Y, acc);                    // s = 5
+  np_dec<C, 3>(R1, S, Y);                 // s = 7
+  np_mfmas<C>(X, acc);                    // s = 6
+  np_read_half<C, 1>(lds, nslot, o, R1);  // step kt + 1, half 1
   __builtin_amdgcn_sched_barrier(0);
   W = Wn;
-  np_scales<TM, 0>(W, S);
-  np_dec<TM, 0>(R0, S, X);                 // step kt + 1, s = 0
-  np_mfmas<TM>(Y, acc);                    // s = 7
+  np_scales<C, 0>(W, S);
+  np_dec<C, 0>(R0, S, X);                 // step kt + 1, s = 0
+  np_mfmas<C>(Y, acc);                    // s = 7
 }
 
 // Store one transposed accumulator with the outer scales: as mx3_store, each
@@ -3185,7 +3190,7 @@ __device__ __forceinline__ void np_store(const v16f &acc, void *out, int64_t N, 
   }
 }
 
-template <bool OUT_F32, int TM>
+template <bool OUT_F32, class C>
 __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
                                         const uint8_t *__restrict__ As,
                                         const float *__restrict__ Ao,
@@ -3193,14 +3198,14 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
                                         const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
                                         const TileInfo &ti, uint8_t *lds, const float *ab,
                                         void *__restrict__ out) {
-  using C = Np<TM>;
   constexpr int FI = C::FI, FJ = C::FJ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
+  const int wm = C::WM == 2 ? wave >> 1 : 0, wn = C::WM == 2 ? wave & 1 : wave;
+  const int h = lane >> 5, r32 = lane & 31;
   const uint32_t KD = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);  // row bytes of data / scales
   const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)C::TMR);
   const int rows_b = (int)min(N - ti.n0, (int64_t)C::TN);
-  NpSrc<TM> L;
+  NpSrc<C> L;
   L.Ab = A + ti.row0 * (int64_t)KD;
   L.Bb = B + (ti.g * N + ti.n0) * (int64_t)KD;
   L.Asb = As + ti.row0 * (int64_t)KS;
@@ -3225,7 +3230,7 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
   }
   NpLane o;
   {
-    const int ra = wm * (C::TMR / 2) + r32, rb = wn * (C::TN / 2) + r32;
+    const int ra = wm * C::WROWS + r32, rb = wn * C::WCOLS + r32;
     o.a0 = mx3_off(ra, 2 * h);
     o.a1 = mx3_off(ra, 2 * h + 1);
     o.b0 = C::TMR * 64 + mx3_off(rb, 2 * h);
@@ -3243,18 +3248,18 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
 
   const int nk = (int)(K / 128);  // even, >= 2
 #pragma unroll
-  for (int s = 0; s < C::NSLOT; ++s) np_issue<TM>(L, min(s, nk - 1), s);
+  for (int s = 0; s < C::NSLOT; ++s) np_issue<C>(L, min(s, nk - 1), s);
   vm_wait<(C::NSLOT - 1) * C::OPS>();  // step 0
   __builtin_amdgcn_s_barrier();
-  NpHalf<TM> R0, R1;
-  NpWords<TM> W;
-  NpScales<TM> S;
-  NpDec<TM> X, Y;
-  np_read_half<TM, 0>(lds, 0, o, R0);
-  np_read_half<TM, 1>(lds, 0, o, R1);
-  np_read_words<TM>(lds, 0, o, W);
-  np_scales<TM, 0>(W, S);
-  np_dec<TM, 0>(R0, S, X);
+  NpHalf<C> R0, R1;
+  NpWords<C> W;
+  NpScales<C> S;
+  NpDec<C> X, Y;
+  np_read_half<C, 0>(lds, 0, o, R0);
+  np_read_half<C, 1>(lds, 0, o, R1);
+  np_read_words<C>(lds, 0, o, W);
+  np_scales<C, 0>(W, S);
+  np_dec<C, 0>(R0, S, X);
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
     // own loads of step kt + 1 done (step kt + 2 may be pending), own reads
@@ -3267,7 +3272,7 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
     const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;
     // past the last step the reads take the slot's repeated last step (in
     // bounds; decoded, never multiplied)
-    np_step<TM>(L, min(kt + C::NSLOT, nk - 1), slot, lds, o, nslot, acc, R0, R1, W, S, X, Y);
+    np_step<C>(L, min(kt + C::NSLOT, nk - 1), slot, lds, o, nslot, acc, R0, R1, W, S, X, Y);
     slot = nslot;
   }
   vm_wait<0>();
@@ -3275,8 +3280,8 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
   for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < FJ; ++j)
-      np_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (C::TMR / 2) + 32 * i,
-                        wn * (C::TN / 2) + 32 * j, Ao, ab);
+      np_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * C::WROWS + 32 * i,
+                        wn * C::WCOLS + 32 * j, Ao, ab);
 }
 
 // 256 x 256 tiles (an expert's last tile of <= 128 rows as 128 x 256);
@@ -3288,8 +3293,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_pipe(
     const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
     void *__restrict__ out) {
-  static_assert(Np<128>::LDS <= Np<256>::LDS, "LDS of the half tile");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[Np<256>::LDS];
+  static_assert(NpPipe128::LDS <= NpPipe256::LDS, "LDS of the half tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NpPipe256::LDS];
   __shared__ float ab[256];
   __shared__ int64_t sh[4];
   TileInfo ti;
@@ -3300,14 +3305,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_pipe(
   }
   __syncthreads();
   if (ti.row_end - ti.row0 <= 128)
-    np_tile<OUT_F32, 128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+    np_tile<OUT_F32, NpPipe128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
   else
-    np_tile<OUT_F32, 256>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+    np_tile<OUT_F32, NpPipe256>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
 }
 
-// 128 x 512 tiles (tile code 1128) for experts of few rows each: a wave
-// holds 64 x 256 outputs, so a sub-step decodes 2 + 8 fragments for 16 MFMAs
-// instead of 2 + 4 for 8.
+// 128 x 512 tiles for experts of few rows each, 1 x 4 waves of 128 x 128
+// (a sub-step decodes 4 + 4 fragments for 16 MFMAs); an expert's last tile
+// multiplies only the 32-row groups that hold rows (with the DeepSeek-V3
+// routing, median 88 rows per expert, 1.11x the routed rows instead of 1.33x).
 template <bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
@@ -3315,7 +3321,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
     const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
     void *__restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[Np<1128>::LDS];
+  using W4 = Np<128, 512, 1, 4>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[W4::LDS];
   __shared__ float ab[512];
   __shared__ int64_t sh[4];
   TileInfo ti;
@@ -3325,7 +3332,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
     ab[c] = col < N ? Bo[(ti.g * N + col) / b_rps] : 0.0f;
   }
   __syncthreads();
-  np_tile<OUT_F32, 1128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+  const int64_t rows = ti.row_end - ti.row0;
+  if (rows > 96)
+    np_tile<OUT_F32, W4>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+  else if (rows > 64)
+    np_tile<OUT_F32, Np<128, 512, 1, 3>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+  else if (rows > 32)
+    np_tile<OUT_F32, Np<128, 512, 1, 2>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+  else
+    np_tile<OUT_F32, Np<128, 512, 1, 1>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
 }
 
 // ------------------------------------------------------------------ launch
