@@ -441,6 +441,30 @@ pqm_status pqm_swiglu_prob_quantize_nvfp4(const uint16_t *c, const float *prob,
                                           float *s_outer, hipStream_t stream);
 
 /*
+ * Opt-in check of an offsets array against the grouped-GEMM contract ([MT]
+ * 5.2: experts' rows in one contiguous buffer described by offsets on the
+ * device); the GEMMs and the glue never check it themselves, since a bad
+ * array is undefined behaviour there.  Scans i = 0 .. G and writes, on the
+ * stream, to result (device, 2 x int32): result[0] = the first failing check
+ * at the smallest failing index (0: the array is valid), result[1] = that
+ * index (-1 when valid).  Checks at index i, in this order:
+ *   PQM_OFFSETS_FIRST_NOT_ZERO  i == 0 and offsets[0] != 0
+ *   PQM_OFFSETS_DECREASING      i < G and offsets[i + 1] < offsets[i]
+ *   PQM_OFFSETS_MISALIGNED      offsets[i] % align != 0 (align = 32 for the
+ *                               MXFP8 weight gradient's padded groups, else 1)
+ *   PQM_OFFSETS_PAST_END        i == G and offsets[G] > M_total
+ * G >= 0, M_total >= 0, align >= 1 (PQM_ERR_SHAPE); offsets 8-byte and result
+ * 4-byte aligned (PQM_ERR_ALIGN), both non-NULL (PQM_ERR_NULL).  Reads
+ * offsets[0 .. G]; one workgroup.
+ */
+#define PQM_OFFSETS_FIRST_NOT_ZERO 1
+#define PQM_OFFSETS_DECREASING 2
+#define PQM_OFFSETS_MISALIGNED 3
+#define PQM_OFFSETS_PAST_END 4
+pqm_status pqm_validate_offsets(const int64_t *offsets, int64_t G, int64_t M_total,
+                                int64_t align, int32_t *result, hipStream_t stream);
+
+/*
  * Combine: out[t, n] = bf16( sum_j y_rows[slot[t, j], n] + shared[t, n] ),
  * summed in binary32 in j order (shared may be NULL).  y_rows, shared, out
  * bf16 with N contiguous; N % 8 == 0.

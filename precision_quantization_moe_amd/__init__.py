@@ -15,5 +15,6 @@ from ._binding import (  # noqa: F401
     moe_gemm_swiglu_quantize_mxfp8, moe_grouped_gemm, moe_route, moe_route_noalloc, pad_rows_bound, quantize_fp8_block,
     quantize_mxfp8,
     quantize_nvfp4_per_token, swiglu_prob, swiglu_prob_quantize_mxfp8, swiglu_prob_quantize_nvfp4,
-    LIB_PATH,
+    validate_offsets, OFFSETS_FIRST_NOT_ZERO, OFFSETS_DECREASING, OFFSETS_MISALIGNED,
+    OFFSETS_PAST_END, LIB_PATH,
 )

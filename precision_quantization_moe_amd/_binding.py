@@ -50,6 +50,7 @@ SIGNATURES = {
     "pqm_swiglu_prob_quantize_mxfp8": ([P, P, P, I64, I64, P, P, P, P], I32),
     "pqm_swiglu_prob_quantize_nvfp4": ([P, P, P, I64, I64, P, P, P, P, P], I32),
     "pqm_moe_combine": ([P, P, P, I64, I64, I64, P, P], I32),
+    "pqm_validate_offsets": ([P, I64, I64, I64, P, P], I32),
 }
 
 
@@ -347,3 +348,18 @@ def moe_combine(y_rows: torch.Tensor, slot: torch.Tensor, shared: torch.Tensor |
     _check(lib().pqm_moe_combine(_ptr(y_rows), _ptr(slot), _ptr(shared), T, k, N, _ptr(out),
                                  _stream(y_rows.device)), "pqm_moe_combine")
     return out
+
+
+OFFSETS_FIRST_NOT_ZERO, OFFSETS_DECREASING, OFFSETS_MISALIGNED, OFFSETS_PAST_END = 1, 2, 3, 4
+
+
+def validate_offsets(offsets: torch.Tensor, M_total: int, align: int = 1):
+    """Opt-in check of an offsets array (int64 [G+1] on the device) against
+    the grouped-GEMM contract.  Returns an int32 device tensor [2]: (first
+    failing check or 0, its index or -1); see pqm_validate_offsets."""
+    G = offsets.numel() - 1
+    res = torch.empty((2,), dtype=torch.int32, device=offsets.device)
+    _check(lib().pqm_validate_offsets(_ptr(offsets), G, M_total, align, _ptr(res),
+                                      _stream(offsets.device)),
+           "pqm_validate_offsets")
+    return res

@@ -445,6 +445,48 @@ hipError_t launch_pad_rows(const void *src, int64_t row_bytes, const int64_t *of
   return hipGetLastError();
 }
 
+// Offsets check for callers that want one (the GEMMs take the offsets on
+// trust): scan i = 0 .. G and report the first index that breaks the
+// contract, with the first check it breaks at that index.  One workgroup;
+// each thread keeps its first failure, then a block minimum.
+__global__ __launch_bounds__(1024) void k_validate_offsets(const int64_t *__restrict__ off,
+                                                            int64_t G, int64_t M_total,
+                                                            int64_t align,
+                                                            int32_t *__restrict__ result) {
+  __shared__ int64_t best[1024];
+  int64_t mine = INT64_MAX;  // (index << 3) | code of this thread's first failure
+  for (int64_t i = threadIdx.x; i <= G; i += blockDim.x) {
+    const int64_t v = off[i];
+    int code = 0;
+    if (i == 0 && v != 0) code = PQM_OFFSETS_FIRST_NOT_ZERO;
+    else if (i < G && off[i + 1] < v) code = PQM_OFFSETS_DECREASING;
+    else if (v % align != 0) code = PQM_OFFSETS_MISALIGNED;
+    else if (i == G && v > M_total) code = PQM_OFFSETS_PAST_END;
+    if (code) {
+      mine = (i << 3) | code;
+      break;  // later indices of this thread are larger
+    }
+  }
+  best[threadIdx.x] = mine;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) best[threadIdx.x] = min(best[threadIdx.x], best[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int64_t b = best[0];
+    result[0] = b == INT64_MAX ? 0 : (int32_t)(b & 7);
+    result[1] = b == INT64_MAX ? -1 : (int32_t)min(b >> 3, (int64_t)INT32_MAX);
+  }
+}
+
+hipError_t launch_validate_offsets(const int64_t *off, int64_t G, int64_t M_total, int64_t align,
+                                   int32_t *result, hipStream_t st) {
+  hipLaunchKernelGGL(k_validate_offsets, dim3(1), dim3(1024), 0, st, off, G, M_total, align,
+                     result);
+  return hipGetLastError();
+}
+
 }  // namespace pqm
 
 namespace {
@@ -564,6 +606,14 @@ pqm_status pqm_moe_combine(const uint16_t *y_rows, const int32_t *slot, const ui
   if (!y_rows || !slot || !out) return PQM_ERR_NULL;
   if (!al(y_rows, 16) || !al(out, 16) || (shared && !al(shared, 16))) return PQM_ERR_ALIGN;
   return st_of(pqm::launch_combine(y_rows, slot, shared, tokens, k, N, out, stream));
+}
+
+pqm_status pqm_validate_offsets(const int64_t *offsets, int64_t G, int64_t M_total, int64_t align,
+                                int32_t *result, hipStream_t stream) {
+  if (G < 0 || M_total < 0 || align < 1) return PQM_ERR_SHAPE;
+  if (!offsets || !result) return PQM_ERR_NULL;
+  if (!al(offsets, 8) || !al(result, 4)) return PQM_ERR_ALIGN;
+  return st_of(pqm::launch_validate_offsets(offsets, G, M_total, align, result, stream));
 }
 
 }  // extern "C"

@@ -54,5 +54,7 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
 // Workspace bytes the grouped GEMM uses for (fmt, kind): a tile counter for
 // the MXFP8 weight gradient, none otherwise.
 int64_t grouped_gemm_workspace_bytes(int fmt, int kind);
+hipError_t launch_validate_offsets(const int64_t *off, int64_t G, int64_t M_total, int64_t align,
+                                   int32_t *result, hipStream_t st);
 
 }  // namespace pqm

@@ -144,6 +144,17 @@ def test_grouped_gemm_workspace_size():
                 assert ws(fmt, kind) == 0
 
 
+def test_validate_offsets_arguments():
+    f = pqm.lib().pqm_validate_offsets
+    assert f(A16, -1, 10, 1, A16, None) == 2
+    assert f(A16, 3, -1, 1, A16, None) == 2
+    assert f(A16, 3, 10, 0, A16, None) == 2
+    assert f(None, 3, 10, 1, A16, None) == 1
+    assert f(A16, 3, 10, 1, None, None) == 1
+    assert f(BAD, 3, 10, 1, A16, None) == 3
+    assert f(A16, 3, 10, 1, BAD, None) == 3
+
+
 def test_glue_validation():
     L = pqm.lib()
     assert L.pqm_moe_route(A16, 8, 0, 4, 0, A16, A16, A16, A16, A16, 1 << 20, None) == 2

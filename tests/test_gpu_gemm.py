@@ -488,6 +488,9 @@ def _nvfp4_case(sizes, N, K, seed, brps=None):
     ([300, 0, 513, 129, 64], 520, 512, 260),   # scale boundaries inside 8-column runs
     ([600, 0, 513, 129], 520, 768, None),      # > 256 rows per expert on average: 256- and 128-row tiles
     ([300, 0, 513, 129, 64], 384, 512, None),  # N < 512: 256- and 128-row tiles
+    # 128 x 512 tiles whose last 32-row groups are partly empty: 1, 2, 3 and 4
+    # groups multiplied, tails of 1, 32, 33, 64, 65, 96, 97, 127 rows
+    ([70, 100, 127, 33, 32, 96, 0, 1, 128, 65, 64, 97], 520, 512, None),
 ])
 def test_nvfp4_fprop_ragged(case):
     sizes, N, K, brps = case

@@ -599,6 +599,17 @@ def test_silu_and_swiglu_identities():
     assert np.allclose(d, [[50.0] * 3, [25.0] * 3], rtol=1e-15)
 
 
+def test_silu_against_torch():
+    """The oracle's silu against an independent implementation (torch's
+    binary64 SiLU, its own exponential): within a few binary64 ulps over
+    [-745, 745], including the range where exp(-z) overflows (result -0)."""
+    z = np.concatenate([np.linspace(-745, 745, 20001), [-1e-300, 1e-300, -50.5, 88.7]])
+    got = oracle.silu(z)
+    want = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    assert np.all(np.abs(got - want) <= 4 * np.finfo(np.float64).eps * np.abs(want) + 1e-300)
+    assert oracle.silu(np.array([-800.0]))[0] == 0.0
+
+
 def test_combine_sums_slots():
     y = np.arange(12, dtype=np.float64).reshape(6, 2)
     slot = np.array([[0, 5], [2, 3], [1, 4]])
