@@ -1138,6 +1138,32 @@ __device__ __forceinline__ int32_t qp_scan512(int32_t v, int32_t &carry, int32_t
   return before + incl - v;
 }
 
+// 4 x 4 transpose of 4-dword groups inside every quad of lanes (lanes
+// 4a + b, b = 0..3): group k of lane b ends up holding what group b of lane
+// k held, in two exchange stages with the lanes b ^ 1 and b ^ 2 (DPP quad
+// permutes, selects only, so the groups stay in registers).  Used to turn a
+// 32 x 32 accumulator layout (one row per lane) into stores that each write
+// eight whole 128-byte rows.
+typedef uint32_t pqm_v16u __attribute__((ext_vector_type(16)));
+template <int S>
+__device__ __forceinline__ pqm_v16u quad_stage(pqm_v16u v, bool hi) {
+  pqm_v16u r = v;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {  // the 8 registers of the groups g0 with bit S clear
+    const int g0 = S == 1 ? 2 * (q >> 2) : (q >> 2), e = q & 3;
+    const int x0 = 4 * g0 + e, x1 = 4 * (g0 | S) + e;
+    const uint32_t send = hi ? v[x0] : v[x1];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, S == 1 ? 0xB1 : 0x4E,
+                                                               0xF, 0xF, false);
+    r[x0] = hi ? recv : v[x0];
+    r[x1] = hi ? v[x1] : recv;
+  }
+  return r;
+}
+__device__ __forceinline__ pqm_v16u quad_transpose(pqm_v16u v, int b) {
+  return quad_stage<2>(quad_stage<1>(v, (b & 1) != 0), (b & 2) != 0);
+}
+
 template <bool OUT_F32>
 __device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffer_rsrc_t rs,
                                          const QpTile &t, int64_t N) {
@@ -1147,25 +1173,41 @@ __device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffe
   const uint32_t Nu = (uint32_t)N;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = t.row0 + wm * 128 + 32 * i + r32;
-    const bool rok = row < t.row_end;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const v16f &a = acc[i][j];
       const int cb = t.n0 + wn * 64 + 32 * j;
       if (OUT_F32) {
+        // binary32: group g of lane (h, r) is row r at columns 8 g + 4 h ..
+        // + 3; after the quad transpose group k of lane (h, 4 a + b) is row
+        // 4 a + k at columns 4 (2 b + h) .. + 3, so each store writes eight
+        // whole 128-byte rows
+        const int b = r32 & 3, a4 = r32 >> 2;
+        const pqm_v16u v = quad_transpose(__builtin_bit_cast(pqm_v16u, a), b);
+        const uint32_t col = (uint32_t)(cb + 4 * (2 * b + h));
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t col = (uint32_t)(cb + 8 * g + 4 * h);
-          const uint32_t off = rok && col < Nu ? ((uint32_t)row * Nu + col) * 4u : QP_OOB;
-          const u32x4 w = {__float_as_uint(a[4 * g]), __float_as_uint(a[4 * g + 1]),
-                           __float_as_uint(a[4 * g + 2]), __float_as_uint(a[4 * g + 3])};
+        for (int k = 0; k < 4; ++k) {
+          const int rowk = t.row0 + wm * 128 + 32 * i + 4 * a4 + k;
+          const uint32_t off =
+              rowk < t.row_end && col < Nu ? ((uint32_t)rowk * Nu + col) * 4u : QP_OOB;
+          const u32x4 w = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
           __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
         }
-      } else {
+      }
+    }
+    if (!OUT_F32) {
+      // bf16: lane (h, r) holds row r's 16-byte chunks 4 j + 2 p + h of the
+      // wave's 64 columns (runs 2p, 2p+1 traded between lane halves as in
+      // mx3_store); a quad transpose of those 4 chunks leaves in chunk k of
+      // lane (h, 4 a + b) row 4 a + k's chunk 2 b + h, so each store writes
+      // eight whole 128-byte rows
+      pqm_v16u v;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          float lo[4], hi[4];  // as mx3_store: runs 2p, 2p+1 traded between lane halves
+          const v16f &a = acc[i][j];
+          float lo[4], hi[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = a[8 * p + e], y = a[8 * p + 4 + e];
@@ -1175,12 +1217,23 @@ __device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffe
             lo[e] = h ? got : x;
             hi[e] = h ? y : got;
           }
-          const uint32_t col = (uint32_t)(cb + 16 * p + 8 * h);
-          const uint32_t off = rok && col < Nu ? ((uint32_t)row * Nu + col) * 2u : QP_OOB;
-          const u32x4 w = {pk_bf16_rne(lo[0], lo[1]), pk_bf16_rne(lo[2], lo[3]),
-                           pk_bf16_rne(hi[0], hi[1]), pk_bf16_rne(hi[2], hi[3])};
-          __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
+          const int m = 2 * j + p;
+          v[4 * m] = pk_bf16_rne(lo[0], lo[1]);
+          v[4 * m + 1] = pk_bf16_rne(lo[2], lo[3]);
+          v[4 * m + 2] = pk_bf16_rne(hi[0], hi[1]);
+          v[4 * m + 3] = pk_bf16_rne(hi[2], hi[3]);
         }
+      }
+      const int b = r32 & 3, a4 = r32 >> 2;
+      v = quad_transpose(v, b);
+      const uint32_t col = (uint32_t)(t.n0 + wn * 64 + 8 * (2 * b + h));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int rowk = t.row0 + wm * 128 + 32 * i + 4 * a4 + k;
+        const uint32_t off =
+            rowk < t.row_end && col < Nu ? ((uint32_t)rowk * Nu + col) * 2u : QP_OOB;
+        const u32x4 w = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
       }
     }
   }
@@ -1801,57 +1854,6 @@ __device__ __forceinline__ void mw_half(const MwSrc &L, const uint8_t *lds, cons
 
 __device__ __forceinline__ int mw_steps(int32_t len) { return len > 0 ? (len + 127) / 128 : 1; }
 
-// Binary32 tile store in whole 128-byte lines.  In the transposed
-// accumulator, lane (h, r) of a 32 x 32 fragment holds row r at columns
-// 8 g + 4 h + e (register 4 g + e), so a plain store writes 32 bytes of each
-// of 32 rows.  A 4 x 4 transpose of the 4-register groups inside every quad
-// of lanes r = 4 a + b (two exchange stages, with the lanes b ^ 1 and b ^ 2)
-// leaves in group k of lane (h, 4 a + b) row 4 a + k at columns
-// 4 (2 b + h) .. + 3, so that store k writes eight whole rows 4 a + k, one
-// 128-byte line each (measured 1.6x faster for a weight gradient's output
-// than the 32-byte pieces).  32 stores per lane, as qp_store; rows past the
-// tile's end or columns past N get the dropped offset.
-template <int S>
-__device__ __forceinline__ v16f mw_quad_stage(v16f v, bool hi) {
-  v16f r = v;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {  // the 8 registers of the groups g0 with bit S clear
-    const int g0 = S == 1 ? 2 * (q >> 2) : (q >> 2), e = q & 3;
-    const int x0 = 4 * g0 + e, x1 = 4 * (g0 | S) + e;
-    const float send = hi ? v[x0] : v[x1];
-    const float recv = __int_as_float(__builtin_amdgcn_update_dpp(
-        0, __float_as_int(send), S == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false));
-    r[x0] = hi ? recv : v[x0];
-    r[x1] = hi ? v[x1] : recv;
-  }
-  return r;
-}
-
-__device__ __forceinline__ void mw_store_f32(const v16f (&acc)[4][2], __amdgpu_buffer_rsrc_t rs,
-                                             const QpTile &t, int64_t N) {
-  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, b = lane & 3, a = (lane >> 2) & 7;
-  const uint32_t Nu = (uint32_t)N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const v16f v = mw_quad_stage<2>(mw_quad_stage<1>(acc[i][j], (b & 1) != 0), (b & 2) != 0);
-      const uint32_t col = (uint32_t)(t.n0 + wn * 64 + 32 * j + 4 * (2 * b + h));
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int row = t.row0 + wm * 128 + 32 * i + 4 * a + k;
-        const uint32_t off =
-            row < t.row_end && col < Nu ? ((uint32_t)row * Nu + col) * 4u : QP_OOB;
-        const u32x4 w = {__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
-                         __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
-      }
-    }
-  }
-}
-
 // The reader's scale byte offsets for tile t: row shift of A row wm 128 + r
 // and of B row wn 64 + r.
 __device__ __forceinline__ void mw_shifts(MqLane &o, const MwTile &t, int64_t M) {
@@ -2021,10 +2023,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_wgrad_qp(
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           static_cast<uint8_t *>(out) + (int64_t)ct.g * N * K * esz, (short)0,
           (int)(N * K * esz), 0x00020000);
-      if (OUT_F32)
-        mw_store_f32(acc, rs, QpTile{ct.n0, (int32_t)N, ct.g, ct.k0}, K);
-      else
-        qp_store<false>(acc, rs, QpTile{ct.n0, (int32_t)N, ct.g, ct.k0}, K);
+      qp_store<OUT_F32>(acc, rs, QpTile{ct.n0, (int32_t)N, ct.g, ct.k0}, K);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
