@@ -2953,6 +2953,7 @@ __device__ __forceinline__ void np_issue(const NpSrc<C> &L, int kt, int slot) {
 // Loads q0 .. q1-1 of np_issue's sequence (A chunks, B chunks, scale words).
 template <class C, int Q0, int Q1>
 __device__ __forceinline__ void np_issue_range(const NpSrc<C> &L, int kt, int slot) {
+  static_assert(0 <= Q0 && Q0 <= Q1 && Q1 <= C::OPS, "load range within the step's loads");
   const uint32_t kb = (uint32_t)kt * 64u, ks = (uint32_t)kt * 8u;
   const uint32_t base = L.dst + (uint32_t)slot * C::SLOT, sbase = L.sdst + (uint32_t)slot * C::SLOT;
 #pragma unroll
@@ -2966,6 +2967,13 @@ __device__ __forceinline__ void np_issue_range(const NpSrc<C> &L, int kt, int sl
       dma4((128 * i < C::TMR ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
     }
   }
+}
+
+// Start of the k-th of 8 near-equal ranges of a step's C::OPS loads (k = 8:
+// the end); ranges past the last load are empty.
+template <class C>
+__host__ __device__ constexpr int np_cut(int k) {
+  return k * ((C::OPS + 7) / 8) < C::OPS ? k * ((C::OPS + 7) / 8) : C::OPS;
 }
 
 struct NpLane {
@@ -3101,38 +3109,43 @@ __device__ __forceinline__ void np_step(const NpSrc<C> &L, int rk, int slot,
                                         v16f (&acc)[C::FI][C::FJ], NpHalf<C> &R0,
                                         NpHalf<C> &R1, NpWords<C> &W, NpScales<C> &S,
                                         NpDec<C> &X, NpDec<C> &Y) {
-  constexpr int NQ = C::OPS, H1 = (NQ + 1) / 2;
+  // the refill of `slot` with step rk: load range k (np_cut) after the
+  // MFMAs of sub-step k
   np_dec<C, 1>(R0, S, Y);                 // s = 1 (block 0)
   np_mfmas<C>(X, acc);                    // s = 0
-  // the refill of `slot` with step rk, in two halves issued while the last
-  // MFMAs of sub-steps 0 and 1 run
-  np_issue_range<C, 0, H1>(L, rk, slot);
+  np_issue_range<C, np_cut<C>(0), np_cut<C>(1)>(L, rk, slot);
   np_scales<C, 1>(W, S);
   np_dec<C, 2>(R0, S, X);                 // s = 2 (block 1)
   np_mfmas<C>(Y, acc);                    // s = 1
-  np_issue_range<C, H1, NQ>(L, rk, slot);
+  np_issue_range<C, np_cut<C>(1), np_cut<C>(2)>(L, rk, slot);
   np_dec<C, 3>(R0, S, Y);                 // s = 3
   np_mfmas<C>(X, acc);                    // s = 2
+  np_issue_range<C, np_cut<C>(2), np_cut<C>(3)>(L, rk, slot);
   np_scales<C, 2>(W, S);
   np_dec<C, 0>(R1, S, X);                 // s = 4 (block 2)
   np_mfmas<C>(Y, acc);                    // s = 3
+  np_issue_range<C, np_cut<C>(3), np_cut<C>(4)>(L, rk, slot);
   np_read_half<C, 0>(lds, nslot, o, R0);  // step kt + 1, half 0
   NpWords<C> Wn;
   np_read_words<C>(lds, nslot, o, Wn);
   __builtin_amdgcn_sched_barrier(0);
   np_dec<C, 1>(R1, S, Y);                 // s = 5
   np_mfmas<C>(X, acc);                    // s = 4
+  np_issue_range<C, np_cut<C>(4), np_cut<C>(5)>(L, rk, slot);
   np_scales<C, 3>(W, S);
   np_dec<C, 2>(R1, S, X);                 // s = 6 (block 3)
   np_mfmas<C>(Y, acc);                    // s = 5
+  np_issue_range<C, np_cut<C>(5), np_cut<C>(6)>(L, rk, slot);
   np_dec<C, 3>(R1, S, Y);                 // s = 7
   np_mfmas<C>(X, acc);                    // s = 6
+  np_issue_range<C, np_cut<C>(6), np_cut<C>(7)>(L, rk, slot);
   np_read_half<C, 1>(lds, nslot, o, R1);  // step kt + 1, half 1
   __builtin_amdgcn_sched_barrier(0);
   W = Wn;
   np_scales<C, 0>(W, S);
   np_dec<C, 0>(R0, S, X);                 // step kt + 1, s = 0
   np_mfmas<C>(Y, acc);                    // s = 7
+  np_issue_range<C, np_cut<C>(7), np_cut<C>(8)>(L, rk, slot);
 }
 
 // Store one transposed accumulator with the outer scales: as mx3_store, each
