@@ -280,6 +280,42 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,
 size_t pqm_moe_grouped_gemm_workspace_size(pqm_format fmt, pqm_gemm_kind kind);
 
 /*
+ * The NVFP4 down projection with online amax compensation ([MT] 5.6, the
+ * single-pass fusion study): the activation P is consumed in 128-wide K-tiles
+ * before each row's full maximum is known.  Per row, a running maximum
+ * gamax = max(|P| over the tiles so far); tile i is encoded under
+ * gs = binary32(gamax / 2688) exactly as pqm_quantize_nvfp4_per_token
+ * encodes a row of maximum gamax (1x16 E4M3 block scales, E2M1 codes), its
+ * block-scaled product with W2 (without gs) is dO_i, and the accumulator
+ * moves to the new scale: O = O (gs_prev / gs) + dO_i, gs_prev = gs.  While
+ * gamax is zero the tile adds nothing and gs_prev stays.  Y = O gs_prev
+ * alpha_W2(n); an all-zero row gives zero.  The encodings depend on when the
+ * row's maximum arrives, so Y can differ from the two-pass path (whole-row
+ * per-token encoding, then pqm_moe_grouped_gemm NVFP4) by the quantization
+ * difference, while the compensation itself is exact up to rounding.
+ *   p        bf16 [M_total, K], routed rows grouped by offsets;
+ *   w_q      packed E2M1 [G, N, K/2], w_scale E4M3 [G, N, K/16] (4-byte
+ *            aligned), w_outer binary32 [(G*N) / w_rows_per_scale];
+ *   out      [M_total, N] bf16 (rounded once) or binary32 per out_dtype;
+ *            rows 0 .. offsets[G]-1 written;
+ *   gs_out   (optional, binary32 [M_total]) each row's final gs;
+ *   q_out, sb_out (optional, both or neither; [M_total, K/2] and
+ *            [M_total, K/16]) the codes and block scales P was encoded
+ *            with, tile by tile.
+ * Accumulation is binary32; gs_prev / gs is one binary32 division.
+ * K must be a positive multiple of 256 and w_rows_per_scale >= 1 dividing
+ * G*N (PQM_ERR_SHAPE); p, w_q, out, q_out 16-byte aligned, offsets 8-byte,
+ * w_scale and gs_out 4-byte (PQM_ERR_ALIGN).  The caller owns every buffer;
+ * nothing is allocated.
+ */
+pqm_status pqm_moe_fc2_online_nvfp4(const uint16_t *p, const uint8_t *w_q,
+                                    const uint8_t *w_scale, const float *w_outer,
+                                    int64_t w_rows_per_scale, const int64_t *offsets,
+                                    int64_t G, int64_t M_total, int64_t N, int64_t K,
+                                    void *out, pqm_dtype out_dtype, float *gs_out,
+                                    uint8_t *q_out, uint8_t *sb_out, hipStream_t stream);
+
+/*
  * The MXFP8 gate_up grouped GEMM with its activation fused into the
  * epilogue ([MT] 5.3-5.4: D = act(gate, up) x prob is produced where C is,
  * and quantized for the down GEMM without another pass; C is not written):

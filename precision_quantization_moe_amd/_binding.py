@@ -39,6 +39,8 @@ SIGNATURES = {
     "pqm_moe_grouped_gemm": ([I32, I32, P, P, P, P, P, P, I64, P, I64, I64, I64, I64,
                               P, I32, P, SZ, P], I32),
     "pqm_moe_grouped_gemm_workspace_size": ([I32, I32], SZ),
+    "pqm_moe_fc2_online_nvfp4": ([P, P, P, P, I64, P, I64, I64, I64, I64, P, I32, P, P, P, P],
+                                 I32),
     "pqm_moe_gemm_swiglu_quantize_mxfp8": ([P, P, P, P, P, I64, I64, I64, I64, P, P, P, P, P],
                                            I32),
     "pqm_moe_route": ([P, I64, I64, I64, I32, P, P, P, P, P, SZ, P], I32),
@@ -200,6 +202,29 @@ def moe_grouped_gemm(fmt: int, kind: int, a, b, offsets: torch.Tensor, N: int, K
                                   _ptr(out), out_dtype, _ptr(ws), ws_bytes, _stream(dev)),
            "pqm_moe_grouped_gemm")
     return out
+
+
+def moe_fc2_online_nvfp4(p: torch.Tensor, w_q, w_scale, w_outer, offsets: torch.Tensor, N: int,
+                         w_rows_per_scale: int = 0, out_dtype: int = OUT_BF16,
+                         encodings: bool = False):
+    """NVFP4 down projection with online amax compensation; see
+    pqm_moe_fc2_online_nvfp4 in pqmoe.h.  p: bf16 [M, K] device.  Returns
+    (y, gs) or, with encodings, (y, gs, q, sb): the output, each row's final
+    outer scale, and the codes / block scales P was encoded with."""
+    G = offsets.numel() - 1
+    M, K = p.shape
+    dev = p.device
+    odt = torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16
+    y = torch.empty((M, N), dtype=odt, device=dev)
+    gs = torch.empty((M,), dtype=torch.float32, device=dev)
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if encodings else None
+    sb = torch.empty((M, K // 16), dtype=torch.uint8, device=dev) if encodings else None
+    _check(lib().pqm_moe_fc2_online_nvfp4(_ptr(p), _ptr(w_q), _ptr(w_scale), _ptr(w_outer),
+                                          w_rows_per_scale or N, _ptr(offsets), G, M, N, K,
+                                          _ptr(y), out_dtype, _ptr(gs), _ptr(q), _ptr(sb),
+                                          _stream(dev)),
+           "pqm_moe_fc2_online_nvfp4")
+    return (y, gs, q, sb) if encodings else (y, gs)
 
 
 # ---------------------------------------------------------------- MoE glue

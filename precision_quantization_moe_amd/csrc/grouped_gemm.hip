@@ -25,6 +25,7 @@
 // with 8 consecutive K per lane (lanes 32..63 hold K 8..15).  Operands whose
 // contraction index is not contiguous in memory (dgrad's weight, both wgrad
 // operands) are transposed while they are staged into LDS.
+#include "nvfp4_encode.hpp"
 #include "pqm_device.hpp"
 #include "pqm_internal.hpp"
 
@@ -2913,16 +2914,23 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(
 // so an expert's last tile of few rows multiplies only whole 32-row groups).
 // With 1 x 4 waves every wave decodes the tile's A fragments and its own
 // quarter of B: 8 decodes per 16 MFMAs at 128 x 512 against 10 with 2 x 2.
-template <int TMR_, int TN_, int WM_, int FI_>
+// AQ: the ring loads the A operand's codes and block scales from memory;
+// otherwise the workgroup writes them into each slot itself (the FC2 kernel
+// with online amax) and the ring carries B only.
+template <int TMR_, int TN_, int WM_, int FI_, bool AQ_ = true>
 struct Np {
   static constexpr int TMR = TMR_, TN = TN_, WM = WM_, ROWS = TMR + TN;
+  static constexpr bool AQ = AQ_;
   static constexpr int SC = ROWS * 64;        // scale area offset in a slot
   static constexpr int SLOT = ROWS * 72;
   static constexpr int NSLOT = 3;  // 4 slots measured no faster
   static constexpr int LDS = NSLOT * SLOT;
   static constexpr int CA = TMR / 64, CB = TN / 64;  // 16-byte data chunks per lane
   static constexpr int NS = ROWS / 128;              // 4-byte scale loads per lane
-  static constexpr int OPS = CA + CB + NS;
+  static constexpr int CAL = AQ ? CA : 0;            // A chunks the ring loads
+  static constexpr int NS0 = AQ ? 0 : TMR / 128;     // first scale load of the ring (A rows first)
+  static constexpr int OPS = CAL + CB + NS - NS0;    // ring loads per lane per step
+  static_assert(AQ || TMR % 128 == 0, "A scale rows are whole scale loads");
   static constexpr int FI = FI_, FJ = TN * WM / 128;
   static constexpr int WROWS = TMR / WM, WCOLS = TN * WM / 4;  // a wave's row / column offset step
   static_assert(FI * 32 <= WROWS && FJ * 32 == WCOLS, "wave tile");
@@ -2937,20 +2945,9 @@ struct NpSrc {
   uint32_t dst, sdst;  // LDS addresses of slot 0's data and scales, this wave
 };
 
-template <class C>
-__device__ __forceinline__ void np_issue(const NpSrc<C> &L, int kt, int slot) {
-  const uint32_t kb = (uint32_t)kt * 64u, ks = (uint32_t)kt * 8u;
-  const uint32_t base = L.dst + (uint32_t)slot * C::SLOT, sbase = L.sdst + (uint32_t)slot * C::SLOT;
-#pragma unroll
-  for (int i = 0; i < C::CA; ++i) dma16(L.Ab + (L.oa[i] + kb), base + i * 4096);
-#pragma unroll
-  for (int i = 0; i < C::CB; ++i) dma16(L.Bb + (L.ob[i] + kb), base + C::TMR * 64 + i * 4096);
-#pragma unroll
-  for (int i = 0; i < C::NS; ++i)  // dwords 256 i + tid: rows 128 i .. (A rows first)
-    dma4((128 * i < C::TMR ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
-}
-
-// Loads q0 .. q1-1 of np_issue's sequence (A chunks, B chunks, scale words).
+// Loads q0 .. q1-1 of a step's ring loads: A chunks (when the ring carries
+// A), B chunks, then scale words (dwords 256 i + tid: rows 128 i .., A rows
+// first).
 template <class C, int Q0, int Q1>
 __device__ __forceinline__ void np_issue_range(const NpSrc<C> &L, int kt, int slot) {
   static_assert(0 <= Q0 && Q0 <= Q1 && Q1 <= C::OPS, "load range within the step's loads");
@@ -2958,15 +2955,21 @@ __device__ __forceinline__ void np_issue_range(const NpSrc<C> &L, int kt, int sl
   const uint32_t base = L.dst + (uint32_t)slot * C::SLOT, sbase = L.sdst + (uint32_t)slot * C::SLOT;
 #pragma unroll
   for (int q = Q0; q < Q1; ++q) {
-    if (q < C::CA) {
+    if (q < C::CAL) {
       dma16(L.Ab + (L.oa[q] + kb), base + q * 4096);
-    } else if (q < C::CA + C::CB) {
-      dma16(L.Bb + (L.ob[q - C::CA] + kb), base + C::TMR * 64 + (q - C::CA) * 4096);
+    } else if (q < C::CAL + C::CB) {
+      dma16(L.Bb + (L.ob[q - C::CAL] + kb), base + C::TMR * 64 + (q - C::CAL) * 4096);
     } else {
-      const int i = q - C::CA - C::CB;
+      const int i = q - C::CAL - C::CB + C::NS0;
       dma4((128 * i < C::TMR ? L.Asb : L.Bsb) + (L.os[i] + ks), sbase + i * 1024);
     }
   }
+}
+
+// Step kt into slot `slot`: all of its ring loads.
+template <class C>
+__device__ __forceinline__ void np_issue(const NpSrc<C> &L, int kt, int slot) {
+  np_issue_range<C, 0, C::OPS>(L, kt, slot);
 }
 
 // Start of the k-th of 8 near-equal ranges of a step's C::OPS loads (k = 8:
@@ -3151,14 +3154,16 @@ __device__ __forceinline__ void np_step(const NpSrc<C> &L, int rk, int slot,
 // Store one transposed accumulator with the outer scales: as mx3_store, each
 // value times alpha_a[row] * alpha_b(column) (the product exact in
 // binary64, one rounding to binary32, then to bf16 for bf16 output).
-// ab: the tile's 256 column scales in LDS.
-template <bool OUT_F32>
+// ab: the tile's column scales in LDS.  ROW_LOCAL: Ao holds the tile's row
+// scales, indexed by the row within the tile (in LDS).
+template <bool OUT_F32, bool ROW_LOCAL = false>
 __device__ __forceinline__ void np_store(const v16f &acc, void *out, int64_t N, int64_t row0,
                                          int64_t row_end, int64_t n0, int rbase, int cbase,
                                          const float *__restrict__ Ao, const float *ab) {
   const int lane = threadIdx.x & 63, h = lane >> 5;
   const int64_t row = row0 + rbase + (lane & 31);
-  const double aa = row < row_end ? (double)Ao[row] : 0.0;
+  const double aa =
+      row < row_end ? (double)(ROW_LOCAL ? Ao[rbase + (lane & 31)] : Ao[row]) : 0.0;
   const bool vec = (N & 7) == 0;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
@@ -3353,6 +3358,267 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
     np_tile<OUT_F32, Np<128, 512, 1, 2>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
   else
     np_tile<OUT_F32, Np<128, 512, 1, 1>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+}
+
+// ------------------------------------------- NVFP4 FC2 with online amax
+// "miniTE technical report", 5.6: FC2 consumes the activation P (the
+// weighted SwiGLU output, bf16) K-tile by K-tile, before a row's full
+// maximum is known.  Each row keeps a running maximum gamax; K-tile i of the
+// row is encoded (1x16 E4M3 block scales, E2M1 codes) under the running outer
+// scale gs = gamax / 2688, multiplied block-scaled with W2 (the product
+// leaves gs out), and the accumulator of the earlier tiles is first moved to
+// the new scale, O = O (gs_prev / gs) + dO_i; Y = O gs_prev alpha_W2.  A row
+// whose maximum is still zero contributes nothing and keeps gs_prev (its
+// codes and block scales are zero).
+//
+// The multiply is the NVFP4 grouped GEMM's step and ring (128 x 256 tiles on
+// 2 x 2 waves) with the A part of each ring slot written by the workgroup:
+// the ring carries W2 only, and P's 128-wide tiles come by DMA through a
+// two-slot LDS ring of their own.  Step kt encodes tile kt + 2 into ring slot
+// (kt + 2) % 3, whose previous step was read during step kt - 2, and then
+// multiplies step kt.  Every column tile of a row block encodes the same P
+// tiles the same way, so all of them agree on each gs without exchanging it.
+
+using NpOn = Np<128, 256, 2, 2, false>;
+constexpr int NPO_PL = 8;               // P-ring loads per lane per tile
+constexpr int NPO_PSLOT = 128 * 256;    // bytes of one P tile (128 rows x 128 bf16)
+
+// Workgroup barrier that no LDS access moves across in the compiler (the
+// encoding's plain LDS stores and loads sit next to it; the caller waits for
+// its own LDS and DMA accesses first).
+__device__ __forceinline__ void npo_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Running state of the rows tid / 8 + 32 j (j = 0..3) of the thread's blocks;
+// the 8 threads of a row hold the same values.
+struct NpoRows {
+  uint32_t gam[4];  // running maximum (bf16 magnitude bits)
+  float gsp[4];     // outer scale after the last tile with a non-zero maximum (0 before)
+};
+
+// P tile t into P-ring slot ps: load i = 2 j + hb of thread tid fetches
+// 16 bytes of row tid / 8 + 32 j (clamped to the tile's rows), bytes
+// 16 (8 hb + tid % 8) .. of the tile (each load covers one 128-byte half of 8
+// rows), to LDS chunk 256 i + tid.
+__device__ __forceinline__ void npo_issue_p(const uint16_t *Pt, int64_t K, int rows_a, int t,
+                                            uint32_t pdst, int ps) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < NPO_PL; ++i) {
+    const int r = min(tid / 8 + 32 * (i >> 1), rows_a - 1);
+    const uint16_t *src = Pt + (int64_t)r * K + 128 * t + 8 * (8 * (i & 1) + (tid & 7));
+    dma16(src, pdst + (uint32_t)(ps * NPO_PSLOT + i * 4096));
+  }
+}
+
+// Encode P tile t (P-ring slot ps) into the A part of ring slot `sp`: thread
+// tid takes the 1x16 blocks (row tid / 8 + 32 j, block tid % 8).  The tile's
+// row maximum joins the running one; gs and the ratio gs_prev / gs (1 while
+// the maximum is zero) go to `ratio` and `gsf` by row.  With q_out, the codes
+// and block scales of the tile's rows are also written to memory.
+__device__ __forceinline__ void npo_encode(const uint8_t *pring, int ps, uint8_t *sp,
+                                           float *ratio, float *gsf, NpoRows &st, int t,
+                                           int rows_a, int64_t row0, int64_t K,
+                                           uint8_t *__restrict__ q_out,
+                                           uint8_t *__restrict__ sb_out) {
+  const int tid = threadIdx.x, blk = tid & 7;
+  const uint8_t *pb = pring + ps * NPO_PSLOT;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = tid / 8 + 32 * j;
+    // chunks 2 blk, 2 blk + 1 of row r: load 2 j + blk / 4, lanes
+    // 8 (tid / 8) + 2 (blk % 4) and the next
+    const uint8_t *src = pb + 4096 * (2 * j + (blk >> 2)) + 16 * (8 * (tid >> 3) + 2 * (blk & 3));
+    const uint4 v0 = *reinterpret_cast<const uint4 *>(src);
+    const uint4 v1 = *reinterpret_cast<const uint4 *>(src + 16);
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t mm = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mm = pk_max_u16(mm, w[k] & 0x7FFF7FFFu);
+    uint32_t m = max(mm & 0xFFFFu, mm >> 16);
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
+    st.gam[j] = max(st.gam[j], m);
+    const Nvfp4Row rc = nvfp4_row(__uint_as_float(st.gam[j] << 16));
+    float rt = 1.0f;
+    if (st.gam[j] != 0) {
+      rt = __fdiv_rn(st.gsp[j], rc.s_g);
+      st.gsp[j] = rc.s_g;
+    }
+    uint32_t sbc;
+    const uint2 packed = nvfp4_block(w, rc, &sbc);
+    *reinterpret_cast<uint2 *>(sp + r * 64 + (((blk >> 1) ^ (r >> 2)) & 3) * 16 + 8 * (blk & 1)) =
+        packed;
+    sp[NpOn::SC + r * 8 + blk] = (uint8_t)sbc;
+    if (blk == 0) {
+      ratio[r] = rt;
+      gsf[r] = st.gsp[j];
+    }
+    if (q_out && r < rows_a) {
+      const int64_t row = row0 + r;
+      *reinterpret_cast<uint2 *>(q_out + row * (K / 2) + 64 * t + 8 * blk) = packed;
+      sb_out[row * (K / 16) + 8 * t + blk] = (uint8_t)sbc;
+    }
+  }
+}
+
+// Move each accumulator row to the step's outer scale (skipped for a
+// fragment whose 32 rows all keep theirs).
+template <class C>
+__device__ __forceinline__ void npo_rescale(const float *ratio, int wm, int r32,
+                                            v16f (&acc)[C::FI][C::FJ]) {
+#pragma unroll
+  for (int i = 0; i < C::FI; ++i) {
+    const float rt = ratio[wm * C::WROWS + 32 * i + r32];
+    if (__builtin_amdgcn_ballot_w64(rt != 1.0f) != 0) {
+#pragma unroll
+      for (int j = 0; j < C::FJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= rt;
+    }
+  }
+}
+
+// Y [M, N] = online-amax FC2 of P [M, K] bf16 with W2 [G N, K] NVFP4
+// (alpha_W2(n) = Bo[(g N + n) / b_rps]); K % 256 == 0.  gs_out: each row's
+// final outer scale; q_out / sb_out: P's codes and block scales as encoded
+// (written by the first column tile).
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_online(
+    const uint16_t *__restrict__ P, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    void *__restrict__ out, float *__restrict__ gs_out, uint8_t *__restrict__ q_out,
+    uint8_t *__restrict__ sb_out) {
+  using C = NpOn;
+  constexpr int FI = C::FI, FJ = C::FJ;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
+  __shared__ __attribute__((aligned(16))) uint8_t pring[2 * NPO_PSLOT];
+  __shared__ float ratio[C::NSLOT][C::TMR];
+  __shared__ float gsf[C::TMR];
+  __shared__ float ab[C::TN];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<C::TN, C::TMR>(offsets, G, ntn, ti, sh)) return;
+  {  // the tile's column scales alpha_W2(n)
+    const int64_t col = ti.n0 + threadIdx.x;
+    ab[threadIdx.x] = col < N ? Bo[(ti.g * N + col) / b_rps] : 0.0f;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  const uint32_t KD = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);
+  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)C::TMR);
+  const int rows_b = (int)min(N - ti.n0, (int64_t)C::TN);
+  NpSrc<C> L;
+  L.Ab = nullptr;
+  L.Asb = nullptr;
+  L.Bb = B + (ti.g * N + ti.n0) * (int64_t)KD;
+  L.Bsb = Bs + (ti.g * N + ti.n0) * (int64_t)KS;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+  L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + C::SC + (uint32_t)wave * 256u);
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) L.oa[i] = 0;
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.ob[i] = (uint32_t)min(r, rows_b - 1) * KD + 16u * k;
+  }
+#pragma unroll
+  for (int i = 0; i < C::NS; ++i) {  // only i >= NS0 (the B rows) are loaded
+    const int d = tid + 256 * i, r = d >> 1, half = d & 1;
+    L.os[i] = r < C::TMR ? 0u : (uint32_t)min(r - C::TMR, rows_b - 1) * KS + 4u * half;
+  }
+  NpLane o;
+  {
+    const int ra = wm * C::WROWS + r32, rb = wn * C::WCOLS + r32;
+    o.a0 = mx3_off(ra, 2 * h);
+    o.a1 = mx3_off(ra, 2 * h + 1);
+    o.b0 = C::TMR * 64 + mx3_off(rb, 2 * h);
+    o.b1 = C::TMR * 64 + mx3_off(rb, 2 * h + 1);
+    o.sa = C::SC + ra * 8 + 4 * h;
+    o.sb = C::SC + (C::TMR + rb) * 8 + 4 * h;
+  }
+  v16f acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const uint16_t *Pt = P + ti.row0 * K;
+  const uint32_t pdst = __builtin_amdgcn_readfirstlane(lds_addr(pring) + (uint32_t)wave * 1024u);
+  uint8_t *qo = ti.n0 == 0 ? q_out : nullptr;
+  NpoRows st;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    st.gam[j] = 0;
+    st.gsp[j] = 0.0f;
+  }
+  const int nk = (int)(K / 128);  // even, >= 2
+  // prologue: W2 steps 0..2, P tiles 0 and 1 encoded into slots 0 and 1,
+  // P tile 2 requested
+#pragma unroll
+  for (int s = 0; s < C::NSLOT; ++s) np_issue<C>(L, min(s, nk - 1), s);
+  npo_issue_p(Pt, K, rows_a, 0, pdst, 0);
+  npo_issue_p(Pt, K, rows_a, 1, pdst, 1);
+  vm_wait<NPO_PL>();  // all but P tile 1
+  npo_barrier();
+  npo_encode(pring, 0, lds, ratio[0], gsf, st, 0, rows_a, ti.row0, K, qo, sb_out);
+  vm_wait<0>();
+  lgkm_wait0();
+  npo_barrier();  // P tile 1 landed; P slot 0 read by every wave
+  npo_encode(pring, 1, lds + C::SLOT, ratio[1], gsf, st, 1, rows_a, ti.row0, K, qo, sb_out);
+  npo_issue_p(Pt, K, rows_a, min(2, nk - 1), pdst, 0);
+  lgkm_wait0();
+  npo_barrier();
+  NpHalf<C> R0, R1;
+  NpWords<C> W;
+  NpScales<C> S;
+  NpDec<C> X, Y;
+  np_read_half<C, 0>(lds, 0, o, R0);
+  np_read_half<C, 1>(lds, 0, o, R1);
+  np_read_words<C>(lds, 0, o, W);
+  np_scales<C, 0>(W, S);
+  np_dec<C, 0>(R0, S, X);
+  int slot = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    // own loads of P tile kt + 2 and of W2 step kt + 1 done (only W2 step
+    // kt + 2, requested during step kt - 1, may be pending; at kt = 0 P tile
+    // 2 is the newest load); after the barrier every wave's are, and P slot
+    // (kt + 1) % 2 and ring slot (kt + 2) % 3 are no longer read
+    if (kt == 0)
+      vm_wait<0>();
+    else
+      vm_wait<C::OPS>();
+    lgkm_wait0();
+    npo_barrier();
+    const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;
+    npo_issue_p(Pt, K, rows_a, min(kt + 3, nk - 1), pdst, (kt + 1) & 1);
+    if (kt + 2 < nk) {
+      const int es = nslot == C::NSLOT - 1 ? 0 : nslot + 1;  // (kt + 2) % 3
+      npo_encode(pring, kt & 1, lds + es * C::SLOT, ratio[es], gsf, st, kt + 2, rows_a, ti.row0,
+                 K, qo, sb_out);
+    }
+    npo_rescale<C>(ratio[slot], wm, r32, acc);
+    // past the last step the reads take the slot's repeated last step (in
+    // bounds; decoded, never multiplied)
+    np_step<C>(L, min(kt + C::NSLOT, nk - 1), slot, lds, o, nslot, acc, R0, R1, W, S, X, Y);
+    slot = nslot;
+  }
+  vm_wait<0>();
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+      np_store<OUT_F32, true>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0,
+                              wm * C::WROWS + 32 * i, wn * C::WCOLS + 32 * j, gsf, ab);
+  if (gs_out && ti.n0 == 0 && tid < rows_a) gs_out[ti.row0 + tid] = gsf[tid];
 }
 
 // ------------------------------------------------------------------ launch
@@ -3658,6 +3924,27 @@ hipError_t launch_gemm_swiglu_mxfp8(const uint8_t *a, const uint8_t *a_scale, co
   const dim3 grid((unsigned)(cdiv((cdiv(M, 256) + G) * ntn, 8) * 8));
   hipLaunchKernelGGL(k_gemm_mxfp8_swiglu, grid, dim3(256), 0, st, a, a_scale, b, b_scale,
                      offsets, G, N, K, ntn, SwigluEpi{prob, src, I, q, s});
+  return hipGetLastError();
+}
+
+// Online-amax FC2 (k_gemm_nvfp4_online): K a positive multiple of 256,
+// 4-byte aligned W2 block scales (their words are loaded whole).
+hipError_t launch_fc2_online_nvfp4(const uint16_t *p, const uint8_t *b, const uint8_t *b_scale,
+                                   const float *b_outer, int64_t b_rows_per_scale,
+                                   const int64_t *offsets, int64_t G, int64_t M, int64_t N,
+                                   int64_t K, void *out, int out_fp32, float *gs_out,
+                                   uint8_t *q_out, uint8_t *sb_out, hipStream_t st) {
+  if (G == 0 || M == 0 || N == 0) return hipSuccess;
+  if (K <= 0 || K % 256 || (uintptr_t)b_scale % 4) return hipErrorNotSupported;
+  const int64_t ntn = cdiv(N, NpOn::TN);
+  const dim3 grid((unsigned)(cdiv((cdiv(M, NpOn::TMR) + G) * ntn, 8) * 8));
+  if (out_fp32)
+    hipLaunchKernelGGL(k_gemm_nvfp4_online<true>, grid, dim3(256), 0, st, p, b, b_scale, b_outer,
+                       b_rows_per_scale, offsets, G, N, K, ntn, out, gs_out, q_out, sb_out);
+  else
+    hipLaunchKernelGGL(k_gemm_nvfp4_online<false>, grid, dim3(256), 0, st, p, b, b_scale,
+                       b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out, gs_out, q_out,
+                       sb_out);
   return hipGetLastError();
 }
 

@@ -155,6 +155,35 @@ def test_validate_offsets_arguments():
     assert f(A16, 3, 10, 1, BAD, None) == 3
 
 
+def test_fc2_online_nvfp4_arguments():
+    """Argument errors of pqm_moe_fc2_online_nvfp4 come back before any
+    launch (p, w_q, w_scale, w_outer, rps, offsets, G, M, N, K, out, dtype,
+    gs_out, q_out, sb_out, stream)."""
+    f = pqm.lib().pqm_moe_fc2_online_nvfp4
+    ok = [A16, A16, A16, A16, 64, A16, 2, 100, 64, 512, A16, 0, A16, A16, A16, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a11=2) == 4                      # out dtype
+    assert call(a9=384) == 2                     # K % 256
+    assert call(a9=0) == 2                       # empty contraction
+    assert call(a7=-1) == 2
+    assert call(a4=0) == 2                       # rows per scale >= 1
+    assert call(a4=3) == 2                       # G * N % rps
+    assert call(a0=None) == 1
+    assert call(a3=None) == 1                    # outer scales
+    assert call(a10=None) == 1                   # out
+    assert call(a14=None) == 1                   # q_out without sb_out
+    assert call(a0=BAD) == 3
+    assert call(a2=ctypes.c_void_p(0x10001)) == 3  # w_scale 4-byte
+    assert call(a13=BAD) == 3                    # q_out 16-byte
+    assert call(a12=ctypes.c_void_p(0x10001)) == 3  # gs_out 4-byte
+    assert call(a6=0) == 0 and call(a7=0) == 0 and call(a8=0) == 0  # nothing to do
+
+
 def test_glue_validation():
     L = pqm.lib()
     assert L.pqm_moe_route(A16, 8, 0, 4, 0, A16, A16, A16, A16, A16, 1 << 20, None) == 2

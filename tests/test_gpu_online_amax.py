@@ -1,0 +1,184 @@
+"""GPU parity of the online-amax NVFP4 down projection
+(pqm_moe_fc2_online_nvfp4, [MT] "miniTE technical report", 5.6) against the
+oracle's loop (oracle.online_amax_fc2, 128-wide K-tiles).
+
+Bars:
+  * the codes and block scales P was encoded with, tile by tile, and each
+    row's final outer scale: bit-exact (quantized decisions, both sides
+    exact);
+  * Y: relative L2 <= 1e-3 per row on binary32 output against the oracle's
+    binary64 loop (the kernel accumulates in binary32 and moves the
+    accumulator by a binary32 gs_prev / gs), plus one bf16 rounding (2^-9)
+    for bf16 output.
+
+W2 is quantized per expert (one outer scale per expert tensor) by the
+library's per-token quantizer on the device and by the oracle's on the host,
+from the same bf16 bytes (their byte equality is established separately)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_quantization_moe_amd as pqm
+from precision_quantization_moe_amd import workloads as wl
+from gpu_util import assert_bytes_equal, dev, dev_bf16, host, host_u16, requires_gpu
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+TOL = 1e-3
+TILE = 128
+
+
+def _offsets(sizes):
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+
+
+def _rel_rows(got, want):
+    num = np.linalg.norm(got.astype(np.float64) - want, axis=1)
+    den = np.linalg.norm(want, axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def _p_rows(rng, R, I):
+    """Weighted SwiGLU rows (bf16 bits) whose maxima arrive in varied tiles:
+    a ramp of gate magnitudes along the row with a per-row exponent, some
+    rows with leading zero tiles, a late burst, or all zeros (signed)."""
+    c = rng.standard_normal((R, 2 * I))
+    c[:, :I] *= rng.uniform(0.2, 3.0, (R, 1)) * np.linspace(0.3, 2.0, I)[None, :] \
+        ** rng.uniform(-2, 2, (R, 1))
+    p = oracle.swiglu_prob(c, rng.uniform(0.05, 1.0, R))
+    r = np.arange(R)
+    p[r % 5 == 1, :TILE] = 0.0                      # first tile skipped
+    p[r % 7 == 2, :2 * TILE] = 0.0                  # two leading zero tiles
+    p[r % 3 == 0, -TILE:] *= 8.0                    # maximum in the last tile
+    bits = oracle.f64_to_bf16(p)
+    bits[r % 11 == 4] = np.where(rng.random((int((r % 11 == 4).sum()), I)) < 0.5,
+                                 0x8000, 0x0000)   # all-zero rows, signed zeros
+    return bits
+
+
+def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    G, M = len(sizes), int(sum(sizes))
+    off = _offsets(sizes)
+    p = _p_rows(rng, max(M, 1), K)[:M]
+    w = wl.normal_bf16((G * N, K), std=0.02, seed=seed + 1)
+    qw, sw, gw = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=N)
+    y, gs, q, sb = pqm.moe_fc2_online_nvfp4(dev_bf16(p), qw, sw, gw, dev(off), N,
+                                            out_dtype=out_dtype, encodings=True)
+    torch.cuda.synchronize()
+    got_y = host(y.float())
+    got = dict(gs=host(gs), q=host(q), sb=host(sb))
+    want_y = np.zeros((M, N))
+    want = dict(gs=np.zeros(M, np.float32), q=np.zeros((M, K // 2), np.uint8),
+                sb=np.zeros((M, K // 16), np.uint8))
+    for g in range(G):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi == lo:
+            continue
+        rq, rsb, rsg = oracle.quantize_nvfp4(w[g * N:(g + 1) * N], rows_per_group=N)
+        yg, rec = oracle.online_amax_fc2(p[lo:hi], TILE, rq, rsb, float(rsg[0]))
+        want_y[lo:hi] = yg
+        want["gs"][lo:hi] = rec["gs"].max(axis=1)   # gs only grows; 0 for a zero row
+        want["q"][lo:hi] = rec["q"]
+        want["sb"][lo:hi] = rec["sb"]
+    return got_y, got, want_y, want
+
+
+@pytest.mark.parametrize("sizes,N,K", [
+    ([130, 0, 33, 256, 7, 1], 520, 512),   # ragged experts and columns, 4 tiles
+    ([300, 129], 256, 768),                # 6 tiles, one column tile
+    ([64, 200, 0], 200, 256),              # 2 tiles (the prologue only), N < one tile
+])
+def test_online_fc2_matches_oracle(sizes, N, K):
+    got_y, got, want_y, want = _case(sizes, N, K, seed=31 + K)
+    assert_bytes_equal(got["gs"].view(np.uint32), want["gs"].view(np.uint32), "final gs")
+    assert_bytes_equal(got["sb"], want["sb"], "block scales")
+    assert_bytes_equal(got["q"], want["q"], "codes")
+    r = _rel_rows(got_y, want_y)
+    print(f"[online] {sizes} N={N} K={K}: max row rel-L2 {r.max():.3e}", flush=True)
+    assert r.max() <= TOL, (float(r.max()), int(r.argmax()))
+    zero = want["gs"] == 0
+    assert zero.any() and not got_y[zero].any()
+
+
+def test_online_fc2_bf16_out_and_deterministic():
+    sizes, N, K = [190, 70], 384, 512
+    got_y, _, want_y, _ = _case(sizes, N, K, seed=41, out_dtype=pqm.OUT_BF16)
+    r = _rel_rows(got_y, want_y)
+    print(f"[online] bf16 out: max row rel-L2 {r.max():.3e}", flush=True)
+    assert r.max() <= TOL + 2.0 ** -9
+    rng = np.random.Generator(np.random.PCG64(42))
+    p = dev_bf16(_p_rows(rng, sum(sizes), K))
+    w = wl.normal_bf16((2 * N, K), std=0.02, seed=43)
+    qw, sw, gw = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=N)
+    off = dev(_offsets(sizes))
+    y1, g1 = pqm.moe_fc2_online_nvfp4(p, qw, sw, gw, off, N)
+    y2, g2 = pqm.moe_fc2_online_nvfp4(p, qw, sw, gw, off, N)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(g1, g2)
+
+
+def test_online_fc2_max_in_first_tile_is_two_pass_encoding():
+    """Rows whose maximum lies in their first tile are encoded exactly as the
+    per-token quantizer encodes the whole row (the two-pass path)."""
+    rng = np.random.Generator(np.random.PCG64(44))
+    R, N, K = 96, 256, 512
+    p = _p_rows(rng, R, K)
+    f = oracle.bf16_to_f64(p)
+    p[:, 0] = oracle.f64_to_bf16(np.abs(f).max(axis=1) * 1.5)  # the row max up front
+    w = wl.normal_bf16((N, K), std=0.02, seed=45)
+    qw, sw, gw = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=N)
+    pd = dev_bf16(p)
+    _, gs, q, sb = pqm.moe_fc2_online_nvfp4(pd, qw, sw, gw, dev(_offsets([R])), N,
+                                            encodings=True)
+    q2, sb2, sg2 = pqm.quantize_nvfp4_per_token(pd)
+    torch.cuda.synchronize()
+    assert_bytes_equal(host(q), host(q2), "codes vs per-token")
+    assert_bytes_equal(host(sb), host(sb2), "block scales vs per-token")
+    assert_bytes_equal(host(gs).view(np.uint32), host(sg2).view(np.uint32), "gs vs per-token")
+
+
+def test_online_fc2_deepseek_down_full_sampled():
+    """DeepSeek-V3 down projection at full size with the online loop: 32768
+    routed rows (half uniform, half Zipf over 256 experts) plus the shared
+    expert's 4096 rows, N = 7168, K = 2048 (16 tiles), weights [257, 7168,
+    2048] N(0, 0.01) drawn on the GPU, one outer scale per expert, bf16
+    output.  P: weighted SwiGLU rows generated on the GPU.  Sampled rows of
+    sampled experts against the oracle's loop (encodings bit-exact, Y at the
+    bar + one bf16 rounding)."""
+    T, E, k, H, I = 4096, 256, 8, 7168, 2048
+    ids = wl.uniform_plus_zipf_routing(T, E, k)
+    off_r, _, _ = oracle.route(ids, E)
+    off = np.concatenate([off_r, [T * k + T]]).astype(np.int64)
+    M = T * k + T
+    gen = torch.Generator(device="cuda").manual_seed(777)
+    c = torch.randn(M, 2 * I, generator=gen, device="cuda").to(torch.bfloat16)
+    prob = torch.rand(M, generator=gen, device="cuda") * 0.5 + 0.05
+    p = pqm.swiglu_prob(c, prob)
+    w = (torch.randn((E + 1) * H, I, generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+    qw, sw, gw = pqm.quantize_nvfp4_per_token(w, rows_per_scale=H)
+    y, gs, q, sb = pqm.moe_fc2_online_nvfp4(p, qw, sw, gw, dev(off), H, encodings=True)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(46))
+    experts = sorted(set(rng.choice(E, 4, replace=False).tolist()) | {0, E - 1, E})
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 4)]))
+        pr = host_u16(p[rows])
+        rq, rsb, rsg = oracle.quantize_nvfp4(host_u16(w[e * H:(e + 1) * H]), rows_per_group=H)
+        want, rec = oracle.online_amax_fc2(pr, TILE, rq, rsb, float(rsg[0]))
+        assert_bytes_equal(host(q[rows]), rec["q"], f"expert {e} codes")
+        assert_bytes_equal(host(sb[rows]), rec["sb"], f"expert {e} block scales")
+        assert_bytes_equal(host(gs[rows]).view(np.uint32),
+                           rec["gs"].max(axis=1).view(np.uint32), f"expert {e} gs")
+        r = _rel_rows(oracle.bf16_to_f64(host_u16(y[rows])), want)
+        print(f"[online] deepseek fc2 expert {e} ({hi - lo} rows): max row rel-L2 {r.max():.3e}",
+              flush=True)
+        assert r.max() <= TOL + 2.0 ** -9, (e, float(r.max()))
+    del w, qw, c
