@@ -3393,11 +3393,21 @@ __device__ __forceinline__ void npo_barrier() {
 }
 
 // Running state of the rows tid / 8 + 32 j (j = 0..3) of the thread's blocks;
-// the 8 threads of a row hold the same values.
+// the 8 threads of a row hold the same values.  rc: the encoding constants of
+// the running maximum (recomputed only when it grows).
 struct NpoRows {
   uint32_t gam[4];  // running maximum (bf16 magnitude bits)
-  float gsp[4];     // outer scale after the last tile with a non-zero maximum (0 before)
+  Nvfp4Row rc[4];   // rc.s_g: outer scale after the last tile with a non-zero maximum (0 before)
 };
+
+// Maximum over the 8 lanes 8 (lane / 8) .. of a wave: quad swaps by 1 and 2,
+// then the mirror within 8 lanes (lane i and 7 - i).
+__device__ __forceinline__ uint32_t max8_lanes(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+  return v;
+}
 
 // P tile t into P-ring slot ps: load i = 2 j + hb of thread tid fetches
 // 16 bytes of row tid / 8 + 32 j (clamped to the tile's rows), bytes
@@ -3426,37 +3436,49 @@ __device__ __forceinline__ void npo_encode(const uint8_t *pring, int ps, uint8_t
                                            uint8_t *__restrict__ sb_out) {
   const int tid = threadIdx.x, blk = tid & 7;
   const uint8_t *pb = pring + ps * NPO_PSLOT;
+  uint32_t w[4][8], m[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = tid / 8 + 32 * j;
-    // chunks 2 blk, 2 blk + 1 of row r: load 2 j + blk / 4, lanes
-    // 8 (tid / 8) + 2 (blk % 4) and the next
+    // chunks 2 blk, 2 blk + 1 of row tid / 8 + 32 j: load 2 j + blk / 4,
+    // lanes 8 (tid / 8) + 2 (blk % 4) and the next
     const uint8_t *src = pb + 4096 * (2 * j + (blk >> 2)) + 16 * (8 * (tid >> 3) + 2 * (blk & 3));
     const uint4 v0 = *reinterpret_cast<const uint4 *>(src);
     const uint4 v1 = *reinterpret_cast<const uint4 *>(src + 16);
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    w[j][0] = v0.x; w[j][1] = v0.y; w[j][2] = v0.z; w[j][3] = v0.w;
+    w[j][4] = v1.x; w[j][5] = v1.y; w[j][6] = v1.z; w[j][7] = v1.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
     uint32_t mm = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) mm = pk_max_u16(mm, w[k] & 0x7FFF7FFFu);
-    uint32_t m = max(mm & 0xFFFFu, mm >> 16);
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 4, 64));
-    st.gam[j] = max(st.gam[j], m);
-    const Nvfp4Row rc = nvfp4_row(__uint_as_float(st.gam[j] << 16));
-    float rt = 1.0f;
-    if (st.gam[j] != 0) {
-      rt = __fdiv_rn(st.gsp[j], rc.s_g);
-      st.gsp[j] = rc.s_g;
+    for (int k = 0; k < 8; ++k) mm = pk_max_u16(mm, w[j][k] & 0x7FFF7FFFu);
+    m[j] = max8_lanes(max(mm & 0xFFFFu, mm >> 16));
+  }
+  float rt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool grew = m[j] > st.gam[j];
+    rt[j] = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+      if (grew) {
+        st.gam[j] = m[j];
+        const Nvfp4Row rc = nvfp4_row(__uint_as_float(m[j] << 16));
+        rt[j] = __fdiv_rn(st.rc[j].s_g, rc.s_g);
+        st.rc[j] = rc;
+      }
     }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = tid / 8 + 32 * j;
     uint32_t sbc;
-    const uint2 packed = nvfp4_block(w, rc, &sbc);
+    const uint2 packed = nvfp4_block(w[j], st.rc[j], &sbc);
     *reinterpret_cast<uint2 *>(sp + r * 64 + (((blk >> 1) ^ (r >> 2)) & 3) * 16 + 8 * (blk & 1)) =
         packed;
     sp[NpOn::SC + r * 8 + blk] = (uint8_t)sbc;
     if (blk == 0) {
-      ratio[r] = rt;
-      gsf[r] = st.gsp[j];
+      ratio[r] = rt[j];
+      gsf[r] = st.rc[j].s_g;
     }
     if (q_out && r < rows_a) {
       const int64_t row = row0 + r;
@@ -3558,7 +3580,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_online(
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     st.gam[j] = 0;
-    st.gsp[j] = 0.0f;
+    st.rc[j] = nvfp4_row(0.0f);  // s_g = 0: the zero row's encoding
   }
   const int nk = (int)(K / 128);  // even, >= 2
   // prologue: W2 steps 0..2, P tiles 0 and 1 encoded into slots 0 and 1,
