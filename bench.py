@@ -32,6 +32,11 @@ seeded input, with all inputs resident in HBM:
                     (the weighted SwiGLU and the FC2 operand's per-token
                     NVFP4 quantize in one fused pass)
   ds_gemm           the two NVFP4 grouped GEMMs of ds_fwd alone
+  ds_fc2_online     ds_fwd's down projection with online amax compensation:
+                    the weighted SwiGLU output (bf16, made once from the
+                    layer's gate_up output) encoded tile by tile under each
+                    row's running maximum inside the FC2 kernel, the
+                    accumulator moved to each new outer scale
   ds_reconstruct    bf16 reconstruction of the forward operands (activations
                     and all 257 experts' weights) for the dequantized backward
 
@@ -70,7 +75,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA BF16 / FP16
 
 ALL_ROWS = ["mxfp8_quant", "nvfp4_token", "nvfp4_joint_w", "q3_wquant", "q3_fwd", "q3_gemm",
             "q3_gemm_fp8b",
-            "q3_dequant", "q3_bwd", "q3_bwd_mx", "ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"]
+            "q3_dequant", "q3_bwd", "q3_bwd_mx", "ds_wquant", "ds_fwd", "ds_gemm", "ds_fc2_online",
+            "ds_reconstruct"]
 EXTRA_ROWS = ["q3_gemm_uniform", "hbm_copy"]
 COPY_BYTES = 512 << 20
 REPEAT_ROWS = ("mxfp8_quant", "nvfp4_token")
@@ -205,7 +211,7 @@ def main():
     # DeepSeek-V3 expert layer (weights drawn on the GPU from a seeded stream)
     T5, K5, E5, H5, I5 = 4096, 8, 256, 7168, 2048
     M5 = T5 * K5 + T5
-    if need("ds_wquant", "ds_fwd", "ds_gemm", "ds_reconstruct"):
+    if need("ds_wquant", "ds_fwd", "ds_gemm", "ds_fc2_online", "ds_reconstruct"):
         st["x5"] = to_dev(wl.activations(T5, H5, seed=6))
         st["ids5"] = torch.from_numpy(wl.uniform_plus_zipf_routing(T5, E5, K5)).to(dev)
         p5 = torch.from_numpy(wl.router_probs(T5, K5, seed=7).reshape(-1)).to(dev)
@@ -315,6 +321,13 @@ def main():
                              a_scale=o["sbd"], a_outer=o["sgd"], b_scale=w2b, b_outer=w2g,
                              b_rows_per_scale=H5, out_dtype=pqm.OUT_BF16, out=o["y"])
 
+    def r_ds_fc2_online(s):
+        o, (w1q, w1b, w1g, w2q, w2b, w2g) = st["ds"], st["dsw"]
+        if "p5" not in st:  # made during the warmup steps: the FC2 input, bf16
+            st["p5"] = pqm.swiglu_prob(o["c"], st["prob5"], o["src"])
+        st["ds_online"] = pqm.moe_fc2_online_nvfp4(st["p5"], w2q, w2b, w2g, o["off"], H5,
+                                                   w_rows_per_scale=H5)
+
     def r_ds_reconstruct(s):
         o, (w1q, w1b, w1g, w2q, w2b, w2g) = st["ds"], st["dsw"]
         prev = st.get("dsr", {})
@@ -333,11 +346,13 @@ def main():
            "q3_gemm_fp8b": r_q3_gemm_fp8b, "q3_gemm_uniform": r_q3_gemm_uniform,
            "q3_dequant": r_q3_dequant, "q3_bwd": r_q3_bwd, "q3_bwd_mx": r_q3_bwd_mx,
            "ds_wquant": r_ds_wquant,
-           "ds_fwd": r_ds_fwd, "ds_gemm": r_ds_gemm, "ds_reconstruct": r_ds_reconstruct}
+           "ds_fwd": r_ds_fwd, "ds_gemm": r_ds_gemm, "ds_fc2_online": r_ds_fc2_online,
+           "ds_reconstruct": r_ds_reconstruct}
     deps = {"q3_fwd": ["q3_wquant"], "q3_gemm": ["q3_wquant", "q3_fwd"],
             "q3_gemm_uniform": ["q3_wquant"],
             "q3_dequant": ["q3_wquant", "q3_fwd"], "q3_bwd": ["q3_wquant", "q3_fwd", "q3_dequant"],
             "ds_fwd": ["ds_wquant"], "ds_gemm": ["ds_wquant", "ds_fwd"],
+            "ds_fc2_online": ["ds_wquant", "ds_fwd"],
             "ds_reconstruct": ["ds_wquant", "ds_fwd"]}
     run = []
     for r in sel:
@@ -428,6 +443,9 @@ def main():
                      frac_bf16=fl_ds / t / 1e12 / BF16_PEAK_TFLOPS)
             if n == "ds_gemm":
                 floor(c, fl_ds, by_ds, BF16_PEAK_TFLOPS, t)
+        elif n == "ds_fc2_online":
+            fl = 2.0 * M5 * H5 * I5
+            c.update(flop=fl, tflops=fl / t / 1e12, frac_bf16=fl / t / 1e12 / BF16_PEAK_TFLOPS)
         elif n == "ds_reconstruct":
             el = M5 * H5 + (E5 + 1) * (2 * I5 * H5 + H5 * I5)
             hbm(c, el * (0.5 + 1 / 16 + 2), t)
