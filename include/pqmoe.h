@@ -259,16 +259,23 @@ pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q,
  * tiles, heaviest experts first, go to whichever workgroup is free; without
  * it they are dealt in a fixed order, same results either way).  NULL / 0,
  * or a buffer that is too small or misaligned, means no workspace.
- * An empty contraction (K == 0) makes FPROP / DGRAD write zeros to rows
- * 0 .. offsets[G]-1 and read no operand; operand, scale and outer-scale
- * pointers are required (non-NULL) only when M_total, N and K are all
- * positive, and out only when Y has elements.
+ * bias (device, optional; FPROP only, else PQM_ERR_ENUM; 4-byte aligned):
+ * binary32 [G, N], the forward epilogue's additive term ([MT] 5.4: the
+ * accumulator times the outer scales, plus bias): Y_g[m, n] = alpha
+ * x accumulator + bias[g, n] in binary32 (NVFP4: the product and the sum
+ * in binary64, rounded once to binary32), then the output rounding.  NULL:
+ * no bias.
+ * An empty contraction (K == 0) makes FPROP / DGRAD write zeros (with a
+ * bias: each routed row's bias row) to rows 0 .. offsets[G]-1 and read no
+ * operand; operand, scale and outer-scale pointers are required (non-NULL)
+ * only when M_total, N and K are all positive, and out only when Y has
+ * elements.
  */
 pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind,
                                 const void *a, const uint8_t *a_scale,
                                 const float *a_outer, const void *b,
                                 const uint8_t *b_scale, const float *b_outer,
-                                int64_t b_rows_per_scale,
+                                int64_t b_rows_per_scale, const float *bias,
                                 const int64_t *offsets, int64_t G,
                                 int64_t M_total, int64_t N, int64_t K,
                                 void *out, pqm_dtype out_dtype,

@@ -264,31 +264,42 @@ def inexact_count() -> int:
 # --------------------------------------------------------------------------
 
 def grouped_gemm(a: np.ndarray, b: np.ndarray, offsets: np.ndarray,
-                 rows: np.ndarray | None = None) -> np.ndarray:
-    """Forward / dgrad: Y[m, :] = sum_k A[m, k] * B_g[:, k] for the group g
-    holding row m (offsets[g] <= m < offsets[g+1]).
+                 rows: np.ndarray | None = None,
+                 bias: np.ndarray | None = None) -> np.ndarray:
+    """Forward / dgrad: Y[m, :] = sum_k A[m, k] * B_g[:, k] (+ bias[g, :])
+    for the group g holding row m (offsets[g] <= m < offsets[g+1]); the
+    forward epilogue's additive term follows [MT] 5.4 (accumulator times the
+    outer scales, plus bias).
 
-    a: [M, K] binary64 operand values; b: [G, N, K] binary64; offsets: [G+1].
-    rows: optional subset of row indices to compute (sampling); the result
-    then has len(rows) rows.  Accumulation is binary64.
+    a: [M, K] binary64 operand values; b: [G, N, K] binary64; offsets: [G+1];
+    bias: optional [G, N].  rows: optional subset of row indices to compute
+    (sampling); the result then has len(rows) rows.  Accumulation is
+    binary64.
     """
     offsets = np.asarray(offsets, np.int64)
     G = b.shape[0]
     assert offsets.shape == (G + 1,) and offsets[0] == 0
     M = a.shape[0]
     assert offsets[-1] == M
+    if bias is not None:
+        bias = np.asarray(bias, np.float64)
+        assert bias.shape == (G, b.shape[1])
     if rows is None:
         y = np.zeros((M, b.shape[1]), np.float64)
         for g in range(G):
             lo, hi = int(offsets[g]), int(offsets[g + 1])
             if hi > lo:
                 y[lo:hi] = a[lo:hi] @ b[g].T
+                if bias is not None:
+                    y[lo:hi] += bias[g]
         return y
     rows = np.asarray(rows, np.int64)
     grp = np.searchsorted(offsets, rows, side="right") - 1
     y = np.zeros((rows.size, b.shape[1]), np.float64)
     for i, (m, g) in enumerate(zip(rows, grp)):
         y[i] = b[g] @ a[m]
+        if bias is not None:
+            y[i] += bias[g]
     return y
 
 

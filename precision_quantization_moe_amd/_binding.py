@@ -36,7 +36,7 @@ SIGNATURES = {
     "pqm_quantize_nvfp4_per_token": ([P, I64, I64, I64, I64, P, P, P, P, SZ, P], I32),
     "pqm_quantize_nvfp4_workspace": ([I64, I64, I64], SZ),
     "pqm_dequantize": ([I32, P, P, P, I64, I64, I64, P, P], I32),
-    "pqm_moe_grouped_gemm": ([I32, I32, P, P, P, P, P, P, I64, P, I64, I64, I64, I64,
+    "pqm_moe_grouped_gemm": ([I32, I32, P, P, P, P, P, P, I64, P, P, I64, I64, I64, I64,
                               P, I32, P, SZ, P], I32),
     "pqm_moe_grouped_gemm_workspace_size": ([I32, I32], SZ),
     "pqm_moe_fc2_online_nvfp4": ([P, P, P, P, I64, P, I64, I64, I64, I64, P, I32, P, P, P, P],
@@ -180,11 +180,12 @@ def dequantize(fmt: int, q: torch.Tensor, s_block: torch.Tensor,
 def moe_grouped_gemm(fmt: int, kind: int, a, b, offsets: torch.Tensor, N: int, K: int,
                      a_scale=None, a_outer=None, b_scale=None, b_outer=None,
                      b_rows_per_scale: int = 0, out_dtype: int = OUT_FP32, out=None,
-                     workspace: bool = True):
+                     workspace: bool = True, bias=None):
     """Grouped GEMM over experts; see pqm_moe_grouped_gemm in pqmoe.h for the
     operand layouts.  offsets: int64 [G+1] on the device.  workspace=False
     passes none (the MXFP8 weight gradient then deals its tiles in a fixed
-    order instead of handing them out)."""
+    order instead of handing them out).  bias: float32 [G, N] on the device
+    (forward only), added in the epilogue."""
     G = offsets.numel() - 1
     # the MXFP8 weight gradient takes the transposed column-wise copies
     M = a.shape[1] if (fmt == FMT_MXFP8 and kind == GEMM_WGRAD) else a.shape[0]
@@ -198,7 +199,7 @@ def moe_grouped_gemm(fmt: int, kind: int, a, b, offsets: torch.Tensor, N: int, K
     ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev) if ws_bytes else None
     _check(L.pqm_moe_grouped_gemm(fmt, kind, _ptr(a), _ptr(a_scale), _ptr(a_outer),
                                   _ptr(b), _ptr(b_scale), _ptr(b_outer),
-                                  b_rows_per_scale, _ptr(offsets), G, M, N, K,
+                                  b_rows_per_scale, _ptr(bias), _ptr(offsets), G, M, N, K,
                                   _ptr(out), out_dtype, _ptr(ws), ws_bytes, _stream(dev)),
            "pqm_moe_grouped_gemm")
     return out

@@ -141,7 +141,8 @@ pqm_status pqm_dequantize(pqm_format fmt, const uint8_t *q, const uint8_t *s_blo
 pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *a,
                                 const uint8_t *a_scale, const float *a_outer, const void *b,
                                 const uint8_t *b_scale, const float *b_outer,
-                                int64_t b_rows_per_scale, const int64_t *offsets, int64_t G,
+                                int64_t b_rows_per_scale, const float *bias,
+                                const int64_t *offsets, int64_t G,
                                 int64_t M_total, int64_t N, int64_t K, void *out,
                                 pqm_dtype out_dtype, void *workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
@@ -153,6 +154,7 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
   if (out_dtype != PQM_OUT_BF16 && out_dtype != PQM_OUT_FP32) return PQM_ERR_ENUM;
   if ((fmt == PQM_FMT_NVFP4 || fmt == PQM_FMT_FP8_BLOCK) && kind != PQM_GEMM_FPROP)
     return PQM_ERR_ENUM;
+  if (bias && kind != PQM_GEMM_FPROP) return PQM_ERR_ENUM;  // the forward epilogue's term
   if (G < 0 || M_total < 0 || N < 0 || K < 0) return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_MXFP8 && kind != PQM_GEMM_WGRAD && K % 32) return PQM_ERR_SHAPE;
   if (fmt == PQM_FMT_MXFP8 && kind == PQM_GEMM_DGRAD &&
@@ -177,7 +179,8 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
     return PQM_ERR_NULL;
   if (reads && (fmt == PQM_FMT_NVFP4 || fmt == PQM_FMT_FP8_BLOCK) && (!a_outer || !b_outer))
     return PQM_ERR_NULL;
-  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(offsets, 8))
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(offsets, 8) ||
+      !aligned(bias, 4))
     return PQM_ERR_ALIGN;
   if (fmt == PQM_FMT_MXFP8 && (!aligned(a_scale, 4) || !aligned(b_scale, 4)))
     return PQM_ERR_ALIGN;
@@ -191,7 +194,7 @@ pqm_status pqm_moe_grouped_gemm(pqm_format fmt, pqm_gemm_kind kind, const void *
                       : nullptr;
   return from_hip(pqm::launch_grouped_gemm((int)fmt, (int)kind, a, a_scale, a_outer, b, b_scale,
                                            b_outer, b_rows_per_scale, offsets, G, M_total, N,
-                                           K, out, out_dtype == PQM_OUT_FP32, ctr, stream));
+                                           K, out, out_dtype == PQM_OUT_FP32, bias, ctr, stream));
 }
 
 size_t pqm_moe_grouped_gemm_workspace_size(pqm_format fmt, pqm_gemm_kind kind) {

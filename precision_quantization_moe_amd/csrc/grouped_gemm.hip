@@ -215,12 +215,13 @@ __device__ __forceinline__ v8i frag_fp8(const uint8_t *lds, int row, int s) {
 }
 
 // Write one 32x32 accumulator tile (rows row0 + rbase .., cols n0 + cbase ..),
-// optionally scaled in binary32 by alpha_row[row] and alpha_col(col).
+// optionally scaled in binary32 by alpha_row[row] and alpha_col(col), plus
+// bias[col] (the expert's bias row, binary32) when given, rounded once.
 template <bool OUT_F32>
 __device__ __forceinline__ void store_acc(const v16f &acc, void *out, int64_t ldo, int64_t row0,
                                           int64_t row_end, int64_t n0, int64_t N, int rbase,
                                           int cbase, const float *alpha_row = nullptr,
-                                          float alpha_col = 1.0f) {
+                                          float alpha_col = 1.0f, const float *bias = nullptr) {
   const int lane = threadIdx.x & 63;
   const int64_t col = n0 + cbase + (lane & 31);
   if (col >= N) return;
@@ -232,7 +233,12 @@ __device__ __forceinline__ void store_acc(const v16f &acc, void *out, int64_t ld
       // alpha_a * alpha_b is exact in binary64; one scaling of the
       // accumulator avoids an intermediate binary32 overflow (a bf16-max
       // token has alpha_a near 2^116)
-      if (alpha_row) v = (float)((double)v * ((double)alpha_row[row] * (double)alpha_col));
+      if (alpha_row) {
+        const double sv = (double)v * ((double)alpha_row[row] * (double)alpha_col);
+        v = (float)(bias ? sv + (double)bias[col] : sv);
+      } else if (bias) {
+        v += bias[col];
+      }
       if (OUT_F32)
         static_cast<float *>(out)[row * ldo + col] = v;
       else
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(256) void k_gemm_mxfp8(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    void *__restrict__ out) {
+    void *__restrict__ out, const float *__restrict__ bias) {
   __shared__ __attribute__((aligned(16))) uint8_t lA[GT_M * GT_PITCH];
   __shared__ __attribute__((aligned(16))) uint8_t lB[GT_N * GT_PITCH];
   __shared__ int64_t sh[4];
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(256) void k_gemm_mxfp8(
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
-                         wn * 64 + 32 * j);
+                         wn * 64 + 32 * j, nullptr, 1.0f, bias ? bias + ti.g * N : nullptr);
 }
 
 // ------------------------------------------------- MXFP8, pipelined large tiles
@@ -470,9 +476,12 @@ __device__ __forceinline__ void mx3_mma(const Mx3Frags<TM> &F,
 // swap between lanes l and l + 32 trades run g = 1 (3) of the low half for
 // run 0 (2) of the high half, after which lane l holds columns
 // 16 p + 8 (l / 32) + 0..7, p = 0, 1: two 16-byte stores per lane.
+// bias: the expert's bias row (binary32, N columns) added to every value
+// before the output rounding, or null.
 template <bool OUT_F32>
 __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N, int64_t row0,
-                                          int64_t row_end, int64_t n0, int rbase, int cbase) {
+                                          int64_t row_end, int64_t n0, int rbase, int cbase,
+                                          const float *bias = nullptr) {
   const int lane = threadIdx.x & 63, h = lane >> 5;
   const int64_t row = row0 + rbase + (lane & 31);
   if (OUT_F32) {
@@ -482,13 +491,17 @@ __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N,
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int64_t col = n0 + cbase + 8 * g + 4 * h;
+      float v[4] = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+      if (bias) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += bias[min(col + e, N - 1)];
+      }
       if ((N & 3) == 0 && col + 3 < N) {
-        *reinterpret_cast<float4 *>(orow + col) =
-            make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        *reinterpret_cast<float4 *>(orow + col) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (col + e < N) orow[col + e] = acc[4 * g + e];
+          if (col + e < N) orow[col + e] = v[e];
       }
     }
     return;
@@ -514,6 +527,13 @@ __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N,
     }
     const int64_t col = n0 + cbase + 16 * p + 8 * h;
     if (row >= row_end) continue;
+    if (bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] += bias[min(col + e, N - 1)];
+        hi[e] += bias[min(col + 4 + e, N - 1)];
+      }
+    }
     if (vec && col + 7 < N) {
       // hardware pair conversion (nearest even, as f32_to_bf16_rne)
       const uint4 w = make_uint4(pk_bf16_rne(lo[0], lo[1]), pk_bf16_rne(lo[2], lo[3]),
@@ -939,7 +959,8 @@ __device__ __forceinline__ void mq_half(const MqSrc<TM> &L, const uint8_t *lds, 
 template <int TM>
 __device__ __forceinline__ void mq_store_staged(const v16f (&acc)[Mq<TM>::FI][Mq<TM>::FJ],
                                                 uint8_t *lds, const TileInfo &ti, int64_t N,
-                                                void *__restrict__ out) {
+                                                void *__restrict__ out,
+                                                const float *bias = nullptr) {
   static_assert(TM * 512 <= Mq<TM>::LDS, "staged tile fits the ring");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
@@ -952,8 +973,14 @@ __device__ __forceinline__ void mq_store_staged(const v16f (&acc)[Mq<TM>::FI][Mq
       for (int g = 0; g < 4; ++g) {
         // columns 64 wn + 32 j + 8 g + 4 h + 0..3: chunk 8 wn + 4 j + g, bytes 8 h ..
         const int x = 8 * wn + 4 * j + g;
-        const uint2 v = make_uint2(pk_bf16_rne(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
-                                   pk_bf16_rne(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]));
+        float f[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                      acc[i][j][4 * g + 3]};
+        if (bias) {
+          const int64_t col = ti.n0 + 64 * wn + 32 * j + 8 * g + 4 * h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] += bias[min(col + e, N - 1)];
+        }
+        const uint2 v = make_uint2(pk_bf16_rne(f[0], f[1]), pk_bf16_rne(f[2], f[3]));
         *reinterpret_cast<uint2 *>(lds + R * 512 + ((x ^ (R & 31)) * 16) + 8 * h) = v;
       }
   }
@@ -985,7 +1012,8 @@ __device__ __forceinline__ void mq_tile(const uint8_t *__restrict__ A,
                                         const uint8_t *__restrict__ B,
                                         const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
                                         int64_t ldb, int64_t bexp, const TileInfo &ti,
-                                        uint8_t *lds, void *__restrict__ out) {
+                                        uint8_t *lds, void *__restrict__ out,
+                                        const float *bias) {
   using C = Mq<TM>;
   constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1067,29 +1095,30 @@ __device__ __forceinline__ void mq_tile(const uint8_t *__restrict__ A,
 #pragma unroll
       for (int j = 0; j < FJ; ++j)
         mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0,
-                           wm * (TM / 2) + 32 * i, wn * 64 + 32 * j);
+                           wm * (TM / 2) + 32 * i, wn * 64 + 32 * j, bias);
   } else {
     lgkm_wait0();
     __builtin_amdgcn_s_barrier();  // the ring is no longer read: stage the tile there
-    mq_store_staged<TM>(acc, lds, ti, N, out);
+    mq_store_staged<TM>(acc, lds, ti, N, out, bias);
   }
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool BIAS>
 __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_q(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    int64_t ldb, int64_t bexp, void *__restrict__ out) {
+    int64_t ldb, int64_t bexp, void *__restrict__ out, const float *__restrict__ bias) {
   static_assert(Mq<128>::LDS <= Mq<256>::LDS, "LDS of the half tile");
   __shared__ __attribute__((aligned(16))) uint8_t lds[Mq<256>::LDS];
   __shared__ int64_t sh[4];
   TileInfo ti;
   if (!lookup_row_tile<256, 256>(offsets, G, ntn, ti, sh)) return;
+  const float *bg = BIAS ? bias + ti.g * N : nullptr;
   if (ti.row_end - ti.row0 <= 128)
-    mq_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
+    mq_tile<OUT_F32, 128>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out, bg);
   else
-    mq_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out);
+    mq_tile<OUT_F32, 256>(A, As, B, Bs, N, K, ldb, bexp, ti, lds, out, bg);
 }
 
 // ------------------------------------------ MXFP8, persistent eight waves
@@ -1165,9 +1194,11 @@ __device__ __forceinline__ pqm_v16u quad_transpose(pqm_v16u v, int b) {
   return quad_stage<2>(quad_stage<1>(v, (b & 1) != 0), (b & 2) != 0);
 }
 
+// bias: the expert's bias row (binary32, N columns) added before the output
+// rounding, or null.
 template <bool OUT_F32>
 __device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffer_rsrc_t rs,
-                                         const QpTile &t, int64_t N) {
+                                         const QpTile &t, int64_t N, const float *bias = nullptr) {
   typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
@@ -1186,12 +1217,21 @@ __device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffe
         const int b = r32 & 3, a4 = r32 >> 2;
         const pqm_v16u v = quad_transpose(__builtin_bit_cast(pqm_v16u, a), b);
         const uint32_t col = (uint32_t)(cb + 4 * (2 * b + h));
+        float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bb[e] = bias[min(col + e, Nu - 1u)];
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int rowk = t.row0 + wm * 128 + 32 * i + 4 * a4 + k;
           const uint32_t off =
               rowk < t.row_end && col < Nu ? ((uint32_t)rowk * Nu + col) * 4u : QP_OOB;
-          const u32x4 w = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+          u32x4 w = {v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+          if (bias) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(__uint_as_float(w[e]) + bb[e]);
+          }
           __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
         }
       }
@@ -1217,6 +1257,14 @@ __device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffe
             const float got = __uint_as_float(h ? sw[0] : sw[1]);
             lo[e] = h ? got : x;
             hi[e] = h ? y : got;
+          }
+          if (bias) {  // chunk 4 j + 2 p + h of the wave's 64 columns
+            const uint32_t c8 = (uint32_t)(t.n0 + wn * 64 + 8 * (4 * j + 2 * p + h));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              lo[e] += bias[min(c8 + e, Nu - 1u)];
+              hi[e] += bias[min(c8 + 4 + e, Nu - 1u)];
+            }
           }
           const int m = 2 * j + p;
           v[4 * m] = pk_bf16_rne(lo[0], lo[1]);
@@ -1340,16 +1388,19 @@ __device__ __forceinline__ void k_gemm_mxfp8_qp_body(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes, const SwigluEpi &ep);
+    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes, const SwigluEpi &ep,
+    const float *__restrict__ bias);
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool BIAS>
 __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes) {
+    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes,
+    const float *__restrict__ bias) {
   k_gemm_mxfp8_qp_body<OUT_F32, false>(A, As, B, Bs, offsets, G, N, K, ntn, ldb, bexp, out,
-                                       out_bytes, SwigluEpi{nullptr, nullptr, 0, nullptr, nullptr});
+                                       out_bytes, SwigluEpi{nullptr, nullptr, 0, nullptr, nullptr},
+                                       BIAS ? bias : nullptr);
 }
 
 template <bool OUT_F32, bool EPI>
@@ -1357,7 +1408,8 @@ __device__ __forceinline__ void k_gemm_mxfp8_qp_body(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes, const SwigluEpi &ep) {
+    int64_t ldb, int64_t bexp, void *__restrict__ out, uint32_t out_bytes, const SwigluEpi &ep,
+    const float *__restrict__ bias) {
   using C = Mq<256>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
   __shared__ QpTile tl[QP_MAXT];
@@ -1488,7 +1540,7 @@ __device__ __forceinline__ void k_gemm_mxfp8_qp_body(
         if (nk <= 2) vm_wait<0>();
         qp_swiglu_store(acc, pr, rs, rss, ct, N / 2);
       } else {
-        qp_store<OUT_F32>(acc, rs, ct, N);
+        qp_store<OUT_F32>(acc, rs, ct, N, bias ? bias + (int64_t)ct.g * N : nullptr);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -1513,7 +1565,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_qp_swiglu(
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
     uint32_t q_bytes, SwigluEpi ep) {
   k_gemm_mxfp8_qp_body<false, true>(A, As, B, Bs, offsets, G, N, K, ntn, K, N * K, nullptr,
-                                    q_bytes, ep);
+                                    q_bytes, ep, nullptr);
 }
 
 // The gate_up grouped GEMM with the fused epilogue: D = SwiGLU(C) x prob
@@ -2106,11 +2158,11 @@ __device__ __forceinline__ void fb_step(const Mx3Src<FB_TM> &L, const uint8_t *l
   fb_mma<FIRST>(cur, part);
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool BIAS>
 __global__ __launch_bounds__(256, 1) void k_gemm_fp8_block(
     const uint8_t *__restrict__ A, const float *__restrict__ As, const uint8_t *__restrict__ B,
     const float *__restrict__ Bs, const int64_t *__restrict__ offsets, int64_t G, int64_t N,
-    int64_t K, int64_t ntn, void *__restrict__ out) {
+    int64_t K, int64_t ntn, void *__restrict__ out, const float *__restrict__ bias) {
   constexpr int TM = FB_TM;
   using C = Mx3<TM>;
   constexpr int FI = C::FI, FJ = C::FJ, TN = C::TN;
@@ -2208,7 +2260,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_block(
 #pragma unroll
     for (int j = 0; j < FJ; ++j)
       mx3_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * (TM / 2) + 32 * i,
-                         wn * 128 + 32 * j);
+                         wn * 128 + 32 * j, BIAS ? bias + ti.g * N : nullptr);
 }
 
 // ------------------------------------------------------------------- BF16
@@ -2257,7 +2309,7 @@ template <bool B_ROW, bool OUT_F32>
 __global__ __launch_bounds__(256) void k_gemm_bf16_rows(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    void *__restrict__ out) {
+    void *__restrict__ out, const float *__restrict__ bias) {
   __shared__ __attribute__((aligned(16))) uint8_t lA[GT_M * GT_PITCH];
   __shared__ __attribute__((aligned(16))) uint8_t lB[GT_N * GT_PITCH];
   __shared__ int64_t sh[4];
@@ -2319,7 +2371,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16_rows(
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
-                         wn * 64 + 32 * j);
+                         wn * 64 + 32 * j, nullptr, 1.0f, bias ? bias + ti.g * N : nullptr);
 }
 
 // WGRAD: Y_g[n, k] = sum_{m in g} A[m, n] B[m, k]; A [M, N], B [M, K], both
@@ -2603,6 +2655,7 @@ struct BpArgs {
   int len;
   void *out;
   int64_t ldo, row0, row_end, col0;
+  const float *bias;  // FPROP: the expert's bias row, or null
 };
 
 template <int KIND, bool OUT_F32, int TM>
@@ -2685,22 +2738,23 @@ __device__ __forceinline__ void bp_tile(const BpArgs &p, uint8_t *lds) {
 #pragma unroll
     for (int j = 0; j < FJ; ++j)
       mx3_store<OUT_F32>(acc[i][j], p.out, p.ldo, p.row0, p.row_end, p.col0,
-                         wm * (TM / 2) + 32 * i, wn * 128 + 32 * j);
+                         wm * (TM / 2) + 32 * i, wn * 128 + 32 * j, p.bias);
 }
 
 // FPROP / DGRAD: row tiles of 256 tokens over the groups (an expert's last
 // tile of <= 128 rows as 128 x 256), 256 output columns; K % 64 == 0.
 // WGRAD: tile (g, 256 rows n, 256 columns k) of Y_g, contraction over the
 // group's rows.
-template <int KIND, bool OUT_F32>
+template <int KIND, bool OUT_F32, bool BIAS = false>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_pipe(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    int64_t ntk, void *__restrict__ out) {
+    int64_t ntk, void *__restrict__ out, const float *__restrict__ bias) {
   static_assert(Bp<128>::LDS <= Bp<256>::LDS, "LDS of the half tile");
   __shared__ __attribute__((aligned(16))) uint8_t lds[Bp<256>::LDS];
   __shared__ int64_t sh[4];
   BpArgs p;
+  p.bias = nullptr;
   if constexpr (KIND == BP_WGRAD) {
     const int64_t t = blockIdx.x;
     const int64_t g = t / (ntn * ntk);
@@ -2740,6 +2794,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_pipe(
   p.row0 = ti.row0;
   p.row_end = ti.row_end;
   p.col0 = ti.n0;
+  if (KIND == BP_FPROP && BIAS) p.bias = bias + ti.g * N;
   if (ti.row_end - ti.row0 <= 128)
     bp_tile<KIND, OUT_F32, 128>(p, lds);
   else
@@ -2833,7 +2888,7 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(
     const float *__restrict__ Ao, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    void *__restrict__ out) {
+    void *__restrict__ out, const float *__restrict__ bias) {
   __shared__ __attribute__((aligned(16))) uint8_t lA[GT_M * GT_PITCH];
   __shared__ __attribute__((aligned(16))) uint8_t lB[GT_N * GT_PITCH];
   __shared__ int64_t sh[4];
@@ -2887,7 +2942,7 @@ __global__ __launch_bounds__(256) void k_gemm_nvfp4(
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       store_acc<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, N, wm * 64 + 32 * i,
-                         wn * 64 + 32 * j, Ao, ab);
+                         wn * 64 + 32 * j, Ao, ab, bias ? bias + ti.g * N : nullptr);
   }
 }
 
@@ -3155,11 +3210,13 @@ __device__ __forceinline__ void np_step(const NpSrc<C> &L, int rk, int slot,
 // value times alpha_a[row] * alpha_b(column) (the product exact in
 // binary64, one rounding to binary32, then to bf16 for bf16 output).
 // ab: the tile's column scales in LDS.  ROW_LOCAL: Ao holds the tile's row
-// scales, indexed by the row within the tile (in LDS).
+// scales, indexed by the row within the tile (in LDS).  bias: the expert's
+// bias row (binary32), added in binary64 before the one rounding, or null.
 template <bool OUT_F32, bool ROW_LOCAL = false>
 __device__ __forceinline__ void np_store(const v16f &acc, void *out, int64_t N, int64_t row0,
                                          int64_t row_end, int64_t n0, int rbase, int cbase,
-                                         const float *__restrict__ Ao, const float *ab) {
+                                         const float *__restrict__ Ao, const float *ab,
+                                         const float *bias = nullptr) {
   const int lane = threadIdx.x & 63, h = lane >> 5;
   const int64_t row = row0 + rbase + (lane & 31);
   const double aa =
@@ -3181,8 +3238,15 @@ __device__ __forceinline__ void np_store(const v16f &acc, void *out, int64_t N, 
     const int64_t col = n0 + c0;
     if (row >= row_end) continue;
     float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (bias) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)((double)v[e] * (aa * (double)ab[c0 + e]));
+      for (int e = 0; e < 8; ++e)
+        v[e] = (float)((double)v[e] * (aa * (double)ab[c0 + e]) +
+                       (double)bias[min(col + e, N - 1)]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (float)((double)v[e] * (aa * (double)ab[c0 + e]));
+    }
     if (vec && col + 7 < N) {
       if (OUT_F32) {
         float *dst = static_cast<float *>(out) + row * N + col;
@@ -3214,7 +3278,7 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
                                         const uint8_t *__restrict__ B,
                                         const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
                                         const TileInfo &ti, uint8_t *lds, const float *ab,
-                                        void *__restrict__ out) {
+                                        void *__restrict__ out, const float *bias) {
   constexpr int FI = C::FI, FJ = C::FJ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = C::WM == 2 ? wave >> 1 : 0, wn = C::WM == 2 ? wave & 1 : wave;
@@ -3298,18 +3362,18 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
 #pragma unroll
     for (int j = 0; j < FJ; ++j)
       np_store<OUT_F32>(acc[i][j], out, N, ti.row0, ti.row_end, ti.n0, wm * C::WROWS + 32 * i,
-                        wn * C::WCOLS + 32 * j, Ao, ab);
+                        wn * C::WCOLS + 32 * j, Ao, ab, bias);
 }
 
 // 256 x 256 tiles (an expert's last tile of <= 128 rows as 128 x 256);
 // K % 256 == 0.
-template <bool OUT_F32>
+template <bool OUT_F32, bool BIAS>
 __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_pipe(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const float *__restrict__ Ao, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    void *__restrict__ out) {
+    void *__restrict__ out, const float *__restrict__ bias) {
   static_assert(NpPipe128::LDS <= NpPipe256::LDS, "LDS of the half tile");
   __shared__ __attribute__((aligned(16))) uint8_t lds[NpPipe256::LDS];
   __shared__ float ab[256];
@@ -3321,23 +3385,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_pipe(
     ab[threadIdx.x] = col < N ? Bo[(ti.g * N + col) / b_rps] : 0.0f;
   }
   __syncthreads();
+  const float *bg = BIAS ? bias + ti.g * N : nullptr;
   if (ti.row_end - ti.row0 <= 128)
-    np_tile<OUT_F32, NpPipe128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+    np_tile<OUT_F32, NpPipe128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out, bg);
   else
-    np_tile<OUT_F32, NpPipe256>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+    np_tile<OUT_F32, NpPipe256>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out, bg);
 }
 
 // 128 x 512 tiles for experts of few rows each, 1 x 4 waves of 128 x 128
 // (a sub-step decodes 4 + 4 fragments for 16 MFMAs); an expert's last tile
 // multiplies only the 32-row groups that hold rows (with the DeepSeek-V3
 // routing, median 88 rows per expert, 1.11x the routed rows instead of 1.33x).
-template <bool OUT_F32>
+template <bool OUT_F32, bool BIAS>
 __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
     const float *__restrict__ Ao, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
     const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
-    void *__restrict__ out) {
+    void *__restrict__ out, const float *__restrict__ bias) {
   using W4 = Np<128, 512, 1, 4>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[W4::LDS];
   __shared__ float ab[512];
@@ -3350,14 +3415,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
   }
   __syncthreads();
   const int64_t rows = ti.row_end - ti.row0;
+  const float *bg = BIAS ? bias + ti.g * N : nullptr;
   if (rows > 96)
-    np_tile<OUT_F32, W4>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+    np_tile<OUT_F32, W4>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out, bg);
   else if (rows > 64)
-    np_tile<OUT_F32, Np<128, 512, 1, 3>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+    np_tile<OUT_F32, Np<128, 512, 1, 3>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out, bg);
   else if (rows > 32)
-    np_tile<OUT_F32, Np<128, 512, 1, 2>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+    np_tile<OUT_F32, Np<128, 512, 1, 2>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out, bg);
   else
-    np_tile<OUT_F32, Np<128, 512, 1, 1>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out);
+    np_tile<OUT_F32, Np<128, 512, 1, 1>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out, bg);
 }
 
 // ------------------------------------------- NVFP4 FC2 with online amax
@@ -3659,13 +3725,36 @@ __global__ __launch_bounds__(256) void k_zero_rows(const int64_t *__restrict__ o
     o[i] = 0;
 }
 
+// K = 0 with a bias: Y[m, :] = bias[g(m), :] for the routed rows (one wave
+// per row; g(m) by binary search of the offsets).
+__global__ __launch_bounds__(256) void k_bias_rows(const int64_t *__restrict__ offsets, int64_t G,
+                                                   int64_t N, const float *__restrict__ bias,
+                                                   int out_f32, void *__restrict__ out) {
+  const int64_t M = offsets[G];
+  for (int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); m < M;
+       m += (int64_t)gridDim.x * 4) {
+    int64_t lo = 0, hi = G - 1;  // the last group g with offsets[g] <= m
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (offsets[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    const float *b = bias + lo * N;
+    for (int64_t n = threadIdx.x & 63; n < N; n += 64) {
+      if (out_f32)
+        static_cast<float *>(out)[m * N + n] = b[n];
+      else
+        static_cast<uint16_t *>(out)[m * N + n] = (uint16_t)f32_to_bf16_rne(b[n]);
+    }
+  }
+}
+
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Persistent MXFP8 grid: one workgroup per CU (a multiple of 8, one range
 // of tiles per XCD), fewer when there are fewer tiles.
 static int64_t qp_grid(int64_t G, int64_t M, int64_t N) {
   const int64_t tiles_ub = (cdiv(M, 256) + G) * cdiv(N, 256);
-  const int64_t cus = resident_workgroups((const void *)k_gemm_mxfp8_qp<false>, 512, 0);
+  const int64_t cus = resident_workgroups((const void *)k_gemm_mxfp8_qp<false, false>, 512, 0);
   return max((int64_t)8, min(cdiv(cus, 8) * 8, cdiv(tiles_ub, 8) * 8));
 }
 
@@ -3715,12 +3804,28 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
                                const float *a_outer, const void *b, const uint8_t *b_scale,
                                const float *b_outer, int64_t b_rows_per_scale,
                                const int64_t *offsets, int64_t G, int64_t M, int64_t N,
-                               int64_t K, void *out, int out_fp32, uint32_t *ctr,
-                               hipStream_t st) {
+                               int64_t K, void *out, int out_fp32, const float *bias,
+                               uint32_t *ctr, hipStream_t st) {
   if (G == 0 || N == 0) return hipSuccess;
+  // kernels with a compile-time bias flag: <OUT_F32, BIAS> picked at run time
+#define PQM_FB(KERN, GRID, BLOCK, ...)                                                  \
+  do {                                                                                 \
+    if (out_fp32) {                                                                    \
+      if (bias) hipLaunchKernelGGL((KERN<true, true>), GRID, BLOCK, 0, st, __VA_ARGS__); \
+      else hipLaunchKernelGGL((KERN<true, false>), GRID, BLOCK, 0, st, __VA_ARGS__);     \
+    } else {                                                                           \
+      if (bias) hipLaunchKernelGGL((KERN<false, true>), GRID, BLOCK, 0, st, __VA_ARGS__); \
+      else hipLaunchKernelGGL((KERN<false, false>), GRID, BLOCK, 0, st, __VA_ARGS__);    \
+    }                                                                                  \
+  } while (0)
   const int64_t U32 = (int64_t)1 << 32;  // the pipelined kernels' per-panel byte offsets
-  if (K == 0 && kind != 2) {  // FPROP / DGRAD over an empty contraction: Y = 0
+  if (K == 0 && kind != 2) {  // FPROP / DGRAD over an empty contraction: Y = 0 (+ bias)
     if (M == 0) return hipSuccess;
+    if (bias) {
+      hipLaunchKernelGGL(k_bias_rows, dim3((unsigned)min(cdiv(M, 4), (int64_t)65536)), dim3(256),
+                         0, st, offsets, G, N, bias, out_fp32, out);
+      return hipGetLastError();
+    }
     const int64_t n = M * N / 2 + 1;
     const unsigned grid = (unsigned)min(cdiv(n, 256), (int64_t)8192);
     hipLaunchKernelGGL(k_zero_rows, dim3(grid), dim3(256), 0, st, offsets, G, N,
@@ -3733,12 +3838,8 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_b = cdiv(N, 256);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, FB_TM) + G) * ntn_b, 8) * 8));
-    if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_fp8_block<true>, grid_b, dim3(256), 0, st, A, a_outer, B,
-                         b_outer, offsets, G, N, K, ntn_b, out);
-    else
-      hipLaunchKernelGGL(k_gemm_fp8_block<false>, grid_b, dim3(256), 0, st, A, a_outer, B,
-                         b_outer, offsets, G, N, K, ntn_b, out);
+    PQM_FB(k_gemm_fp8_block, grid_b, dim3(256), A, a_outer, B, b_outer, offsets, G, N, K, ntn_b,
+           out, bias);
     return hipGetLastError();
   }
   if (fmt == 1 && kind == 2) {  // WGRAD (MXFP8, column-wise copies)
@@ -3780,11 +3881,11 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     const int64_t ntn_b = cdiv(N, Mq<256>::TN);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
     if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_mxfp8_q<true>, grid_b, dim3(512), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_b, G * K, K, out);
+      hipLaunchKernelGGL((k_gemm_mxfp8_q<true, false>), grid_b, dim3(512), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_b, G * K, K, out, nullptr);
     else
-      hipLaunchKernelGGL(k_gemm_mxfp8_q<false>, grid_b, dim3(512), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_b, G * K, K, out);
+      hipLaunchKernelGGL((k_gemm_mxfp8_q<false, false>), grid_b, dim3(512), 0, st, A, a_scale, B,
+                         b_scale, offsets, G, N, K, ntn_b, G * K, K, out, nullptr);
     return hipGetLastError();
   }
   if (kind == 2 && K > 0 && M * N * 2 < U32 && M * K * 2 < U32) {  // WGRAD (bf16), pipelined
@@ -3793,10 +3894,10 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     const uint16_t *A = static_cast<const uint16_t *>(a), *B = static_cast<const uint16_t *>(b);
     if (out_fp32)
       hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_WGRAD, true>), grid, dim3(256), 0, st, A, B,
-                         offsets, G, N, K, ntn, ntk, out);
+                         offsets, G, N, K, ntn, ntk, out, nullptr);
     else
       hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_WGRAD, false>), grid, dim3(256), 0, st, A, B,
-                         offsets, G, N, K, ntn, ntk, out);
+                         offsets, G, N, K, ntn, ntk, out, nullptr);
     return hipGetLastError();
   }
   if (kind == 2) {  // WGRAD (bf16)
@@ -3823,34 +3924,26 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     const int64_t ntn_b = cdiv(N, 256);
     const dim3 grid_p((unsigned)qp_grid(G, M, N));
     const uint32_t ob = (uint32_t)(M * N * (out_fp32 ? 4 : 2));
-    if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_mxfp8_qp<true>, grid_p, dim3(512), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_b, K, N * K, out, ob);
-    else
-      hipLaunchKernelGGL(k_gemm_mxfp8_qp<false>, grid_p, dim3(512), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_b, K, N * K, out, ob);
+    PQM_FB(k_gemm_mxfp8_qp, grid_p, dim3(512), A, a_scale, B, b_scale, offsets, G, N, K, ntn_b,
+           K, N * K, out, ob, bias);
     return hipGetLastError();
   }
   if (fmt == 1 && K > 0 && K % 128 == 0 && 256 * K < U32) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_b = cdiv(N, Mq<256>::TN);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
-    if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_mxfp8_q<true>, grid_b, dim3(512), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_b, K, N * K, out);
-    else
-      hipLaunchKernelGGL(k_gemm_mxfp8_q<false>, grid_b, dim3(512), 0, st, A, a_scale, B,
-                         b_scale, offsets, G, N, K, ntn_b, K, N * K, out);
+    PQM_FB(k_gemm_mxfp8_q, grid_b, dim3(512), A, a_scale, B, b_scale, offsets, G, N, K, ntn_b,
+           K, N * K, out, bias);
     return hipGetLastError();
   }
   if (fmt == 1) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     if (out_fp32)
       hipLaunchKernelGGL(k_gemm_mxfp8<true>, grid, dim3(256), 0, st, A, a_scale, B, b_scale,
-                         offsets, G, N, K, ntn, out);
+                         offsets, G, N, K, ntn, out, bias);
     else
       hipLaunchKernelGGL(k_gemm_mxfp8<false>, grid, dim3(256), 0, st, A, a_scale, B, b_scale,
-                         offsets, G, N, K, ntn, out);
+                         offsets, G, N, K, ntn, out, bias);
     return hipGetLastError();
   }
   if (fmt == 0 && K % 64 == 0 && (kind == 0 || K * N * 2 < U32)) {
@@ -3858,19 +3951,28 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     const int64_t ntn_b = cdiv(N, 256);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
     if (kind == 0) {
-      if (out_fp32)
-        hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_FPROP, true>), grid_b, dim3(256), 0, st, A, B,
-                           offsets, G, N, K, ntn_b, (int64_t)0, out);
-      else
-        hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_FPROP, false>), grid_b, dim3(256), 0, st, A, B,
-                           offsets, G, N, K, ntn_b, (int64_t)0, out);
+      if (out_fp32) {
+        if (bias)
+          hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_FPROP, true, true>), grid_b, dim3(256), 0, st,
+                             A, B, offsets, G, N, K, ntn_b, (int64_t)0, out, bias);
+        else
+          hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_FPROP, true>), grid_b, dim3(256), 0, st, A, B,
+                             offsets, G, N, K, ntn_b, (int64_t)0, out, nullptr);
+      } else {
+        if (bias)
+          hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_FPROP, false, true>), grid_b, dim3(256), 0, st,
+                             A, B, offsets, G, N, K, ntn_b, (int64_t)0, out, bias);
+        else
+          hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_FPROP, false>), grid_b, dim3(256), 0, st, A,
+                             B, offsets, G, N, K, ntn_b, (int64_t)0, out, nullptr);
+      }
     } else {
       if (out_fp32)
         hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_DGRAD, true>), grid_b, dim3(256), 0, st, A, B,
-                           offsets, G, N, K, ntn_b, (int64_t)0, out);
+                           offsets, G, N, K, ntn_b, (int64_t)0, out, nullptr);
       else
         hipLaunchKernelGGL((k_gemm_bf16_pipe<BP_DGRAD, false>), grid_b, dim3(256), 0, st, A, B,
-                           offsets, G, N, K, ntn_b, (int64_t)0, out);
+                           offsets, G, N, K, ntn_b, (int64_t)0, out, nullptr);
     }
     return hipGetLastError();
   }
@@ -3879,17 +3981,17 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     if (kind == 0) {
       if (out_fp32)
         hipLaunchKernelGGL((k_gemm_bf16_rows<false, true>), grid, dim3(256), 0, st, A, B,
-                           offsets, G, N, K, ntn, out);
+                           offsets, G, N, K, ntn, out, bias);
       else
         hipLaunchKernelGGL((k_gemm_bf16_rows<false, false>), grid, dim3(256), 0, st, A, B,
-                           offsets, G, N, K, ntn, out);
+                           offsets, G, N, K, ntn, out, bias);
     } else {
       if (out_fp32)
         hipLaunchKernelGGL((k_gemm_bf16_rows<true, true>), grid, dim3(256), 0, st, A, B,
-                           offsets, G, N, K, ntn, out);
+                           offsets, G, N, K, ntn, out, nullptr);
       else
         hipLaunchKernelGGL((k_gemm_bf16_rows<true, false>), grid, dim3(256), 0, st, A, B,
-                           offsets, G, N, K, ntn, out);
+                           offsets, G, N, K, ntn, out, nullptr);
     }
     return hipGetLastError();
   }
@@ -3898,36 +4000,29 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_w = cdiv(N, 512);
     const dim3 grid_w((unsigned)(cdiv((cdiv(M, 128) + G) * ntn_w, 8) * 8));
-    if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_nvfp4_wide<true>, grid_w, dim3(256), 0, st, A, a_scale, a_outer, B,
-                         b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_w, out);
-    else
-      hipLaunchKernelGGL(k_gemm_nvfp4_wide<false>, grid_w, dim3(256), 0, st, A, a_scale, a_outer,
-                         B, b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_w, out);
+    PQM_FB(k_gemm_nvfp4_wide, grid_w, dim3(256), A, a_scale, a_outer, B, b_scale, b_outer,
+           b_rows_per_scale, offsets, G, N, K, ntn_w, out, bias);
     return hipGetLastError();
   }
   if (fmt == 2 && K > 0 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_b = cdiv(N, 256);
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
-    if (out_fp32)
-      hipLaunchKernelGGL(k_gemm_nvfp4_pipe<true>, grid_b, dim3(256), 0, st, A, a_scale, a_outer,
-                         B, b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_b, out);
-    else
-      hipLaunchKernelGGL(k_gemm_nvfp4_pipe<false>, grid_b, dim3(256), 0, st, A, a_scale, a_outer,
-                         B, b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn_b, out);
+    PQM_FB(k_gemm_nvfp4_pipe, grid_b, dim3(256), A, a_scale, a_outer, B, b_scale, b_outer,
+           b_rows_per_scale, offsets, G, N, K, ntn_b, out, bias);
     return hipGetLastError();
   }
   if (fmt == 2) {
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     if (out_fp32)
       hipLaunchKernelGGL(k_gemm_nvfp4<true>, grid, dim3(256), 0, st, A, a_scale, a_outer, B,
-                         b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out);
+                         b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out, bias);
     else
       hipLaunchKernelGGL(k_gemm_nvfp4<false>, grid, dim3(256), 0, st, A, a_scale, a_outer, B,
-                         b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out);
+                         b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out, bias);
     return hipGetLastError();
   }
+#undef PQM_FB
   return hipErrorNotSupported;
 }
 

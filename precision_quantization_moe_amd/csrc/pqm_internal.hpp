@@ -49,8 +49,8 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
                                const float *a_outer, const void *b, const uint8_t *b_scale,
                                const float *b_outer, int64_t b_rows_per_scale,
                                const int64_t *offsets, int64_t G, int64_t M, int64_t N,
-                               int64_t K, void *out, int out_fp32, uint32_t *ctr,
-                               hipStream_t st);
+                               int64_t K, void *out, int out_fp32, const float *bias,
+                               uint32_t *ctr, hipStream_t st);
 // Workspace bytes the grouped GEMM uses for (fmt, kind): a tile counter for
 // the MXFP8 weight gradient, none otherwise.
 int64_t grouped_gemm_workspace_bytes(int fmt, int kind);

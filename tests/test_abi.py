@@ -105,8 +105,8 @@ def test_grouped_gemm_validation():
     L = pqm.lib()
     f = L.pqm_moe_grouped_gemm
     args = lambda **kw: [kw.get("fmt", 1), kw.get("kind", 0), A16, A16, None, A16, A16, None,
-                         kw.get("brps", 0), A16, kw.get("G", 4), kw.get("M", 64), 64,
-                         kw.get("K", 64), A16, kw.get("out", 1), None, 0, None]
+                         kw.get("brps", 0), kw.get("bias"), A16, kw.get("G", 4), kw.get("M", 64),
+                         64, kw.get("K", 64), A16, kw.get("out", 1), None, 0, None]
     assert f(*args(fmt=5)) == 4
     assert f(*args(kind=9)) == 4
     assert f(*args(out=3)) == 4
@@ -131,6 +131,10 @@ def test_grouped_gemm_validation():
     a = args()
     a[2] = BAD
     assert f(*a) == 3
+    assert f(*args(kind=1, K=128, bias=A16)) == 4   # bias: forward only
+    assert f(*args(kind=2, bias=A16)) == 4
+    assert f(*args(bias=ctypes.c_void_p(0x10002))) == 3  # bias 4-byte aligned
+    assert f(*args(G=0, bias=A16)) == 0
 
 
 def test_grouped_gemm_workspace_size():

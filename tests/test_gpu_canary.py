@@ -160,7 +160,7 @@ def test_grouped_gemm_stays_inside_output(fmt, kind, N, K, out_dtype):
                                                       for n in ("a_scale", "a_outer")),
                                   _p(b), *(None if kw[n] is None else _p(kw[n])
                                            for n in ("b_scale", "b_outer")),
-                                  N, _p(off), G, M, N, K, out.ptr, out_dtype, None, 0,
+                                  N, None, _p(off), G, M, N, K, out.ptr, out_dtype, None, 0,
                                   _stream())
     _run(code, "gemm", out)
     if not wgrad:

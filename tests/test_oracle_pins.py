@@ -417,6 +417,15 @@ def test_grouped_gemm_vs_fraction_triple_loop():
     rows = np.array([6, 0, 4])
     Ys = oracle.grouped_gemm(A, B, offsets, rows=rows)
     assert np.array_equal(Ys, Y[rows])
+    # the forward epilogue's bias ([MT] 5.4): + bias[g, n] of the row's group
+    bias = g.standard_normal((G, N))
+    Yb = oracle.grouped_gemm(A, B, offsets, bias=bias)
+    for m in range(7):
+        grp = 0 if m < 3 else 2
+        for n in range(N):
+            exact = sum(Fr(A[m, k]) * Fr(B[grp, n, k]) for k in range(K)) + Fr(bias[grp, n])
+            assert abs(Fr(Yb[m, n]) - exact) <= abs(exact) * Fr(1, 2 ** 44) + Fr(1, 2 ** 200)
+    assert np.array_equal(oracle.grouped_gemm(A, B, offsets, rows=rows, bias=bias), Yb[rows])
     # wgrad: dW_g = dY_g^T X_g
     dy = g.standard_normal((7, N))
     W = oracle.grouped_gemm_wgrad(dy, A, offsets)
