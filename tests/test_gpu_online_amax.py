@@ -11,9 +11,10 @@ Bars:
     accumulator by a binary32 gs_prev / gs), plus one bf16 rounding (2^-9)
     for bf16 output.
 
-W2 is quantized per expert (one outer scale per expert tensor) by the
-library's per-token quantizer on the device and by the oracle's on the host,
-from the same bf16 bytes (their byte equality is established separately)."""
+W2 is quantized with one outer scale per expert tensor (or per scope of
+w_rows_per_scale rows) by the library's per-token quantizer on the device and
+by the oracle's on the host, from the same bf16 bytes (their byte equality is
+established separately)."""
 from __future__ import annotations
 
 import numpy as np
@@ -59,15 +60,20 @@ def _p_rows(rng, R, I):
     return bits
 
 
-def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32):
+def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32, rps=None):
+    """rps: W2 rows per outer scale (default N, one per expert); with rps < N
+    the oracle's loop (one W2 scale) runs once per scale scope of W2 rows,
+    whose output columns it then fills."""
+    rps = rps or N
     rng = np.random.Generator(np.random.PCG64(seed))
     G, M = len(sizes), int(sum(sizes))
     off = _offsets(sizes)
     p = _p_rows(rng, max(M, 1), K)[:M]
     w = wl.normal_bf16((G * N, K), std=0.02, seed=seed + 1)
-    qw, sw, gw = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=N)
+    qw, sw, gw = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=rps)
     y, gs, q, sb = pqm.moe_fc2_online_nvfp4(dev_bf16(p), qw, sw, gw, dev(off), N,
-                                            out_dtype=out_dtype, encodings=True)
+                                            w_rows_per_scale=rps, out_dtype=out_dtype,
+                                            encodings=True)
     torch.cuda.synchronize()
     got_y = host(y.float())
     got = dict(gs=host(gs), q=host(q), sb=host(sb))
@@ -78,27 +84,38 @@ def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32):
         lo, hi = int(off[g]), int(off[g + 1])
         if hi == lo:
             continue
-        rq, rsb, rsg = oracle.quantize_nvfp4(w[g * N:(g + 1) * N], rows_per_group=N)
-        yg, rec = oracle.online_amax_fc2(p[lo:hi], TILE, rq, rsb, float(rsg[0]))
-        want_y[lo:hi] = yg
+        for c0 in range(0, N, rps):
+            wr = w[g * N + c0:g * N + c0 + rps]
+            rq, rsb, rsg = oracle.quantize_nvfp4(wr, rows_per_group=rps)
+            yg, rec = oracle.online_amax_fc2(p[lo:hi], TILE, rq, rsb, float(rsg[0]))
+            want_y[lo:hi, c0:c0 + rps] = yg
         want["gs"][lo:hi] = rec["gs"].max(axis=1)   # gs only grows; 0 for a zero row
         want["q"][lo:hi] = rec["q"]
         want["sb"][lo:hi] = rec["sb"]
     return got_y, got, want_y, want
 
 
-@pytest.mark.parametrize("sizes,N,K", [
-    ([130, 0, 33, 256, 7, 1], 520, 512),   # ragged experts and columns, 4 tiles
-    ([300, 129], 256, 768),                # 6 tiles, one column tile
-    ([64, 200, 0], 200, 256),              # 2 tiles (the prologue only), N < one tile
+def _many_small(G, seed):
+    sizes = np.random.Generator(np.random.PCG64(seed)).choice([0, 0, 1, 2, 5, 33], size=G)
+    sizes[G // 2] = 300
+    return sizes.tolist()
+
+
+@pytest.mark.parametrize("sizes,N,K,rps", [
+    ([130, 0, 33, 256, 7, 1], 520, 512, None),   # ragged experts and columns, 4 tiles
+    ([300, 129], 256, 768, None),                # 6 tiles, one column tile
+    ([64, 200, 0], 200, 256, None),              # 2 tiles (the prologue only), N < one tile
+    ([200, 77], 512, 512, 256),                  # W2 scaled per half (gate / up style scopes)
+    (_many_small(600, 35), 256, 256, None),      # > 512 experts: the tile lookup's general path
 ])
-def test_online_fc2_matches_oracle(sizes, N, K):
-    got_y, got, want_y, want = _case(sizes, N, K, seed=31 + K)
+def test_online_fc2_matches_oracle(sizes, N, K, rps):
+    got_y, got, want_y, want = _case(sizes, N, K, seed=31 + K, rps=rps)
     assert_bytes_equal(got["gs"].view(np.uint32), want["gs"].view(np.uint32), "final gs")
     assert_bytes_equal(got["sb"], want["sb"], "block scales")
     assert_bytes_equal(got["q"], want["q"], "codes")
     r = _rel_rows(got_y, want_y)
-    print(f"[online] {sizes} N={N} K={K}: max row rel-L2 {r.max():.3e}", flush=True)
+    what = sizes if len(sizes) <= 12 else f"{len(sizes)} experts, {sum(sizes)} rows"
+    print(f"[online] {what} N={N} K={K}: max row rel-L2 {r.max():.3e}", flush=True)
     assert r.max() <= TOL, (float(r.max()), int(r.argmax()))
     zero = want["gs"] == 0
     assert zero.any() and not got_y[zero].any()
