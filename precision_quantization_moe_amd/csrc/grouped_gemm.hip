@@ -387,6 +387,15 @@ __device__ __forceinline__ void vm_wait() {
 }
 __device__ __forceinline__ void lgkm_wait0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Workgroup barrier that no LDS access moves across in the compiler (for
+// plain LDS stores and loads next to it; the caller waits for its own LDS and
+// DMA accesses first).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)p;
 }
@@ -2993,12 +3002,51 @@ struct Np {
 using NpPipe256 = Np<256, 256, 2, 4>;
 using NpPipe128 = Np<128, 256, 2, 2>;
 
-template <class C>
-struct NpSrc {
+// The ring's load sources (the same type for every fragment count of a tile
+// shape, so a persistent loop can keep one across tiles).
+template <int CA, int CB, int NS>
+struct NpRing {
   const uint8_t *Ab, *Bb, *Asb, *Bsb;
-  uint32_t oa[C::CA], ob[C::CB], os[C::NS];  // step-0 offsets
+  uint32_t oa[CA], ob[CB], os[NS];  // step-0 offsets
   uint32_t dst, sdst;  // LDS addresses of slot 0's data and scales, this wave
 };
+template <class C>
+using NpSrc = NpRing<C::CA, C::CB, C::NS>;
+
+// Point the ring's loads at the tile (g, rows row0 .. row_end - 1, columns
+// n0 ..): per-lane offsets of step 0 (rows past the tile's end clamped to its
+// last row).
+template <class C>
+__device__ __forceinline__ void np_loader(NpSrc<C> &L, const uint8_t *__restrict__ A,
+                                          const uint8_t *__restrict__ As,
+                                          const uint8_t *__restrict__ B,
+                                          const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
+                                          int64_t g, int64_t row0, int64_t row_end, int64_t n0) {
+  const int tid = threadIdx.x;
+  const uint32_t KD = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);  // row bytes of data / scales
+  const int rows_a = (int)min(row_end - row0, (int64_t)C::TMR);
+  const int rows_b = (int)min(N - n0, (int64_t)C::TN);
+  L.Ab = A + row0 * (int64_t)KD;
+  L.Bb = B + (g * N + n0) * (int64_t)KD;
+  L.Asb = As + row0 * (int64_t)KS;
+  L.Bsb = Bs + (g * N + n0) * (int64_t)KS;
+#pragma unroll
+  for (int i = 0; i < C::CA; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.oa[i] = (uint32_t)min(r, rows_a - 1) * KD + 16u * k;
+  }
+#pragma unroll
+  for (int i = 0; i < C::CB; ++i) {
+    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
+    L.ob[i] = (uint32_t)min(r, rows_b - 1) * KD + 16u * k;
+  }
+#pragma unroll
+  for (int i = 0; i < C::NS; ++i) {
+    const int d = tid + 256 * i, r = d >> 1, half = d & 1;
+    L.os[i] = r < C::TMR ? (uint32_t)min(r, rows_a - 1) * KS + 4u * half
+                          : (uint32_t)min(r - C::TMR, rows_b - 1) * KS + 4u * half;
+  }
+}
 
 // Loads q0 .. q1-1 of a step's ring loads: A chunks (when the ring carries
 // A), B chunks, then scale words (dwords 256 i + tid: rows 128 i .., A rows
@@ -3283,32 +3331,10 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = C::WM == 2 ? wave >> 1 : 0, wn = C::WM == 2 ? wave & 1 : wave;
   const int h = lane >> 5, r32 = lane & 31;
-  const uint32_t KD = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);  // row bytes of data / scales
-  const int rows_a = (int)min(ti.row_end - ti.row0, (int64_t)C::TMR);
-  const int rows_b = (int)min(N - ti.n0, (int64_t)C::TN);
   NpSrc<C> L;
-  L.Ab = A + ti.row0 * (int64_t)KD;
-  L.Bb = B + (ti.g * N + ti.n0) * (int64_t)KD;
-  L.Asb = As + ti.row0 * (int64_t)KS;
-  L.Bsb = Bs + (ti.g * N + ti.n0) * (int64_t)KS;
+  np_loader<C>(L, A, As, B, Bs, N, K, ti.g, ti.row0, ti.row_end, ti.n0);
   L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
   L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + C::SC + (uint32_t)wave * 256u);
-#pragma unroll
-  for (int i = 0; i < C::CA; ++i) {
-    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
-    L.oa[i] = (uint32_t)min(r, rows_a - 1) * KD + 16u * k;
-  }
-#pragma unroll
-  for (int i = 0; i < C::CB; ++i) {
-    const int c = tid + 256 * i, r = c >> 2, k = (c & 3) ^ ((r >> 2) & 3);
-    L.ob[i] = (uint32_t)min(r, rows_b - 1) * KD + 16u * k;
-  }
-#pragma unroll
-  for (int i = 0; i < C::NS; ++i) {
-    const int d = tid + 256 * i, r = d >> 1, half = d & 1;
-    L.os[i] = r < C::TMR ? (uint32_t)min(r, rows_a - 1) * KS + 4u * half
-                          : (uint32_t)min(r - C::TMR, rows_b - 1) * KS + 4u * half;
-  }
   NpLane o;
   {
     const int ra = wm * C::WROWS + r32, rb = wn * C::WCOLS + r32;
@@ -3426,6 +3452,312 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
     np_tile<OUT_F32, Np<128, 512, 1, 1>>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out, bg);
 }
 
+// ------------------------------------- NVFP4, persistent 128 x 512 tiles
+// k_gemm_nvfp4_wide as a persistent kernel (bf16 output, no bias): one
+// workgroup per CU walks its tiles (dealt as the tile list below says) as one
+// unbroken stream of ring steps.  The ring refills run three
+// steps ahead across tile boundaries (the loader moves on to the next tile
+// when a refill reaches its step 0), together with that tile's outer scales
+// (128 alpha_a and 512 alpha_b values, by DMA into one of two LDS buffers);
+// a tile's output leaves by buffer stores of fixed count (NPW_ST per lane,
+// rows and columns outside the tile dropped by an out-of-range offset), so
+// the next tile's first waits can leave them in flight.  Each workgroup
+// keeps its CU, so neither the tile's prologue nor its stores wait for a
+// workgroup to end and another to start.
+
+template <int FI_>
+using NpW = Np<128, 512, 1, FI_>;
+constexpr int NPW_MAXT = 256;  // tiles per workgroup
+constexpr int NPW_ST = 32;     // bf16 stores per lane per tile (4 x 4 fragments x 2)
+constexpr int NPW_AL = 768;    // alpha floats per buffer: 128 rows, 512 columns, padding
+
+// Exclusive prefix of v over the 256 threads (thread order) plus `carry`,
+// which then grows by the 256 values' sum.  wsum: 4 shared slots.
+__device__ __forceinline__ int32_t np_scan256(int32_t v, int32_t &carry, int32_t *wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int32_t before = carry, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  carry += all;
+  __syncthreads();
+  return before + incl - v;
+}
+
+// The outer scales of tile t by DMA: entry e = tid + 256 i (i = 0..2) of the
+// buffer is alpha_a of row row0 + e (e < 128, clamped to the tile's rows) or
+// alpha_b(n0 + e - 128) (clamped to column N - 1); entries 640.. repeat
+// alpha_a of row row0.  abase: this wave's LDS address in the buffer.
+__device__ __forceinline__ void npw_alpha_issue(const float *__restrict__ Ao,
+                                                const float *__restrict__ Bo, int64_t b_rps,
+                                                int64_t N, const QpTile &t, uint32_t abase) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int e = tid + 256 * i;
+    const float *src;
+    if (e < 128) {
+      src = Ao + min((int64_t)t.row0 + e, (int64_t)t.row_end - 1);
+    } else if (e < 640) {
+      const int64_t col = min((int64_t)t.n0 + (e - 128), N - 1);
+      src = Bo + ((int64_t)t.g * N + col) / b_rps;
+    } else {
+      src = Ao + t.row0;
+    }
+    dma4(src, abase + (uint32_t)i * 1024u);
+  }
+}
+
+// The tile's bf16 output: NPW_ST buffer stores per lane whatever the tile's
+// fragment count (fragments i >= FI and cells outside the tile get an
+// out-of-range offset); values as np_store scales them (binary64 product of
+// the accumulator and alpha_a alpha_b, one rounding to binary32, then bf16).
+template <class C>
+__device__ __forceinline__ void npw_store(const v16f (&acc)[C::FI][C::FJ],
+                                          __amdgpu_buffer_rsrc_t rs, const QpTile &t, int64_t N,
+                                          const float *al) {
+  static_assert(C::WM == 1 && C::FJ == 4, "1 x 4 waves of 128 x 128");
+  typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 32 * i + r32;  // row within the tile
+    const int64_t row = (int64_t)t.row0 + rl;
+    const double aa = (double)al[rl];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int c0 = wave * C::WCOLS + 32 * j + 16 * p + 8 * h;  // column within the tile
+        const int64_t col = (int64_t)t.n0 + c0;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        uint32_t off = QP_OOB;
+        if (i < C::FI) {
+          const v16f &a = acc[i < C::FI ? i : 0][j];
+          float lo[4], hi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = a[8 * p + e], y = a[8 * p + 4 + e];
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h ? x : y),
+                                                             __float_as_uint(h ? x : y), false,
+                                                             false);
+            const float got = __uint_as_float(h ? sw[0] : sw[1]);
+            lo[e] = h ? got : x;
+            hi[e] = h ? y : got;
+          }
+          float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (float)((double)v[e] * (aa * (double)al[128 + c0 + e]));
+          w = u32x4{pk_bf16_rne(v[0], v[1]), pk_bf16_rne(v[2], v[3]), pk_bf16_rne(v[4], v[5]),
+                    pk_bf16_rne(v[6], v[7])};
+          if (row < t.row_end && col < N) off = (uint32_t)((row * N + col) * 2);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(w, rs, (int)off, 0, 0);
+      }
+    }
+  }
+}
+
+// One tile of the persistent stream (C: its fragment count); slot: the ring
+// slot of the tile's step 0 on entry, of the next tile's step 0 on exit.
+template <class C>
+__device__ __forceinline__ void npw_tile(NpSrc<C> &L, const QpTile *tl, int t, int S, int nk,
+                                         int &slot, const uint8_t *lds, const NpLane &o,
+                                         const uint8_t *__restrict__ A,
+                                         const uint8_t *__restrict__ As,
+                                         const float *__restrict__ Ao,
+                                         const uint8_t *__restrict__ B,
+                                         const uint8_t *__restrict__ Bs,
+                                         const float *__restrict__ Bo, int64_t b_rps, int64_t N,
+                                         int64_t K, uint32_t abase, const float *al,
+                                         __amdgpu_buffer_rsrc_t rs) {
+  constexpr int FI = C::FI, FJ = C::FJ;
+  if (t > 0) {
+    // own loads of this tile's step 0 done (its steps 1 and 2 and the last
+    // tile's stores may be pending); after the barrier every wave's are
+    vm_wait<2 * C::OPS + NPW_ST>();
+    lgkm_wait0();
+    wg_barrier();
+  }
+  NpHalf<C> R0, R1;
+  NpWords<C> W;
+  NpScales<C> S_;
+  NpDec<C> X, Y;
+  np_read_half<C, 0>(lds, slot, o, R0);
+  np_read_half<C, 1>(lds, slot, o, R1);
+  np_read_words<C>(lds, slot, o, W);
+  np_scales<C, 0>(W, S_);
+  np_dec<C, 0>(R0, S_, X);
+  v16f acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  for (int k = 0; k < nk; ++k) {
+    // own loads of step k + 1 done; at the tile's first two steps the last
+    // tile's stores came after them and may stay in flight
+    if (t > 0 && k < 2)
+      vm_wait<C::OPS + NPW_ST>();
+    else
+      vm_wait<C::OPS>();
+    lgkm_wait0();
+    wg_barrier();
+    const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;
+    // the refill: stream step v, past the end the last step again (in
+    // bounds; read, never multiplied)
+    const int v = t * nk + k + C::NSLOT;
+    int rk = nk - 1;
+    if (v < S) {
+      rk = v % nk;
+      if (rk == 0) {  // the refills move on to tile v / nk, with its outer scales
+        const QpTile tn = tl[v / nk];
+        np_loader<C>(L, A, As, B, Bs, N, K, tn.g, tn.row0, tn.row_end, tn.n0);
+        npw_alpha_issue(Ao, Bo, b_rps, N, tn, abase + (uint32_t)((v / nk) & 1) * (NPW_AL * 4));
+      }
+    }
+    np_step<C>(L, rk, slot, lds, o, nslot, acc, R0, R1, W, S_, X, Y);
+    slot = nslot;
+  }
+  npw_store<C>(acc, rs, tl[t], N, al);
+}
+
+__global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide_p(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const float *__restrict__ Ao, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    void *__restrict__ out, uint32_t out_bytes) {
+  using W4 = NpW<4>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[W4::LDS];
+  __shared__ __attribute__((aligned(16))) float alpha[2 * NPW_AL];
+  __shared__ QpTile tl[NPW_MAXT];
+  __shared__ int32_t wsum[4], nt_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, r32 = lane & 31;
+
+  // ---- tile list.  Row tiles in four classes by the fragments they
+  // multiply (a full tile or a tail of 97..127 rows: 4; tails of 65..96: 3;
+  // 33..64: 2; 1..32: 1), heaviest class first, experts in order within a
+  // class; row tile R goes to XCD R % 8 with its column tiles (so they share
+  // that XCD's L2), and an XCD deals its tiles, in that order, round-robin
+  // to its workgroups: every workgroup gets a like mix of heavy and light
+  // tiles.  pre[c (G + 1) + g]: row tiles of class 4 - c before expert g.
+  int32_t *pre = reinterpret_cast<int32_t *>(lds);  // 4 (G + 1) entries (checked on the host)
+  {
+    int32_t carry[4] = {0, 0, 0, 0};
+    for (int64_t b0 = 0; b0 < G; b0 += 256) {
+      const int64_t g = b0 + tid;
+      const int64_t rows = g < G ? offsets[g + 1] - offsets[g] : 0;
+      const int32_t full = (int32_t)(rows / 128), tc = (int32_t)((rows % 128 + 31) / 32);
+      const int32_t v[4] = {full + (tc == 4), tc == 3, tc == 2, tc == 1};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int32_t x = np_scan256(v[c], carry[c], wsum);
+        if (g < G) pre[c * (G + 1) + g] = x;
+      }
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) pre[c * (G + 1) + G] = carry[c];
+    }
+  }
+  __syncthreads();
+  {
+    int32_t cnt[4], nrt = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      cnt[c] = pre[c * (G + 1) + G];
+      nrt += cnt[c];
+    }
+    const int x = (int)(blockIdx.x % 8), w = (int)(blockIdx.x / 8), nw = (int)(gridDim.x / 8);
+    const int64_t nq = (int64_t)(nrt > x ? (nrt - x + 7) / 8 : 0) * ntn;  // this XCD's tiles
+    const int nt = nq > w ? (int)((nq - w + nw - 1) / nw) : 0;
+    if (tid == 0) nt_sh = min(nt, NPW_MAXT);
+    for (int k = tid; k < nt && k < NPW_MAXT; k += 256) {
+      const int64_t q = w + (int64_t)k * nw;
+      const int32_t R = (int32_t)(8 * (q / ntn) + x);
+      int c = 0;
+      int32_t r = R;
+      while (c < 3 && r >= cnt[c]) r -= cnt[c++];
+      const int32_t *pc = pre + c * (G + 1);
+      int a = 0, bb = (int)G;  // largest g with pc[g] <= r (pc[G] > r)
+      while (bb - a > 1) {
+        const int m = (a + bb) >> 1;
+        if (pc[m] <= r) a = m; else bb = m;
+      }
+      const int64_t rows = offsets[a + 1] - offsets[a];
+      QpTile t;
+      t.g = a;
+      t.row0 = (int32_t)(offsets[a] + 128 * (c == 0 ? (int64_t)(r - pc[a]) : rows / 128));
+      t.row_end = (int32_t)offsets[a + 1];
+      t.n0 = (int32_t)((q % ntn) * 512);
+      tl[k] = t;
+    }
+  }
+  __syncthreads();  // the tile list is complete and pre is no longer read
+  const int nt = nt_sh;
+  if (nt == 0) return;
+  const int nk = (int)(K / 128);  // >= 3
+  const int S = nt * nk;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(out, (short)0, (int)out_bytes, 0x00020000);
+  NpSrc<W4> L;
+  L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
+  L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + W4::SC + (uint32_t)wave * 256u);
+  const uint32_t abase = __builtin_amdgcn_readfirstlane(lds_addr(alpha) + (uint32_t)wave * 256u);
+  NpLane o;
+  {
+    const int ra = r32, rb = wave * W4::WCOLS + r32;
+    o.a0 = mx3_off(ra, 2 * h);
+    o.a1 = mx3_off(ra, 2 * h + 1);
+    o.b0 = W4::TMR * 64 + mx3_off(rb, 2 * h);
+    o.b1 = W4::TMR * 64 + mx3_off(rb, 2 * h + 1);
+    o.sa = W4::SC + ra * 8 + 4 * h;
+    o.sb = W4::SC + (W4::TMR + rb) * 8 + 4 * h;
+  }
+  // prologue: tile 0's outer scales and its steps 0 .. 2
+  {
+    const QpTile t0 = tl[0];
+    np_loader<W4>(L, A, As, B, Bs, N, K, t0.g, t0.row0, t0.row_end, t0.n0);
+    npw_alpha_issue(Ao, Bo, b_rps, N, t0, abase);
+#pragma unroll
+    for (int s = 0; s < W4::NSLOT; ++s) np_issue<W4>(L, s, s);
+  }
+  vm_wait<(W4::NSLOT - 1) * W4::OPS>();  // the outer scales and step 0
+  lgkm_wait0();
+  wg_barrier();
+  int slot = 0;
+  for (int t = 0; t < nt; ++t) {
+    const int rows = tl[t].row_end - tl[t].row0;
+    const float *al = alpha + (t & 1) * NPW_AL;
+    if (rows > 96)
+      npw_tile<W4>(L, tl, t, S, nk, slot, lds, o, A, As, Ao, B, Bs, Bo, b_rps, N, K, abase, al,
+                   rs);
+    else if (rows > 64)
+      npw_tile<NpW<3>>(L, tl, t, S, nk, slot, lds, o, A, As, Ao, B, Bs, Bo, b_rps, N, K, abase,
+                       al, rs);
+    else if (rows > 32)
+      npw_tile<NpW<2>>(L, tl, t, S, nk, slot, lds, o, A, As, Ao, B, Bs, Bo, b_rps, N, K, abase,
+                       al, rs);
+    else
+      npw_tile<NpW<1>>(L, tl, t, S, nk, slot, lds, o, A, As, Ao, B, Bs, Bo, b_rps, N, K, abase,
+                       al, rs);
+  }
+  vm_wait<0>();  // stores done and no load still targets this workgroup's LDS
+}
+
 // ------------------------------------------- NVFP4 FC2 with online amax
 // "miniTE technical report", 5.6: FC2 consumes the activation P (the
 // weighted SwiGLU output, bf16) K-tile by K-tile, before a row's full
@@ -3449,14 +3781,6 @@ using NpOn = Np<128, 256, 2, 2, false>;
 constexpr int NPO_PL = 8;               // P-ring loads per lane per tile
 constexpr int NPO_PSLOT = 128 * 256;    // bytes of one P tile (128 rows x 128 bf16)
 
-// Workgroup barrier that no LDS access moves across in the compiler (the
-// encoding's plain LDS stores and loads sit next to it; the caller waits for
-// its own LDS and DMA accesses first).
-__device__ __forceinline__ void npo_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Running state of the rows tid / 8 + 32 j (j = 0..3) of the thread's blocks;
 // the 8 threads of a row hold the same values.  rc: the encoding constants of
@@ -3656,15 +3980,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_online(
   npo_issue_p(Pt, K, rows_a, 0, pdst, 0);
   npo_issue_p(Pt, K, rows_a, 1, pdst, 1);
   vm_wait<NPO_PL>();  // all but P tile 1
-  npo_barrier();
+  wg_barrier();
   npo_encode(pring, 0, lds, ratio[0], gsf, st, 0, rows_a, ti.row0, K, qo, sb_out);
   vm_wait<0>();
   lgkm_wait0();
-  npo_barrier();  // P tile 1 landed; P slot 0 read by every wave
+  wg_barrier();  // P tile 1 landed; P slot 0 read by every wave
   npo_encode(pring, 1, lds + C::SLOT, ratio[1], gsf, st, 1, rows_a, ti.row0, K, qo, sb_out);
   npo_issue_p(Pt, K, rows_a, min(2, nk - 1), pdst, 0);
   lgkm_wait0();
-  npo_barrier();
+  wg_barrier();
   NpHalf<C> R0, R1;
   NpWords<C> W;
   NpScales<C> S;
@@ -3685,7 +4009,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_online(
     else
       vm_wait<C::OPS>();
     lgkm_wait0();
-    npo_barrier();
+    wg_barrier();
     const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;
     npo_issue_p(Pt, K, rows_a, min(kt + 3, nk - 1), pdst, (kt + 1) & 1);
     if (kt + 2 < nk) {
@@ -3770,6 +4094,26 @@ static bool qp_fits(int64_t G, int64_t M, int64_t N, int64_t K, int esize) {
   const int64_t tiles_ub = (cdiv(M, 256) + G) * cdiv(N, 256);
   const int64_t nw = qp_grid(G, M, N) / 8;
   return cdiv(cdiv(tiles_ub, 8), nw) <= QP_MAXT;
+}
+
+// Persistent NVFP4 grid: one workgroup per CU (a multiple of 8), fewer when
+// there are fewer tiles; its limits: the expert tile counts fit the ring's
+// LDS for the scan, every workgroup's tiles fit its list, the bf16 output is
+// below 2^31 bytes (store offsets and the dropped offset), whole 16-byte
+// output vectors, and at least 3 steps per tile (the refills run 3 ahead).
+static int64_t npw_tiles_ub(int64_t G, int64_t M, int64_t N) {
+  return (cdiv(M, 128) + G) * cdiv(N, 512);
+}
+static int64_t npw_grid(int64_t G, int64_t M, int64_t N) {
+  const int64_t cus = resident_workgroups((const void *)k_gemm_nvfp4_wide_p, 256, 0);
+  return max((int64_t)8, min(cdiv(cus, 8) * 8, cdiv(npw_tiles_ub(G, M, N), 8) * 8));
+}
+static bool npw_fits(int64_t G, int64_t M, int64_t N, int64_t K) {
+  if (4 * (G + 1) * 4 > NpW<4>::LDS) return false;
+  if (N % 8 || K / 128 < 3) return false;
+  if (M * N * 2 >= (int64_t)QP_OOB) return false;
+  const int64_t nw = npw_grid(G, M, N) / 8;
+  return cdiv(cdiv(cdiv(M, 128) + G, 8) * cdiv(N, 512), nw) <= NPW_MAXT;
 }
 
 int64_t grouped_gemm_workspace_bytes(int fmt, int kind) {
@@ -3993,6 +4337,15 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
         hipLaunchKernelGGL((k_gemm_bf16_rows<true, false>), grid, dim3(256), 0, st, A, B,
                            offsets, G, N, K, ntn, out, nullptr);
     }
+    return hipGetLastError();
+  }
+  if (fmt == 2 && K > 0 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0 &&
+      N >= 512 && M <= 256 * G && !out_fp32 && !bias && npw_fits(G, M, N, K)) {
+    // experts of 256 rows or fewer on average, bf16 output: persistent
+    const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
+    hipLaunchKernelGGL(k_gemm_nvfp4_wide_p, dim3((unsigned)npw_grid(G, M, N)), dim3(256), 0, st, A,
+                       a_scale, a_outer, B, b_scale, b_outer, b_rows_per_scale, offsets, G, N, K,
+                       cdiv(N, 512), out, (uint32_t)(M * N * 2));
     return hipGetLastError();
   }
   if (fmt == 2 && K > 0 && K % 256 == 0 && (uintptr_t)a_scale % 4 == 0 && (uintptr_t)b_scale % 4 == 0 &&

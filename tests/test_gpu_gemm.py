@@ -16,7 +16,7 @@ import torch
 import oracle
 import precision_quantization_moe_amd as pqm
 from precision_quantization_moe_amd import workloads as wl
-from gpu_util import dev, dev_bf16, host, host_u16, requires_gpu
+from gpu_util import assert_bytes_equal, dev, dev_bf16, host, host_u16, requires_gpu
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -594,6 +594,46 @@ def test_bf16_output_is_rne_of_binary32_output(fmt, sizes, N, K):
     print(f"[gemm] {fmt} K={K} bf16 output vs RNE(binary32 output): {bad} mismatches "
           f"of {got.size}", flush=True)
     assert bad == 0
+
+
+@pytest.mark.parametrize("case", [
+    # tails of 1 .. 128 rows (1, 2, 3 and 4 fragments), 4 steps per tile
+    ([70, 100, 127, 33, 32, 96, 0, 1, 128, 65, 64, 97], 520, 512),
+    ([400, 0, 513, 129, 64], 1024, 1024),    # experts of several row tiles, 2 column tiles
+    ("many", 512, 768),                       # 300 mostly tiny experts: many tiles per workgroup
+    ([1], 512, 512),                          # one tile: every other workgroup has none
+])
+def test_nvfp4_persistent_bf16(case):
+    """The persistent NVFP4 kernel (bf16 output of the 128 x 512 tile path):
+    against the oracle at the bar plus one bf16 rounding, and bit for bit
+    the nearest-even rounding of the binary32 output (another kernel, the
+    same accumulation order and scaling)."""
+    sizes, N, K = case
+    if sizes == "many":
+        sizes = _many_small_groups(300, seed=94)
+    G, M = len(sizes), int(sum(sizes))
+    assert M <= 256 * G
+    x = wl.activations(M, K, seed=95)
+    w = wl.normal_bf16((G * N, K), std=0.01, seed=96)
+    off = _offsets(sizes)
+    qa, sa, ga = pqm.quantize_nvfp4_per_token(dev_bf16(x))
+    qb, sb, gb = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=N)
+    kw = dict(a_scale=sa, a_outer=ga, b_scale=sb, b_outer=gb, b_rows_per_scale=N)
+    print(f"[gemm] nvfp4 persistent G={G} M={M} N={N} K={K}", flush=True)
+    y16 = pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, qa, qb, dev(off), N, K,
+                               out_dtype=pqm.OUT_BF16, **kw)
+    y32 = pqm.moe_grouped_gemm(pqm.FMT_NVFP4, pqm.GEMM_FPROP, qa, qb, dev(off), N, K,
+                               out_dtype=pqm.OUT_FP32, **kw)
+    torch.cuda.synchronize()
+    got = host_u16(y16)
+    assert_bytes_equal(got, _rne_bf16_bits(host(y32)), "bf16 vs RNE(binary32)")
+    ra, rsa, rga = oracle.quantize_nvfp4(x)
+    rb, rsb, rgb = oracle.quantize_nvfp4(w, rows_per_group=N)
+    want = oracle.grouped_gemm(oracle.decode_nvfp4(ra, rsa, rga),
+                               oracle.decode_nvfp4(rb, rsb, rgb, N).reshape(G, N, K), off)
+    r = rel_l2_rows(oracle.bf16_to_f64(got), want)
+    print(f"[gemm] nvfp4 persistent: max row rel-L2 {r.max():.3e}", flush=True)
+    assert r.max() <= TOL + 2.0 ** -9, (float(r.max()), int(r.argmax()))
 
 
 # ------------------------------------------------- degenerate and large-G
