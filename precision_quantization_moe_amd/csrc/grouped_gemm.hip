@@ -3022,7 +3022,8 @@ __device__ __forceinline__ void np_loader(NpSrc<C> &L, const uint8_t *__restrict
                                           const uint8_t *__restrict__ B,
                                           const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
                                           int64_t g, int64_t row0, int64_t row_end, int64_t n0) {
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // recomputed where called, not kept live across a loop
   const uint32_t KD = (uint32_t)(K / 2), KS = (uint32_t)(K / 16);  // row bytes of data / scales
   const int rows_a = (int)min(row_end - row0, (int64_t)C::TMR);
   const int rows_b = (int)min(N - n0, (int64_t)C::TN);
@@ -3501,7 +3502,8 @@ __device__ __forceinline__ int32_t np_scan256(int32_t v, int32_t &carry, int32_t
 __device__ __forceinline__ void npw_alpha_issue(const float *__restrict__ Ao,
                                                 const float *__restrict__ Bo, int64_t b_rps,
                                                 int64_t N, const QpTile &t, uint32_t abase) {
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     const int e = tid + 256 * i;
