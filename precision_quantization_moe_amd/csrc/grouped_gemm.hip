@@ -487,6 +487,18 @@ __device__ __forceinline__ void mx3_mma(const Mx3Frags<TM> &F,
 // 16 p + 8 (l / 32) + 0..7, p = 0, 1: two 16-byte stores per lane.
 // bias: the expert's bias row (binary32, N columns) added to every value
 // before the output rounding, or null.
+// Lane (h, r) holds a and b; one swap of the upper half-wave's a with the
+// lower half-wave's b leaves lane (0, r) with lo = its a, hi = lane (1, r)'s
+// a, and lane (1, r) with lo = lane (0, r)'s b, hi = its b.  (Rows r of a
+// 32 x 32 fragment: a, b the runs of 4 columns at 8 g + 4 h and 8 g + 8 +
+// 4 h give each lane 8 consecutive columns.)
+__device__ __forceinline__ void half_trade(float a, float b, float &lo, float &hi) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                   false);
+  lo = __uint_as_float(sw[0]);
+  hi = __uint_as_float(sw[1]);
+}
+
 template <bool OUT_F32>
 __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N, int64_t row0,
                                           int64_t row_end, int64_t n0, int rbase, int cbase,
@@ -523,17 +535,7 @@ __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N,
     // low half's run 2p+1
     float lo[4], hi[4];  // this lane's first and second 4 columns after the swap
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = acc[8 * p + e], b = acc[8 * p + 4 + e];  // runs 2p, 2p+1
-      // swap: low-half lanes give b (run 2p+1) and get the high half's a
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h ? a : b),
-                                                       __float_as_uint(h ? a : b), false, false);
-      // the value from the other half arrives in element 1 (the second
-      // operand's new value) for low-half lanes and element 0 for high ones
-      const float got = __uint_as_float(h ? sw[0] : sw[1]);
-      lo[e] = h ? got : a;   // high half: the low half's run 2p+1 comes first
-      hi[e] = h ? b : got;
-    }
+    for (int e = 0; e < 4; ++e) half_trade(acc[8 * p + e], acc[8 * p + 4 + e], lo[e], hi[e]);
     const int64_t col = n0 + cbase + 16 * p + 8 * h;
     if (row >= row_end) continue;
     if (bias) {
@@ -1135,11 +1137,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_q(
 // tiles (those of its XCD's contiguous range, 32 apart) with one unbroken
 // stream of ring steps, so the first two steps of tile n+1 are loaded while
 // tile n finishes and no tile starts with an empty ring.  Tile n's output
-// leaves by buffer stores issued right after its last step, the same number
-// of store instructions in every wave (rows past the tile's end get an
-// offset beyond the buffer, which the hardware drops), so that the first
-// step of tile n+1 can wait for its own loads (issued before the stores)
-// with vmcnt <= stores and let the stores drain under its MFMAs.  On an
+// leaves by buffer stores issued right after its last step (rows past the
+// tile's end get an offset beyond the buffer, which the hardware drops); the
+// first step of tile n+1 waits for them with its own loads, which were
+// issued before them (only loads keep their order in vmcnt, so a wait that
+// let the stores stay in flight could release early).  On an
 // expert's last tile of at most 128 rows the four waves of rows 128..255
 // skip their MFMAs (their rows are beyond the tile).  The tile list is made
 // once at the start: a scan of the per-expert tile counts (in the ring's
@@ -1187,15 +1189,16 @@ typedef uint32_t pqm_v16u __attribute__((ext_vector_type(16)));
 template <int S>
 __device__ __forceinline__ pqm_v16u quad_stage(pqm_v16u v, bool hi) {
   pqm_v16u r = v;
+  constexpr int ctrl = S == 1 ? 0xB1 : 0x4E;  // quad_perm lane b ^ S
 #pragma unroll
   for (int q = 0; q < 8; ++q) {  // the 8 registers of the groups g0 with bit S clear
     const int g0 = S == 1 ? 2 * (q >> 2) : (q >> 2), e = q & 3;
     const int x0 = 4 * g0 + e, x1 = 4 * (g0 | S) + e;
-    const uint32_t send = hi ? v[x0] : v[x1];
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, S == 1 ? 0xB1 : 0x4E,
-                                                               0xF, 0xF, false);
-    r[x0] = hi ? recv : v[x0];
-    r[x1] = hi ? v[x1] : recv;
+    // the partner's registers (each select takes its moved operand directly)
+    const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[x1], ctrl, 0xF, 0xF, false);
+    const uint32_t p0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[x0], ctrl, 0xF, 0xF, false);
+    r[x0] = !hi ? v[x0] : p1;
+    r[x1] = hi ? v[x1] : p0;
   }
   return r;
 }
@@ -1246,40 +1249,46 @@ __device__ __forceinline__ void qp_store(const v16f (&acc)[4][2], __amdgpu_buffe
       }
     }
     if (!OUT_F32) {
-      // bf16: lane (h, r) holds row r's 16-byte chunks 4 j + 2 p + h of the
-      // wave's 64 columns (runs 2p, 2p+1 traded between lane halves as in
-      // mx3_store); a quad transpose of those 4 chunks leaves in chunk k of
-      // lane (h, 4 a + b) row 4 a + k's chunk 2 b + h, so each store writes
-      // eight whole 128-byte rows
+      // bf16: lane (h, r) holds row r's columns 16 p + 4 h .. + 3 (x) and
+      // 16 p + 8 + 4 h .. + 3 (y) of the fragment's 32; packed in pairs, one
+      // lane swap of the upper half-wave's x with the lower half-wave's y
+      // leaves lane (0, r) with chunk 2 p (its own x, then lane (1, r)'s) and
+      // lane (1, r) with chunk 2 p + 1 (lane (0, r)'s y, then its own): chunk
+      // 4 j + 2 p + h of the wave's 64 columns.  A quad transpose of those 4
+      // chunks leaves in chunk k of lane (h, 4 a + b) row 4 a + k's chunk
+      // 2 b + h, so each store writes eight whole 128-byte rows
       pqm_v16u v;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const v16f &a = acc[i][j];
-          float lo[4], hi[4];
+          float x[4], y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float x = a[8 * p + e], y = a[8 * p + 4 + e];
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(h ? x : y),
-                                                             __float_as_uint(h ? x : y), false, false);
-            const float got = __uint_as_float(h ? sw[0] : sw[1]);
-            lo[e] = h ? got : x;
-            hi[e] = h ? y : got;
+            x[e] = a[8 * p + e];
+            y[e] = a[8 * p + 4 + e];
           }
-          if (bias) {  // chunk 4 j + 2 p + h of the wave's 64 columns
-            const uint32_t c8 = (uint32_t)(t.n0 + wn * 64 + 8 * (4 * j + 2 * p + h));
+          if (bias) {
+            // runs of 4 columns start on a multiple of 4 and N % 8 == 0, so a
+            // run is inside N or wholly past it (then any run will do)
+            const uint32_t c = (uint32_t)(t.n0 + wn * 64 + 32 * j + 16 * p + 4 * h);
+            const float *bx = bias + min(c, Nu - 4u), *by = bias + min(c + 8, Nu - 4u);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              lo[e] += bias[min(c8 + e, Nu - 1u)];
-              hi[e] += bias[min(c8 + 4 + e, Nu - 1u)];
+              x[e] += bx[e];
+              y[e] += by[e];
             }
           }
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pk_bf16_rne(x[0], x[1]),
+                                                           pk_bf16_rne(y[0], y[1]), false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pk_bf16_rne(x[2], x[3]),
+                                                           pk_bf16_rne(y[2], y[3]), false, false);
           const int m = 2 * j + p;
-          v[4 * m] = pk_bf16_rne(lo[0], lo[1]);
-          v[4 * m + 1] = pk_bf16_rne(lo[2], lo[3]);
-          v[4 * m + 2] = pk_bf16_rne(hi[0], hi[1]);
-          v[4 * m + 3] = pk_bf16_rne(hi[2], hi[3]);
+          v[4 * m] = s0[0];
+          v[4 * m + 1] = s1[0];
+          v[4 * m + 2] = s0[1];
+          v[4 * m + 3] = s1[1];
         }
       }
       const int b = r32 & 3, a4 = r32 >> 2;
@@ -1515,10 +1524,11 @@ __device__ __forceinline__ void k_gemm_mxfp8_qp_body(
   for (int u = 0; u < S; ++u) {
     const int slot = u & 1, k = u % nk;
     mq_half<256>(L, lds, o, acc, F, slot, 1, false, 0u, 0, active);
-    if (k == 0 && u > 0)
-      vm_wait<EPI ? 8 : (OUT_F32 ? 32 : 16)>();  // loads of step u+1 came before the last tile's stores
-    else
-      vm_wait<0>();
+    // own loads of step u+1 arrived; at a tile's first step the last tile's
+    // stores came after them and are waited for too (a count that let them
+    // stay in flight could release early: a store whose lanes are all out of
+    // range need not hold its place in the count)
+    vm_wait<0>();
     lgkm_wait0();
     __builtin_amdgcn_s_barrier();
     const int v = u + 2;
@@ -1940,7 +1950,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_wgrad_qp(
   __shared__ int32_t seq[4];  // DYN: tile j of this workgroup's sequence at j % 4
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
-  constexpr int STORES = OUT_F32 ? 32 : 16;  // store instructions per lane and tile
 
   // ---- experts ranked by steps, descending (ties by index)
   int32_t *stp = reinterpret_cast<int32_t *>(lds);  // setup only, before any ring load
@@ -2049,10 +2058,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_wgrad_qp(
   for (int u = 0;; ++u) {
     const int slot = u & 1;
     mw_half(L, lds, o, acc, F, slot, 1, false, 0, 0, active);
-    if (ck == 0 && u > 0)
-      vm_wait<STORES>();  // loads of step u+1 came before the last tile's stores
-    else
-      vm_wait<0>();
+    // own loads of step u+1 arrived (at a tile's first step after the last
+    // tile's stores, which are waited for too: only loads keep their order
+    // in the count)
+    vm_wait<0>();
     if (DYN && pend) {  // (thread 0 only) tile ci + 3 of the sequence
       seq[(ci + 3) & 3] = P + (int32_t)fetched;
       pend = false;
@@ -3460,9 +3469,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_wide(
 // steps ahead across tile boundaries (the loader moves on to the next tile
 // when a refill reaches its step 0), together with that tile's outer scales
 // (128 alpha_a and 512 alpha_b values, by DMA into one of two LDS buffers);
-// a tile's output leaves by buffer stores of fixed count (NPW_ST per lane,
-// rows and columns outside the tile dropped by an out-of-range offset), so
-// the next tile's first waits can leave them in flight.  Each workgroup
+// a tile's output leaves by buffer stores issued after its last step (NPW_ST
+// per lane, rows and columns outside the tile dropped by an out-of-range
+// offset).  The waits count loads only (loads complete in order among
+// themselves; a store, above all one with every lane out of range, need not
+// keep its place in vmcnt), so the stores hold the next tile's first waits up
+// only while they outnumber the younger loads still out.  Each workgroup
 // keeps its CU, so neither the tile's prologue nor its stores wait for a
 // workgroup to end and another to start.
 
@@ -3585,9 +3597,11 @@ __device__ __forceinline__ void npw_tile(NpSrc<C> &L, const QpTile *tl, int t, i
                                          __amdgpu_buffer_rsrc_t rs) {
   constexpr int FI = C::FI, FJ = C::FJ;
   if (t > 0) {
-    // own loads of this tile's step 0 done (its steps 1 and 2 and the last
-    // tile's stores may be pending); after the barrier every wave's are
-    vm_wait<2 * C::OPS + NPW_ST>();
+    // own loads of this tile's step 0 done (the loads of its steps 1 and 2
+    // may be pending: the count names loads only, which complete in order,
+    // while the last tile's stores, some with every lane out of range, need
+    // not hold their place); after the barrier every wave's are
+    vm_wait<2 * C::OPS>();
     lgkm_wait0();
     wg_barrier();
   }
@@ -3608,12 +3622,8 @@ __device__ __forceinline__ void npw_tile(NpSrc<C> &L, const QpTile *tl, int t, i
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   for (int k = 0; k < nk; ++k) {
-    // own loads of step k + 1 done; at the tile's first two steps the last
-    // tile's stores came after them and may stay in flight
-    if (t > 0 && k < 2)
-      vm_wait<C::OPS + NPW_ST>();
-    else
-      vm_wait<C::OPS>();
+    // own loads of step k + 1 done (one step's refill may be pending)
+    vm_wait<C::OPS>();
     lgkm_wait0();
     wg_barrier();
     const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;

@@ -146,8 +146,8 @@ def test_mxfp8_qwen3_gate_up_full_sampled():
 
 
 def test_mxfp8_qwen3_down_full_sampled():
-    """Full Qwen3-30B-A3B FC2 shape (the two-workgroups-per-CU kernel that
-    runs K <= 1024): 65536 routed rows of D [.., 768] under Zipf(1.1) load,
+    """Full Qwen3-30B-A3B FC2 shape (the persistent 256 x 256 kernel, bf16
+    output): 65536 routed rows of D [.., 768] under Zipf(1.1) load,
     N = 2048, K = 768, bf16 output as in the layer; sampled rows of every
     checked expert against the binary64 product (bar + one bf16 rounding)."""
     T, E, k, H, I = 8192, 128, 8, 2048, 768
@@ -562,8 +562,8 @@ def _rne_bf16_bits(f32: np.ndarray) -> np.ndarray:
 
 
 @pytest.mark.parametrize("fmt,sizes,N,K", [
-    ("mxfp8", [300, 0, 513, 129, 64], 520, 2048),  # 256 x 256 kernel
-    ("mxfp8", [300, 0, 513, 129, 64], 520, 768),   # 128 x 256 two-per-CU kernel
+    ("mxfp8", [300, 0, 513, 129, 64], 520, 2048),  # the persistent 256 x 256 kernel
+    ("mxfp8", [300, 0, 513, 129, 64], 520, 768),
     ("nvfp4", [300, 0, 513, 129, 64], 520, 768),
 ])
 def test_bf16_output_is_rne_of_binary32_output(fmt, sizes, N, K):
@@ -633,6 +633,44 @@ def test_nvfp4_persistent_bf16(case):
                                oracle.decode_nvfp4(rb, rsb, rgb, N).reshape(G, N, K), off)
     r = rel_l2_rows(oracle.bf16_to_f64(got), want)
     print(f"[gemm] nvfp4 persistent: max row rel-L2 {r.max():.3e}", flush=True)
+    assert r.max() <= TOL + 2.0 ** -9, (float(r.max()), int(r.argmax()))
+
+
+@pytest.mark.parametrize("case", [
+    # tails of 1 .. 128 rows (the waves of rows 128..255 idle), 4 steps per tile
+    ([70, 100, 127, 33, 32, 96, 0, 1, 128, 65, 64, 97], 520, 512),
+    ([400, 0, 513, 129, 64], 1024, 640),     # several row tiles, 4 column tiles, 5 steps
+    ("many", 256, 512),                       # 600 mostly tiny experts: many tiles per workgroup
+    ([1], 264, 1024),                         # one row, two column tiles (the second 8 wide)
+])
+def test_mxfp8_persistent_bf16(case):
+    """The persistent MXFP8 kernel's bf16 epilogue (pairs packed, then traded
+    between the half-waves and transposed within quads): against the oracle
+    at the bar plus one bf16 rounding, and bit for bit the nearest-even
+    rounding of the same kernel's binary32 output."""
+    sizes, N, K = case
+    if sizes == "many":
+        sizes = _many_small_groups(600, seed=97)
+    G, M = len(sizes), int(sum(sizes))
+    x = wl.activations(M, K, seed=98)
+    w = wl.normal_bf16((G * N, K), std=0.02, seed=99)
+    off = _offsets(sizes)
+    qa, sa, _, _ = pqm.quantize_mxfp8(dev_bf16(x), colwise=False)
+    qb, sb, _, _ = pqm.quantize_mxfp8(dev_bf16(w), colwise=False)
+    print(f"[gemm] mxfp8 persistent G={G} M={M} N={N} K={K}", flush=True)
+    y16 = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, qb, dev(off), N, K,
+                               a_scale=sa, b_scale=sb, out_dtype=pqm.OUT_BF16)
+    y32 = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_FPROP, qa, qb, dev(off), N, K,
+                               a_scale=sa, b_scale=sb, out_dtype=pqm.OUT_FP32)
+    torch.cuda.synchronize()
+    got = host_u16(y16)
+    assert_bytes_equal(got, _rne_bf16_bits(host(y32)), "bf16 vs RNE(binary32)")
+    ra, rsa = oracle.quantize_mxfp8_rowwise(x)
+    rb, rsb = oracle.quantize_mxfp8_rowwise(w)
+    want = oracle.grouped_gemm(oracle.decode_mxfp8(ra, rsa),
+                               oracle.decode_mxfp8(rb, rsb).reshape(G, N, K), off)
+    r = rel_l2_rows(oracle.bf16_to_f64(got), want)
+    print(f"[gemm] mxfp8 persistent: max row rel-L2 {r.max():.3e}", flush=True)
     assert r.max() <= TOL + 2.0 ** -9, (float(r.max()), int(r.argmax()))
 
 
