@@ -4235,6 +4235,13 @@ hipError_t launch_grouped_gemm(int fmt, int kind, const void *a, const uint8_t *
       return hipErrorNotSupported;
     const uint8_t *A = static_cast<const uint8_t *>(a), *B = static_cast<const uint8_t *>(b);
     const int64_t ntn_b = cdiv(N, Mq<256>::TN);
+    if (256 * K < U32 && qp_fits(G, M, N, K, out_fp32 ? 4 : 2)) {
+      // the persistent forward kernel with B's row stride G K and expert stride K
+      const uint32_t ob = (uint32_t)(M * N * (out_fp32 ? 4 : 2));
+      PQM_FB(k_gemm_mxfp8_qp, dim3((unsigned)qp_grid(G, M, N)), dim3(512), A, a_scale, B, b_scale,
+             offsets, G, N, K, ntn_b, G * K, K, out, ob, nullptr);
+      return hipGetLastError();
+    }
     const dim3 grid_b((unsigned)(cdiv((cdiv(M, 256) + G) * ntn_b, 8) * 8));
     if (out_fp32)
       hipLaunchKernelGGL((k_gemm_mxfp8_q<true, false>), grid_b, dim3(512), 0, st, A, a_scale, B,
