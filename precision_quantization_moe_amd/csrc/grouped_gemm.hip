@@ -907,12 +907,20 @@ struct MqFrags {
   int sa[Mq<TM>::FI], sb[Mq<TM>::FJ];
 };
 
+// The ring's 16-byte chunk swizzle: logical chunk c of LDS row r sits at
+// physical chunk c ^ mq_swz(r).  A fragment read (16 bytes per lane) serves
+// 16 lanes, i.e. 16 consecutive rows, per LDS cycle, and two 128-byte rows
+// share one 256-byte row of banks, so the key is taken from r / 2: the 16
+// rows of a read then reach 16 distinct bank groups (r % 8 as the key left
+// rows r and r + 8 on the same banks, a 2-way conflict on every read).
+__device__ __forceinline__ int mq_swz(int r) { return (r >> 1) & 7; }
+
 // Per-lane LDS offsets: first A / B row's chunks h and 2 + h of K-half 0
 // (K-half t adds 64 bytes before the swizzle: chunk 4 t + x), fragments 32
 // rows (4096 bytes) apart; scale bytes of the first A / B row, block h.
 struct MqLane {
   int a0, a1, b0, b1;  // chunk byte offsets for half 0
-  int x;               // row % 8 (the swizzle; the same for every fragment row)
+  int x;               // mq_swz(row) (the same for every fragment row of the lane)
   int sa, sb;          // scale byte offsets (half 0)
 };
 
@@ -1039,16 +1047,16 @@ __device__ __forceinline__ void mq_tile(const uint8_t *__restrict__ A,
   L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
   L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + C::DATA + (uint32_t)wave * 256u);
   // load q, lane tid: row 64 q + tid / 8 of the operand, physical chunk
-  // tid % 8 holding logical chunk (tid % 8) ^ (row % 8); rows past the
+  // tid % 8 holding logical chunk (tid % 8) ^ mq_swz(row); rows past the
   // expert's end or past N load a clamped valid row
 #pragma unroll
   for (int q = 0; q < C::CA; ++q) {
-    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
+    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ mq_swz(r);
     L.oa[q] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * c;
   }
 #pragma unroll
   for (int q = 0; q < C::CB; ++q) {
-    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
+    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ mq_swz(r);
     L.ob[q] = (uint32_t)min(r, rows_b - 1) * (uint32_t)ldb + 16u * c;
   }
   // scale word of lane tid: tile row tid (A rows first; lanes past the
@@ -1061,7 +1069,7 @@ __device__ __forceinline__ void mq_tile(const uint8_t *__restrict__ A,
   MqLane o;
   {
     const int ra = wm * (TM / 2) + r32, rb = wn * 64 + r32;
-    o.x = r32 & 7;
+    o.x = mq_swz(r32);
     o.a0 = ra * 128 + ((h ^ o.x) * 16);
     o.a1 = ra * 128 + (((2 + h) ^ o.x) * 16);
     o.b0 = TM * 128 + rb * 128 + ((h ^ o.x) * 16);
@@ -1340,12 +1348,12 @@ __device__ __forceinline__ void qp_loader(MqSrc<256> &L, const QpTile &t,
   L.Bb = uniform_ptr(B + t.g * bexp + (EPI ? 0 : t.n0 * ldb));
 #pragma unroll
   for (int q = 0; q < C::CA; ++q) {
-    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
+    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ mq_swz(r);
     L.oa[q] = (uint32_t)min(r, rows_a - 1) * Ku + 16u * c;
   }
 #pragma unroll
   for (int q = 0; q < C::CB; ++q) {
-    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ (r & 7);
+    const int r = 64 * q + (tid >> 3), c = (tid & 7) ^ mq_swz(r);
     const int64_t wr = EPI ? qp_swiglu_w_row(r, tn, N / 2) : (int64_t)min(r, rows_b - 1);
     L.ob[q] = (uint32_t)wr * (uint32_t)ldb + 16u * c;
   }
@@ -1490,7 +1498,7 @@ __device__ __forceinline__ void k_gemm_mxfp8_qp_body(
   MqLane o;
   {
     const int ra = wm * 128 + r32, rb = wn * 64 + r32;
-    o.x = r32 & 7;
+    o.x = mq_swz(r32);
     o.a0 = ra * 128 + ((h ^ o.x) * 16);
     o.a1 = ra * 128 + (((2 + h) ^ o.x) * 16);
     o.b0 = 256 * 128 + rb * 128 + ((h ^ o.x) * 16);
@@ -1845,14 +1853,15 @@ struct MwSrc {
 
 // Offsets of tile t: load q (0..3) of lane tid brings row 64 q + tid / 8 of
 // the A and of the B panel, physical chunk tid % 8 = logical chunk
-// (tid % 8) ^ (row % 8) (the ring's swizzle), so every load of a lane covers
+// (tid % 8) ^ mq_swz(row) = (tid % 8) ^ (tid / 16 % 8) (the ring's swizzle),
+// so every load of a lane covers
 // the same 16 tokens tc .. tc + 15 of a step.  Scale word op 0 brings word
 // tid % 2 of A row tid / 2, op 1 the same of B row tid / 2.
 __device__ __forceinline__ void mw_loader(MwSrc &L, const MwTile &t, int64_t M, int64_t N,
                                           int64_t K) {
   const int tid = threadIdx.x;
   const uint32_t Mu = (uint32_t)M, MS = (uint32_t)(M / 32);
-  const uint32_t c16 = 16u * (uint32_t)((tid & 7) ^ ((tid >> 3) & 7));
+  const uint32_t c16 = 16u * (uint32_t)((tid & 7) ^ ((tid >> 4) & 7));
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 64 * q + (tid >> 3);
@@ -1996,13 +2005,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mxfp8_wgrad_qp(
   L.rb = __builtin_amdgcn_make_buffer_rsrc((void *)Bt, (short)0, (int)(K * M), 0x00020000);
   L.rsa = __builtin_amdgcn_make_buffer_rsrc((void *)Ats, (short)0, (int)(N * (M / 32)), 0x00020000);
   L.rsb = __builtin_amdgcn_make_buffer_rsrc((void *)Bts, (short)0, (int)(K * (M / 32)), 0x00020000);
-  L.tc = 16u * (uint32_t)((tid & 7) ^ ((tid >> 3) & 7));
+  L.tc = 16u * (uint32_t)((tid & 7) ^ ((tid >> 4) & 7));
   L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
   L.sdst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + Mw::DATA + (uint32_t)wave * 256u);
   MqLane o;
   {
     const int ra = wm * 128 + r32, rb = wn * 64 + r32;
-    o.x = r32 & 7;
+    o.x = mq_swz(r32);
     o.a0 = ra * 128 + ((h ^ o.x) * 16);
     o.a1 = ra * 128 + (((2 + h) ^ o.x) * 16);
     o.b0 = 256 * 128 + rb * 128 + ((h ^ o.x) * 16);
