@@ -206,6 +206,38 @@ def test_mxfp8_dgrad(sizes, N, K):
     check_rows(host(y), want, f"mxfp8 dgrad {sizes} N={N} K={K}")
 
 
+@pytest.mark.parametrize("sizes,N,K", [
+    ([0, 37, 128, 1, 300, 513], 544, 768),    # ragged, a last column tile 32 wide, 6 steps
+    ("many", 256, 512),                       # 600 mostly tiny experts: many tiles per workgroup
+])
+def test_mxfp8_dgrad_bf16_out(sizes, N, K):
+    """The dgrad on the persistent kernel (B's row stride G K, expert stride
+    K) with bf16 output: bit for bit the nearest-even rounding of its binary32
+    output, and the oracle bar plus one bf16 rounding."""
+    if sizes == "many":
+        sizes = _many_small_groups(600, seed=23)
+    G, M = len(sizes), int(sum(sizes))
+    dy = wl.activations(M, K, seed=24)
+    w = wl.normal_bf16((G * K, N), std=0.02, seed=25)
+    off = _offsets(sizes)
+    qa, sa, _, _ = pqm.quantize_mxfp8(dev_bf16(dy), colwise=False)
+    _, _, qT, sT = pqm.quantize_mxfp8(dev_bf16(w), rowwise=False)
+    print(f"[gemm] mxfp8 dgrad bf16 G={G} M={M} N={N} K={K}", flush=True)
+    y16 = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_DGRAD, qa, qT, dev(off), N, K,
+                               a_scale=sa, b_scale=sT, out_dtype=pqm.OUT_BF16)
+    y32 = pqm.moe_grouped_gemm(pqm.FMT_MXFP8, pqm.GEMM_DGRAD, qa, qT, dev(off), N, K,
+                               a_scale=sa, b_scale=sT, out_dtype=pqm.OUT_FP32)
+    torch.cuda.synchronize()
+    got = host_u16(y16)
+    assert_bytes_equal(got, _rne_bf16_bits(host(y32)), "bf16 vs RNE(binary32)")
+    ra, rsa = oracle.quantize_mxfp8_rowwise(dy)
+    rT, rsT = oracle.quantize_mxfp8_colwise(w)
+    want = oracle.grouped_gemm(oracle.decode_mxfp8(ra, rsa), _colwise_b_groups(rT, rsT, G, K), off)
+    r = rel_l2_rows(oracle.bf16_to_f64(got), want)
+    print(f"[gemm] mxfp8 dgrad bf16: max row rel-L2 {r.max():.3e}", flush=True)
+    assert r.max() <= TOL + 2.0 ** -9, (float(r.max()), int(r.argmax()))
+
+
 def _padded(sizes, align=32):
     return [-(-s // align) * align for s in sizes]
 
