@@ -3636,16 +3636,19 @@ __device__ __forceinline__ void npw_tile(NpSrc<C> &L, const QpTile *tl, int t, i
     lgkm_wait0();
     wg_barrier();
     const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;
-    // the refill: stream step v, past the end the last step again (in
-    // bounds; read, never multiplied)
-    const int v = t * nk + k + C::NSLOT;
+    // the refill: stream step t nk + k + NSLOT, i.e. step vk of tile vt
+    // (nk >= NSLOT, so at most one tile ahead; counted, not divided, since a
+    // division by the run-time nk costs a few dozen instructions a step);
+    // past the end the last step again (in bounds; read, never multiplied)
+    const int kv = k + C::NSLOT;
+    const int vt = kv >= nk ? t + 1 : t, vk = kv >= nk ? kv - nk : kv;
     int rk = nk - 1;
-    if (v < S) {
-      rk = v % nk;
-      if (rk == 0) {  // the refills move on to tile v / nk, with its outer scales
-        const QpTile tn = tl[v / nk];
+    if (vt * nk + vk < S) {
+      rk = vk;
+      if (vk == 0) {  // the refills move on to tile vt, with its outer scales
+        const QpTile tn = tl[vt];
         np_loader<C>(L, A, As, B, Bs, N, K, tn.g, tn.row0, tn.row_end, tn.n0);
-        npw_alpha_issue(Ao, Bo, b_rps, N, tn, abase + (uint32_t)((v / nk) & 1) * (NPW_AL * 4));
+        npw_alpha_issue(Ao, Bo, b_rps, N, tn, abase + (uint32_t)(vt & 1) * (NPW_AL * 4));
       }
     }
     np_step<C>(L, rk, slot, lds, o, nslot, acc, R0, R1, W, S_, X, Y);
