@@ -463,30 +463,6 @@ __device__ __forceinline__ void mx3_read(const uint8_t *lds, int kt, int slot, c
   }
 }
 
-// The weight fragment is the instruction's first operand, the token
-// fragment its second, so each accumulator holds a transposed 32 x 32 tile:
-// lane l owns token row l % 32 and output columns 8 g + 4 (l / 32) + 0..3
-// (g = 0..3), four runs of 4 consecutive columns (see mx3_store).
-template <int TM>
-__device__ __forceinline__ void mx3_mma(const Mx3Frags<TM> &F,
-                                        v16f (&acc)[Mx3<TM>::FI][Mx3<TM>::FJ]) {
-#pragma unroll
-  for (int j = 0; j < Mx3<TM>::FJ; ++j)
-#pragma unroll
-    for (int i = 0; i < Mx3<TM>::FI; ++i)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0, 0,
-                                                                   0, F.sb[j], 0, F.sa[i]);
-}
-
-// Write one transposed accumulator (token rows row0 + rbase + 0..31, output
-// columns n0 + cbase + 0..31).  Lane l holds columns 8 g + 4 (l / 32) + 0..3
-// of its row.  binary32: one 16-byte store per run, so the two lanes of a
-// row fill a whole 32-byte sector per instruction.  bf16: the gfx950 lane
-// swap between lanes l and l + 32 trades run g = 1 (3) of the low half for
-// run 0 (2) of the high half, after which lane l holds columns
-// 16 p + 8 (l / 32) + 0..7, p = 0, 1: two 16-byte stores per lane.
-// bias: the expert's bias row (binary32, N columns) added to every value
-// before the output rounding, or null.
 // Lane (h, r) holds a and b; one swap of the upper half-wave's a with the
 // lower half-wave's b leaves lane (0, r) with lo = its a, hi = lane (1, r)'s
 // a, and lane (1, r) with lo = lane (0, r)'s b, hi = its b.  (Rows r of a
@@ -499,6 +475,19 @@ __device__ __forceinline__ void half_trade(float a, float b, float &lo, float &h
   hi = __uint_as_float(sw[1]);
 }
 
+// The weight fragment is the MFMA's first operand, the token fragment its
+// second, so each accumulator holds a transposed 32 x 32 tile: lane l owns
+// token row l % 32 and output columns 8 g + 4 (l / 32) + 0..3 (g = 0..3),
+// four runs of 4 consecutive columns.
+// Write one transposed accumulator (token rows row0 + rbase + 0..31, output
+// columns n0 + cbase + 0..31).  Lane l holds columns 8 g + 4 (l / 32) + 0..3
+// of its row.  binary32: one 16-byte store per run, so the two lanes of a
+// row fill a whole 32-byte sector per instruction.  bf16: the gfx950 lane
+// swap between lanes l and l + 32 trades run g = 1 (3) of the low half for
+// run 0 (2) of the high half, after which lane l holds columns
+// 16 p + 8 (l / 32) + 0..7, p = 0, 1: two 16-byte stores per lane.
+// bias: the expert's bias row (binary32, N columns) added to every value
+// before the output rounding, or null.
 template <bool OUT_F32>
 __device__ __forceinline__ void mx3_store(const v16f &acc, void *out, int64_t N, int64_t row0,
                                           int64_t row_end, int64_t n0, int rbase, int cbase,
@@ -2608,22 +2597,6 @@ __device__ __forceinline__ void bp_read(const uint8_t *lds, int slot, const int 
   const uint8_t *reg = lds + slot * Bp<TM>::SLOT;
   bp_read_op<Bp<TM>::FI, KIND == BP_WGRAD>(reg, offA, F.a);
   bp_read_op<Bp<TM>::FJ, KIND != BP_FPROP>(reg, offB, F.b);
-}
-
-// Weights (B) are the first operand, tokens (A) the second: transposed
-// accumulators as in the MXFP8 pipeline.
-template <int TM>
-__device__ __forceinline__ void bp_mma(const BpFrags<TM> &F,
-                                       v16f (&acc)[Bp<TM>::FI][Bp<TM>::FJ]) {
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int j = 0; j < Bp<TM>::FJ; ++j)
-#pragma unroll
-      for (int i = 0; i < Bp<TM>::FI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(v8bf, F.b[j][s]), __builtin_bit_cast(v8bf, F.a[i][s]), acc[i][j],
-            0, 0, 0);
 }
 
 // Step kt from `slot` (operands in `cur`): as mx3_step.
