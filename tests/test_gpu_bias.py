@@ -5,7 +5,7 @@ persistent, four-wave and register-staged kernels, the NVFP4 wide,
 pipelined and register-staged kernels, block FP8, the BF16 pipelined and
 register-staged kernels, and an empty contraction (the output is the bias).
 
-Bar: relative L2 <= 1e-3 per row on binary32 output (+ 2^-9 for bf16)."""
+Bar: relative L2 <= 1e-3 per row on binary32 output (+ 2^-8 for bf16)."""
 from __future__ import annotations
 
 import numpy as np
@@ -90,7 +90,7 @@ def test_forward_bias(fmt, sizes, N, K, path, out_dtype):
     torch.cuda.synchronize()
     want = oracle.grouped_gemm(A, B, off, bias=bias)
     r = _rel_rows(host(y.float()), want)
-    bar = TOL if out_dtype == pqm.OUT_FP32 else TOL + 2.0 ** -9
+    bar = TOL if out_dtype == pqm.OUT_FP32 else TOL + 2.0 ** -8
     print(f"[bias] max row rel-L2 {r.max():.3e}", flush=True)
     assert r.max() <= bar, (float(r.max()), int(r.argmax()))
 

@@ -2,8 +2,9 @@
 the same exactly-decoded operands.
 
 Bar: relative L2 <= 1e-3 on binary32 output, per row (a row whose oracle
-values overflow binary32 is excluded).  bf16 output adds one rounding of
-at most 2^-9 relative per element to that bar.
+values overflow binary32 is excluded).  bf16 output adds one nearest-even
+rounding to 8 significant bits, at most 2^-8 relative per element, to that
+bar.
 
 The oracle quantizes the operands itself from the same generated bf16 bytes
 (byte equality of the two quantizers is established separately)."""
@@ -87,14 +88,14 @@ def test_mxfp8_fprop_ragged(case):
 @pytest.mark.parametrize("N", [128, 100])
 def test_mxfp8_fprop_bf16_out(N):
     """bf16 output vs the binary64 product: the GEMM bar (1e-3) plus one
-    bf16 rounding of the output (at most 2^-9 relative per element).  N =
+    bf16 rounding of the output (at most 2^-8 relative per element).  N =
     100 (rows of 200 bytes, not whole 16-byte vectors) runs the
     non-persistent kernel."""
     y, want = _mxfp8_case([64, 0, 100, 300], N, 256, seed=4, out_dtype=pqm.OUT_BF16)
     got = oracle.bf16_to_f64(host_u16(y))
     r = rel_l2_rows(got, want)
     print(f"[gemm] mxfp8 bf16 out vs fp64: max row rel-L2 {r.max():.3e}", flush=True)
-    assert r.max() <= TOL + 2.0 ** -9
+    assert r.max() <= TOL + 2.0 ** -8
 
 
 def test_mxfp8_tiny_contract_expert_gemm():
@@ -173,7 +174,7 @@ def test_mxfp8_qwen3_down_full_sampled():
         r = rel_l2_rows(yh[rows], want)
         print(f"[gemm] qwen3 fc2 expert {e} ({hi - lo} rows): max row rel-L2 {r.max():.3e}",
               flush=True)
-        assert r.max() <= TOL + 2.0 ** -9, (e, float(r.max()))
+        assert r.max() <= TOL + 2.0 ** -8, (e, float(r.max()))
 
 
 # ------------------------------------------------- MXFP8 backward GEMMs
@@ -235,7 +236,7 @@ def test_mxfp8_dgrad_bf16_out(sizes, N, K):
     want = oracle.grouped_gemm(oracle.decode_mxfp8(ra, rsa), _colwise_b_groups(rT, rsT, G, K), off)
     r = rel_l2_rows(oracle.bf16_to_f64(got), want)
     print(f"[gemm] mxfp8 dgrad bf16: max row rel-L2 {r.max():.3e}", flush=True)
-    assert r.max() <= TOL + 2.0 ** -9, (float(r.max()), int(r.argmax()))
+    assert r.max() <= TOL + 2.0 ** -8, (float(r.max()), int(r.argmax()))
 
 
 def _padded(sizes, align=32):
@@ -330,7 +331,7 @@ def test_mxfp8_wgrad_bf16_out():
     for g in (0, 2):
         r = rel_l2_rows(oracle.bf16_to_f64(got[g]), want[g])
         print(f"[gemm] mxfp8 wgrad bf16 out group {g}: max row rel-L2 {r.max():.3e}", flush=True)
-        assert r.max() <= TOL + 2.0 ** -9
+        assert r.max() <= TOL + 2.0 ** -8
     assert not got[1].any()
 
 
@@ -367,7 +368,7 @@ def test_fp8_block_fprop(sizes, N, K):
 def test_fp8_block_fprop_bf16_out_and_contract_tensor():
     y, want = _fp8b_case([64, 0, 100], 256, 256, seed=62, out_dtype=pqm.OUT_BF16)
     r = rel_l2_rows(oracle.bf16_to_f64(host_u16(y)), want)
-    assert r.max() <= TOL + 2.0 ** -9
+    assert r.max() <= TOL + 2.0 ** -8
     x = wl.tiny_contract_tensor()
     w = wl.normal_bf16((256, 256), std=0.02, seed=63)
     off = np.array([0, 128], np.int64)
@@ -451,7 +452,7 @@ def test_bf16_dgrad(sizes, N, K):
 
 
 def test_bf16_dgrad_bf16_out():
-    """bf16 output: the GEMM bar plus one bf16 rounding (2^-9 relative)."""
+    """bf16 output: the GEMM bar plus one bf16 rounding (2^-8 relative)."""
     sizes, N, K = [300, 0, 129, 64], 264, 192
     G, M = len(sizes), sum(sizes)
     dy = wl.normal_bf16((M, K), seed=13)
@@ -465,7 +466,7 @@ def test_bf16_dgrad_bf16_out():
     want = oracle.grouped_gemm(oracle.bf16_to_f64(dy), wt, off)
     r = rel_l2_rows(oracle.bf16_to_f64(host_u16(y)), want)
     print(f"[gemm] bf16 dgrad bf16 out: max row rel-L2 {r.max():.3e}", flush=True)
-    assert r.max() <= TOL + 2.0 ** -9
+    assert r.max() <= TOL + 2.0 ** -8
 
 
 @pytest.mark.parametrize("sizes,N,K", [([0, 37, 128, 1, 300], 192, 320), ([700], 64, 136),
@@ -665,7 +666,7 @@ def test_nvfp4_persistent_bf16(case):
                                oracle.decode_nvfp4(rb, rsb, rgb, N).reshape(G, N, K), off)
     r = rel_l2_rows(oracle.bf16_to_f64(got), want)
     print(f"[gemm] nvfp4 persistent: max row rel-L2 {r.max():.3e}", flush=True)
-    assert r.max() <= TOL + 2.0 ** -9, (float(r.max()), int(r.argmax()))
+    assert r.max() <= TOL + 2.0 ** -8, (float(r.max()), int(r.argmax()))
 
 
 @pytest.mark.parametrize("case", [
@@ -703,7 +704,7 @@ def test_mxfp8_persistent_bf16(case):
                                oracle.decode_mxfp8(rb, rsb).reshape(G, N, K), off)
     r = rel_l2_rows(oracle.bf16_to_f64(got), want)
     print(f"[gemm] mxfp8 persistent: max row rel-L2 {r.max():.3e}", flush=True)
-    assert r.max() <= TOL + 2.0 ** -9, (float(r.max()), int(r.argmax()))
+    assert r.max() <= TOL + 2.0 ** -8, (float(r.max()), int(r.argmax()))
 
 
 # ------------------------------------------------- degenerate and large-G
@@ -860,7 +861,7 @@ def test_nvfp4_deepseek_down_full_sampled():
         r = rel_l2_rows(yh[rows], want)
         print(f"[gemm] deepseek fc2 expert {e} ({hi - lo} rows): max row rel-L2 {r.max():.3e}",
               flush=True)
-        assert r.max() <= TOL + 2.0 ** -9, (e, float(r.max()))
+        assert r.max() <= TOL + 2.0 ** -8, (e, float(r.max()))
     del w, qb
 
 
@@ -910,7 +911,7 @@ def test_bf16_backward_qwen3_full_sampled(proj):
         r = rel_l2_rows(oracle.bf16_to_f64(host_u16(dx[ri])), want)
         print(f"[gemm] qwen3 {proj} bf16 dgrad expert {e} ({hi - lo} rows): "
               f"max row rel-L2 {r.max():.3e}", flush=True)
-        assert r.max() <= TOL + 2.0 ** -9, (e, float(r.max()))
+        assert r.max() <= TOL + 2.0 ** -8, (e, float(r.max()))
         outs = np.unique(np.concatenate([[0, Kd - 1], rng.integers(0, Kd, 6)]))
         dyg = oracle.bf16_to_f64(host_u16(dy[lo:hi]))
         xg = oracle.bf16_to_f64(host_u16(xs[lo:hi]))

@@ -8,7 +8,7 @@ Bars:
     exact);
   * Y: relative L2 <= 1e-3 per row on binary32 output against the oracle's
     binary64 loop (the kernel accumulates in binary32 and moves the
-    accumulator by a binary32 gs_prev / gs), plus one bf16 rounding (2^-9)
+    accumulator by a binary32 gs_prev / gs), plus one bf16 rounding (2^-8)
     for bf16 output.
 
 W2 is quantized with one outer scale per expert tensor (or per scope of
@@ -126,7 +126,7 @@ def test_online_fc2_bf16_out_and_deterministic():
     got_y, _, want_y, _ = _case(sizes, N, K, seed=41, out_dtype=pqm.OUT_BF16)
     r = _rel_rows(got_y, want_y)
     print(f"[online] bf16 out: max row rel-L2 {r.max():.3e}", flush=True)
-    assert r.max() <= TOL + 2.0 ** -9
+    assert r.max() <= TOL + 2.0 ** -8
     rng = np.random.Generator(np.random.PCG64(42))
     p = dev_bf16(_p_rows(rng, sum(sizes), K))
     w = wl.normal_bf16((2 * N, K), std=0.02, seed=43)
@@ -197,5 +197,5 @@ def test_online_fc2_deepseek_down_full_sampled():
         r = _rel_rows(oracle.bf16_to_f64(host_u16(y[rows])), want)
         print(f"[online] deepseek fc2 expert {e} ({hi - lo} rows): max row rel-L2 {r.max():.3e}",
               flush=True)
-        assert r.max() <= TOL + 2.0 ** -9, (e, float(r.max()))
+        assert r.max() <= TOL + 2.0 ** -8, (e, float(r.max()))
     del w, qw, c
