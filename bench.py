@@ -35,8 +35,8 @@ seeded input, with all inputs resident in HBM:
   ds_fc2_online     ds_fwd's down projection with online amax compensation:
                     the weighted SwiGLU output (bf16, made once from the
                     layer's gate_up output) encoded tile by tile under each
-                    row's running maximum inside the FC2 kernel, the
-                    accumulator moved to each new outer scale
+                    row's running maximum (one pass over the rows), then the
+                    FC2 GEMM moving its accumulator to each new outer scale
   ds_reconstruct    bf16 reconstruction of the forward operands (activations
                     and all 257 experts' weights) for the dequantized backward
 
@@ -325,8 +325,8 @@ def main():
         o, (w1q, w1b, w1g, w2q, w2b, w2g) = st["ds"], st["dsw"]
         if "p5" not in st:  # made during the warmup steps: the FC2 input, bf16
             st["p5"] = pqm.swiglu_prob(o["c"], st["prob5"], o["src"])
-        st["ds_online"] = pqm.moe_fc2_online_nvfp4(st["p5"], w2q, w2b, w2g, o["off"], H5,
-                                                   w_rows_per_scale=H5)
+        st["ds_online"] = pqm.moe_fc2_online_nvfp4_split(st["p5"], w2q, w2b, w2g, o["off"], H5,
+                                                         w_rows_per_scale=H5)
 
     def r_ds_reconstruct(s):
         o, (w1q, w1b, w1g, w2q, w2b, w2g) = st["ds"], st["dsw"]

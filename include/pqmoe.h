@@ -323,6 +323,36 @@ pqm_status pqm_moe_fc2_online_nvfp4(const uint16_t *p, const uint8_t *w_q,
                                     uint8_t *q_out, uint8_t *sb_out, hipStream_t stream);
 
 /*
+ * The same online-amax FC2 ([MT] 5.6) in two passes.  A row's encoding
+ * depends on its K-tiles only, not on the output column, so the first pass
+ * encodes every routed row once.  The second pass is the NVFP4 grouped GEMM
+ * on those codes, which moves its accumulator rows by the stored ratios
+ * before each K-tile.  The codes, block scales and gs are those of
+ * pqm_moe_fc2_online_nvfp4, and so is Y bit for bit: the same accumulation
+ * order and the same epilogue.  The single-pass entry point encodes P again
+ * in every 256-column tile.
+ *   p, w_q, w_scale, w_outer, offsets, out, out_dtype: as
+ *            pqm_moe_fc2_online_nvfp4;
+ *   gs_out   binary32 [M_total], each row's final gs (written);
+ *   q_out, sb_out [M_total, K/2] and [M_total, K/16], the codes and block
+ *            scales P was encoded with (written, then read by the GEMM);
+ *   ratio_out binary32 [M_total, K/128], each tile's gs_prev / gs (1 when
+ *            the row's maximum did not grow; written, then read).
+ * Rows 0 .. offsets[G]-1 of every output are written.  All four buffers
+ * are required (PQM_ERR_NULL).  K is a positive multiple of 256 and at most
+ * 4096 (PQM_ERR_SHAPE).  p, w_q, out and q_out must be 16-byte aligned,
+ * offsets 8-byte, and w_scale, sb_out, gs_out and ratio_out 4-byte
+ * (PQM_ERR_ALIGN).  The caller owns every buffer; nothing is allocated.
+ */
+pqm_status pqm_moe_fc2_online_nvfp4_split(const uint16_t *p, const uint8_t *w_q,
+                                          const uint8_t *w_scale, const float *w_outer,
+                                          int64_t w_rows_per_scale, const int64_t *offsets,
+                                          int64_t G, int64_t M_total, int64_t N, int64_t K,
+                                          void *out, pqm_dtype out_dtype, float *gs_out,
+                                          uint8_t *q_out, uint8_t *sb_out, float *ratio_out,
+                                          hipStream_t stream);
+
+/*
  * The MXFP8 gate_up grouped GEMM with its activation fused into the
  * epilogue ([MT] 5.3-5.4: D = act(gate, up) x prob is produced where C is,
  * and quantized for the down GEMM without another pass; C is not written):

@@ -12,7 +12,7 @@ from __future__ import annotations
 from ._binding import (  # noqa: F401
     FMT_BF16, FMT_FP8_BLOCK, FMT_MXFP8, FMT_NVFP4, GEMM_DGRAD, GEMM_FPROP, GEMM_WGRAD,
     OUT_BF16, OUT_FP32, PqmError, dequantize, lib, moe_combine, moe_gather_rows, moe_pad_rows,
-    moe_fc2_online_nvfp4, moe_gemm_swiglu_quantize_mxfp8, moe_grouped_gemm, moe_route, moe_route_noalloc, pad_rows_bound, quantize_fp8_block,
+    moe_fc2_online_nvfp4, moe_fc2_online_nvfp4_split, moe_gemm_swiglu_quantize_mxfp8, moe_grouped_gemm, moe_route, moe_route_noalloc, pad_rows_bound, quantize_fp8_block,
     quantize_mxfp8,
     quantize_nvfp4_per_token, swiglu_prob, swiglu_prob_quantize_mxfp8, swiglu_prob_quantize_nvfp4,
     validate_offsets, OFFSETS_FIRST_NOT_ZERO, OFFSETS_DECREASING, OFFSETS_MISALIGNED,

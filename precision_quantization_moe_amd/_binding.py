@@ -41,6 +41,8 @@ SIGNATURES = {
     "pqm_moe_grouped_gemm_workspace_size": ([I32, I32], SZ),
     "pqm_moe_fc2_online_nvfp4": ([P, P, P, P, I64, P, I64, I64, I64, I64, P, I32, P, P, P, P],
                                  I32),
+    "pqm_moe_fc2_online_nvfp4_split": ([P, P, P, P, I64, P, I64, I64, I64, I64, P, I32, P, P, P,
+                                        P, P], I32),
     "pqm_moe_gemm_swiglu_quantize_mxfp8": ([P, P, P, P, P, I64, I64, I64, I64, P, P, P, P, P],
                                            I32),
     "pqm_moe_route": ([P, I64, I64, I64, I32, P, P, P, P, P, SZ, P], I32),
@@ -226,6 +228,30 @@ def moe_fc2_online_nvfp4(p: torch.Tensor, w_q, w_scale, w_outer, offsets: torch.
                                           _stream(dev)),
            "pqm_moe_fc2_online_nvfp4")
     return (y, gs, q, sb) if encodings else (y, gs)
+
+
+def moe_fc2_online_nvfp4_split(p: torch.Tensor, w_q, w_scale, w_outer, offsets: torch.Tensor,
+                               N: int, w_rows_per_scale: int = 0, out_dtype: int = OUT_BF16,
+                               encodings: bool = False):
+    """The same FC2 in two passes (encode once, then the GEMM with the
+    stored ratios); see pqm_moe_fc2_online_nvfp4_split in pqmoe.h.  The
+    codes, block scales, gs and ratio buffers it needs are allocated here.
+    Returns (y, gs) or, with encodings, (y, gs, q, sb, ratio)."""
+    G = offsets.numel() - 1
+    M, K = p.shape
+    dev = p.device
+    odt = torch.float32 if out_dtype == OUT_FP32 else torch.bfloat16
+    y = torch.empty((M, N), dtype=odt, device=dev)
+    gs = torch.empty((M,), dtype=torch.float32, device=dev)
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sb = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    ratio = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    _check(lib().pqm_moe_fc2_online_nvfp4_split(_ptr(p), _ptr(w_q), _ptr(w_scale), _ptr(w_outer),
+                                                w_rows_per_scale or N, _ptr(offsets), G, M, N, K,
+                                                _ptr(y), out_dtype, _ptr(gs), _ptr(q), _ptr(sb),
+                                                _ptr(ratio), _stream(dev)),
+           "pqm_moe_fc2_online_nvfp4_split")
+    return (y, gs, q, sb, ratio) if encodings else (y, gs)
 
 
 # ---------------------------------------------------------------- MoE glue

@@ -222,6 +222,30 @@ pqm_status pqm_moe_fc2_online_nvfp4(const uint16_t *p, const uint8_t *w_q,
                                                stream));
 }
 
+pqm_status pqm_moe_fc2_online_nvfp4_split(const uint16_t *p, const uint8_t *w_q,
+                                          const uint8_t *w_scale, const float *w_outer,
+                                          int64_t w_rows_per_scale, const int64_t *offsets,
+                                          int64_t G, int64_t M_total, int64_t N, int64_t K,
+                                          void *out, pqm_dtype out_dtype, float *gs_out,
+                                          uint8_t *q_out, uint8_t *sb_out, float *ratio_out,
+                                          hipStream_t stream) {
+  if (out_dtype != PQM_OUT_BF16 && out_dtype != PQM_OUT_FP32) return PQM_ERR_ENUM;
+  if (G < 0 || M_total < 0 || N < 0 || K <= 0 || K % 256 || K > 4096) return PQM_ERR_SHAPE;
+  if (w_rows_per_scale < 1 || (G * N) % w_rows_per_scale) return PQM_ERR_SHAPE;
+  if (G == 0 || M_total == 0 || N == 0) return PQM_OK;
+  if (!p || !w_q || !w_scale || !w_outer || !offsets || !out || !gs_out || !q_out || !sb_out ||
+      !ratio_out)
+    return PQM_ERR_NULL;
+  if (!aligned(p, 16) || !aligned(w_q, 16) || !aligned(out, 16) || !aligned(q_out, 16) ||
+      !aligned(offsets, 8) || !aligned(w_scale, 4) || !aligned(sb_out, 4) ||
+      !aligned(gs_out, 4) || !aligned(ratio_out, 4))
+    return PQM_ERR_ALIGN;
+  return from_hip(pqm::launch_fc2_online_nvfp4_split(p, w_q, w_scale, w_outer, w_rows_per_scale,
+                                                     offsets, G, M_total, N, K, out,
+                                                     out_dtype == PQM_OUT_FP32, gs_out, q_out,
+                                                     sb_out, ratio_out, stream));
+}
+
 pqm_status pqm_moe_gemm_swiglu_quantize_mxfp8(const uint8_t *a, const uint8_t *a_scale,
                                               const uint8_t *b, const uint8_t *b_scale,
                                               const int64_t *offsets, int64_t G, int64_t M_total,

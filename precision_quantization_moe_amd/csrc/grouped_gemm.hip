@@ -3311,6 +3311,15 @@ __device__ __forceinline__ void np_store(const v16f &acc, void *out, int64_t N, 
   }
 }
 
+template <class C>
+__device__ __forceinline__ void npo_rescale(const float *ratio, int wm, int r32,
+                                            v16f (&acc)[C::FI][C::FJ]);
+
+// One tile of the NVFP4 grouped GEMM.  With a ratio array (binary32
+// [rows, K / 128], row-major from the tile's first row), each step first
+// moves the accumulator rows by their ratio for that step, as the online-amax
+// FC2 does (O = O (gs_prev / gs) + dO); rl: LDS for the tile's ratios,
+// stored step-major (C::TMR per step).
 template <bool OUT_F32, class C>
 __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
                                         const uint8_t *__restrict__ As,
@@ -3318,11 +3327,21 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
                                         const uint8_t *__restrict__ B,
                                         const uint8_t *__restrict__ Bs, int64_t N, int64_t K,
                                         const TileInfo &ti, uint8_t *lds, const float *ab,
-                                        void *__restrict__ out, const float *bias) {
+                                        void *__restrict__ out, const float *bias,
+                                        const float *__restrict__ ratio = nullptr,
+                                        float *rl = nullptr) {
   constexpr int FI = C::FI, FJ = C::FJ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = C::WM == 2 ? wave >> 1 : 0, wn = C::WM == 2 ? wave & 1 : wave;
   const int h = lane >> 5, r32 = lane & 31;
+  if (ratio) {  // before any ring load, so that the ring's load counts stay as they are
+    const int nk = (int)(K / 128), rows = (int)min(ti.row_end - ti.row0, (int64_t)C::TMR);
+    for (int i = tid; i < nk * C::TMR; i += 256) {
+      const int kt = i / C::TMR, r = min(i % C::TMR, rows - 1);
+      rl[i] = ratio[(ti.row0 + r) * nk + kt];
+    }
+    __syncthreads();
+  }
   NpSrc<C> L;
   np_loader<C>(L, A, As, B, Bs, N, K, ti.g, ti.row0, ti.row_end, ti.n0);
   L.dst = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)wave * 1024u);
@@ -3369,6 +3388,7 @@ __device__ __forceinline__ void np_tile(const uint8_t *__restrict__ A,
     lgkm_wait0();
     __builtin_amdgcn_s_barrier();
     const int nslot = slot == C::NSLOT - 1 ? 0 : slot + 1;
+    if (ratio) npo_rescale<C>(rl + kt * C::TMR, wm, r32, acc);
     // past the last step the reads take the slot's repeated last step (in
     // bounds; decoded, never multiplied)
     np_step<C>(L, min(kt + C::NSLOT, nk - 1), slot, lds, o, nslot, acc, R0, R1, W, S, X, Y);
@@ -4030,6 +4050,84 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_online(
   if (gs_out && ti.n0 == 0 && tid < rows_a) gs_out[ti.row0 + tid] = gsf[tid];
 }
 
+// The same FC2 in two passes: the encoding of P does not depend on the
+// output column, so one pass encodes every routed row once (the running
+// maximum, gs, E4M3 block scales and E2M1 codes of each 128-wide K-tile, as
+// npo_encode computes them, and each tile's gs_prev / gs), and the GEMM then
+// reads the codes like any NVFP4 operand and moves its accumulator rows by
+// the stored ratios before each step.  The accumulation and the epilogue
+// (the final gs as the row's outer scale) are those of the one-pass kernel,
+// whose column tiles each encode P again.
+constexpr int NPO_MAX_NK = 32;  // K / 128 ratios of a tile row held in LDS
+
+// Encode pass: 8 lanes per row, lane b taking the 1x16 block b of every
+// 128-wide tile, in K order.  q [rows, K/2], sb [rows, K/16], gs [rows],
+// ratio [rows, K/128] for the rows 0 .. offsets[G]-1.
+__global__ __launch_bounds__(256) void k_online_encode_nvfp4(
+    const uint16_t *__restrict__ P, const int64_t *__restrict__ offsets, int64_t G, int64_t K,
+    uint8_t *__restrict__ q, uint8_t *__restrict__ sb, float *__restrict__ gs,
+    float *__restrict__ ratio) {
+  const int64_t rows = offsets[G];
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  if ((int64_t)blockIdx.x * 32 >= rows) return;  // whole workgroup: no lane of it has a row
+  const int blk = threadIdx.x & 7;
+  const bool ok = row < rows;
+  const uint16_t *pr = P + min(row, rows - 1) * K + 16 * blk;
+  const int nk = (int)(K / 128);
+  uint32_t gam = 0;
+  Nvfp4Row rc = nvfp4_row(0.0f);  // s_g = 0 while the maximum is zero
+  for (int t = 0; t < nk; ++t) {
+    const uint4 v0 = *reinterpret_cast<const uint4 *>(pr + 128 * t);
+    const uint4 v1 = *reinterpret_cast<const uint4 *>(pr + 128 * t + 8);
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t mm = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mm = pk_max_u16(mm, w[k] & 0x7FFF7FFFu);
+    const uint32_t m = max8_lanes(max(mm & 0xFFFFu, mm >> 16));
+    float rt = 1.0f;
+    if (m > gam) {
+      gam = m;
+      const Nvfp4Row n = nvfp4_row(__uint_as_float(m << 16));
+      rt = __fdiv_rn(rc.s_g, n.s_g);
+      rc = n;
+    }
+    uint32_t sbc;
+    const uint2 packed = nvfp4_block(w, rc, &sbc);
+    if (ok) {
+      *reinterpret_cast<uint2 *>(q + row * (K / 2) + 64 * t + 8 * blk) = packed;
+      sb[row * (K / 16) + 8 * t + blk] = (uint8_t)sbc;
+      if (blk == 0) ratio[row * nk + t] = rt;
+    }
+  }
+  if (ok && blk == 0) gs[row] = rc.s_g;
+}
+
+// GEMM pass: the pipelined NVFP4 kernel's 128 x 256 tiles (2 x 2 waves,
+// the one-pass kernel's shape) with the per-step rescale; A = the encode
+// pass's codes and block scales, its outer scale the final gs.  (256-row
+// tiles keep 256 accumulators per lane, which the rescale's multiplies
+// would have to move through VGPRs: 272 spilled registers.)
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_rescale(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As,
+    const float *__restrict__ Ao, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, const float *__restrict__ Bo, int64_t b_rps,
+    const int64_t *__restrict__ offsets, int64_t G, int64_t N, int64_t K, int64_t ntn,
+    void *__restrict__ out, const float *__restrict__ ratio) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NpPipe128::LDS];
+  __shared__ float rl[NPO_MAX_NK * 128];
+  __shared__ float ab[256];
+  __shared__ int64_t sh[4];
+  TileInfo ti;
+  if (!lookup_row_tile<256, 128>(offsets, G, ntn, ti, sh)) return;
+  {
+    const int64_t col = ti.n0 + threadIdx.x;
+    ab[threadIdx.x] = col < N ? Bo[(ti.g * N + col) / b_rps] : 0.0f;
+  }
+  __syncthreads();
+  np_tile<OUT_F32, NpPipe128>(A, As, Ao, B, Bs, N, K, ti, lds, ab, out, nullptr, ratio, rl);
+}
+
 // ------------------------------------------------------------------ launch
 
 // K = 0: the product over an empty contraction is zero, so rows 0 ..
@@ -4419,6 +4517,31 @@ hipError_t launch_fc2_online_nvfp4(const uint16_t *p, const uint8_t *b, const ui
     hipLaunchKernelGGL(k_gemm_nvfp4_online<false>, grid, dim3(256), 0, st, p, b, b_scale,
                        b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out, gs_out, q_out,
                        sb_out);
+  return hipGetLastError();
+}
+
+// Online-amax FC2 in two passes (k_online_encode_nvfp4, then
+// k_gemm_nvfp4_rescale): K a positive multiple of 256 and at most
+// 128 NPO_MAX_NK, 4-byte aligned W2 block scales.
+hipError_t launch_fc2_online_nvfp4_split(const uint16_t *p, const uint8_t *b,
+                                         const uint8_t *b_scale, const float *b_outer,
+                                         int64_t b_rows_per_scale, const int64_t *offsets,
+                                         int64_t G, int64_t M, int64_t N, int64_t K, void *out,
+                                         int out_fp32, float *gs, uint8_t *q, uint8_t *sb,
+                                         float *ratio, hipStream_t st) {
+  if (G == 0 || M == 0 || N == 0) return hipSuccess;
+  if (K <= 0 || K % 256 || K / 128 > NPO_MAX_NK || (uintptr_t)b_scale % 4)
+    return hipErrorNotSupported;
+  hipLaunchKernelGGL(k_online_encode_nvfp4, dim3((unsigned)cdiv(M, 32)), dim3(256), 0, st, p,
+                     offsets, G, K, q, sb, gs, ratio);
+  const int64_t ntn = cdiv(N, NpPipe128::TN);
+  const dim3 grid((unsigned)(cdiv((cdiv(M, 128) + G) * ntn, 8) * 8));
+  if (out_fp32)
+    hipLaunchKernelGGL(k_gemm_nvfp4_rescale<true>, grid, dim3(256), 0, st, q, sb, gs, b, b_scale,
+                       b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out, ratio);
+  else
+    hipLaunchKernelGGL(k_gemm_nvfp4_rescale<false>, grid, dim3(256), 0, st, q, sb, gs, b,
+                       b_scale, b_outer, b_rows_per_scale, offsets, G, N, K, ntn, out, ratio);
   return hipGetLastError();
 }
 

@@ -59,6 +59,12 @@ hipError_t launch_fc2_online_nvfp4(const uint16_t *p, const uint8_t *b, const ui
                                    const int64_t *offsets, int64_t G, int64_t M, int64_t N,
                                    int64_t K, void *out, int out_fp32, float *gs_out,
                                    uint8_t *q_out, uint8_t *sb_out, hipStream_t st);
+hipError_t launch_fc2_online_nvfp4_split(const uint16_t *p, const uint8_t *b,
+                                         const uint8_t *b_scale, const float *b_outer,
+                                         int64_t b_rows_per_scale, const int64_t *offsets,
+                                         int64_t G, int64_t M, int64_t N, int64_t K, void *out,
+                                         int out_fp32, float *gs, uint8_t *q, uint8_t *sb,
+                                         float *ratio, hipStream_t st);
 hipError_t launch_validate_offsets(const int64_t *off, int64_t G, int64_t M_total, int64_t align,
                                    int32_t *result, hipStream_t st);
 

@@ -1,6 +1,7 @@
 """GPU parity of the online-amax NVFP4 down projection
-(pqm_moe_fc2_online_nvfp4, [MT] "miniTE technical report", 5.6) against the
-oracle's loop (oracle.online_amax_fc2, 128-wide K-tiles).
+(pqm_moe_fc2_online_nvfp4 and its two-pass form
+pqm_moe_fc2_online_nvfp4_split, [MT] "miniTE technical report", 5.6) against
+the oracle's loop (oracle.online_amax_fc2, 128-wide K-tiles).
 
 Bars:
   * the codes and block scales P was encoded with, tile by tile, and each
@@ -9,7 +10,10 @@ Bars:
   * Y: relative L2 <= 1e-3 per row on binary32 output against the oracle's
     binary64 loop (the kernel accumulates in binary32 and moves the
     accumulator by a binary32 gs_prev / gs), plus one bf16 rounding (2^-8)
-    for bf16 output.
+    for bf16 output;
+  * two-pass form: each tile's stored gs_prev / gs bit-exact against one
+    binary32 division of the oracle's per-tile gs, and Y, gs, codes and
+    block scales bit for bit those of the one-pass kernel.
 
 W2 is quantized with one outer scale per expert tensor (or per scope of
 w_rows_per_scale rows) by the library's per-token quantizer on the device and
@@ -60,10 +64,20 @@ def _p_rows(rng, R, I):
     return bits
 
 
-def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32, rps=None):
+def _want_ratio(gs_rec):
+    """Each tile's gs_prev / gs from the oracle's per-tile gs (0 while the
+    row's maximum is zero): one binary32 division, 1 for a skipped tile."""
+    prev = np.concatenate([np.zeros((gs_rec.shape[0], 1), np.float32), gs_rec[:, :-1]], axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = prev / gs_rec
+    return np.where(gs_rec > 0, q, np.float32(1.0)).astype(np.float32)
+
+
+def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32, rps=None, split=False):
     """rps: W2 rows per outer scale (default N, one per expert); with rps < N
     the oracle's loop (one W2 scale) runs once per scale scope of W2 rows,
-    whose output columns it then fills."""
+    whose output columns it then fills.  split: the two-pass entry point
+    (encode once, then the GEMM with the stored ratios)."""
     rps = rps or N
     rng = np.random.Generator(np.random.PCG64(seed))
     G, M = len(sizes), int(sum(sizes))
@@ -71,15 +85,19 @@ def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32, rps=None):
     p = _p_rows(rng, max(M, 1), K)[:M]
     w = wl.normal_bf16((G * N, K), std=0.02, seed=seed + 1)
     qw, sw, gw = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=rps)
-    y, gs, q, sb = pqm.moe_fc2_online_nvfp4(dev_bf16(p), qw, sw, gw, dev(off), N,
-                                            w_rows_per_scale=rps, out_dtype=out_dtype,
-                                            encodings=True)
+    fn = pqm.moe_fc2_online_nvfp4_split if split else pqm.moe_fc2_online_nvfp4
+    res = fn(dev_bf16(p), qw, sw, gw, dev(off), N, w_rows_per_scale=rps, out_dtype=out_dtype,
+             encodings=True)
     torch.cuda.synchronize()
+    y, gs, q, sb = res[:4]
     got_y = host(y.float())
     got = dict(gs=host(gs), q=host(q), sb=host(sb))
     want_y = np.zeros((M, N))
     want = dict(gs=np.zeros(M, np.float32), q=np.zeros((M, K // 2), np.uint8),
                 sb=np.zeros((M, K // 16), np.uint8))
+    if split:
+        got["ratio"] = host(res[4])
+        want["ratio"] = np.ones((M, K // TILE), np.float32)
     for g in range(G):
         lo, hi = int(off[g]), int(off[g + 1])
         if hi == lo:
@@ -92,6 +110,8 @@ def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32, rps=None):
         want["gs"][lo:hi] = rec["gs"].max(axis=1)   # gs only grows; 0 for a zero row
         want["q"][lo:hi] = rec["q"]
         want["sb"][lo:hi] = rec["sb"]
+        if split:
+            want["ratio"][lo:hi] = _want_ratio(rec["gs"])
     return got_y, got, want_y, want
 
 
@@ -108,14 +128,18 @@ def _many_small(G, seed):
     ([200, 77], 512, 512, 256),                  # W2 scaled per half (gate / up style scopes)
     (_many_small(600, 35), 256, 256, None),      # > 512 experts: the tile lookup's general path
 ])
-def test_online_fc2_matches_oracle(sizes, N, K, rps):
-    got_y, got, want_y, want = _case(sizes, N, K, seed=31 + K, rps=rps)
+@pytest.mark.parametrize("split", [False, True], ids=["one-pass", "two-pass"])
+def test_online_fc2_matches_oracle(sizes, N, K, rps, split):
+    got_y, got, want_y, want = _case(sizes, N, K, seed=31 + K, rps=rps, split=split)
     assert_bytes_equal(got["gs"].view(np.uint32), want["gs"].view(np.uint32), "final gs")
     assert_bytes_equal(got["sb"], want["sb"], "block scales")
     assert_bytes_equal(got["q"], want["q"], "codes")
+    if split:
+        assert_bytes_equal(got["ratio"].view(np.uint32), want["ratio"].view(np.uint32),
+                           "per-tile gs_prev / gs")
     r = _rel_rows(got_y, want_y)
     what = sizes if len(sizes) <= 12 else f"{len(sizes)} experts, {sum(sizes)} rows"
-    print(f"[online] {what} N={N} K={K}: max row rel-L2 {r.max():.3e}", flush=True)
+    print(f"[online] {what} N={N} K={K} split={split}: max row rel-L2 {r.max():.3e}", flush=True)
     assert r.max() <= TOL, (float(r.max()), int(r.argmax()))
     zero = want["gs"] == 0
     assert zero.any() and not got_y[zero].any()
@@ -137,6 +161,27 @@ def test_online_fc2_bf16_out_and_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(g1, g2)
+
+
+@pytest.mark.parametrize("sizes,N,K", [([130, 0, 33, 256, 7, 1], 520, 512),
+                                         (_many_small(600, 36), 256, 768),
+                                         ([1000, 3], 384, 4096)])
+def test_online_fc2_two_pass_matches_one_pass(sizes, N, K):
+    """The two-pass entry point against the one-pass kernel on the same
+    inputs: output (binary32 and bf16), gs, codes and block scales bit for
+    bit (the same encoding, accumulation order and epilogue)."""
+    rng = np.random.Generator(np.random.PCG64(50 + K))
+    G, M = len(sizes), sum(sizes)
+    p = dev_bf16(_p_rows(rng, M, K))
+    w = wl.normal_bf16((G * N, K), std=0.02, seed=51)
+    qw, sw, gw = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=N)
+    off = dev(_offsets(sizes))
+    for od in (pqm.OUT_FP32, pqm.OUT_BF16):
+        a = pqm.moe_fc2_online_nvfp4(p, qw, sw, gw, off, N, out_dtype=od, encodings=True)
+        b = pqm.moe_fc2_online_nvfp4_split(p, qw, sw, gw, off, N, out_dtype=od, encodings=True)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("Y", "gs", "codes", "block scales"), a, b[:4]):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (name, od)
 
 
 def test_online_fc2_max_in_first_tile_is_two_pass_encoding():
@@ -179,7 +224,12 @@ def test_online_fc2_deepseek_down_full_sampled():
     w = (torch.randn((E + 1) * H, I, generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
     qw, sw, gw = pqm.quantize_nvfp4_per_token(w, rows_per_scale=H)
     y, gs, q, sb = pqm.moe_fc2_online_nvfp4(p, qw, sw, gw, dev(off), H, encodings=True)
+    y2, gs2, q2, sb2, _ = pqm.moe_fc2_online_nvfp4_split(p, qw, sw, gw, dev(off), H,
+                                                         encodings=True)
     torch.cuda.synchronize()
+    for name, a, b in (("Y", y, y2), ("gs", gs, gs2), ("codes", q, q2), ("block scales", sb, sb2)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"two-pass {name}"
+    del y2, gs2, q2, sb2
     rng = np.random.Generator(np.random.PCG64(46))
     experts = sorted(set(rng.choice(E, 4, replace=False).tolist()) | {0, E - 1, E})
     for e in experts:
