@@ -323,13 +323,13 @@ pqm_status pqm_moe_fc2_online_nvfp4(const uint16_t *p, const uint8_t *w_q,
                                     uint8_t *q_out, uint8_t *sb_out, hipStream_t stream);
 
 /*
- * The same online-amax FC2 ([MT] 5.6) in two passes.  A row's encoding
- * depends on its K-tiles only, not on the output column, so the first pass
- * encodes every routed row once.  The second pass is the NVFP4 grouped GEMM
+ * The same online-amax FC2 ([MT] 5.6) split into two kernels.  A row's encoding
+ * depends on its K-tiles only, not on the output column, so the first kernel
+ * encodes every routed row once.  The second is the NVFP4 grouped GEMM
  * on those codes, which moves its accumulator rows by the stored ratios
  * before each K-tile.  The codes, block scales and gs are those of
  * pqm_moe_fc2_online_nvfp4, and so is Y bit for bit: the same accumulation
- * order and the same epilogue.  The single-pass entry point encodes P again
+ * order and the same epilogue.  The one-kernel entry point encodes P again
  * in every 256-column tile.
  *   p, w_q, w_scale, w_outer, offsets, out, out_dtype: as
  *            pqm_moe_fc2_online_nvfp4;

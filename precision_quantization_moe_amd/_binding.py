@@ -233,8 +233,8 @@ def moe_fc2_online_nvfp4(p: torch.Tensor, w_q, w_scale, w_outer, offsets: torch.
 def moe_fc2_online_nvfp4_split(p: torch.Tensor, w_q, w_scale, w_outer, offsets: torch.Tensor,
                                N: int, w_rows_per_scale: int = 0, out_dtype: int = OUT_BF16,
                                encodings: bool = False):
-    """The same FC2 in two passes (encode once, then the GEMM with the
-    stored ratios); see pqm_moe_fc2_online_nvfp4_split in pqmoe.h.  The
+    """The same FC2 split into two kernels (encode once, then the GEMM with
+    the stored ratios); see pqm_moe_fc2_online_nvfp4_split in pqmoe.h.  The
     codes, block scales, gs and ratio buffers it needs are allocated here.
     Returns (y, gs) or, with encodings, (y, gs, q, sb, ratio)."""
     G = offsets.numel() - 1

@@ -4050,13 +4050,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nvfp4_online(
   if (gs_out && ti.n0 == 0 && tid < rows_a) gs_out[ti.row0 + tid] = gsf[tid];
 }
 
-// The same FC2 in two passes: the encoding of P does not depend on the
+// The same FC2 split into two kernels: the encoding of P does not depend on the
 // output column, so one pass encodes every routed row once (the running
 // maximum, gs, E4M3 block scales and E2M1 codes of each 128-wide K-tile, as
 // npo_encode computes them, and each tile's gs_prev / gs), and the GEMM then
 // reads the codes like any NVFP4 operand and moves its accumulator rows by
 // the stored ratios before each step.  The accumulation and the epilogue
-// (the final gs as the row's outer scale) are those of the one-pass kernel,
+// (the final gs as the row's outer scale) are those of the one-kernel path,
 // whose column tiles each encode P again.
 constexpr int NPO_MAX_NK = 32;  // K / 128 ratios of a tile row held in LDS
 
@@ -4103,7 +4103,7 @@ __global__ __launch_bounds__(256) void k_online_encode_nvfp4(
 }
 
 // GEMM pass: the pipelined NVFP4 kernel's 128 x 256 tiles (2 x 2 waves,
-// the one-pass kernel's shape) with the per-step rescale; A = the encode
+// the one-kernel path's shape) with the per-step rescale; A = the encode
 // pass's codes and block scales, its outer scale the final gs.  (256-row
 // tiles keep 256 accumulators per lane, which the rescale's multiplies
 // would have to move through VGPRs: 272 spilled registers.)
@@ -4520,7 +4520,7 @@ hipError_t launch_fc2_online_nvfp4(const uint16_t *p, const uint8_t *b, const ui
   return hipGetLastError();
 }
 
-// Online-amax FC2 in two passes (k_online_encode_nvfp4, then
+// Online-amax FC2 split into two kernels (k_online_encode_nvfp4, then
 // k_gemm_nvfp4_rescale): K a positive multiple of 256 and at most
 // 128 NPO_MAX_NK, 4-byte aligned W2 block scales.
 hipError_t launch_fc2_online_nvfp4_split(const uint16_t *p, const uint8_t *b,

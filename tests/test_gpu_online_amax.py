@@ -1,5 +1,5 @@
 """GPU parity of the online-amax NVFP4 down projection
-(pqm_moe_fc2_online_nvfp4 and its two-pass form
+(pqm_moe_fc2_online_nvfp4 and its split form
 pqm_moe_fc2_online_nvfp4_split, [MT] "miniTE technical report", 5.6) against
 the oracle's loop (oracle.online_amax_fc2, 128-wide K-tiles).
 
@@ -11,9 +11,9 @@ Bars:
     binary64 loop (the kernel accumulates in binary32 and moves the
     accumulator by a binary32 gs_prev / gs), plus one bf16 rounding (2^-8)
     for bf16 output;
-  * two-pass form: each tile's stored gs_prev / gs bit-exact against one
+  * split form: each tile's stored gs_prev / gs bit-exact against one
     binary32 division of the oracle's per-tile gs, and Y, gs, codes and
-    block scales bit for bit those of the one-pass kernel.
+    block scales bit for bit those of the one-kernel path.
 
 W2 is quantized with one outer scale per expert tensor (or per scope of
 w_rows_per_scale rows) by the library's per-token quantizer on the device and
@@ -76,7 +76,7 @@ def _want_ratio(gs_rec):
 def _case(sizes, N, K, seed, out_dtype=pqm.OUT_FP32, rps=None, split=False):
     """rps: W2 rows per outer scale (default N, one per expert); with rps < N
     the oracle's loop (one W2 scale) runs once per scale scope of W2 rows,
-    whose output columns it then fills.  split: the two-pass entry point
+    whose output columns it then fills.  split: the split entry point
     (encode once, then the GEMM with the stored ratios)."""
     rps = rps or N
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -128,7 +128,7 @@ def _many_small(G, seed):
     ([200, 77], 512, 512, 256),                  # W2 scaled per half (gate / up style scopes)
     (_many_small(600, 35), 256, 256, None),      # > 512 experts: the tile lookup's general path
 ])
-@pytest.mark.parametrize("split", [False, True], ids=["one-pass", "two-pass"])
+@pytest.mark.parametrize("split", [False, True], ids=["one-kernel", "split"])
 def test_online_fc2_matches_oracle(sizes, N, K, rps, split):
     got_y, got, want_y, want = _case(sizes, N, K, seed=31 + K, rps=rps, split=split)
     assert_bytes_equal(got["gs"].view(np.uint32), want["gs"].view(np.uint32), "final gs")
@@ -166,8 +166,8 @@ def test_online_fc2_bf16_out_and_deterministic():
 @pytest.mark.parametrize("sizes,N,K", [([130, 0, 33, 256, 7, 1], 520, 512),
                                          (_many_small(600, 36), 256, 768),
                                          ([1000, 3], 384, 4096)])
-def test_online_fc2_two_pass_matches_one_pass(sizes, N, K):
-    """The two-pass entry point against the one-pass kernel on the same
+def test_online_fc2_split_matches_one_kernel(sizes, N, K):
+    """The split entry point against the one-kernel path on the same
     inputs: output (binary32 and bf16), gs, codes and block scales bit for
     bit (the same encoding, accumulation order and epilogue)."""
     rng = np.random.Generator(np.random.PCG64(50 + K))
@@ -228,7 +228,7 @@ def test_online_fc2_deepseek_down_full_sampled():
                                                          encodings=True)
     torch.cuda.synchronize()
     for name, a, b in (("Y", y, y2), ("gs", gs, gs2), ("codes", q, q2), ("block scales", sb, sb2)):
-        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"two-pass {name}"
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"split {name}"
     del y2, gs2, q2, sb2
     rng = np.random.Generator(np.random.PCG64(46))
     experts = sorted(set(rng.choice(E, 4, replace=False).tolist()) | {0, E - 1, E})
