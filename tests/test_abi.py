@@ -188,6 +188,32 @@ def test_fc2_online_nvfp4_arguments():
     assert call(a6=0) == 0 and call(a7=0) == 0 and call(a8=0) == 0  # nothing to do
 
 
+def test_fc2_online_nvfp4_split_arguments():
+    """Argument errors of pqm_moe_fc2_online_nvfp4_split come back before any
+    launch (p, w_q, w_scale, w_outer, rps, offsets, G, M, N, K, out, dtype,
+    gs_out, q_out, sb_out, ratio_out, stream): every buffer is required, K is
+    at most 4096 (the ratios of a tile row held in LDS)."""
+    f = pqm.lib().pqm_moe_fc2_online_nvfp4_split
+    ok = [A16, A16, A16, A16, 64, A16, 2, 100, 64, 512, A16, 0, A16, A16, A16, A16, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a11=2) == 4                      # out dtype
+    assert call(a9=384) == 2                     # K % 256
+    assert call(a9=4096 + 256) == 2              # K above 4096
+    assert call(a9=0) == 2
+    assert call(a4=3) == 2                       # G * N % rps
+    for i in (0, 1, 2, 3, 5, 10, 12, 13, 14, 15):  # every buffer is required
+        assert call(**{f"a{i}": None}) == 1, i
+    assert call(a13=BAD) == 3                    # q_out 16-byte
+    assert call(a14=ctypes.c_void_p(0x10001)) == 3  # sb_out 4-byte
+    assert call(a15=ctypes.c_void_p(0x10002)) == 3  # ratio_out 4-byte
+    assert call(a6=0) == 0 and call(a7=0) == 0 and call(a8=0) == 0  # nothing to do
+
+
 def test_glue_validation():
     L = pqm.lib()
     assert L.pqm_moe_route(A16, 8, 0, 4, 0, A16, A16, A16, A16, A16, 1 << 20, None) == 2

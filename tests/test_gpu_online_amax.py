@@ -184,6 +184,46 @@ def test_online_fc2_split_matches_one_kernel(sizes, N, K):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (name, od)
 
 
+def _split_random_cases(n=8, seed=2025):
+    """n seeded (sizes, N, K, seed) cases: expert counts 1 to 300 with empty,
+    one-row and multi-tile experts, N below, at and across the 256-column
+    tile, K from 2 to 32 tiles."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        G = int(rng.choice([1, 3, 17, 300]))
+        sizes = rng.choice([0, 0, 1, 2, 31, 64, 129, 300], size=G).tolist()
+        if sum(sizes) == 0:
+            sizes[0] = 7
+        N = int(rng.choice([40, 136, 256, 520, 1024]))
+        K = int(rng.choice([256, 512, 1024, 2048, 4096]))
+        if G * N * K > 4e7 or sum(sizes) * K > 2e7:
+            continue
+        out.append((sizes, N, K, int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("case", _split_random_cases(),
+                         ids=lambda c: f"G{len(c[0])}-M{sum(c[0])}-{c[1]}x{c[2]}")
+def test_online_fc2_split_random_shapes(case):
+    """The split entry point equals the one-kernel path bit for bit on
+    seeded random shapes (both output types, gs, codes, block scales)."""
+    sizes, N, K, seed = case
+    G, M = len(sizes), sum(sizes)
+    print(f"[online] split random G={G} M={M} N={N} K={K}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    p = dev_bf16(_p_rows(rng, M, K))
+    w = wl.normal_bf16((G * N, K), std=0.02, seed=seed + 1)
+    qw, sw, gw = pqm.quantize_nvfp4_per_token(dev_bf16(w), rows_per_scale=N)
+    off = dev(_offsets(sizes))
+    for od in (pqm.OUT_FP32, pqm.OUT_BF16):
+        a = pqm.moe_fc2_online_nvfp4(p, qw, sw, gw, off, N, out_dtype=od, encodings=True)
+        b = pqm.moe_fc2_online_nvfp4_split(p, qw, sw, gw, off, N, out_dtype=od, encodings=True)
+        torch.cuda.synchronize()
+        for name, x, y in zip(("Y", "gs", "codes", "block scales"), a, b[:4]):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), (name, od)
+
+
 def test_online_fc2_max_in_first_tile_is_two_pass_encoding():
     """Rows whose maximum lies in their first tile are encoded exactly as the
     per-token quantizer encodes the whole row (the two-pass path)."""
