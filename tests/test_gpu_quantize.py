@@ -283,6 +283,60 @@ def test_dequantize_nvfp4_double_rounding_cases():
     assert_bytes_equal(host_u16(y), want, "double rounding")
 
 
+# ------------------------------------------------- seeded random shapes
+
+def _random_quant_cases(n=16, seed=77):
+    """n (kind, rows, cols, param, seed) cases cycling over MXFP8 (row-wise,
+    plus the column-wise copy when rows % 32 == 0; param: a leading-dimension
+    pad), per-token / per-group NVFP4 (param: rows per outer scale, a divisor
+    of rows) and block FP8 (param: 1 or 128 rows per block)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        kind = ("mxfp8", "nvfp4", "fp8b")[len(out) % 3]
+        if kind == "mxfp8":
+            rows = int(rng.choice([int(rng.integers(1, 700)), 32 * int(rng.integers(1, 20))]))
+            cols = 32 * int(rng.integers(1, 129))
+            param = int(rng.choice([0, 0, 32, 64]))
+        elif kind == "nvfp4":
+            rows = int(rng.integers(1, 600))
+            cols = 16 * int(rng.integers(1, 513))
+            divs = [d for d in range(1, rows + 1) if rows % d == 0]
+            param = int(rng.choice(divs))
+        else:
+            param = int(rng.choice([1, 128]))
+            rows = int(rng.integers(1, 700)) if param == 1 else 128 * int(rng.integers(1, 5))
+            cols = 128 * int(rng.integers(1, 33))
+        if rows * cols > 3e6:
+            continue
+        out.append((kind, rows, cols, param, int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_quant_cases(),
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-p{c[3]}")
+def test_quantizers_random_shapes(case):
+    """Every quantizer on seeded random shapes: bytes and scales equal the
+    oracle's (activations with a log-normal token scale and outlier channels;
+    one row of zeros and one of boundary values where the shape allows)."""
+    kind, rows, cols, param, seed = case
+    x = wl.activations(rows, cols, seed=seed)
+    if rows > 2:
+        x[rows // 2] = 0
+        x[-1] = wl.boundary_tensor(cols=cols)[0]
+    if kind == "mxfp8":
+        _check_mxfp8(x, "random", ld_pad=param)
+    elif kind == "nvfp4":
+        _check_nvfp4(x, "random", rps=param)
+    else:
+        q, sc = pqm.quantize_fp8_block(dev_bf16(x), param)
+        torch.cuda.synchronize()
+        print(f"[fp8b] random block_rows={param} {rows}x{cols}", flush=True)
+        rq, rs = oracle.quantize_fp8_block(x, param)
+        assert_bytes_equal(host(sc).view(np.uint32), rs.view(np.uint32), "scales")
+        assert_bytes_equal(host(q), rq, "E4M3 bytes")
+
+
 # ------------------------------------------------------ block-scaled FP8
 
 @pytest.mark.parametrize("block_rows,shape", [(1, (64, 384)), (1, (300, 2048)), (128, (256, 384)),
