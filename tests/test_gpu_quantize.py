@@ -337,6 +337,34 @@ def test_quantizers_random_shapes(case):
         assert_bytes_equal(host(q), rq, "E4M3 bytes")
 
 
+@pytest.mark.parametrize("case", [c for c in _random_quant_cases(n=24, seed=78) if c[0] != "fp8b"],
+                         ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}-p{c[3]}")
+def test_dequantize_random_shapes(case):
+    """Dequantize on seeded random shapes: the bf16 reconstruction of the
+    oracle's own codes and scales (MXFP8 row-wise and, when rows % 32 == 0,
+    the column-wise copy; NVFP4 per token or per group) equals the oracle's
+    bytes."""
+    kind, rows, cols, param, seed = case
+    x = wl.activations(rows, cols, seed=seed)
+    print(f"[dequant] random {kind} {rows}x{cols} p={param}", flush=True)
+    if kind == "mxfp8":
+        rq, rs = oracle.quantize_mxfp8_rowwise(x)
+        y = pqm.dequantize(pqm.FMT_MXFP8, dev(rq), dev(rs))
+        torch.cuda.synchronize()
+        assert_bytes_equal(host_u16(y), oracle.dequantize_mxfp8(rq, rs), "deq row")
+        if rows % 32 == 0:
+            cq, cs = oracle.quantize_mxfp8_colwise(x)
+            yT = pqm.dequantize(pqm.FMT_MXFP8, dev(cq), dev(cs))
+            torch.cuda.synchronize()
+            assert_bytes_equal(host_u16(yT), oracle.dequantize_mxfp8(cq, cs), "deq col")
+    else:
+        rq, rsb, rsg = oracle.quantize_nvfp4(x, rows_per_group=param)
+        y = pqm.dequantize(pqm.FMT_NVFP4, dev(rq), dev(rsb), dev(rsg), rows_per_scale=param)
+        torch.cuda.synchronize()
+        assert_bytes_equal(host_u16(y), oracle.dequantize_nvfp4(rq, rsb, rsg, param),
+                           f"deq nvfp4 rps={param}")
+
+
 # ------------------------------------------------------ block-scaled FP8
 
 @pytest.mark.parametrize("block_rows,shape", [(1, (64, 384)), (1, (300, 2048)), (128, (256, 384)),
