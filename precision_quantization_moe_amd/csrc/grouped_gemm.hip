@@ -4076,9 +4076,18 @@ __global__ __launch_bounds__(256) void k_online_encode_nvfp4(
   const int nk = (int)(K / 128);
   uint32_t gam = 0;
   Nvfp4Row rc = nvfp4_row(0.0f);  // s_g = 0 while the maximum is zero
+  // tiles t + 1 and t + 2 are loaded while tile t is encoded (nk >= 2; a
+  // load past the last tile re-reads the last one and is not used)
+  uint4 a0 = *reinterpret_cast<const uint4 *>(pr), a1 = *reinterpret_cast<const uint4 *>(pr + 8);
+  uint4 b0 = *reinterpret_cast<const uint4 *>(pr + 128),
+        b1 = *reinterpret_cast<const uint4 *>(pr + 128 + 8);
   for (int t = 0; t < nk; ++t) {
-    const uint4 v0 = *reinterpret_cast<const uint4 *>(pr + 128 * t);
-    const uint4 v1 = *reinterpret_cast<const uint4 *>(pr + 128 * t + 8);
+    const uint4 v0 = a0, v1 = a1;
+    a0 = b0;
+    a1 = b1;
+    const int tn = min(t + 2, nk - 1);
+    b0 = *reinterpret_cast<const uint4 *>(pr + 128 * tn);
+    b1 = *reinterpret_cast<const uint4 *>(pr + 128 * tn + 8);
     const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t mm = 0;
 #pragma unroll
